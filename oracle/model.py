@@ -1,0 +1,151 @@
+"""fp64 forward pass of a diffusion-augmented decoder (oracle, test infrastructure).
+
+Follows the pages' description of the architecture: every layer keeps its
+autoregressive weights and adds rank-r LoRA "diffusion weights" with scale
+alpha/r; drafting runs the AR + LoRA weights and verification runs the AR
+weights alone, over one shared KV cache (picx.dev summary, "Methodology /
+Architecture: Diffusion-Augmented LLMs" and "Practical Implications";
+paperglide reader, "The Uno Framework").  The first position of a drafted block
+is computed with the AR weights only, the remaining positions with AR + LoRA
+(paperglide reader, "The Psi-Speculative Sampler", "Sampler Extensions"): a
+per-row gate g in {0, 1} multiplies the LoRA term.  The LoRA term sits on the
+seven linears q, k, v, o, gate, up, down ("small trainable modules ... every
+weight matrix", paperglide reader, "Empirical Results").
+
+The decoder body itself (pre-norm, RMSNorm, rotate-half RoPE, grouped-query
+attention, SwiGLU MLP, untied LM head, no biases) is the standard one the model
+configurations name; the pages call the base model a standard LLM and print no
+layer equations.  Readings: RMSNorm epsilon is a config value; attention
+scale 1/sqrt(head_dim); RoPE frequencies theta^(-2i/head_dim); q head h reads
+kv head floor(h / (n_q_heads / n_kv_heads)).
+
+Everything here is fp64 numpy on logical (unpacked) weight layouts:
+  embed [V, D], lm_head [V, D], final_norm [D];
+  per layer: attn_norm [D], mlp_norm [D], q [Hq*hd, D], k [Hkv*hd, D],
+  v [Hkv*hd, D], o [D, Hq*hd], gate [F, D], up [F, D], down [D, F];
+  LoRA: lora_a[p] [r, in_p], lora_b[p] [out_p, r] for p in PROJ.
+
+Parity: logit VALUES are "parity unpinned" against the pages (none are printed).
+Structural pins in tests/test_oracle_model.py: LoRA linear == dense
+x (W + s B A)^T; B = 0 makes the LoRA linear the plain linear; the cached block
+forward equals a full uncached causal recompute; attention, RMSNorm and SiLU
+agree with independent torch CPU routines.
+"""
+import numpy as np
+
+PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def rms_norm(h, gain, eps):
+    """h / sqrt(mean(h^2) + eps) * gain, row-wise."""
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps) * gain
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def rope(x, pos, theta):
+    """Rotate-half rotary embedding. x [R, H, hd], pos [R] (absolute positions)."""
+    hd = x.shape[-1]
+    half = hd // 2
+    inv_freq = float(theta) ** (-np.arange(half, dtype=np.float64) * 2.0 / hd)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def lora_linear(x, w, a, b, scale, gate):
+    """y = x W^T + gate_row * scale * (x A^T) B^T; a/b None means no LoRA."""
+    y = x @ w.T
+    if a is not None and b is not None:
+        y = y + (gate[:, None] * scale) * ((x @ a.T) @ b.T)
+    return y
+
+
+class KVCache:
+    """One sequence's cache: per layer K and V [capacity, Hkv, hd], fp64."""
+
+    def __init__(self, cfg, capacity):
+        shape = (capacity, cfg["n_kv_heads"], cfg["head_dim"])
+        self.k = [np.zeros(shape) for _ in range(cfg["n_layers"])]
+        self.v = [np.zeros(shape) for _ in range(cfg["n_layers"])]
+        self.capacity = capacity
+
+    def copy(self):
+        c = KVCache.__new__(KVCache)
+        c.k = [a.copy() for a in self.k]
+        c.v = [a.copy() for a in self.v]
+        c.capacity = self.capacity
+        return c
+
+
+def attention(q, cache_k, cache_v, key_limit, n_kv_heads):
+    """Per row r and q head h: softmax over keys 0..key_limit[r] of the cache.
+
+    q [R, Hq, hd]; cache_k/v [cap, Hkv, hd]; returns [R, Hq, hd].
+    """
+    R, Hq, hd = q.shape
+    group = Hq // n_kv_heads
+    out = np.zeros_like(q)
+    scale = 1.0 / np.sqrt(hd)
+    for r in range(R):
+        lim = int(key_limit[r]) + 1
+        for h in range(Hq):
+            g = h // group
+            s = cache_k[:lim, g, :] @ q[r, h] * scale
+            s = s - s.max()
+            p = np.exp(s)
+            p = p / p.sum()
+            out[r, h] = p @ cache_v[:lim, g, :]
+    return out
+
+
+def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True):
+    """One pass over a block of rows of ONE sequence.
+
+    Writes the block's K/V (after RoPE) into ``cache`` at ``pos`` before the
+    attention of each layer, then attends row r to cache keys 0..key_limit[r].
+    Returns fp64 logits [R, V].
+    """
+    ids = np.asarray(ids)
+    pos = np.asarray(pos)
+    gate = np.asarray(gate, dtype=np.float64)
+    Hq, Hkv, hd = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    eps = cfg["rms_eps"]
+    scale = cfg["lora_alpha"] / cfg["lora_rank"]
+    R = len(ids)
+    h = wts["embed"][ids].astype(np.float64)
+    for li, lw in enumerate(wts["layers"]):
+        def lin(x, p):
+            a = lw["lora_a"].get(p) if lora else None
+            b = lw["lora_b"].get(p) if lora else None
+            return lora_linear(x, lw[p], a, b, scale, gate)
+
+        x = rms_norm(h, lw["attn_norm"], eps)
+        q = lin(x, "q").reshape(R, Hq, hd)
+        k = lin(x, "k").reshape(R, Hkv, hd)
+        v = lin(x, "v").reshape(R, Hkv, hd)
+        q = rope(q, pos, cfg["rope_theta"])
+        k = rope(k, pos, cfg["rope_theta"])
+        cache.k[li][pos] = k
+        cache.v[li][pos] = v
+        o = attention(q, cache.k[li], cache.v[li], key_limit, Hkv).reshape(R, Hq * hd)
+        h = h + lin(o, "o")
+        x = rms_norm(h, lw["mlp_norm"], eps)
+        h = h + lin(silu(lin(x, "gate")) * lin(x, "up"), "down")
+    x = rms_norm(h, wts["final_norm"], eps)
+    return x @ wts["lm_head"].T
+
+
+def full_causal_logits(cfg, wts, tokens):
+    """Textbook AR forward over a whole token sequence, no cache reuse, AR weights.
+
+    Row i is the next-token logit vector after tokens[0..i].
+    """
+    n = len(tokens)
+    cache = KVCache(cfg, n)
+    pos = np.arange(n)
+    return forward(cfg, wts, cache, tokens, pos, np.zeros(n), pos, lora=False)

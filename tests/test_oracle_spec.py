@@ -1,0 +1,314 @@
+"""Losslessness and structure pins of the oracle's decode step.
+
+Exact enumeration (vocab 8, K = 1, 2, 3): the real ``oracle.spec.step`` is
+replayed along every path of random decisions; each decision's probability is
+counted exactly over the 2^24 values of its uniform (by bisection on the
+oracle's own monotone sampler primitives).  The committed tokens, continued by
+exact AR sampling, must reproduce the AR model's distribution (computed by a
+plain uncached forward) within 1e-6.  A two-step enumeration (K = 1) checks the
+cache/commit hand-over between steps.
+
+Prefix-independent rows (vocab 512, K = 8): acceptance at each position equals
+sum_v min(p, q) = 1 - TV(p, q) exactly up to the 2^-24 grid, and a 10^6-sample
+chi-square of a vectorised replay of the oracle's sampler (cross-checked draw by
+draw against ``oracle.spec.spec_accept``) against the first-token-at-position-j
+law p_j.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.stats
+
+import synth
+from oracle import canonical as cn
+from oracle import model as om
+from oracle import spec
+from oracle.philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, uniform24_np
+
+TWO24 = 1 << 24
+
+
+def _lowest_u(pred):
+    lo, hi = 0, TWO24
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if pred(mid):
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+class _Branch(Exception):
+    def __init__(self, dist):
+        self.dist = dist
+
+
+class _EnumDraws:
+    """Replays a fixed list of decisions; at the first new one, raises its exact
+    distribution (decision -> probability over U)."""
+
+    def __init__(self, path):
+        self.path = path
+        self.i = 0
+
+    def _take(self, dist_fn):
+        if self.i < len(self.path):
+            d = self.path[self.i]
+            self.i += 1
+            return d
+        raise _Branch(dist_fn())
+
+    def categorical(self, slot, j, weights):
+        def dist():
+            w = list(weights)
+            starts = [_lowest_u(lambda u, v=v: cn.categorical(w, u) >= v) for v in range(len(w))]
+            starts.append(TWO24)
+            return {v: Fraction(starts[v + 1] - starts[v], TWO24)
+                    for v in range(len(w)) if starts[v + 1] > starts[v]}
+        return self._take(dist)
+
+    def accept(self, slot, j, wq_d, sq, wp_d, sp):
+        def dist():
+            thr = _lowest_u(lambda u: not cn.accept(wq_d, sq, wp_d, sp, u))
+            out = {}
+            if thr > 0:
+                out[True] = Fraction(thr, TWO24)
+            if thr < TWO24:
+                out[False] = Fraction(TWO24 - thr, TWO24)
+            return out
+        return self._take(dist)
+
+
+def _enumerate_step(cfg, w, seq, K, inv_t):
+    """{committed tuple: probability} of one step from ``seq`` (exact)."""
+    out = {}
+    stack = [([], Fraction(1))]
+    while stack:
+        path, prob = stack.pop()
+        s = seq.copy()
+        try:
+            r = spec.step(cfg, w, s, K, inv_t, _EnumDraws(path))
+        except _Branch as br:
+            for dec, p in br.dist.items():
+                stack.append((path + [dec], prob * p))
+            continue
+        key = tuple(r["committed"])
+        out[key] = out.get(key, Fraction(0)) + prob
+    return out
+
+
+def _ar_probs(cfg, w, prefix, inv_t):
+    z = om.full_causal_logits(cfg, w, list(prefix))[-1] * inv_t
+    p = np.exp(z - z.max())
+    return p / p.sum()
+
+
+@pytest.fixture(scope="module")
+def toy():
+    cfg = synth.VOCAB8
+    wts = synth.make_weights(cfg, 3)
+    # larger LoRA B so that q differs visibly from p (more rejections)
+    for lw in wts["layers"]:
+        for p in lw["lora_b"]:
+            lw["lora_b"][p] = lw["lora_b"][p] * 40
+    return cfg, synth.to_f64(wts)
+
+
+def _check_one_step(cfg, w, prompt, K, inv_t):
+    seq = spec.Sequence(cfg, prompt, capacity=len(prompt) + 2 * K + 4)
+    spec.prefill(cfg, w, seq)
+    dist = _enumerate_step(cfg, w, seq, K, inv_t)
+    assert abs(sum(dist.values()) - 1) == 0
+    for c in dist:
+        assert 2 <= len(c) <= K + 1          # tokens per step within [2, K+1]
+    # continue each outcome with exact AR sampling up to K+1 tokens
+    m = K + 1
+    ar_cache = {}
+
+    def ar(prefix):
+        if prefix not in ar_cache:
+            ar_cache[prefix] = _ar_probs(cfg, w, prefix, inv_t)
+        return ar_cache[prefix]
+
+    got = {}
+    for c, pc in dist.items():
+        frontier = [(tuple(c), float(pc))]
+        while frontier:
+            s, ps = frontier.pop()
+            if len(s) >= m:
+                got[s[:m]] = got.get(s[:m], 0.0) + ps
+                continue
+            probs = ar(tuple(prompt) + s)
+            for v in range(cfg["vocab"]):
+                frontier.append((s + (v,), ps * probs[v]))
+    worst = 0.0
+    for s, pg in got.items():
+        pref = tuple(prompt)
+        pe = 1.0
+        for t in s:
+            pe *= ar(pref)[t]
+            pref = pref + (t,)
+        worst = max(worst, abs(pg - pe))
+    assert worst < 1e-6, worst
+    return dist
+
+
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_exact_enumeration_one_step_lossless(toy, K):
+    cfg, w = toy
+    prompt = [1, 5, 2, 6, 0]
+    dist = _check_one_step(cfg, w, prompt, K, 1.0)
+    if K >= 2:
+        # some rejections happen, so the check covers the residual branch
+        assert any(len(c) < K + 1 for c in dist)
+
+
+def test_exact_enumeration_temperature(toy):
+    cfg, w = toy
+    _check_one_step(cfg, w, [4, 4, 1], 2, np.float32(1.0 / 0.7))
+
+
+def test_exact_enumeration_two_steps_k1(toy):
+    cfg, w = toy
+    prompt = [2, 3, 0]
+    seq = spec.Sequence(cfg, prompt, capacity=16)
+    spec.prefill(cfg, w, seq)
+    first = _enumerate_step(cfg, w, seq, 1, 1.0)
+    got = {}
+    for c1, p1 in first.items():
+        # replay the first step along path c1 so that its cache writes and
+        # commit are exactly the ones the step makes
+        s2 = seq.copy()
+        r = spec.step(cfg, w, s2, 1, 1.0, _FixedDraws(c1))
+        assert tuple(r["committed"]) == c1
+        for c2, p2 in _enumerate_step(cfg, w, s2, 1, 1.0).items():
+            key = c1 + c2
+            got[key] = got.get(key, 0) + float(p1 * p2)
+    worst = 0.0
+    for s, pg in got.items():
+        pref, pe = tuple(prompt), 1.0
+        for t in s:
+            pe *= _ar_probs(cfg, w, pref, 1.0)[t]
+            pref += (t,)
+        worst = max(worst, abs(pg - pe))
+    assert abs(sum(got.values()) - 1) < 1e-12 and worst < 1e-6
+
+
+class _FixedDraws:
+    """Forces the decisions that produce a given committed tuple (K = 1)."""
+
+    def __init__(self, committed):
+        self.c = committed
+
+    def categorical(self, slot, j, weights):
+        return self.c[0] if slot == SLOT_DRAFT else self.c[1]
+
+    def accept(self, *a):
+        raise AssertionError("K = 1 has no accept test")
+
+
+# ---------------- prefix-independent rows: closed forms and chi-square ----------------
+
+def _indep_rows(V=512, K=8, seed=0, sigma=1.0, noise=0.6):
+    zq, zp = synth.sampler_logits(1, K, V, seed, sigma_p=sigma, sigma_noise=noise)
+    return zq[0], zp[0]
+
+
+def test_acceptance_rate_is_one_minus_tv():
+    zq, zp = _indep_rows()
+    K = zq.shape[0]
+    for i in range(2, K + 1):
+        wq, sq = cn.row_weights(zq[i - 1], 1.0)
+        wp, sp = cn.row_weights(zp[i - 2], 1.0)
+        # actual draft law (exact counts over U) times exact accept probability
+        cum = np.cumsum(wq)
+        starts = [0] + [((int(c) << 24) + sq - 1) // sq for c in cum]   # ceil(C * 2^24 / S)
+        acc = Fraction(0)
+        for d in range(len(wq)):
+            cnt = min(starts[d + 1], TWO24) - min(starts[d], TWO24)
+            if cnt == 0:
+                continue
+            thr = _lowest_u(lambda u: not cn.accept(int(wq[d]), sq, int(wp[d]), sp, u))
+            acc += Fraction(cnt, TWO24) * Fraction(thr, TWO24)
+        beta = sum(min(Fraction(int(a), sp), Fraction(int(b), sq)) for a, b in zip(wp, wq))
+        assert abs(float(acc - beta)) < 600 * 2.0 ** -24     # V entries, each off by < 2^-24
+
+
+def _vectorised_replay(zq, zp, n, seed, inv_t=1.0):
+    """The oracle's sampler on prefix-independent rows, vectorised over n
+    sequences b = 0..n-1 at step 0.  Returns (drafts [n,K], a [n], extra [n])."""
+    K, V = zq.shape
+    q = [cn.row_weights(zq[j], inv_t) for j in range(K)]
+    p = {1: q[0]}
+    for i in range(2, K + 2):
+        p[i] = cn.row_weights(zp[i - 2], inv_t)
+    b = np.arange(n, dtype=np.uint64)
+    drafts = np.zeros((n, K), dtype=np.int64)
+    for j in range(K):
+        w, s = q[j]
+        u = uniform24_np(seed, SLOT_DRAFT, j, b, 0).astype(object)
+        t = np.array([(int(x) * s) >> 24 for x in u], dtype=np.uint64)
+        drafts[:, j] = np.searchsorted(np.cumsum(w), t, side="right")
+    a = np.full(n, K)
+    alive = np.ones(n, dtype=bool)
+    for i in range(2, K + 1):
+        wq, sq = q[i - 1]
+        wp, sp = p[i]
+        d = drafts[:, i - 1]
+        u = uniform24_np(seed, SLOT_ACCEPT, i - 1, b, 0)
+        lhs = u.astype(object) * wq[d].astype(object) * sp
+        rhs = wp[d].astype(object) * sq * TWO24
+        rej = alive & ~(lhs < rhs).astype(bool)
+        a[rej] = i - 1
+        alive &= ~rej
+    extra = np.zeros(n, dtype=np.int64)
+    for av in range(1, K + 1):
+        sel = np.nonzero(a == av)[0]
+        if sel.size == 0:
+            continue
+        if av < K:
+            wp, sp = p[av + 1]
+            wq, sq = q[av]
+            r = cn.residual_weights(wp, sp, wq, sq)
+            if sum(r) == 0:
+                r = [int(x) for x in wp]
+        else:
+            r = [int(x) for x in p[K + 1][0]]
+        cum = np.cumsum(np.array(r, dtype=object))
+        tot = int(cum[-1])
+        u = uniform24_np(seed, SLOT_EXTRA, av, b[sel], 0)
+        for k, uu in zip(sel, u):
+            t = (int(uu) * tot) >> 24
+            extra[k] = int(np.searchsorted(cum, t, side="right"))
+    return drafts, a, extra
+
+
+def test_vectorised_replay_matches_oracle_step_logic():
+    zq, zp = _indep_rows(V=256, K=6, seed=4)
+    drafts, a, extra = _vectorised_replay(zq, zp, 1500, seed=9)
+    for bb in range(1500):
+        dr = spec.draft_sample(zq, 1.0, spec.PhiloxDraws(9, bb, 0))
+        assert dr == list(drafts[bb])
+        aa, comm, ex = spec.spec_accept(zq, zp, dr, 1.0, spec.PhiloxDraws(9, bb, 0))
+        assert (aa, ex) == (a[bb], extra[bb])
+
+
+def test_chi_square_first_token_law_1e6_samples():
+    """Position j's committed token, given that the step reaches position j
+    without an earlier rejection, follows p_j: the token there is either the
+    kept draft or the residual/bonus draw."""
+    zq, zp = _indep_rows(V=512, K=8, seed=1)
+    n = 1_000_000
+    drafts, a, extra = _vectorised_replay(zq, zp, n, seed=0)
+    K, V = zq.shape
+    for j in (2, 5, 8):
+        reached = a >= j - 1                 # positions 1..j-1 kept
+        tok = np.where(a[reached] >= j, drafts[reached, j - 1], extra[reached])
+        wp, sp = cn.row_weights(zp[j - 2], 1.0)
+        exp = wp.astype(np.float64) / sp * tok.size
+        obs = np.bincount(tok, minlength=V).astype(np.float64)
+        keep = exp > 5
+        stat, pval = scipy.stats.chisquare(obs[keep], exp[keep] * obs[keep].sum() / exp[keep].sum())
+        assert pval > 0.01, (j, pval)
