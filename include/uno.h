@@ -1,0 +1,202 @@
+/*
+ * uno.h -- C ABI of the Psi-Spec draft-and-verify decode step on one gfx950 GPU.
+ *
+ * The method ("Unlocking Lossless Speedups in LLMs via Discrete Diffusion"):
+ * a decoder whose every linear carries rank-r LoRA "diffusion weights" drafts a
+ * block of tokens in one forward pass with AR + LoRA weights, verifies the
+ * block in one forward pass with the AR weights alone over the same KV cache,
+ * and keeps the drafted prefix that speculative rejection sampling accepts, plus
+ * one residual or bonus token (picx.dev summary, "Methodology" and
+ * "Psi-Speculative Sampler"; paperglide reader, "The Uno Framework",
+ * "The Psi-Speculative Sampler", "Sampler Extensions").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked [dev] are device (HBM) pointers; [host] are host pointers.
+ *   The caller owns every buffer (weights, KV pages, page table, lengths,
+ *   logits, tokens, workspace).  The library allocates and frees nothing and
+ *   keeps no mutable global state, so calls are re-entrant.
+ * - Every call validates its host-visible arguments, then enqueues kernels on
+ *   `stream` (a hipStream_t; NULL = the default stream) and returns without a
+ *   host synchronisation.  No call issues hipMemset/hipMemcpy or allocates, so a
+ *   whole step can be captured into a HIP graph.  Outputs are valid once the
+ *   stream has reached them.
+ * - Return value: UNO_OK, or an error code; on error nothing was enqueued.
+ *   Conditions only the device can see (a kv_len that would overflow the page
+ *   table, a token id outside the vocabulary, a page id outside the pool, a
+ *   non-finite logit in a sampled row) are reported per sequence through the
+ *   optional `status` array [dev, int32, batch]: the kernels OR bit flags
+ *   UNO_DEV_* into it and skip the offending write or draw; the caller clears it.
+ * - Shapes: R = batch * K rows per pass; V = vocab.  All matrices are row-major.
+ * - Tokens are int32.  Random draws use Philox4x64-10 with key (seed, 0) and
+ *   counter (slot, j, b, step[b]); the uniform is the top 24 bits of word 0.
+ *   Slots: 0 draft token j+1; 1 accept test of draft j+1; 2 extra token (j = a).
+ */
+#ifndef UNO_H
+#define UNO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  UNO_OK = 0,
+  UNO_ERR_INVALID_ARG = 1,  /* null pointer, size out of range, bad stride      */
+  UNO_ERR_UNSUPPORTED = 2,  /* shape the kernels do not implement              */
+  UNO_ERR_CAPACITY = 3,     /* (host-checkable) page table too small for K     */
+  UNO_ERR_WORKSPACE = 4,    /* workspace smaller than uno_*_workspace_bytes()  */
+  UNO_ERR_HIP = 5           /* a kernel launch failed (see uno_last_hip_error) */
+};
+
+/* Device-side status bits (OR-ed into status[b]). */
+enum {
+  UNO_DEV_CAPACITY = 1,     /* a K/V slot fell outside the sequence's pages     */
+  UNO_DEV_BAD_TOKEN = 2,    /* a token id outside [0, vocab)                    */
+  UNO_DEV_BAD_PAGE = 4,     /* a page id outside [0, n_pages)                   */
+  UNO_DEV_NONFINITE = 8,    /* a sampled logit row held NaN or Inf              */
+  UNO_DEV_BAD_ACCEPT = 16   /* a forced / given accept length outside [0, K]    */
+};
+
+/* Model shape.  Supported: head_dim 64 or 128; n_q_heads a multiple of
+ * n_kv_heads; d_model, d_ffn, n_q_heads*head_dim multiples of 64; page_size a
+ * multiple of 16; lora_rank a multiple of 16 and <= 256; vocab a multiple of
+ * 16 and <= 2^20. */
+typedef struct uno_config {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, mask_id;
+  float rms_eps;      /* RMSNorm epsilon                                      */
+  float rope_theta;   /* rotate-half RoPE base                                */
+  int32_t lora_rank;  /* r                                                    */
+  float lora_scale;   /* alpha / r                                            */
+  uint32_t lora_mask; /* bit p set: LoRA on projection p; p = 0 q, 1 k, 2 v,
+                         3 o, 4 gate, 5 up, 6 down.  q,k,v must agree, and
+                         gate,up must agree.                                  */
+  int32_t page_size;  /* tokens per KV page (16)                              */
+} uno_config;
+
+/* One layer's weights [dev].  Base weights are bf16 [out, in] (row-major,
+ * `in` contiguous); LoRA factors are bf16 A [r, in] and B [out, r]; norm gains
+ * are fp32 [d_model].  LoRA pointers of projections whose bit is clear in
+ * lora_mask are ignored. */
+typedef struct uno_layer_weights {
+  const void *attn_norm, *mlp_norm;                    /* fp32 [D]             */
+  const void *wq, *wk, *wv, *wo, *wgate, *wup, *wdown; /* bf16                  */
+  const void *lora_a[7];                               /* bf16 [r, in_p]        */
+  const void *lora_b[7];                               /* bf16 [out_p, r]       */
+} uno_layer_weights;
+
+typedef struct uno_weights {
+  const void *embed;       /* bf16 [V, D] [dev]                                 */
+  const void *lm_head;     /* bf16 [V, D] [dev] (untied, no LoRA)               */
+  const void *final_norm;  /* fp32 [D]    [dev]                                 */
+  const uno_layer_weights *layers; /* [host] array of n_layers                  */
+} uno_weights;
+
+/* Paged KV cache shared by the draft and the verify pass.
+ * k_pages: bf16 [n_layers][n_pages][n_kv_heads][page_size][head_dim]
+ * v_pages: bf16 [n_layers][n_pages][n_kv_heads][head_dim][page_size]
+ *          (V is stored transposed inside a page: the keys of one page are
+ *           contiguous for each channel)
+ * Token position t of sequence b lives in page page_table[b*max_pages + t/ps]
+ * at slot t % ps.  kv_len[b] counts the committed positions; positions
+ * kv_len[b].. are scratch that the next pass overwrites. */
+typedef struct uno_kv {
+  void *k_pages, *v_pages;       /* [dev]                                     */
+  int64_t n_pages;               /* pages per layer in the pool               */
+  const int32_t *page_table;     /* [dev] int32 [batch, max_pages_per_seq]    */
+  int32_t max_pages_per_seq;
+  int32_t *kv_len;               /* [dev] int32 [batch]                       */
+} uno_kv;
+
+/* Bytes of workspace the two forward passes need for `batch` sequences of up
+ * to `K` rows and up to `max_ctx` cached positions (the split of the attention
+ * over the context is sized from it). */
+size_t uno_workspace_bytes(const uno_config *cfg, int batch, int K, int max_ctx);
+
+/* Draft block (paperglide reader, "The Psi-Speculative Sampler" and "Sampler
+ * Extensions"; picx.dev summary, "Architecture").
+ * Rows of sequence b: [anchor[b], mask_id x (K-1)] at positions kv_len[b] ..
+ * kv_len[b]+K-1.  Row 0 runs with the AR weights and attends causally (keys
+ * <= kv_len[b]); rows 1..K-1 add the LoRA term (scale lora_scale) and attend to
+ * every key up to kv_len[b]+K-1.  The pass writes the rows' K/V into the cache
+ * at those positions (the anchor's entry is final; the mask rows' are scratch)
+ * and leaves kv_len unchanged.
+ *   anchor        [dev] int32 [batch]
+ *   draft_logits  [dev] fp32 [batch, K, V]   q_1..q_K (untempered logits)
+ *   draft_tokens  [dev] int32 [batch, K]     d_j+1 ~ q_j+1 at temperature 1/inv_temp
+ *   step          [dev] uint64 [batch]       Philox step counter per sequence
+ *   status        [dev] int32 [batch] or NULL
+ *   ws/ws_bytes   [dev] workspace of uno_workspace_bytes(cfg, batch, K, max_ctx)
+ * 1 <= K <= 64, batch >= 1, inv_temp > 0 and finite. */
+int uno_draft_block(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
+                    const int32_t *anchor, int batch, int K, int max_ctx,
+                    float inv_temp, uint64_t seed, const uint64_t *step,
+                    float *draft_logits, int32_t *draft_tokens, int32_t *status,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Verify block (picx.dev summary, "Architecture": verification uses the AR
+ * weights only).  Rows of sequence b: rows[b, 0..K-1] at positions
+ * kv_len[b] + pos_offset + j, causal (row j sees keys <= its own position),
+ * no LoRA.  Writes the rows' K/V into the cache (pending until a commit).
+ * pos_offset = 1 after a draft block (the anchor sits at kv_len[b]);
+ * pos_offset = 0 for a prompt chunk (prefill, followed by a commit with
+ * accept_len = K-1).  verify_logits [dev] fp32 [batch, K, V] may be NULL to
+ * skip the LM head.  1 <= K <= 4096. */
+int uno_verify_block(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
+                     const int32_t *rows, int batch, int K, int max_ctx, int pos_offset,
+                     float *verify_logits, int32_t *status,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Draft sampling alone (the categorical draw that uno_draft_block ends with):
+ * tokens[b, j] = integer-weight categorical draw from logits[b, j, :] at
+ * temperature 1/inv_temp with the slot-0 uniform of (j, b, step[b]).
+ * logits [dev] fp32 [batch, K, V]; tokens [dev] int32 [batch, K]. */
+int uno_draft_sample(const float *logits, int batch, int K, int vocab, float inv_temp,
+                     uint64_t seed, const uint64_t *step, int32_t *tokens,
+                     int32_t *status, void *stream);
+
+/* Workspace for uno_spec_accept: per-row statistics of both logit sets. */
+size_t uno_spec_accept_workspace_bytes(int batch, int K);
+
+/* Lossless accept / resample (picx.dev summary, "Psi-Speculative Sampler";
+ * paperglide reader, "The Psi-Speculative Sampler", "Sampler Extensions").
+ * Draft row j of sequence b is q_{j+1}; verify row j is p_{j+2}; p_1 = q_1, so
+ * d_1 is always kept.  For i = 2..K: keep d_i iff
+ *   U * Wq_i[d_i] * Sp_i < Wp_i[d_i] * Sq_i * 2^24
+ * (integer weights W = floor(exp_c((z - max z) * inv_temp) * 2^31), zero below
+ * -22, S their exact sum), stopping at the first rejection; a = kept drafts.
+ * If forced_accept != NULL, a = forced_accept[b] in [0, K] replaces it.
+ * a < K: extra token ~ R_v = max(0, Wp_{a+1,v} Sq_{a+1} - Wq_{a+1,v} Sp_{a+1})
+ * (p_{a+1} itself if R is all zero); a = K: bonus token ~ p_{K+1}.
+ *   draft_logits, verify_logits [dev] fp32 [batch, K, V]
+ *   draft_tokens [dev] int32 [batch, K]
+ *   forced_accept [dev] int32 [batch] or NULL
+ *   accept_len   [dev] int32 [batch]           a
+ *   committed    [dev] int32 [batch, K+1]      d_1..d_a, extra, then -1
+ *   extra_token  [dev] int32 [batch]           the new anchor
+ *   ws/ws_bytes  [dev] uno_spec_accept_workspace_bytes(batch, K) bytes */
+int uno_spec_accept(const float *draft_logits, const float *verify_logits,
+                    const int32_t *draft_tokens, int batch, int K, int vocab,
+                    float inv_temp, uint64_t seed, const uint64_t *step,
+                    const int32_t *forced_accept, int32_t *accept_len,
+                    int32_t *committed, int32_t *extra_token, int32_t *status,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* KV commit / rollback (picx.dev summary, "Practical Implications": one KV
+ * cache serves drafting and verification).  kv_len[b] += 1 + accept_len[b]:
+ * the anchor and the kept drafts stay, every later position becomes scratch
+ * that the next pass overwrites.  step[b] += 1 when step != NULL.  An
+ * accept_len outside [0, K] sets UNO_DEV_BAD_ACCEPT and leaves kv_len[b]. */
+int uno_kv_commit(const uno_kv *kv, const int32_t *accept_len, int batch, int K,
+                  uint64_t *step, int32_t *status, void *stream);
+
+/* Text of a status code, and of the last HIP error a call reported. */
+const char *uno_status_string(int status);
+const char *uno_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UNO_H */

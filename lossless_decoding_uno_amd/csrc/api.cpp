@@ -1,0 +1,353 @@
+// C ABI of libuno: argument validation, workspace carving and the layer loop of
+// the draft and verify passes ("Unlocking Lossless Speedups in LLMs via
+// Discrete Diffusion": picx.dev summary, "Methodology"; paperglide reader, "The
+// Psi-Speculative Sampler", "Sampler Extensions").  Every kernel runs on the
+// caller's stream; nothing here allocates, copies or synchronises.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "uno_internal.h"
+
+using namespace uno;
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return UNO_ERR_HIP;
+}
+
+enum Proj { P_Q = 0, P_K, P_V, P_O, P_GATE, P_UP, P_DOWN };
+
+bool bit(const uno_config& c, int p) { return (c.lora_mask >> p) & 1u; }
+
+int check_config(const uno_config* c) {
+  if (!c) return UNO_ERR_INVALID_ARG;
+  if (c->n_layers < 1 || c->d_model < 64 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->d_ffn < 64 || c->vocab < 16 || c->page_size < 16 || c->lora_rank < 0)
+    return UNO_ERR_INVALID_ARG;
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return UNO_ERR_INVALID_ARG;
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f) || !isfinite(c->lora_scale))
+    return UNO_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return UNO_ERR_UNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads) return UNO_ERR_UNSUPPORTED;
+  if (c->d_model % 64 || c->d_ffn % 64 || (c->n_q_heads * c->head_dim) % 64)
+    return UNO_ERR_UNSUPPORTED;
+  if (c->vocab % 16 || c->vocab > (1 << 20)) return UNO_ERR_UNSUPPORTED;
+  if (c->page_size % 16) return UNO_ERR_UNSUPPORTED;
+  if (c->lora_mask & ~0x7Fu) return UNO_ERR_INVALID_ARG;
+  if (c->lora_mask) {
+    if (c->lora_rank < 16 || c->lora_rank % 16 || c->lora_rank > 256) return UNO_ERR_UNSUPPORTED;
+    const bool q = bit(*c, P_Q), k = bit(*c, P_K), v = bit(*c, P_V);
+    if (q != k || k != v) return UNO_ERR_UNSUPPORTED;
+    if (bit(*c, P_GATE) != bit(*c, P_UP)) return UNO_ERR_UNSUPPORTED;
+  }
+  return UNO_OK;
+}
+
+int check_kv(const uno_config& c, const uno_kv* kv, int K, int max_extra) {
+  if (!kv || !kv->k_pages || !kv->v_pages || !kv->page_table || !kv->kv_len)
+    return UNO_ERR_INVALID_ARG;
+  if (kv->n_pages < 1 || kv->max_pages_per_seq < 1) return UNO_ERR_INVALID_ARG;
+  if ((int64_t)kv->max_pages_per_seq * c.page_size < (int64_t)K + max_extra)
+    return UNO_ERR_CAPACITY;
+  return UNO_OK;
+}
+
+// rank used by the fused kernels: 16 stays 16 (tiny models) else multiple of 32
+int lora_rank_eff(const uno_config& c) { return c.lora_mask ? c.lora_rank : 0; }
+
+struct PassWs {
+  float* h;          // [R, D]
+  uint16_t* xn;      // [R, max(D, F, Hq*hd)]
+  float* qkv;        // [R, (Hq+2Hkv)*hd]
+  uint16_t* qb;      // [R, Hq*hd]
+  uint16_t* ao;      // [R, Hq*hd]
+  float* gu;         // [R, 2F]
+  uint16_t* act;     // [R, F]
+  uint16_t* t;       // [R, 3r]
+  float2* cs;        // [R, hd/2]
+  float* part_o;
+  float* part_ml;
+  size_t total;
+};
+
+PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
+  PassWs w;
+  const size_t R = (size_t)B * K;
+  const size_t D = c.d_model, F = c.d_ffn, QD = (size_t)c.n_q_heads * c.head_dim;
+  const size_t QKV = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t X = D > F ? (D > QD ? D : QD) : (F > QD ? F : QD);
+  const size_t r = (size_t)(lora_rank_eff(c) ? lora_rank_eff(c) : 16);
+  const AttnPlan p = attn_plan(c, B, K, max_ctx);
+  const size_t parts = (size_t)B * c.n_kv_heads * p.n_qgroups * p.n_wave_splits * 64;
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* ptr = b ? b + off : nullptr;
+    off += align_up(bytes, 256);
+    return ptr;
+  };
+  w.h = reinterpret_cast<float*>(take(R * D * 4));
+  w.xn = reinterpret_cast<uint16_t*>(take(R * X * 2));
+  w.qkv = reinterpret_cast<float*>(take(R * QKV * 4));
+  w.qb = reinterpret_cast<uint16_t*>(take(R * QD * 2));
+  w.ao = reinterpret_cast<uint16_t*>(take(R * QD * 2));
+  w.gu = reinterpret_cast<float*>(take(R * 2 * F * 4));
+  w.act = reinterpret_cast<uint16_t*>(take(R * F * 2));
+  w.t = reinterpret_cast<uint16_t*>(take(R * 3 * r * 2));
+  w.cs = reinterpret_cast<float2*>(take(R * (c.head_dim / 2) * sizeof(float2)));
+  w.part_o = reinterpret_cast<float*>(take(parts * c.head_dim * 4));
+  w.part_ml = reinterpret_cast<float*>(take(parts * 2 * 4));
+  w.total = off;
+  return w;
+}
+
+int check_layers(const uno_config& c, const uno_weights* w, bool lora) {
+  if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->layers) return UNO_ERR_INVALID_ARG;
+  for (int li = 0; li < c.n_layers; ++li) {
+    const uno_layer_weights& L = w->layers[li];
+    if (!L.attn_norm || !L.mlp_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.wgate || !L.wup ||
+        !L.wdown)
+      return UNO_ERR_INVALID_ARG;
+    if (lora)
+      for (int p = 0; p < 7; ++p)
+        if (bit(c, p) && (!L.lora_a[p] || !L.lora_b[p])) return UNO_ERR_INVALID_ARG;
+  }
+  return UNO_OK;
+}
+
+const bf16_raw_t* bp(const void* p) { return static_cast<const bf16_raw_t*>(p); }
+
+// One forward pass of B*K rows (draft when `anchor` != null, verify otherwise).
+int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const int32_t* anchor,
+             const int32_t* rows, int B, int K, int max_ctx, int pos_offset, bool lora,
+             float* logits, int32_t* status, void* ws, hipStream_t s) {
+  const PassWs W = carve(c, B, K, max_ctx, ws);
+  const int R = B * K;
+  const int D = c.d_model, F = c.d_ffn, hd = c.head_dim;
+  const int Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int QD = Hq * hd, KD = Hkv * hd, QKV = QD + 2 * KD;
+  const int r = lora ? lora_rank_eff(c) : 0;
+  const bool draft = anchor != nullptr;
+  hipError_t e;
+#define UNO_TRY(x) do { e = (x); if (e != hipSuccess) return hip_fail(e); } while (0)
+
+  UNO_TRY(launch_embed(c, bp(w->embed), anchor, rows, B, K, W.h, status, s));
+  UNO_TRY(launch_rope_table(kv->kv_len, B, K, draft ? 0 : pos_offset, hd / 2, c.rope_theta,
+                            W.cs, s));
+  const AttnPlan plan = attn_plan(c, B, K, max_ctx);
+  const size_t layer_elems = (size_t)kv->n_pages * Hkv * c.page_size * hd;
+
+  auto lora_t = [&](const bf16_raw_t* x, int ldx, int Kd, const void* const* a_ptrs, int n_a) {
+    GemmArgs g = {};
+    g.x = x; g.M = R; g.Kd = Kd; g.ldx = ldx;
+    for (int i = 0; i < n_a; ++i) g.seg[i] = GemmSeg{bp(a_ptrs[i]), r, nullptr, 0};
+    g.n_seg = n_a;
+    g.epi = EPI_LORA_T; g.out = W.t; g.ldo = n_a * r; g.scale = c.lora_scale; g.rows_per_seq = K;
+    return launch_gemm(g, s);
+  };
+
+  for (int li = 0; li < c.n_layers; ++li) {
+    const uno_layer_weights& L = w->layers[li];
+    const bool lq = r && bit(c, P_Q), lo = r && bit(c, P_O), lg = r && bit(c, P_GATE),
+               ld = r && bit(c, P_DOWN);
+    // ---- attention block
+    UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.attn_norm), R, D, c.rms_eps, W.xn, s));
+    if (lq) {
+      const void* a3[3] = {L.lora_a[P_Q], L.lora_a[P_K], L.lora_a[P_V]};
+      UNO_TRY(lora_t(W.xn, D, D, a3, 3));
+    }
+    {
+      GemmArgs g = {};
+      g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
+      g.seg[0] = GemmSeg{bp(L.wq), QD, lq ? bp(L.lora_b[P_Q]) : nullptr, 0};
+      g.seg[1] = GemmSeg{bp(L.wk), KD, lq ? bp(L.lora_b[P_K]) : nullptr, r};
+      g.seg[2] = GemmSeg{bp(L.wv), KD, lq ? bp(L.lora_b[P_V]) : nullptr, 2 * r};
+      g.n_seg = 3;
+      g.t = lq ? W.t : nullptr; g.ldt = 3 * r; g.rank = r;
+      g.epi = EPI_STORE_F32; g.out = W.qkv; g.ldo = QKV;
+      UNO_TRY(launch_gemm(g, s));
+    }
+    UNO_TRY(launch_rope_kv_write(c, W.qkv, W.cs, *kv, li, B, K, draft ? 0 : pos_offset, W.qb,
+                                 status, s));
+    {
+      AttnArgs a = {};
+      a.q = W.qb;
+      a.k_layer = static_cast<const uint16_t*>(kv->k_pages) + (size_t)li * layer_elems;
+      a.v_layer = static_cast<const uint16_t*>(kv->v_pages) + (size_t)li * layer_elems;
+      a.page_table = kv->page_table; a.kv_len = kv->kv_len;
+      a.max_pages = kv->max_pages_per_seq; a.n_pages = kv->n_pages;
+      a.B = B; a.K = K; a.pos_offset = draft ? 0 : pos_offset; a.draft = draft ? 1 : 0;
+      a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.ps = c.page_size; a.plan = plan;
+      a.part_o = W.part_o; a.part_ml = W.part_ml; a.out = W.ao; a.status = status;
+      UNO_TRY(launch_attention(a, s));
+    }
+    if (lo) {
+      const void* a1[1] = {L.lora_a[P_O]};
+      UNO_TRY(lora_t(W.ao, QD, QD, a1, 1));
+    }
+    {
+      GemmArgs g = {};
+      g.x = W.ao; g.M = R; g.Kd = QD; g.ldx = QD;
+      g.seg[0] = GemmSeg{bp(L.wo), D, lo ? bp(L.lora_b[P_O]) : nullptr, 0};
+      g.n_seg = 1;
+      g.t = lo ? W.t : nullptr; g.ldt = r; g.rank = r;
+      g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
+      UNO_TRY(launch_gemm(g, s));
+    }
+    // ---- MLP block
+    UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.mlp_norm), R, D, c.rms_eps, W.xn, s));
+    if (lg) {
+      const void* a2[2] = {L.lora_a[P_GATE], L.lora_a[P_UP]};
+      UNO_TRY(lora_t(W.xn, D, D, a2, 2));
+    }
+    {
+      GemmArgs g = {};
+      g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
+      g.seg[0] = GemmSeg{bp(L.wgate), F, lg ? bp(L.lora_b[P_GATE]) : nullptr, 0};
+      g.seg[1] = GemmSeg{bp(L.wup), F, lg ? bp(L.lora_b[P_UP]) : nullptr, r};
+      g.n_seg = 2;
+      g.t = lg ? W.t : nullptr; g.ldt = 2 * r; g.rank = r;
+      g.epi = EPI_STORE_F32; g.out = W.gu; g.ldo = 2 * F;
+      UNO_TRY(launch_gemm(g, s));
+    }
+    UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
+    if (ld) {
+      const void* a1[1] = {L.lora_a[P_DOWN]};
+      UNO_TRY(lora_t(W.act, F, F, a1, 1));
+    }
+    {
+      GemmArgs g = {};
+      g.x = W.act; g.M = R; g.Kd = F; g.ldx = F;
+      g.seg[0] = GemmSeg{bp(L.wdown), D, ld ? bp(L.lora_b[P_DOWN]) : nullptr, 0};
+      g.n_seg = 1;
+      g.t = ld ? W.t : nullptr; g.ldt = r; g.rank = r;
+      g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
+      UNO_TRY(launch_gemm(g, s));
+    }
+  }
+  if (logits) {
+    UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(w->final_norm), R, D, c.rms_eps, W.xn, s));
+    GemmArgs g = {};
+    g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
+    g.seg[0] = GemmSeg{bp(w->lm_head), c.vocab, nullptr, 0};
+    g.n_seg = 1;
+    g.epi = EPI_STORE_F32; g.out = logits; g.ldo = c.vocab;
+    UNO_TRY(launch_gemm(g, s));
+  }
+#undef UNO_TRY
+  return UNO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t uno_workspace_bytes(const uno_config* cfg, int batch, int K, int max_ctx) {
+  if (check_config(cfg) != UNO_OK || batch < 1 || K < 1) return 0;
+  return carve(*cfg, batch, K, max_ctx, nullptr).total;
+}
+
+int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
+                    const int32_t* anchor, int batch, int K, int max_ctx, float inv_temp,
+                    uint64_t seed, const uint64_t* step, float* draft_logits,
+                    int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || K < 1 || K > 64 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
+  if (!anchor || !step || !draft_logits || !draft_tokens || !ws) return UNO_ERR_INVALID_ARG;
+  if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
+  if ((rc = check_kv(*cfg, kv, K, 0))) return rc;
+  if ((rc = check_layers(*cfg, w, true))) return rc;
+  if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = run_pass(*cfg, w, kv, anchor, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
+                draft_logits, status, ws, s);
+  if (rc) return rc;
+  const hipError_t e = launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed,
+                                           step, draft_tokens, status, s);
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+int uno_verify_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
+                     const int32_t* rows, int batch, int K, int max_ctx, int pos_offset,
+                     float* verify_logits, int32_t* status, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || K < 1 || K > 4096 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
+  if (pos_offset < 0 || pos_offset > 1) return UNO_ERR_INVALID_ARG;
+  if (!rows || !ws) return UNO_ERR_INVALID_ARG;
+  if ((rc = check_kv(*cfg, kv, K, pos_offset))) return rc;
+  if ((rc = check_layers(*cfg, w, false))) return rc;
+  if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
+  return run_pass(*cfg, w, kv, nullptr, rows, batch, K, max_ctx, pos_offset, false,
+                  verify_logits, status, ws, static_cast<hipStream_t>(stream));
+}
+
+int uno_draft_sample(const float* logits, int batch, int K, int vocab, float inv_temp,
+                     uint64_t seed, const uint64_t* step, int32_t* tokens, int32_t* status,
+                     void* stream) {
+  if (!logits || !step || !tokens) return UNO_ERR_INVALID_ARG;
+  if (batch < 1 || K < 1 || vocab < 1 || vocab > (1 << 20)) return UNO_ERR_INVALID_ARG;
+  if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
+  const hipError_t e = launch_draft_sample(logits, batch, K, vocab, inv_temp, seed, step, tokens,
+                                           status, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+size_t uno_spec_accept_workspace_bytes(int batch, int K) {
+  if (batch < 1 || K < 1) return 0;
+  return spec_accept_ws_bytes(batch, K);
+}
+
+int uno_spec_accept(const float* draft_logits, const float* verify_logits,
+                    const int32_t* draft_tokens, int batch, int K, int vocab, float inv_temp,
+                    uint64_t seed, const uint64_t* step, const int32_t* forced_accept,
+                    int32_t* accept_len, int32_t* committed, int32_t* extra_token,
+                    int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (!draft_logits || !verify_logits || !draft_tokens || !step || !accept_len || !committed ||
+      !extra_token || !ws)
+    return UNO_ERR_INVALID_ARG;
+  if (batch < 1 || K < 1 || K > 4096 || vocab < 1 || vocab > (1 << 20))
+    return UNO_ERR_INVALID_ARG;
+  if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
+  if (ws_bytes < spec_accept_ws_bytes(batch, K)) return UNO_ERR_WORKSPACE;
+  const hipError_t e = launch_spec_accept(draft_logits, verify_logits, draft_tokens, batch, K,
+                                          vocab, inv_temp, seed, step, forced_accept, accept_len,
+                                          committed, extra_token, status, ws,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+int uno_kv_commit(const uno_kv* kv, const int32_t* accept_len, int batch, int K, uint64_t* step,
+                  int32_t* status, void* stream) {
+  if (!kv || !kv->kv_len || !accept_len) return UNO_ERR_INVALID_ARG;
+  if (batch < 1 || K < 0) return UNO_ERR_INVALID_ARG;
+  const hipError_t e = launch_kv_commit(kv->kv_len, accept_len, batch, K, step, status,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+const char* uno_status_string(int status) {
+  switch (status) {
+    case UNO_OK: return "ok";
+    case UNO_ERR_INVALID_ARG: return "invalid argument";
+    case UNO_ERR_UNSUPPORTED: return "unsupported shape";
+    case UNO_ERR_CAPACITY: return "page table too small for the block";
+    case UNO_ERR_WORKSPACE: return "workspace too small";
+    case UNO_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* uno_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+}  // extern "C"

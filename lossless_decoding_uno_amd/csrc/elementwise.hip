@@ -1,0 +1,229 @@
+// Small per-row kernels of the draft / verify passes for gfx950: block
+// assembly + embedding gather, RMSNorm, the rotary table, RoPE + paged KV
+// write, SiLU * up, and the KV commit.
+//
+// Block assembly follows the draft/verify layout of the step ("Unlocking
+// Lossless Speedups in LLMs via Discrete Diffusion", paperglide reader, "The
+// Psi-Speculative Sampler"): a draft block is the anchor followed by mask
+// tokens; a verify block is the drafted tokens.  The KV commit keeps the anchor
+// and the kept drafts of the one shared cache (picx.dev summary, "Practical
+// Implications").
+#include "uno_device.h"
+#include "uno_internal.h"
+
+namespace uno {
+
+// ------------------------------------------------------------ embedding
+// One workgroup per row r = b*K + j.  Draft mode (anchor != null): id =
+// anchor[b] for j == 0, mask_id otherwise.  Verify mode: id = rows[r].
+__global__ void __launch_bounds__(256)
+k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
+        const int32_t* __restrict__ rows, int K, int D, int V, int mask_id,
+        float* __restrict__ h, int32_t* __restrict__ status) {
+  const int r = blockIdx.x;
+  const int b = r / K, j = r % K;
+  int id = anchor ? (j == 0 ? anchor[b] : mask_id) : rows[r];
+  const bool bad = id < 0 || id >= V;
+  if (bad) {
+    if (threadIdx.x == 0 && status) atomicOr(status + b, UNO_DEV_BAD_TOKEN);
+    id = 0;
+  }
+  const uint16_t* src = embed + (size_t)id * D;
+  float* dst = h + (size_t)r * D;
+  for (int i = threadIdx.x * 8; i < D; i += 256 * 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(src + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float4 lo, hi;
+    lo.x = bad ? 0.f : __uint_as_float(w[0] << 16); lo.y = bad ? 0.f : __uint_as_float(w[0] & 0xFFFF0000u);
+    lo.z = bad ? 0.f : __uint_as_float(w[1] << 16); lo.w = bad ? 0.f : __uint_as_float(w[1] & 0xFFFF0000u);
+    hi.x = bad ? 0.f : __uint_as_float(w[2] << 16); hi.y = bad ? 0.f : __uint_as_float(w[2] & 0xFFFF0000u);
+    hi.z = bad ? 0.f : __uint_as_float(w[3] << 16); hi.w = bad ? 0.f : __uint_as_float(w[3] & 0xFFFF0000u);
+    *reinterpret_cast<float4*>(dst + i) = lo;
+    *reinterpret_cast<float4*>(dst + i + 4) = hi;
+  }
+}
+
+hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
+                        const int32_t* rows, int B, int K, float* h, int32_t* status,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(B * K), dim3(256), 0, s, embed, anchor, rows, K, c.d_model,
+                     c.vocab, c.mask_id, h, status);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RMSNorm
+// out = bf16(h / sqrt(mean(h^2) + eps) * gain); one workgroup per row, the sum
+// of squares reduced in a fixed order (run-to-run identical).
+__global__ void __launch_bounds__(256)
+k_rmsnorm(const float* __restrict__ h, const float* __restrict__ gain, int D, float eps,
+          uint16_t* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float* x = h + (size_t)r * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x * 4; i < D; i += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(x + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if (lane_id() == 0) red[threadIdx.x / UNO_WAVE] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+  uint16_t* o = out + (size_t)r * D;
+  for (int i = threadIdx.x * 4; i < D; i += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(x + i);
+    const float4 g = *reinterpret_cast<const float4*>(gain + i);
+    uint2 pk;
+    pk.x = pack_bf16x2(v.x * inv * g.x, v.y * inv * g.y);
+    pk.y = pack_bf16x2(v.z * inv * g.z, v.w * inv * g.w);
+    *reinterpret_cast<uint2*>(o + i) = pk;
+  }
+}
+
+hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
+                          bf16_raw_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(R), dim3(256), 0, s, h, gain, D, eps, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ rotary table
+// cs[r, i] = (cos, sin)(pos_r * theta^(-2i/hd)), angle in fp64 so that large
+// positions keep full fp32 accuracy.
+__global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_offset, int half,
+                             double log_theta, float2* __restrict__ cs) {
+  const int r = blockIdx.x;
+  const int b = r / K, j = r % K;
+  const double pos = (double)(kv_len[b] + pos_offset + j);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double inv_freq = exp(-log_theta * (2.0 * i) / (2.0 * half));
+    double sn, cn;
+    sincos(pos * inv_freq, &sn, &cn);
+    cs[(size_t)r * half + i] = make_float2((float)cn, (float)sn);
+  }
+}
+
+hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
+                             float theta, float2* cs, hipStream_t s) {
+  hipLaunchKernelGGL(k_rope_table, dim3(B * K), dim3(64), 0, s, kv_len, K, pos_offset, half,
+                     log((double)theta), cs);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RoPE + KV write
+// qkv row layout: [q heads | k heads | v heads], each head hd wide, fp32.
+// q -> bf16 [R, Hq*hd] (rotated); k (rotated) -> K page [slot][hd];
+// v -> V page transposed [hd][slot].
+__global__ void __launch_bounds__(256)
+k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, int K,
+                int Hq, int Hkv, int hd, int pos_offset, const int32_t* __restrict__ kv_len,
+                const int32_t* __restrict__ page_table, int max_pages, int64_t n_pages,
+                int ps, uint16_t* __restrict__ k_layer, uint16_t* __restrict__ v_layer,
+                uint16_t* __restrict__ q_out, int32_t* __restrict__ status) {
+  const int r = blockIdx.x;
+  const int b = r / K, j = r % K;
+  const int half = hd / 2;
+  const int width = (Hq + 2 * Hkv) * hd;
+  const float* row = qkv + (size_t)r * width;
+  const float2* c = cs + (size_t)r * half;
+  const int pos = kv_len[b] + pos_offset + j;
+  const int pidx = pos / ps, slot = pos % ps;
+  int page = -1;
+  if (pos >= 0 && pidx < max_pages) {
+    page = page_table[(size_t)b * max_pages + pidx];
+    if (page < 0 || page >= n_pages) {
+      if (threadIdx.x == 0 && status) atomicOr(status + b, UNO_DEV_BAD_PAGE);
+      page = -1;
+    }
+  } else if (threadIdx.x == 0 && status) {
+    atomicOr(status + b, UNO_DEV_CAPACITY);
+  }
+  // rotation pairs of q and k heads
+  const int n_pairs = (Hq + Hkv) * half;
+  for (int t = threadIdx.x; t < n_pairs; t += blockDim.x) {
+    const int head = t / half, i = t % half;
+    const float x1 = row[head * hd + i], x2 = row[head * hd + i + half];
+    const float2 a = c[i];
+    const float y1 = x1 * a.x - x2 * a.y;
+    const float y2 = x2 * a.x + x1 * a.y;
+    if (head < Hq) {
+      uint16_t* q = q_out + (size_t)r * Hq * hd + head * hd;
+      q[i] = f32_to_bf16(y1);
+      q[i + half] = f32_to_bf16(y2);
+    } else if (page >= 0) {
+      const int g = head - Hq;
+      uint16_t* kp = k_layer + (((size_t)page * Hkv + g) * ps + slot) * hd;
+      kp[i] = f32_to_bf16(y1);
+      kp[i + half] = f32_to_bf16(y2);
+    }
+  }
+  if (page >= 0) {
+    for (int t = threadIdx.x; t < Hkv * hd; t += blockDim.x) {
+      const int g = t / hd, d = t % hd;
+      const float v = row[(Hq + Hkv) * hd + t];
+      v_layer[(((size_t)page * Hkv + g) * hd + d) * ps + slot] = f32_to_bf16(v);
+    }
+  }
+}
+
+hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
+                                const uno_kv& kv, int layer, int B, int K, int pos_offset,
+                                bf16_raw_t* q_out, int32_t* status, hipStream_t s) {
+  const size_t layer_elems =
+      (size_t)kv.n_pages * c.n_kv_heads * c.page_size * c.head_dim;
+  uint16_t* kl = static_cast<uint16_t*>(kv.k_pages) + (size_t)layer * layer_elems;
+  uint16_t* vl = static_cast<uint16_t*>(kv.v_pages) + (size_t)layer * layer_elems;
+  hipLaunchKernelGGL(k_rope_kv_write, dim3(B * K), dim3(256), 0, s, qkv, cs, K, c.n_q_heads,
+                     c.n_kv_heads, c.head_dim, pos_offset, kv.kv_len, kv.page_table,
+                     kv.max_pages_per_seq, kv.n_pages, c.page_size, kl, vl, q_out, status);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ SiLU * up
+__global__ void __launch_bounds__(256)
+k_silu_mul(const float* __restrict__ gu, int F, uint16_t* __restrict__ act) {
+  const int r = blockIdx.y;
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= F) return;
+  const float* g = gu + (size_t)r * 2 * F;
+  const float4 gv = *reinterpret_cast<const float4*>(g + i);
+  const float4 uv = *reinterpret_cast<const float4*>(g + F + i);
+  const float a0 = gv.x / (1.0f + __expf(-gv.x)) * uv.x;
+  const float a1 = gv.y / (1.0f + __expf(-gv.y)) * uv.y;
+  const float a2 = gv.z / (1.0f + __expf(-gv.z)) * uv.z;
+  const float a3 = gv.w / (1.0f + __expf(-gv.w)) * uv.w;
+  uint2 pk;
+  pk.x = pack_bf16x2(a0, a1);
+  pk.y = pack_bf16x2(a2, a3);
+  *reinterpret_cast<uint2*>(act + (size_t)r * F + i) = pk;
+}
+
+hipError_t launch_silu_mul(const float* gu, int R, int F, bf16_raw_t* act, hipStream_t s) {
+  hipLaunchKernelGGL(k_silu_mul, dim3((F / 4 + 255) / 256, R), dim3(256), 0, s, gu, F, act);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ KV commit
+// kv_len[b] += 1 + a (anchor + kept drafts); later slots become scratch.
+__global__ void k_kv_commit(int32_t* __restrict__ kv_len, const int32_t* __restrict__ accept_len,
+                            int B, int K, uint64_t* __restrict__ step,
+                            int32_t* __restrict__ status) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int a = accept_len[b];
+  if (a < 0 || a > K) {
+    if (status) atomicOr(status + b, UNO_DEV_BAD_ACCEPT);
+    return;
+  }
+  kv_len[b] += 1 + a;
+  if (step) step[b] += 1;
+}
+
+hipError_t launch_kv_commit(int32_t* kv_len, const int32_t* accept_len, int B, int K,
+                            uint64_t* step, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_kv_commit, dim3((B + 255) / 256), dim3(256), 0, s, kv_len, accept_len, B,
+                     K, step, status);
+  return hipGetLastError();
+}
+
+}  // namespace uno

@@ -1,0 +1,92 @@
+// Device-side helpers shared by the gfx950 kernels of libuno.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#define UNO_WAVE 64
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+// round-to-nearest-even (inputs are finite in this library)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, UNO_WAVE));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, UNO_WAVE);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, UNO_WAVE);
+  return v;
+}
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (UNO_WAVE - 1); }
+
+// ---------------------------------------------------------------- 128-bit unsigned
+struct u128 {
+  uint64_t lo, hi;
+};
+__device__ __forceinline__ u128 u128_make(uint64_t lo, uint64_t hi) { u128 r; r.lo = lo; r.hi = hi; return r; }
+__device__ __forceinline__ u128 mul_64x64(uint64_t a, uint64_t b) {
+  return u128_make(a * b, __umul64hi(a, b));
+}
+__device__ __forceinline__ u128 u128_add(u128 a, u128 b) {
+  u128 r;
+  r.lo = a.lo + b.lo;
+  r.hi = a.hi + b.hi + (r.lo < a.lo ? 1ull : 0ull);
+  return r;
+}
+__device__ __forceinline__ u128 u128_sub(u128 a, u128 b) {  // a >= b
+  u128 r;
+  r.lo = a.lo - b.lo;
+  r.hi = a.hi - b.hi - (a.lo < b.lo ? 1ull : 0ull);
+  return r;
+}
+__device__ __forceinline__ bool u128_lt(u128 a, u128 b) {
+  return a.hi < b.hi || (a.hi == b.hi && a.lo < b.lo);
+}
+__device__ __forceinline__ bool u128_is_zero(u128 a) { return (a.lo | a.hi) == 0; }
+__device__ __forceinline__ u128 u128_shfl_xor(u128 v, int o) {
+  return u128_make(__shfl_xor(v.lo, o, UNO_WAVE), __shfl_xor(v.hi, o, UNO_WAVE));
+}
+__device__ __forceinline__ u128 u128_shfl(u128 v, int src) {
+  return u128_make(__shfl(v.lo, src, UNO_WAVE), __shfl(v.hi, src, UNO_WAVE));
+}
+__device__ __forceinline__ u128 u128_shfl_up(u128 v, int d) {
+  return u128_make(__shfl_up(v.lo, d, UNO_WAVE), __shfl_up(v.hi, d, UNO_WAVE));
+}
+__device__ __forceinline__ u128 wave_sum_u128(u128 v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = u128_add(v, u128_shfl_xor(v, o));
+  return v;
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ u128 wave_inclusive_scan_u128(u128 v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < UNO_WAVE; d <<= 1) {
+    u128 o = u128_shfl_up(v, d);
+    if (l >= d) v = u128_add(v, o);
+  }
+  return v;
+}

@@ -1,0 +1,104 @@
+// Internal launchers of libuno (host side).  Every launcher only enqueues on
+// the given stream and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/uno.h"
+
+namespace uno {
+
+typedef uint16_t bf16_raw_t;  // bf16 bits in memory
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- sampler
+hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
+                               uint64_t seed, const uint64_t* step, int32_t* tokens,
+                               int32_t* status, hipStream_t s);
+size_t spec_accept_ws_bytes(int B, int K);
+hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* drafts, int B,
+                              int K, int V, float inv_temp, uint64_t seed, const uint64_t* step,
+                              const int32_t* forced, int32_t* accept_len, int32_t* committed,
+                              int32_t* extra_token, int32_t* status, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise / small ops
+// Block rows: draft (anchor + mask ids) or given rows; gathers embeddings into
+// the fp32 residual stream h [R, D]; also writes ids [R].
+hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
+                        const int32_t* rows, int B, int K, float* h, int32_t* status,
+                        hipStream_t s);
+// RMSNorm of fp32 rows into bf16 rows.
+hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
+                          bf16_raw_t* out, hipStream_t s);
+// cos/sin table [R, head_dim/2] (fp32, angles evaluated in fp64) for the rows'
+// absolute positions kv_len[b] + pos_offset + j.
+hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
+                             float theta, float2* cs, hipStream_t s);
+// RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]), q -> bf16
+// [R, Hq*hd], k/v -> paged cache at the rows' positions.
+hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
+                                const uno_kv& kv, int layer, int B, int K, int pos_offset,
+                                bf16_raw_t* q_out, int32_t* status, hipStream_t s);
+// act = silu(g) * u, gu fp32 [R, 2F] (gate then up) -> bf16 [R, F]
+hipError_t launch_silu_mul(const float* gu, int R, int F, bf16_raw_t* act, hipStream_t s);
+hipError_t launch_kv_commit(int32_t* kv_len, const int32_t* accept_len, int B, int K,
+                            uint64_t* step, int32_t* status, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+// Y[m, n] = sum_k X[m, k] W[n, k]  (+ LoRA)  for up to 3 column segments.
+struct GemmSeg {
+  const bf16_raw_t* w;      // [n, K] bf16
+  int n;                    // columns of this segment (multiple of 16)
+  const bf16_raw_t* lora_b; // [n, r] bf16 or null
+  int t_col;                // first column of this segment's LoRA input in T
+};
+enum GemmEpilogue { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_BF16 = 2, EPI_LORA_T = 3 };
+struct GemmArgs {
+  const bf16_raw_t* x;   // [M, Kd] bf16, row stride ldx
+  int M, Kd, ldx;
+  GemmSeg seg[3];
+  int n_seg;
+  const bf16_raw_t* t;   // LoRA input [M, ldt] bf16 (already scaled and gated) or null
+  int ldt, rank;
+  int epi;
+  void* out;             // [M, ldo]
+  int ldo;
+  // EPI_LORA_T: out[m, n] = bf16(scale * gate(m) * acc); gate(m) = (m % K != 0)
+  float scale;
+  int rows_per_seq;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// Block attention of a pass over the paged cache.  Query rows of sequence b
+// and kv head g are ordered qr = j * G + hh (G = Hq / Hkv).  Keys are split
+// into n_wave_splits ranges of split_len positions (the last range runs to the
+// end of the keys); every wave of the attention kernel owns one range of one
+// group of 64 query rows and writes a partial (max, sum, output) that the merge
+// kernel combines.
+struct AttnPlan {
+  int n_qgroups, n_wave_splits, split_len;
+};
+AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx);
+size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx);
+struct AttnArgs {
+  const uint16_t* q;          // [R, Hq, hd] bf16, post-RoPE
+  const uint16_t* k_layer;    // this layer's K pages
+  const uint16_t* v_layer;    // this layer's V pages (transposed inside a page)
+  const int32_t* page_table;
+  const int32_t* kv_len;
+  int max_pages;
+  int64_t n_pages;
+  int B, K, pos_offset, draft;
+  int Hq, Hkv, hd, ps;
+  AttnPlan plan;
+  float* part_o;              // [B*Hkv, n_qgroups, n_wave_splits, 64, hd]
+  float* part_ml;             // [B*Hkv, n_qgroups, n_wave_splits, 64, 2]
+  uint16_t* out;              // [R, Hq*hd] bf16
+  int32_t* status;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace uno

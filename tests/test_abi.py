@@ -1,0 +1,72 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/uno.h declares, sizes its workspaces, and rejects bad
+arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uno.h")
+LIB = os.path.join(ROOT, "lossless_decoding_uno_amd", "libuno.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libuno.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(uno_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    import lossless_decoding_uno_amd as U
+    lib = U.load_library()
+    names = _declared()
+    assert set(names) == set(U.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_sizes_and_status_strings():
+    import lossless_decoding_uno_amd as U
+    lib = U.load_library()
+    cfg = U.make_config(synth.QWEN3_8B)
+    ws1 = lib.uno_workspace_bytes(ctypes.byref(cfg), 1, 16, 1024)
+    ws64 = lib.uno_workspace_bytes(ctypes.byref(cfg), 64, 16, 9216)
+    assert 0 < ws1 < ws64 < 4 << 30
+    assert lib.uno_spec_accept_workspace_bytes(64, 16) >= 2 * 64 * 16 * 12
+    assert lib.uno_status_string(0) == b"ok"
+    assert lib.uno_status_string(4) == b"workspace too small"
+    bad = U.make_config(dict(synth.QWEN3_8B, head_dim=96))
+    assert lib.uno_workspace_bytes(ctypes.byref(bad), 1, 16, 1024) == 0
+
+
+def test_entry_points_reject_bad_arguments_on_the_host():
+    import lossless_decoding_uno_amd as U
+    lib = U.load_library()
+    cfg = U.make_config(synth.TINY)
+    w = U.UnoWeights()
+    kv = U.UnoKV()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    # null anchor / logits
+    assert lib.uno_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), None, 1, 4,
+                               64, 1.0, 0, fake, fake, fake, None, fake, 1 << 20, None) == 1
+    # K out of range
+    assert lib.uno_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 65,
+                               64, 1.0, 0, fake, fake, fake, None, fake, 1 << 20, None) == 1
+    # bad temperature
+    assert lib.uno_draft_sample(fake, 1, 4, 512, 0.0, 0, fake, fake, None, None) == 1
+    # workspace too small
+    assert lib.uno_spec_accept(fake, fake, fake, 2, 4, 512, 1.0, 0, fake, None, fake, fake, fake,
+                               None, fake, 8, None) == 4
+    # unsupported head_dim
+    bad = U.make_config(dict(synth.TINY, head_dim=48))
+    assert lib.uno_verify_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
+                                64, 1, fake, None, fake, 1 << 20, None) == 2
+    # verify: empty kv struct
+    assert lib.uno_verify_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
+                                64, 1, fake, None, fake, 1 << 30, None) == 1
+    assert lib.uno_kv_commit(None, fake, 1, 4, None, None, None) == 1

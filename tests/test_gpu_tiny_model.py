@@ -1,0 +1,248 @@
+"""GPU parity of the full decode step on the tiny model (2 layers, d_model 256,
+4 heads x 64, SwiGLU 1024, vocab 512, LoRA r16 alpha 32, K = 4, T = 1, 64 new
+tokens after a 32-token prompt, Philox seed 0), teacher-forced by the oracle.
+
+Every step both sides start from the oracle's committed state.  Draft and
+verify logits must agree within 2e-2 abs + 1e-2 rel.  Draft tokens, accept
+lengths, committed and extra tokens must agree exactly, except for a draw
+whose uniform falls so close to an interval edge (for the oracle's own
+weights) that the measured logit difference could move the edge past it; such
+draws are counted, and they must stay rare.  The GPU is then advanced with the
+oracle's decisions (its verify rows are the oracle's drafts, its commit uses the
+oracle's accept length), so the two caches hold the same tokens."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import canonical as cn
+from oracle import spec as ospec
+
+from gpu_util import (assert_logits_close, cat_margin, gpu_or_fail, kv_to_logical, progress,
+                      shift_bound, u24)
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0
+K = 4
+N_NEW = 64
+
+
+def _draft_robust(zq32, j, u, inv_t, dz):
+    w, _ = cn.row_weights(zq32[j], inv_t)
+    _, margin = cat_margin(w, u)
+    return margin > shift_bound(dz, inv_t)
+
+
+def _accept_decisions_robust(zq32, zp32, drafts, a, inv_t, dz, seed, b, step):
+    """True if every accept test the oracle evaluated has a margin larger than
+    what a logit error of dz can move."""
+    Kb = len(drafts)
+    for i in range(2, min(a + 1, Kb) + 1):
+        d = drafts[i - 1]
+        wq, sq = cn.row_weights(zq32[i - 1], inv_t)
+        wp, sp = cn.row_weights(zp32[i - 2], inv_t)
+        ratio = (int(wp[d]) / sp) / (int(wq[d]) / sq)
+        u = u24(seed, 1, i - 1, b, step) / 2.0 ** 24
+        lo = min(1.0, ratio * math.exp(-4 * dz * inv_t))
+        hi = min(1.0, ratio * math.exp(4 * dz * inv_t))
+        if lo <= u < hi:
+            return False
+    return True
+
+
+def _extra_robust(zq32, zp32, a, inv_t, dz, seed, b, step):
+    Kb = zq32.shape[0]
+    u = u24(seed, 2, a, b, step)
+    if a == Kb:
+        w, _ = cn.row_weights(zp32[Kb - 1], inv_t)
+        return cat_margin(w, u)[1] > shift_bound(dz, inv_t)
+    wp, sp = cn.row_weights(zq32[0] if a == 0 else zp32[a - 1], inv_t)
+    wq, sq = cn.row_weights(zq32[a], inv_t)
+    r = cn.residual_weights(wp, sp, wq, sq)
+    tot = sum(r)
+    if tot == 0:
+        return cat_margin(wp, u)[1] > shift_bound(dz, inv_t)
+    mass = tot / (sp * sq)           # residual mass sum max(0, p - q)
+    return cat_margin(r, u)[1] > 4 * shift_bound(dz, inv_t) / max(mass, 1e-30)
+
+
+@pytest.fixture(scope="module")
+def setup():
+    U = gpu_or_fail()
+    cfg = synth.TINY
+    wts = synth.make_weights(cfg, 0)
+    model = U.Model(cfg, wts)
+    return U, cfg, wts, synth.to_f64(wts), model
+
+
+def _prefill_gpu(U, model, kv, prompt, ws, max_ctx):
+    rows = torch.from_numpy(np.asarray(prompt[:-1], dtype=np.int32)).reshape(1, -1).cuda()
+    U.verify_block(model, kv, rows, max_ctx, 0, None, ws)
+    acc = torch.tensor([rows.shape[1] - 1], dtype=torch.int32, device="cuda")
+    U.kv_commit(kv, acc, rows.shape[1])
+
+
+def test_tiny_model_teacher_forced_generation(setup):
+    U, cfg, wts, w64, model = setup
+    prompt = synth.prompt_ids(cfg, 32, 1)
+    cap = len(prompt) + N_NEW + 2 * K + 8
+    max_ctx = cap
+    kv = U.PagedKV(cfg, 1, cap, page_order=torch.randperm(
+        (cap + 15) // 16 + 3, generator=torch.Generator().manual_seed(3)), extra_pages=3)
+    ws = U.alloc_workspace(max(U.workspace_bytes(model, 1, K, max_ctx),
+                               U.workspace_bytes(model, 1, len(prompt), max_ctx)))
+    _prefill_gpu(U, model, kv, prompt, ws, max_ctx)
+    seq = ospec.Sequence(cfg, prompt, capacity=cap)
+    ospec.prefill(cfg, w64, seq)
+    assert int(kv.kv_len.item()) == seq.kv_len == len(prompt) - 1
+
+    # the prefilled cache holds the oracle's K/V (bf16-rounded)
+    for li in range(cfg["n_layers"]):
+        kg, vg = kv_to_logical(kv, li, 0, seq.kv_len)
+        assert_logits_close(kg, seq.cache.k[li][: seq.kv_len], "prefill K layer %d" % li)
+        assert_logits_close(vg, seq.cache.v[li][: seq.kv_len], "prefill V layer %d" % li)
+
+    V = cfg["vocab"]
+    dev = "cuda"
+    zq_g = torch.empty((1, K, V), dtype=torch.float32, device=dev)
+    zp_g = torch.empty((1, K, V), dtype=torch.float32, device=dev)
+    d_g = torch.empty((1, K), dtype=torch.int32, device=dev)
+    a_g = torch.empty(1, dtype=torch.int32, device=dev)
+    c_g = torch.empty((1, K + 1), dtype=torch.int32, device=dev)
+    e_g = torch.empty(1, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    step_g = torch.zeros(1, dtype=torch.uint64).to(dev)
+    aws = U.alloc_workspace(U.spec_accept_workspace_bytes(1, K))
+    n_dec = n_skip = 0
+    worst = 0.0
+    while len(seq.tokens) - len(prompt) < N_NEW:
+        st = seq.step
+        anchor = torch.tensor([seq.tokens[-1]], dtype=torch.int32, device=dev)
+        U.draft_block(model, kv, anchor, K, max_ctx, 1.0, SEED, step_g, zq_g, d_g, ws, status)
+        zq = ospec.draft_logits(cfg, w64, seq, K)
+        zq32 = zq.astype(np.float32)
+        draws = ospec.PhiloxDraws(SEED, 0, st)
+        drafts = ospec.draft_sample(zq32, 1.0, draws)
+        zq_gpu = zq_g.cpu().numpy()[0]
+        worst = max(worst, assert_logits_close(zq_gpu, zq, "draft logits step %d" % st))
+        dz_q = float(np.abs(zq_gpu - zq).max())
+        dg = d_g.cpu().numpy()[0]
+        for j in range(K):
+            n_dec += 1
+            if dg[j] != drafts[j]:
+                assert not _draft_robust(zq32, j, u24(SEED, 0, j, 0, st), 1.0, dz_q), (st, j)
+                n_skip += 1
+
+        rows = torch.tensor([drafts], dtype=torch.int32, device=dev)
+        U.verify_block(model, kv, rows, max_ctx, 1, zp_g, ws, status)
+        zp = ospec.verify_logits(cfg, w64, seq, drafts)
+        zp32 = zp.astype(np.float32)
+        zp_gpu = zp_g.cpu().numpy()[0]
+        worst = max(worst, assert_logits_close(zp_gpu, zp, "verify logits step %d" % st))
+        dz = max(dz_q, float(np.abs(zp_gpu - zp).max()))
+
+        a, committed, extra = ospec.spec_accept(zq32, zp32, drafts, 1.0, draws)
+        U.spec_accept(zq_g, zp_g, rows, 1.0, SEED, step_g, a_g, c_g, e_g, aws, status=status)
+        ag, eg = int(a_g.item()), int(e_g.item())
+        n_dec += 2
+        if ag != a:
+            assert not _accept_decisions_robust(zq32, zp32, drafts, max(a, ag), 1.0, dz, SEED, 0,
+                                                st), (st, ag, a)
+            n_skip += 2
+        elif eg != extra:
+            assert not _extra_robust(zq32, zp32, a, 1.0, dz, SEED, 0, st), (st, eg, extra)
+            n_skip += 1
+        else:
+            cg = c_g.cpu().numpy()[0]
+            np.testing.assert_array_equal(cg, committed + [-1] * (K + 1 - len(committed)))
+
+        # advance both sides with the oracle's decisions
+        U.kv_commit(kv, torch.tensor([a], dtype=torch.int32, device=dev), K, step_g, status)
+        ospec.commit(seq, a, committed)
+        assert int(kv.kv_len.item()) == seq.kv_len
+        assert int(step_g.item()) == seq.step
+    assert int(status.item()) == 0
+    progress("tiny model: %d steps, worst logit error %.2e, %d of %d decisions skipped near an "
+             "edge" % (seq.step, worst, n_skip, n_dec))
+    assert n_skip <= max(2, n_dec // 20)
+
+
+def test_zero_lora_b_reproduces_ar_weights(setup):
+    """B = 0 makes the draft pass identical (bit for bit) to the same pass with
+    the LoRA path switched off."""
+    U, cfg, wts, _, model = setup
+    m0 = U.Model(cfg, synth.zero_lora_b(wts))
+    m_off = U.Model(cfg, wts, lora=False)
+    prompt = synth.prompt_ids(cfg, 20, 4)
+    outs = []
+    for m in (m0, m_off):
+        kv = U.PagedKV(cfg, 1, 64)
+        ws = U.alloc_workspace(max(U.workspace_bytes(m, 1, 20, 64), U.workspace_bytes(m, 1, K, 64)))
+        _prefill_gpu(U, m, kv, prompt, ws, 64)
+        zq = torch.empty((1, K, cfg["vocab"]), dtype=torch.float32, device="cuda")
+        d = torch.empty((1, K), dtype=torch.int32, device="cuda")
+        U.draft_block(m, kv, torch.tensor([int(prompt[-1])], dtype=torch.int32, device="cuda"), K,
+                      64, 1.0, 0, torch.zeros(1, dtype=torch.uint64).cuda(), zq, d, ws)
+        torch.cuda.synchronize()
+        outs.append(zq.cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_batched_ragged_draft_verify_matches_oracle(setup):
+    """Batch of 3 sequences with different committed lengths and shuffled pages:
+    one draft + verify pass, logits of every row against the oracle."""
+    U, cfg, wts, w64, model = setup
+    lens = [7, 23, 40]
+    prompts = [synth.random_tokens(n, cfg["vocab"], 10 + i, (n,)) for i, n in enumerate(lens)]
+    cap = max(lens) + 2 * K + 8
+    B = len(lens)
+    n_pages = B * ((cap + 15) // 16)
+    kv = U.PagedKV(cfg, B, cap, page_order=torch.randperm(
+        n_pages, generator=torch.Generator().manual_seed(9)))
+    ws = U.alloc_workspace(U.workspace_bytes(model, B, max(K, max(lens)), cap))
+    seqs = []
+    for b, p in enumerate(prompts):
+        s = ospec.Sequence(cfg, p, capacity=cap)
+        ospec.prefill(cfg, w64, s)
+        seqs.append(s)
+    # GPU prefill one sequence at a time through a batch-of-one view of the cache
+    for b, p in enumerate(prompts):
+        sub = U.PagedKV.__new__(U.PagedKV)
+        sub.__dict__.update(kv.__dict__)
+        sub.page_table = kv.page_table[b:b + 1].contiguous()
+        sub.kv_len = kv.kv_len[b:b + 1]
+        sub.struct = U.UnoKV(kv.k_pages.data_ptr(), kv.v_pages.data_ptr(), kv.n_pages,
+                             sub.page_table.data_ptr(), kv.max_pages, sub.kv_len.data_ptr())
+        _prefill_gpu(U, model, sub, p, ws, cap)
+    torch.cuda.synchronize()
+    assert kv.kv_len.cpu().tolist() == [n - 1 for n in lens]
+    anchor = torch.tensor([int(p[-1]) for p in prompts], dtype=torch.int32, device="cuda")
+    zq = torch.empty((B, K, cfg["vocab"]), dtype=torch.float32, device="cuda")
+    d = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    U.draft_block(model, kv, anchor, K, cap, 1.0, 0, torch.zeros(B, dtype=torch.uint64).cuda(), zq, d, ws)
+    rows = synth.random_tokens(K, cfg["vocab"], 77, (B, K))
+    zp = torch.empty((B, K, cfg["vocab"]), dtype=torch.float32, device="cuda")
+    U.verify_block(model, kv, torch.from_numpy(rows).cuda(), cap, 1, zp, ws)
+    zq_c, zp_c = zq.cpu().numpy(), zp.cpu().numpy()
+    for b, s in enumerate(seqs):
+        assert_logits_close(zq_c[b], ospec.draft_logits(cfg, w64, s, K), "draft seq %d" % b)
+        assert_logits_close(zp_c[b], ospec.verify_logits(cfg, w64, s, list(rows[b])),
+                            "verify seq %d" % b)
+
+
+def test_kv_commit_ragged_and_rollback(setup):
+    U, cfg, _, _, _ = setup
+    B = 6
+    kv = U.PagedKV(cfg, B, 128)
+    kv.kv_len.copy_(torch.tensor([0, 5, 17, 31, 64, 100], dtype=torch.int32))
+    step = torch.tensor([0, 1, 2, 3, 4, 5], dtype=torch.uint64).cuda()
+    acc = torch.tensor([0, 3, K, 1, -1, K + 1], dtype=torch.int32, device="cuda")
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    U.kv_commit(kv, acc, K, step, status)
+    torch.cuda.synchronize()
+    assert kv.kv_len.cpu().tolist() == [1, 9, 22, 33, 64, 100]
+    assert step.cpu().tolist() == [1, 2, 3, 4, 4, 5]
+    assert status.cpu().tolist() == [0, 0, 0, 0, U.DEV_BAD_ACCEPT, U.DEV_BAD_ACCEPT]
