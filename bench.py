@@ -1,0 +1,298 @@
+"""Throughput of the Psi-Spec draft-and-verify decode step on one MI355X.
+
+Workload (default): Qwen3-8B-shaped random-init bf16 model (36 layers, d_model
+4096, 32 q / 8 kv heads x 128, SwiGLU 12288, vocab 151936, LoRA rank 128
+alpha 256 on all seven linears), batch 64, per-sequence context 9216 in 16-token
+pages with a seeded page permutation, block K = 16, temperature 1.  Each step
+is draft block (36 layers, AR + LoRA) -> draft sampling -> verify block (36
+layers, AR) -> accept / resample -> KV commit, entirely device resident.  As in
+the pages' fixed-length throughput test, each step commits a forced number of
+drafts a ~ U{0..16} per sequence (staggered, exercising ragged commit and
+rollback); accepted tokens per step = sum_b (a_b + 1).  KV content and weights
+are seeded synthetic data.
+
+Prints one JSON line.  `roofline` covers the kernel class that takes the most
+time per step (found in an untimed probe step), timed with HIP events that the
+library records around each of its launches inside the timed region.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--ctx", type=int, default=9216)
+    ap.add_argument("--K", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Device state of one (batch, context, K) decode workload."""
+
+    def __init__(self, U, torch, synth, model, cfg, B, ctx, K, n_steps, seed):
+        self.U, self.torch = U, torch
+        self.B, self.ctx, self.K = B, ctx, K
+        self.cfg = cfg
+        dev = "cuda"
+        self.capacity = ctx + n_steps * (K + 1) + K + 2
+        n_pages_seq = (self.capacity + 15) // 16
+        n_pages = B * n_pages_seq
+        perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(seed))
+        self.kv = U.PagedKV(cfg, B, self.capacity, page_order=perm)
+        synth.fill_kv_device(self.kv.k_pages, self.kv.v_pages, seed)
+        self.kv.kv_len.fill_(ctx)
+        self.max_ctx = self.capacity
+        V = cfg["vocab"]
+        self.ws = U.alloc_workspace(U.workspace_bytes(model, B, K, self.max_ctx))
+        self.aws = U.alloc_workspace(U.spec_accept_workspace_bytes(B, K))
+        self.zq = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+        self.zp = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+        self.d = torch.empty((B, K), dtype=torch.int32, device=dev)
+        self.a = torch.empty(B, dtype=torch.int32, device=dev)
+        self.c = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        self.e = torch.from_numpy(synth.prompt_ids(cfg, B, seed)).to(dev)   # first anchors
+        self.step_ctr = torch.zeros(B, dtype=torch.uint64).to(dev)
+        self.forced_host = synth.forced_accepts(B, K, n_steps, seed=2)
+        self.forced = torch.from_numpy(self.forced_host).to(dev)
+        self.kv_len_host = np.full(B, ctx, dtype=np.int64)
+        self.model = model
+
+    def step(self, i):
+        U = self.U
+        U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, 1.0, 0, self.step_ctr,
+                      self.zq, self.d, self.ws)
+        U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws)
+        U.spec_accept(self.zq, self.zp, self.d, 1.0, 0, self.step_ctr, self.a, self.c, self.e,
+                      self.aws, forced_accept=self.forced[i])
+        U.kv_commit(self.kv, self.a, self.K, self.step_ctr)
+
+    def attn_bytes(self, i):
+        """Algorithmic bytes of the two attention launches of one layer at step i:
+        every cached K/V entry a row may see (read once), q in, out written."""
+        cfg = self.cfg
+        per_tok = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * 2
+        qo = 2 * self.B * self.K * cfg["n_q_heads"] * cfg["head_dim"] * 2
+        kl = self.kv_len_host
+        draft = int(np.sum(kl + self.K)) * per_tok + qo
+        verify = int(np.sum(kl + 1 + self.K)) * per_tok + qo
+        return draft, verify
+
+    def advance_host(self, i):
+        self.kv_len_host += self.forced_host[i].astype(np.int64) + 1
+
+
+def gemm_flops_per_pass(cfg, R, draft):
+    D, F = cfg["d_model"], cfg["d_ffn"]
+    qd = cfg["n_q_heads"] * cfg["head_dim"]
+    kd = cfg["n_kv_heads"] * cfg["head_dim"]
+    r = cfg["lora_rank"]
+    per_layer = (qd + 2 * kd) * D + D * qd + 2 * F * D + D * F
+    if draft:    # LoRA B product fused as r extra K steps on every output column
+        per_layer += (qd + 2 * kd + D + 2 * F + D) * r
+    return 2.0 * R * per_layer * cfg["n_layers"]
+
+
+def run_timed(W, steps, warmup, torch, timer=None):
+    for i in range(warmup):
+        W.step(i)
+        W.advance_host(i)
+    torch.cuda.synchronize()
+    kv0 = W.kv_len_host.copy()
+    if timer is not None:
+        timer.arm()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    attn_bytes = []
+    for i in range(warmup, warmup + steps):
+        db, vb = W.attn_bytes(i)
+        attn_bytes += [db] * W.cfg["n_layers"] + [vb] * W.cfg["n_layers"]
+        W.step(i)
+        W.advance_host(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    used = timer.disarm() if timer is not None else 0
+    ms = t0.elapsed_time(t1)
+    tokens = int(np.sum(W.forced_host[warmup:warmup + steps].astype(np.int64) + 1))
+    got = W.kv.kv_len.cpu().numpy()
+    assert np.array_equal(got, W.kv_len_host), "device kv_len diverged from the forced schedule"
+    return ms, wall, tokens, used, attn_bytes, kv0
+
+
+def probe_classes(U, W, i, torch):
+    """Untimed: total ms per kernel class over one step (one class per rerun)."""
+    totals = {}
+    names = {U.TIME_ATTENTION: "attention", U.TIME_GEMM: "gemm", U.TIME_LORA_A: "lora_a",
+             U.TIME_LM_HEAD: "lm_head", U.TIME_SAMPLER: "sampler"}
+    for cls, name in names.items():
+        timer = U.KernelTimer(cls, 200)
+        kv_save = W.kv.kv_len.clone()
+        step_save = W.step_ctr.clone()
+        e_save = W.e.clone()
+        torch.cuda.synchronize()
+        timer.arm()
+        W.step(i)
+        used = timer.disarm()
+        torch.cuda.synchronize()
+        totals[name] = float(sum(timer.durations_ms(used)))
+        timer.close()
+        W.kv.kv_len.copy_(kv_save)
+        W.step_ctr.copy_(step_save)
+        W.e.copy_(e_save)
+    torch.cuda.synchronize()
+    return totals
+
+
+def cpu_baseline(K, ctx, forced_mean_tokens):
+    """The oracle (fp64 model, exact-integer sampler) on one sequence of the
+    workload: a whole step (best of two) with 1 and with 5 layers of the 8B
+    shape (full LM head, context `ctx` of synthetic cache), extrapolated
+    linearly to 36 layers."""
+    import torch
+    import synth
+    from oracle import spec as ospec
+    cfg = synth.QWEN3_8B
+    times = {}
+    for L in (1, 5):
+        c = dict(cfg, n_layers=L)
+        w = synth.to_f64(synth.make_weights(c, seed=5))
+        prompt = synth.prompt_ids(c, ctx + 1, 3)
+        k, v = synth.kv_values(c, ctx, seed=4)
+        best = None
+        for rep in range(2):
+            seq = ospec.Sequence(c, prompt, capacity=ctx + 2 * K + 4)
+            for li in range(L):
+                seq.cache.k[li][:ctx] = k[li].double().numpy()
+                seq.cache.v[li][:ctx] = v[li].double().numpy()
+            seq.kv_len = ctx
+            t = time.perf_counter()
+            ospec.step(c, w, seq, K, 1.0, ospec.PhiloxDraws(0, 0, 0), forced=K // 2)
+            dt = time.perf_counter() - t
+            best = dt if best is None else min(best, dt)
+        times[L] = best
+        del w
+    per_layer = max((times[5] - times[1]) / 4.0, 1e-9)
+    t36 = times[1] + (cfg["n_layers"] - 1) * per_layer
+    return {"value": forced_mean_tokens / t36, "unit": "accepted tokens/s",
+            "cores": int(torch.get_num_threads()), "kind": "oracle",
+            "sample": ("one sequence of the workload, one full step (draft+sample+verify+accept+"
+                       "commit) at context %d, K=%d, timed with 1 and 5 of the 36 layers "
+                       "(%.2f s, %.2f s; best of 2), extrapolated linearly to 36 layers "
+                       "(%.2f s/step); %.1f accepted tokens per step (the forced schedule's mean)"
+                       % (ctx, K, times[1], times[5], t36, forced_mean_tokens))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the batch would "
+              "shard by sequence with no per-step communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import lossless_decoding_uno_amd as U
+    import synth
+    U.load_library()
+    assert torch.cuda.is_available(), "no GPU"
+    cfg = synth.QWEN3_8B
+    K = args.K
+    log("generating weights on the GPU")
+    model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))
+    torch.cuda.synchronize()
+    n_steps = args.warmup + args.steps + 1
+    log("allocating KV for batch %d context %d" % (args.batch, args.ctx))
+    W = Workload(U, torch, synth, model, cfg, args.batch, args.ctx, K, n_steps, seed=1)
+    torch.cuda.synchronize()
+    log("probe step (per-kernel-class times)")
+    W.step(0)
+    torch.cuda.synchronize()
+    W.kv.kv_len.fill_(args.ctx)
+    W.step_ctr.copy_(torch.zeros(args.batch, dtype=torch.uint64))
+    classes = probe_classes(U, W, 0, torch)
+    log("class ms per step: %s" % json.dumps({k: round(v, 3) for k, v in classes.items()}))
+    dominant = max(classes, key=classes.get)
+    cls_id = {"attention": U.TIME_ATTENTION, "gemm": U.TIME_GEMM, "lora_a": U.TIME_LORA_A,
+              "lm_head": U.TIME_LM_HEAD, "sampler": U.TIME_SAMPLER}[dominant]
+    n_launch = {"attention": 2 * cfg["n_layers"], "gemm": 8 * cfg["n_layers"],
+                "lora_a": 4 * cfg["n_layers"], "lm_head": 2, "sampler": 2}[dominant]
+    timer = U.KernelTimer(cls_id, n_launch * args.steps)
+    log("timed region: %d steps after %d warmup (dominant class: %s)" % (args.steps, args.warmup,
+                                                                       dominant))
+    ms, wall, tokens, used, attn_bytes, kv0 = run_timed(W, args.steps, args.warmup, torch, timer)
+    durs = np.array(timer.durations_ms(used))
+    timer.close()
+    ms_step = ms / args.steps
+    value = tokens / (ms / 1e3)
+    R = args.batch * K
+    if dominant == "attention":
+        achieved = float(np.sum(attn_bytes[:used])) / (durs.sum() / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_attention<128>", "launches": int(used),
+                "avg_launch_us": round(float(durs.mean()) * 1e3, 2)}
+    elif dominant == "gemm":
+        fl = (gemm_flops_per_pass(cfg, R, True) + gemm_flops_per_pass(cfg, R, False)) * args.steps
+        achieved = fl / (durs.sum() / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "k_gemm (4 projections per layer, both passes)", "launches": int(used),
+                "avg_launch_us": round(float(durs.mean()) * 1e3, 2)}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": None, "traffic": None, "kernel": dominant, "launches": int(used),
+                "avg_launch_us": round(float(durs.mean()) * 1e3, 2)}
+    out = {"metric": "accepted tokens/s/GPU (Qwen3-8B shape, Psi-Spec draft+verify step)",
+           "value": round(value, 1), "unit": "accepted tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded random-init weights and KV, forced accept lengths)",
+           "config": {"workload": "qwen3-8b-shape b%d ctx%d K%d forced a~U{0..%d}" % (
+               args.batch, args.ctx, K, K), "global_batch": args.batch, "seq_len": args.ctx,
+               "block_K": K, "parallelism": "none (1 GPU)"},
+           "roofline": roof,
+           "kernel_class_ms_per_step": {k: round(v, 3) for k, v in classes.items()},
+           "forward_passes_per_s": round(2 * args.steps / (ms / 1e3), 2),
+           "wall_s_timed": round(wall, 3)}
+    del W
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        log("secondary: batch 1, context 1024")
+        W1 = Workload(U, torch, synth, model, cfg, 1, 1024, K, 40 + 6, seed=7)
+        ms1, _, tok1, _, _, _ = run_timed(W1, 40, 5, torch)
+        out["secondary"] = {"workload": "qwen3-8b-shape b1 ctx1024 K%d forced" % K,
+                            "value": round(tok1 / (ms1 / 1e3), 1), "unit": "accepted tokens/s",
+                            "ms_per_step": round(ms1 / 40, 3)}
+        del W1
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(K, args.ctx, (K + 2) / 2.0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

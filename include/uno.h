@@ -192,6 +192,25 @@ int uno_spec_accept(const float *draft_logits, const float *verify_logits,
 int uno_kv_commit(const uno_kv *kv, const int32_t *accept_len, int batch, int K,
                   uint64_t *step, int32_t *status, void *stream);
 
+/* Measurement hook (not part of the decode path; for benchmarks and
+ * profilers).  While set, every launch of one kernel class made by the entry
+ * points above is bracketed by hipEventRecord(start[i]) / hipEventRecord(stop[i])
+ * on the launching stream, i = 0, 1, ... until n pairs are used; later
+ * launches are not bracketed.  start/stop are [host] arrays of hipEvent_t
+ * owned by the caller and must outlive their use.  kernel_class 0 clears the
+ * hook.  The hook is process-wide state: set it from one thread, with no other
+ * call of this library in flight.  uno_timing_events_used() returns i. */
+enum {
+  UNO_TIME_ATTENTION = 1, /* block attention (the split-KV partial kernel)    */
+  UNO_TIME_GEMM = 2,      /* the four projections of every layer (q|k|v, o,
+                             gate|up, down), LoRA B fused when drafting       */
+  UNO_TIME_LORA_A = 3,    /* the LoRA A products (x A^T, gated and scaled)    */
+  UNO_TIME_LM_HEAD = 4,   /* the final vocabulary projection                  */
+  UNO_TIME_SAMPLER = 5    /* draft sampling and the accept / resample kernels */
+};
+int uno_set_timing_events(int kernel_class, void *const *start, void *const *stop, int n);
+int uno_timing_events_used(void);
+
 /* Text of a status code, and of the last HIP error a call reported. */
 const char *uno_status_string(int status);
 const char *uno_last_hip_error(void);

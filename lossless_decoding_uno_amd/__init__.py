@@ -25,7 +25,10 @@ DEV_CAPACITY, DEV_BAD_TOKEN, DEV_BAD_PAGE, DEV_NONFINITE, DEV_BAD_ACCEPT = 1, 2,
 
 EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_verify_block", "uno_draft_sample",
            "uno_spec_accept_workspace_bytes", "uno_spec_accept", "uno_kv_commit",
-           "uno_status_string", "uno_last_hip_error")
+           "uno_set_timing_events", "uno_timing_events_used", "uno_status_string",
+           "uno_last_hip_error")
+
+TIME_ATTENTION, TIME_GEMM, TIME_LORA_A, TIME_LM_HEAD, TIME_SAMPLER = 1, 2, 3, 4, 5
 
 
 class UnoConfig(ctypes.Structure):
@@ -87,6 +90,10 @@ def load_library():
     lib.uno_status_string.argtypes = [I]
     lib.uno_last_hip_error.restype = ctypes.c_char_p
     lib.uno_last_hip_error.argtypes = []
+    lib.uno_set_timing_events.restype = I
+    lib.uno_set_timing_events.argtypes = [I, P, P, I]
+    lib.uno_timing_events_used.restype = I
+    lib.uno_timing_events_used.argtypes = []
     _lib = lib
     return lib
 
@@ -286,3 +293,51 @@ def kv_commit(kv, accept_len, K, step=None, status=None):
         _need(step, torch.uint64, (B,), "step")
     _check(lib.uno_kv_commit(ctypes.byref(kv.struct), _ptr(accept_len), B, K, _ptr(step),
                              _ptr(status), _stream()))
+
+
+class KernelTimer:
+    """HIP events that libuno records around every launch of one kernel class
+    (uno_set_timing_events), on the stream each launch uses."""
+
+    def __init__(self, kernel_class, n):
+        self.lib = load_library()
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = n
+        self.kernel_class = kernel_class
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for arr in (self.start, self.stop):
+            for i in range(n):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise UnoError("hipEventCreate failed")
+                arr[i] = ev.value
+
+    def arm(self):
+        _check(self.lib.uno_set_timing_events(self.kernel_class, self.start, self.stop, self.n))
+
+    def disarm(self):
+        used = self.lib.uno_timing_events_used()
+        _check(self.lib.uno_set_timing_events(0, None, None, 0))
+        return used
+
+    def durations_ms(self, used):
+        """Elapsed ms of the first `used` bracketed launches (stream synchronised)."""
+        out = []
+        for i in range(used):
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) != 0:
+                raise UnoError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for arr in (self.start, self.stop):
+            for i in range(self.n):
+                if arr[i]:
+                    self.hip.hipEventDestroy(arr[i])
+                    arr[i] = None

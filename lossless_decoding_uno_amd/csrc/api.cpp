@@ -17,6 +17,26 @@ namespace {
 
 thread_local std::string g_last_hip_error;
 
+// Measurement hook (uno_set_timing_events): brackets launches of one kernel
+// class with caller-owned HIP events on the launching stream.
+struct TimingHook {
+  int cls = 0;
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+  int n = 0;
+  int count = 0;
+};
+TimingHook g_hook;
+
+template <class F>
+hipError_t timed(int cls, hipStream_t s, F&& launch) {
+  const bool on = g_hook.cls == cls && g_hook.count < g_hook.n;
+  if (on) hipEventRecord(g_hook.start[g_hook.count], s);
+  const hipError_t e = launch();
+  if (on) hipEventRecord(g_hook.stop[g_hook.count++], s);
+  return e;
+}
+
 int hip_fail(hipError_t e) {
   g_last_hip_error = hipGetErrorString(e);
   return UNO_ERR_HIP;
@@ -150,7 +170,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
     for (int i = 0; i < n_a; ++i) g.seg[i] = GemmSeg{bp(a_ptrs[i]), r, nullptr, 0};
     g.n_seg = n_a;
     g.epi = EPI_LORA_T; g.out = W.t; g.ldo = n_a * r; g.scale = c.lora_scale; g.rows_per_seq = K;
-    return launch_gemm(g, s);
+    return timed(UNO_TIME_LORA_A, s, [&] { return launch_gemm(g, s); });
   };
 
   for (int li = 0; li < c.n_layers; ++li) {
@@ -172,7 +192,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 3;
       g.t = lq ? W.t : nullptr; g.ldt = 3 * r; g.rank = r;
       g.epi = EPI_STORE_F32; g.out = W.qkv; g.ldo = QKV;
-      UNO_TRY(launch_gemm(g, s));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
     }
     UNO_TRY(launch_rope_kv_write(c, W.qkv, W.cs, *kv, li, B, K, draft ? 0 : pos_offset, W.qb,
                                  status, s));
@@ -186,7 +206,8 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       a.B = B; a.K = K; a.pos_offset = draft ? 0 : pos_offset; a.draft = draft ? 1 : 0;
       a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.ps = c.page_size; a.plan = plan;
       a.part_o = W.part_o; a.part_ml = W.part_ml; a.out = W.ao; a.status = status;
-      UNO_TRY(launch_attention(a, s));
+      UNO_TRY(timed(UNO_TIME_ATTENTION, s, [&] { return launch_attention(a, s); }));
+      UNO_TRY(launch_attn_merge(a, s));
     }
     if (lo) {
       const void* a1[1] = {L.lora_a[P_O]};
@@ -199,7 +220,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 1;
       g.t = lo ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
-      UNO_TRY(launch_gemm(g, s));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
     }
     // ---- MLP block
     UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.mlp_norm), R, D, c.rms_eps, W.xn, s));
@@ -215,7 +236,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 2;
       g.t = lg ? W.t : nullptr; g.ldt = 2 * r; g.rank = r;
       g.epi = EPI_STORE_F32; g.out = W.gu; g.ldo = 2 * F;
-      UNO_TRY(launch_gemm(g, s));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
     }
     UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
     if (ld) {
@@ -229,7 +250,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 1;
       g.t = ld ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
-      UNO_TRY(launch_gemm(g, s));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
     }
   }
   if (logits) {
@@ -239,7 +260,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
     g.seg[0] = GemmSeg{bp(w->lm_head), c.vocab, nullptr, 0};
     g.n_seg = 1;
     g.epi = EPI_STORE_F32; g.out = logits; g.ldo = c.vocab;
-    UNO_TRY(launch_gemm(g, s));
+    UNO_TRY(timed(UNO_TIME_LM_HEAD, s, [&] { return launch_gemm(g, s); }));
   }
 #undef UNO_TRY
   return UNO_OK;
@@ -271,8 +292,10 @@ int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* k
   rc = run_pass(*cfg, w, kv, anchor, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
                 draft_logits, status, ws, s);
   if (rc) return rc;
-  const hipError_t e = launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed,
-                                           step, draft_tokens, status, s);
+  const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
+    return launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed, step,
+                               draft_tokens, status, s);
+  });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 
@@ -320,10 +343,12 @@ int uno_spec_accept(const float* draft_logits, const float* verify_logits,
     return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
   if (ws_bytes < spec_accept_ws_bytes(batch, K)) return UNO_ERR_WORKSPACE;
-  const hipError_t e = launch_spec_accept(draft_logits, verify_logits, draft_tokens, batch, K,
-                                          vocab, inv_temp, seed, step, forced_accept, accept_len,
-                                          committed, extra_token, status, ws,
-                                          static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
+    return launch_spec_accept(draft_logits, verify_logits, draft_tokens, batch, K, vocab,
+                              inv_temp, seed, step, forced_accept, accept_len, committed,
+                              extra_token, status, ws, s);
+  });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 
@@ -335,6 +360,23 @@ int uno_kv_commit(const uno_kv* kv, const int32_t* accept_len, int batch, int K,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
+
+int uno_set_timing_events(int kernel_class, void* const* start, void* const* stop, int n) {
+  if (kernel_class == 0) {
+    g_hook = TimingHook();
+    return UNO_OK;
+  }
+  if (kernel_class < 0 || kernel_class > UNO_TIME_SAMPLER || !start || !stop || n < 1)
+    return UNO_ERR_INVALID_ARG;
+  g_hook.cls = kernel_class;
+  g_hook.start = reinterpret_cast<hipEvent_t*>(const_cast<void**>(start));
+  g_hook.stop = reinterpret_cast<hipEvent_t*>(const_cast<void**>(stop));
+  g_hook.n = n;
+  g_hook.count = 0;
+  return UNO_OK;
+}
+
+int uno_timing_events_used(void) { return g_hook.count; }
 
 const char* uno_status_string(int status) {
   switch (status) {

@@ -244,15 +244,16 @@ size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.plan.n_wave_splits / 4, a.plan.n_qgroups, a.B * a.Hkv);
+  if (a.hd == 128) hipLaunchKernelGGL(k_attention<128>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_attention<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const dim3 mgrid(G * a.K, a.B * a.Hkv);
-  if (a.hd == 128) {
-    hipLaunchKernelGGL(k_attention<128>, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_attn_merge<128>, mgrid, dim3(128), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(k_attention<64>, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_attn_merge<64>, mgrid, dim3(64), 0, s, a);
-  }
+  if (a.hd == 128) hipLaunchKernelGGL(k_attn_merge<128>, mgrid, dim3(128), 0, s, a);
+  else hipLaunchKernelGGL(k_attn_merge<64>, mgrid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -151,7 +151,7 @@ k_gemm_skinny(GemmArgs a) {
   }
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s) {
   int tiles = 0;
   for (int i = 0; i < a.n_seg; ++i) tiles += a.seg[i].n / 16;
   const dim3 block(kSkWaves * 64);
@@ -163,6 +163,188 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_gemm_skinny<4>, dim3(tiles, (a.M + 63) / 64), block, 0, s, a);
   }
   return hipGetLastError();
+}
+
+
+// ============================================================================
+// Tiled kernel (many rows: batched decode blocks, prompt chunks).
+// Workgroup tile 256 x 128 (rows of X x columns of W), 4 waves in a 2 x 2
+// grid, each wave 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Both
+// operands are staged through LDS in 64-wide K slices, double buffered: the
+// global loads of slice s+1 are issued before the MFMAs of slice s and stored
+// to the other LDS buffer after them.  LDS rows are 128 bytes (8 chunks of 16
+// bytes) with the chunk index XOR-swizzled by the row, so the 16-byte fragment
+// reads of 32 consecutive rows spread over the banks.  The LoRA product runs
+// as r/64 extra K slices with T and B as operands.  Tiles are ordered so that
+// the workgroups sharing one W tile run on the same XCD (same L2).  Split-K
+// (grid.z) accumulates with fp32 atomics into the residual stream.
+// ============================================================================
+namespace big {
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kLdsA = BM * BK * 2;      // bytes per stage
+constexpr int kLdsB = BN * BK * 2;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return (row * 8 + (chunk ^ (row & 7))) * 16; }
+}  // namespace big
+
+__global__ void __launch_bounds__(big::kThreads)
+k_gemm_tiled(GemmArgs a, int m_tiles, int n_tiles, int splits) {
+  using namespace big;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wm = w >> 1, wn = w & 1;
+
+  // XCD-aware order: linear id -> (xcd, slot); tiles of one N column stay together
+  const int nwg = m_tiles * n_tiles;
+  const int id = blockIdx.x;
+  const int per_xcd = (nwg + 7) / 8;
+  int lin = (id % 8) * per_xcd + id / 8;
+  if (nwg % 8 != 0) lin = id;             // keep it simple when the grid is ragged
+  const int mt = lin % m_tiles, nt = lin / m_tiles;
+  if (nt >= n_tiles) return;
+  const int m0 = mt * BM;
+  const SegView sv = pick_segment(a, nt * (BN / 16));
+  const int n0 = sv.n0;
+
+  // K slices of this split
+  const int nk_base = a.Kd / BK;
+  const int nk_lora = (a.t && sv.lb) ? a.rank / BK : 0;
+  const int z = blockIdx.z;
+  const int kb0 = nk_base * z / splits, kb1 = nk_base * (z + 1) / splits;
+  const int nk = (kb1 - kb0) + (z == splits - 1 ? nk_lora : 0);
+
+  // global load mapping: 8 threads per 128-byte row; A: 256 rows (8 per thread),
+  // B: 128 rows (4 per thread)
+  const int lrow = tid >> 3, lch = tid & 7;
+  uint4 ra[8], rb[4];
+  auto gload = [&](int s) {
+    const int kk = kb0 + s;
+    const bool lora = kk >= kb1;
+    const uint16_t* xa;
+    size_t lda;
+    const uint16_t* wb;
+    size_t ldb;
+    if (!lora) {
+      xa = a.x + (size_t)kk * BK; lda = a.ldx;
+      wb = sv.w + (size_t)kk * BK; ldb = a.Kd;
+    } else {
+      const int rs = kk - kb1;
+      xa = a.t + sv.t_col + (size_t)rs * BK; lda = a.ldt;
+      wb = sv.lb + (size_t)rs * BK; ldb = a.rank;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = lrow + i * 32, m = m0 + row;
+      ra[i] = m < a.M ? *reinterpret_cast<const uint4*>(xa + (size_t)m * lda + lch * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lrow + i * 32;
+      rb[i] = *reinterpret_cast<const uint4*>(wb + (size_t)(n0 + row) * ldb + lch * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char* A = lds + buf * (kLdsA + kLdsB);
+    unsigned char* B = A + kLdsA;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(A + swz(lrow + i * 32, lch)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + swz(lrow + i * 32, lch)) = rb[i];
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nk) gload(s + 1);
+    const unsigned char* A = lds + buf * (kLdsA + kLdsB);
+    const unsigned char* B = A + kLdsA;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int ch = 2 * kk + (l >> 5);
+      Frag fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i].u = *reinterpret_cast<const uint4*>(A + swz(wm * 128 + i * 32 + (l & 31), ch));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j].u = *reinterpret_cast<const uint4*>(B + swz(wn * 64 + j * 32 + (l & 31), ch));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i].v, fb[j].v, acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows (e/4)*8 + (l/32)*4 + e%4, column l%32 of each 32x32 tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
+        if (m >= a.M) continue;
+        const int n = sv.col_base + n0 + wn * 64 + j * 32 + (l & 31);
+        const size_t o = (size_t)m * a.ldo + n;
+        const float v = acc[i][j][e];
+        switch (a.epi) {
+          case EPI_STORE_F32: static_cast<float*>(a.out)[o] = v; break;
+          case EPI_ADD_F32:
+            if (splits > 1) atomicAdd(static_cast<float*>(a.out) + o, v);
+            else static_cast<float*>(a.out)[o] += v;
+            break;
+          case EPI_STORE_BF16: static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v); break;
+          default: {
+            const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
+            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(g * v);
+          }
+        }
+      }
+}
+
+static bool tiled_ok(const GemmArgs& a) {
+  if (a.M < 128 || a.Kd % big::BK) return false;
+  for (int i = 0; i < a.n_seg; ++i)
+    if (a.seg[i].n % big::BN) return false;
+  if (a.t && a.rank % big::BK) return false;
+  return true;
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
+  int n_tiles = 0;
+  for (int i = 0; i < a.n_seg; ++i) n_tiles += a.seg[i].n / big::BN;
+  const int m_tiles = (a.M + big::BM - 1) / big::BM;
+  int splits = 1;
+  if (a.epi == EPI_ADD_F32) {
+    const int wgs = m_tiles * n_tiles;
+    while (wgs * splits < 256 && splits < 4 && (a.Kd / big::BK) / (splits * 2) >= 8) splits *= 2;
+  }
+  const size_t lds = 2 * (big::kLdsA + big::kLdsB);
+  hipLaunchKernelGGL(k_gemm_tiled, dim3(m_tiles * n_tiles, 1, splits), dim3(big::kThreads), lds,
+                     s, a, m_tiles, n_tiles, splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (tiled_ok(a)) return launch_gemm_tiled(a, s);
+  return launch_gemm_skinny(a, s);
 }
 
 }  // namespace uno

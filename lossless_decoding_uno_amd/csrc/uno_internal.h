@@ -99,6 +99,7 @@ struct AttnArgs {
   uint16_t* out;              // [R, Hq*hd] bf16
   int32_t* status;
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);   // partials
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);  // combine -> out
 
 }  // namespace uno

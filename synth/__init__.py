@@ -29,6 +29,9 @@ QWEN3_8B = dict(n_layers=36, d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=
                 d_ffn=12288, vocab=151936, mask_id=151935, rms_eps=1e-6,
                 rope_theta=1000000.0, lora_rank=128, lora_alpha=256.0)
 
+# the tiny shape with a LoRA rank that fills whole 64-wide K slices
+TINY_R64 = dict(TINY, lora_rank=64, lora_alpha=128.0)
+
 # enumeration vocabulary toy: vocab 8 (mask id 7)
 VOCAB8 = dict(n_layers=1, d_model=32, n_q_heads=2, n_kv_heads=1, head_dim=16,
               d_ffn=64, vocab=8, mask_id=7, rms_eps=1e-6, rope_theta=10000.0,
@@ -177,3 +180,44 @@ def kv_values(cfg, seq_len, seed, seq=0, std=1.0):
     k = normal_bf16(shape, std, [seed, 23, seq, 0])
     v = normal_bf16(shape, std, [seed, 23, seq, 1])
     return k, v
+
+
+def make_weights_device(cfg, seed=0, device="cuda", lora=True):
+    """Whole model drawn directly on the GPU (torch's seeded device generator),
+    same shapes and distributions as ``make_weights`` but different values;
+    for throughput runs, where no oracle reads the weights."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+
+    def draw(shape, std, key):
+        gen.manual_seed(int(np.random.SeedSequence(key).generate_state(1, np.uint64)[0] >> 1))
+        t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        return t.mul_(std).to(torch.bfloat16)
+
+    shp = proj_shapes(cfg)
+    r = cfg["lora_rank"]
+    D = cfg["d_model"]
+    out = {"embed": draw((cfg["vocab"], D), W_STD, [seed, 0]),
+           "lm_head": draw((cfg["vocab"], D), W_STD, [seed, 1]),
+           "final_norm": torch.ones(D, dtype=torch.float32, device=dev), "layers": []}
+    for li in range(cfg["n_layers"]):
+        lw = {"attn_norm": torch.ones(D, dtype=torch.float32, device=dev),
+              "mlp_norm": torch.ones(D, dtype=torch.float32, device=dev),
+              "lora_a": {}, "lora_b": {}}
+        for p in PROJ:
+            o, i = shp[p]
+            lw[p] = draw((o, i), W_STD, [seed, tensor_index(li, p)])
+            if lora:
+                lw["lora_a"][p] = draw((r, i), LORA_A_STD, [seed, tensor_index(li, "lora_a_" + p)])
+                lw["lora_b"][p] = draw((o, r), LORA_B_STD, [seed, tensor_index(li, "lora_b_" + p)])
+        out["layers"].append(lw)
+    return out
+
+
+def fill_kv_device(k_pages, v_pages, seed, std=1.0):
+    """Seeded N(0, std^2) content for every page of a device KV pool."""
+    gen = torch.Generator(device=k_pages.device)
+    for li in range(k_pages.shape[0]):
+        for which, t in ((0, k_pages), (1, v_pages)):
+            gen.manual_seed(int(seed) * 1000003 + li * 2 + which)
+            t[li].normal_(0.0, std, generator=gen)

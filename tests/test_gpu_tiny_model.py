@@ -246,3 +246,47 @@ def test_kv_commit_ragged_and_rollback(setup):
     assert kv.kv_len.cpu().tolist() == [1, 9, 22, 33, 64, 100]
     assert step.cpu().tolist() == [1, 2, 3, 4, 4, 5]
     assert status.cpu().tolist() == [0, 0, 0, 0, U.DEV_BAD_ACCEPT, U.DEV_BAD_ACCEPT]
+
+
+@pytest.mark.parametrize("B,K_blk,prompt_len", [(40, 4, 150), (9, 16, 300)])
+def test_many_rows_tiled_gemm_matches_oracle(B, K_blk, prompt_len):
+    """Passes of >= 128 rows (the tiled GEMM with fused LoRA, split-K on the
+    residual projections, a ragged last row tile) and a long prompt chunk,
+    against the oracle on a rank-64 variant of the tiny model."""
+    U = gpu_or_fail()
+    cfg = synth.TINY_R64
+    wts = synth.make_weights(cfg, 2)
+    w64 = synth.to_f64(wts)
+    model = U.Model(cfg, wts)
+    lens = [prompt_len - 3 * b for b in range(B)]
+    cap = max(lens) + 2 * K_blk + 8
+    n_pages = B * ((cap + 15) // 16)
+    kv = U.PagedKV(cfg, B, cap, page_order=torch.randperm(
+        n_pages, generator=torch.Generator().manual_seed(B)))
+    ws = U.alloc_workspace(max(U.workspace_bytes(model, B, K_blk, cap),
+                               U.workspace_bytes(model, 1, max(lens), cap)))
+    prompts = [synth.random_tokens(n, cfg["vocab"], 100 + b, (n,)) for b, n in enumerate(lens)]
+    for b, p in enumerate(prompts):   # prefill: one long chunk per sequence (>= 128 rows)
+        sub = U.PagedKV.__new__(U.PagedKV)
+        sub.__dict__.update(kv.__dict__)
+        sub.page_table = kv.page_table[b:b + 1].contiguous()
+        sub.kv_len = kv.kv_len[b:b + 1]
+        sub.struct = U.UnoKV(kv.k_pages.data_ptr(), kv.v_pages.data_ptr(), kv.n_pages,
+                             sub.page_table.data_ptr(), kv.max_pages, sub.kv_len.data_ptr())
+        _prefill_gpu(U, model, sub, p, ws, cap)
+    anchor = torch.tensor([int(p[-1]) for p in prompts], dtype=torch.int32, device="cuda")
+    V = cfg["vocab"]
+    zq = torch.empty((B, K_blk, V), dtype=torch.float32, device="cuda")
+    d = torch.empty((B, K_blk), dtype=torch.int32, device="cuda")
+    U.draft_block(model, kv, anchor, K_blk, cap, 1.0, 0, torch.zeros(B, dtype=torch.uint64).cuda(),
+                  zq, d, ws)
+    rows = synth.random_tokens(K_blk, V, 55, (B, K_blk))
+    zp = torch.empty((B, K_blk, V), dtype=torch.float32, device="cuda")
+    U.verify_block(model, kv, torch.from_numpy(rows).cuda(), cap, 1, zp, ws)
+    zq_c, zp_c = zq.cpu().numpy(), zp.cpu().numpy()
+    for b in range(0, B, max(1, B // 6)):
+        s = ospec.Sequence(cfg, prompts[b], capacity=cap)
+        ospec.prefill(cfg, w64, s)
+        assert_logits_close(zq_c[b], ospec.draft_logits(cfg, w64, s, K_blk), "draft seq %d" % b)
+        assert_logits_close(zp_c[b], ospec.verify_logits(cfg, w64, s, list(rows[b])),
+                            "verify seq %d" % b)
