@@ -105,7 +105,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   const size_t X = D > F ? (D > QD ? D : QD) : (F > QD ? F : QD);
   const size_t r = (size_t)(lora_rank_eff(c) ? lora_rank_eff(c) : 16);
   const AttnPlan p = attn_plan(c, B, K, max_ctx);
-  const size_t parts = (size_t)B * c.n_kv_heads * p.n_qgroups * p.n_wave_splits * 64;
+  const size_t parts = (size_t)B * c.n_kv_heads * p.n_qgroups * p.n_wave_splits * 128;
   size_t off = 0;
   char* b = static_cast<char*>(base);
   auto take = [&](size_t bytes) {

@@ -9,17 +9,22 @@
 //   draft : j == 0 sees keys <= kv_len; j >= 1 sees keys <= kv_len + K - 1
 //   verify: row j sees keys <= kv_len + pos_offset + j (causal)
 //
-// Kernel shape.  One wave owns 64 query rows (4 MFMA tiles of 16: GQA heads of
-// one kv head times block rows) and one contiguous range of keys, walked 32
-// keys per step.  It computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16
-// keys x 32 channels read straight from a K page, B = the wave's Q held in
-// registers), so each lane ends with 8 consecutive keys of one query row; the
-// key-to-MFMA-row order is permuted so that those 8 keys are contiguous, which
-// makes P (bf16) the A operand of O += P V with no data exchange.  V pages are
-// stored channel-major ([hd][page_size]) so the B operand of P V is one 16-byte
-// load of 8 keys of one channel.  Softmax is online (base 2); the partial
-// (max, sum, O) of every wave goes to a workspace and a merge kernel combines
-// them.  All KV bytes are read once from HBM per pass.
+// Kernel shape.  A workgroup of 4 waves owns up to 64 query rows of one
+// (sequence, kv head) -- GQA heads times block rows, wave w the rows
+// 16w..16w+15 -- and one range of keys, walked in chunks of 64 keys (four
+// 16-token pages).  Each chunk's K and V are copied once from HBM into LDS with
+// coalesced 16-byte loads (double buffered: chunk c+1 is in flight while chunk c
+// is computed) and read by all four waves.  S^T = K Q^T runs on
+// v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 channels from LDS, B = the wave's
+// Q held in registers), so each lane ends with 8 consecutive keys of one query
+// row; the key-to-MFMA-row order is permuted so that those 8 keys are
+// contiguous, which makes P (bf16) the A operand of O += P V with no data
+// exchange.  V pages are stored channel-major ([hd][page_size]) in HBM and in
+// LDS ([hd][64 keys]), so the B operand of P V is one 16-byte LDS read of 8
+// keys of one channel.  Softmax is online (base 2).  With one key range per
+// row the kernel writes the normalised output; otherwise each workgroup writes
+// a partial (max, sum, O) and a merge kernel combines them.  Every KV byte is
+// read from HBM once per pass.
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -35,221 +40,343 @@ __device__ __forceinline__ int row_limit(int j, int kvl, int K, int pos_offset, 
   return kvl + pos_offset + j;
 }
 
-template <int HD>
-__global__ void __launch_bounds__(256)
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+// Counts above the 6-bit field wait for more than needed (always safe).
+template <int N0>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int N = N0 < 63 ? N0 : 63;
+  static_assert(N >= 0, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane DMA from global memory into LDS: lane i's bytes land at
+// lds_dst + 16*i (lds_dst wave-uniform).  Written as inline asm so that the
+// compiler does not serialise the ring of in-flight chunks with vmcnt(0)
+// waits; completion is awaited explicitly with wait_vmcnt + a barrier.  The
+// instruction has no destination register.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+  const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(off);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(src)
+               : "memory", "m0");
+}
+
+constexpr int kStages = 4;         // KV chunks of 64 keys resident in LDS
+constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
+
+// A workgroup of NW waves owns 16*NW query rows of one (sequence, kv head) --
+// wave w the rows 16w..16w+15 -- and one range of keys, walked in chunks of 64
+// keys.  Chunks stream HBM -> LDS with global_load_lds_dwordx4 (no registers),
+// kStages deep, and every wave reads each chunk from LDS.  LDS layouts
+// (16-byte chunks XOR-swizzled; the swizzle is applied by choosing which
+// source address each lane loads, since lane i of a DMA writes 16*i):
+//   K: [64 keys][HD]  row = one key,      chunk index ^ (key % (HD/8))
+//   V: [HD][64 keys]  row = one channel,  key-group index ^ (channel % 8)
+template <int HD, int NW>
+__global__ void __launch_bounds__(NW * 64)
 k_attention(AttnArgs a) {
-  constexpr int DS = HD / 32;  // 32-channel steps of S
-  constexpr int NT = HD / 16;  // 16-channel tiles of O
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  constexpr int DS = HD / 32;             // 32-channel MFMA steps of S
+  constexpr int NT = HD / 16;             // 16-channel tiles of O
+  constexpr int KROW = HD * 2;            // bytes per key row in LDS
+  constexpr int KCH = HD / 8;             // 16-byte chunks per key row
+  constexpr int KBYTES = 64 * KROW;       // K bytes per chunk (= V bytes)
+  constexpr int STAGE = 2 * KBYTES;
+  constexpr int NINSTR = STAGE / 1024;    // 1 KB DMA instructions per chunk
+  constexpr int IW = NINSTR / NW;         // per wave
+  static_assert(NINSTR % NW == 0, "chunk copy must split evenly over the waves");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  int* pages = reinterpret_cast<int*>(lds + kStages * STAGE);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int lr = l & 15, lg = l >> 4;
   const int bg = blockIdx.z, b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.K;
-  const int qg = blockIdx.y, qbase = qg * 64;
-  const int NWS = a.plan.n_wave_splits;
-  const int sigma = blockIdx.x * 4 + w;
+  const int QPW = 16 * NW;                 // query rows per workgroup
+  const int qg = blockIdx.y, qbase = qg * QPW;
+  const int split = blockIdx.x, n_split = a.plan.n_wave_splits;
   const int kvl = a.kv_len[b];
 
-  // key range of this wave
-  const int j_last = min(a.K - 1, (min(qbase + 63, QR - 1)) / G);
-  const int kv_end = (a.draft ? (j_last >= 1 ? kvl + a.K : kvl + 1)
-                              : kvl + a.pos_offset + j_last + 1);
-  const int lo = sigma * a.plan.split_len;
-  const int hi = (sigma == NWS - 1) ? kv_end : min(kv_end, lo + a.plan.split_len);
+  const int j_last = min(a.K - 1, min(qbase + QPW - 1, QR - 1) / G);
+  const int kv_end = a.draft ? (j_last >= 1 ? kvl + a.K : kvl + 1) : kvl + a.pos_offset + j_last + 1;
+  const int lo = split * a.plan.split_len;
+  int hi = (split == n_split - 1) ? kv_end : min(kv_end, lo + a.plan.split_len);
+  // a range longer than the LDS page cache (only if max_ctx understated the
+  // context) is cut short and flagged
+  const int hi_cap = (lo / a.ps + kMaxPagesLds - 1) * a.ps;
+  if (hi > hi_cap) {
+    if (tid == 0 && a.status) atomicOr(a.status + b, UNO_DEV_CAPACITY);
+    hi = hi_cap;
+  }
+  const int n_chunks = hi > lo ? (hi - lo + 63) / 64 : 0;
 
-  // Q as the B operand: lane holds Q[q = lr][ch = ds*32 + lg*8 .. +7]
-  AFrag qf[4][DS];
-  int lim[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int qr = qbase + mt * 16 + lr;
-    const bool ok = qr < QR;
-    const int j = ok ? qr / G : 0, hh = ok ? qr % G : 0;
-    lim[mt] = ok ? row_limit(j, kvl, a.K, a.pos_offset, a.draft) : -1;
-    const uint16_t* qp = a.q + ((size_t)(b * a.K + j) * a.Hq + g * G + hh) * HD + lg * 8;
+  // page ids of [lo, hi) -> LDS (-1 where outside the table or the pool)
+  const int p_lo = lo / a.ps;
+  const int n_pg = n_chunks > 0 ? (lo + n_chunks * 64 - 1) / a.ps - p_lo + 1 : 0;
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  int bad_page = 0;
+  for (int i = tid; i < n_pg && i < kMaxPagesLds; i += NW * 64) {
+    const int pi = p_lo + i;
+    int page = pi < a.max_pages ? pt[pi] : -1;
+    if (page >= a.n_pages) page = -1;
+    if (page < 0 && pi * a.ps < hi) bad_page = 1;
+    pages[i] = page;
+  }
+
+  // this wave's 16 query rows: Q as the B operand of S^T = K Q^T
+  const int qr = qbase + w * 16 + lr;
+  const bool q_ok = qr < QR;
+  const int qj = q_ok ? qr / G : 0, qh = q_ok ? qr % G : 0;
+  const int lim = q_ok ? row_limit(qj, kvl, a.K, a.pos_offset, a.draft) : -1;
+  AFrag qf[DS];
+  {
+    const uint16_t* qp = a.q + ((size_t)(b * a.K + qj) * a.Hq + g * G + qh) * HD + lg * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
-      qf[mt][ds].u = ok ? *reinterpret_cast<const uint4*>(qp + ds * 32) : make_uint4(0, 0, 0, 0);
+      qf[ds].u = q_ok ? *reinterpret_cast<const uint4*>(qp + ds * 32) : make_uint4(0, 0, 0, 0);
   }
+  // Q and the page list are complete before the first DMA, so that no wait for
+  // them is left inside the chunk loop (where it would drain the DMA ring)
+  wait_vmcnt<0>();
+  __syncthreads();   // page list visible
+
+  const size_t head_stride = (size_t)a.ps * HD;   // elements of one (page, head) block
+  // issue the DMA of chunk c into stage c % kStages (this wave's IW instructions)
+  auto issue = [&](int c) {
+    const int k0 = lo + c * 64;
+    unsigned char* K_ = lds + (c % kStages) * STAGE;
+#pragma unroll
+    for (int ii = 0; ii < IW; ++ii) {
+      const int ins = w * IW + ii;                 // 0 .. NINSTR-1
+      const uint16_t* src = a.k_layer;             // safe default for invalid lanes
+      if (ins < NINSTR / 2) {                      // K: 1024/KROW keys per instruction
+        const int key = ins * (1024 / KROW) + l / KCH;
+        const int ch = (l % KCH) ^ (key % KCH);
+        const int kabs = k0 + key;
+        const int page = kabs < hi ? pages[kabs / a.ps - p_lo] : -1;
+        if (page >= 0)
+          src = a.k_layer + ((size_t)page * a.Hkv + g) * head_stride + (size_t)(kabs % a.ps) * HD +
+                ch * 8;
+      } else {                                     // V: 8 channels per instruction
+        const int d = (ins - NINSTR / 2) * 8 + l / 8;
+        const int kg8 = (l % 8) ^ (d & 7);
+        const int kabs = k0 + kg8 * 8;
+        const int page = kabs < hi ? pages[kabs / a.ps - p_lo] : -1;
+        if (page >= 0)
+          src = a.v_layer + ((size_t)page * a.Hkv + g) * head_stride + (size_t)d * a.ps +
+                (kabs % a.ps);
+      }
+      lds_dma16(src, K_ + ins * 1024);
+    }
+  };
 
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  float m_run[4], l_run[4];
-  f32x4 o[4][NT];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    m_run[mt] = -INFINITY;
-    l_run[mt] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  const size_t head_stride = (size_t)a.ps * HD;
-  int bad_page = 0;
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = lo; k0 < hi; k0 += 32) {
-    // ---- K: MFMA row rho = lr of tile tt is physical key 8*(rho/4) + 4*tt + rho%4
-    AFrag kf[2][DS];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int key = k0 + 8 * (lr >> 2) + 4 * tt + (lr & 3);
-      bool ok = key < hi && key / a.ps < a.max_pages;
-      int page = ok ? pt[key / a.ps] : 0;
-      if (ok && (page < 0 || page >= a.n_pages)) { bad_page = 1; ok = false; }
-      const uint16_t* kp = a.k_layer + ((size_t)page * a.Hkv + g) * head_stride +
-                           (size_t)(key % a.ps) * HD + lg * 8;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        kf[tt][ds].u = ok ? *reinterpret_cast<const uint4*>(kp + ds * 32) : make_uint4(0, 0, 0, 0);
-    }
-    // ---- V: lane holds V[keys k0 + 8*lg .. +7][ch = nt*16 + lr]
-    AFrag vf[NT];
-    {
-      const int key = k0 + 8 * lg;
-      bool ok = key < hi && key / a.ps < a.max_pages;
-      int page = ok ? pt[key / a.ps] : 0;
-      if (ok && (page < 0 || page >= a.n_pages)) { bad_page = 1; ok = false; }
-      const uint16_t* vp = a.v_layer + ((size_t)page * a.Hkv + g) * head_stride + (key % a.ps);
-      const int n_ok = min(8, hi - key);  // keys of this group inside the range
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        uint4 u = ok ? *reinterpret_cast<const uint4*>(vp + (size_t)(nt * 16 + lr) * a.ps)
-                     : make_uint4(0, 0, 0, 0);
-        if (ok && n_ok < 8) {  // zero channels of keys past the range (may hold garbage)
-          uint32_t* e = reinterpret_cast<uint32_t*>(&u);
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-            if (c >= n_ok) e[c >> 1] &= (c & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  for (int c = 0; c < kStages - 1; ++c)
+    if (c < n_chunks) issue(c);
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const int ahead = min(kStages - 2, n_chunks - 1 - c);   // chunks issued after c
+    if (ahead >= 2) wait_vmcnt<2 * IW>();
+    else if (ahead == 1) wait_vmcnt<IW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    const int k0 = lo + c * 64;
+    unsigned char* K_ = lds + (c % kStages) * STAGE;
+    unsigned char* V_ = K_ + KBYTES;
+    // keys past the range or on a missing page: zero their V (K is masked)
+    bool clean = k0 + 64 <= hi;
+    for (int pp = 0; pp < 64 / a.ps && clean; ++pp) clean = pages[(k0 + pp * a.ps) / a.ps - p_lo] >= 0;
+    if (!clean) {
+      for (int e = tid; e < HD * 64; e += NW * 64) {
+        const int d = e / 64, key = e % 64, kabs = k0 + key;
+        const bool ok = kabs < hi && pages[kabs / a.ps - p_lo] >= 0;
+        if (!ok) {
+          const int kg8 = key / 8;
+          *reinterpret_cast<uint16_t*>(V_ + d * 128 + ((kg8 ^ (d & 7)) << 4) + (key % 8) * 2) = 0;
         }
-        vf[nt].u = u;
+      }
+      __syncthreads();
+    }
+    if (c + kStages - 1 < n_chunks) issue(c + kStages - 1);
+
+    // S^T tiles: MFMA row rho of key tile kt is key 32*(kt/2) + 8*(rho/4) + 4*(kt%2) + rho%4
+    f32x4 s4[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = 32 * (kt >> 1) + 8 * (lr >> 2) + 4 * (kt & 1) + (lr & 3);
+      s4[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const int ch = ds * 4 + lg;
+        AFrag kf;
+        kf.u = *reinterpret_cast<const uint4*>(K_ + key * KROW + ((ch ^ (key % KCH)) << 4));
+        s4[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qf[ds].v, s4[kt], 0, 0, 0);
       }
     }
-    // ---- S^T tiles and online softmax per query row
+    // lane holds keys 32h + 8*lg + c (h = kt/2, c = 4*(kt%2) + i) of query row lr
+    float p[2][8];
+    float rmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 s[2];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ds].v, qf[mt][ds].v, s[tt], 0, 0, 0);
+      for (int cc = 0; cc < 8; ++cc) {
+        const int key = k0 + 32 * h + 8 * lg + cc;
+        const float v = s4[2 * h + (cc >> 2)][cc & 3] * scale_log2;
+        p[h][cc] = (key <= lim && key < hi) ? v : -INFINITY;
+        rmax = fmaxf(rmax, p[h][cc]);
       }
-      float p[8];
-      float rmax = -INFINITY;
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+    const float m_new = fmaxf(m_run, rmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float rsum = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int key = k0 + 8 * lg + c;
-        const float v = s[c >> 2][c & 3] * scale_log2;
-        p[c] = (key <= lim[mt] && key < hi) ? v : -INFINITY;
-        rmax = fmaxf(rmax, p[c]);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        p[h][cc] = exp2f(p[h][cc] - m_use);
+        rsum += p[h][cc];
       }
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-      const float m_new = fmaxf(m_run[mt], rmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[mt] - m_use);
-      float rsum = 0.f;
+    rsum += __shfl_xor(rsum, 16, 64);
+    rsum += __shfl_xor(rsum, 32, 64);
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+    float al[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        p[c] = exp2f(p[c] - m_use);
-        rsum += p[c];
-      }
-      rsum += __shfl_xor(rsum, 16, 64);
-      rsum += __shfl_xor(rsum, 32, 64);
-      l_run[mt] = l_run[mt] * alpha + rsum;
-      m_run[mt] = m_new;
-      // O rows of this lane are q = 4*lg + i; their alphas live in lanes 4*lg + i
-      float al[4];
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
       AFrag pf;
       uint32_t* pe = reinterpret_cast<uint32_t*>(&pf.u);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pe[c] = pack_bf16x2(p[2 * c], p[2 * c + 1]);
+      for (int cc = 0; cc < 4; ++cc) pe[cc] = pack_bf16x2(p[h][2 * cc], p[h][2 * cc + 1]);
+      const int kg8 = 4 * h + lg;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[mt][nt][i] *= al[i];
-        o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.v, vf[nt].v, o[mt][nt], 0, 0, 0);
+        const int d = nt * 16 + lr;
+        AFrag vf;
+        vf.u = *reinterpret_cast<const uint4*>(V_ + d * 128 + ((kg8 ^ (d & 7)) << 4));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.v, vf.v, o[nt], 0, 0, 0);
       }
     }
   }
   if (bad_page && a.status) atomicOr(a.status + b, UNO_DEV_BAD_PAGE);
 
-  // ---- partials
-  const size_t part = ((size_t)bg * a.plan.n_qgroups + qg) * NWS + sigma;
-  float* po = a.part_o + part * 64 * HD;
-  float* pml = a.part_ml + part * 64 * 2;
+  // O rows of this lane: q = 4*lg + i of the wave's 16
+  if (n_split == 1) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(l_run, 4 * lg + i, 64);
+      const int r = qbase + w * 16 + 4 * lg + i;
+      if (r >= QR) continue;
+      const int j = r / G, hh = r % G;
+      uint16_t* op = a.out + ((size_t)(b * a.K + j) * a.Hq + g * G + hh) * HD;
+      const float inv = li > 0.f ? 1.0f / li : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) op[nt * 16 + lr] = f32_to_bf16(o[nt][i] * inv);
+    }
+  } else {
+    const size_t part = ((size_t)bg * a.plan.n_qgroups + qg) * n_split + split;
+    float* po = a.part_o + part * 128 * HD;
+    float* pml = a.part_ml + part * 128 * 2;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        po[(size_t)(mt * 16 + 4 * lg + i) * HD + nt * 16 + lr] = o[mt][nt][i];
+      for (int i = 0; i < 4; ++i) po[(size_t)(w * 16 + 4 * lg + i) * HD + nt * 16 + lr] = o[nt][i];
     if (lg == 0) {
-      pml[(mt * 16 + lr) * 2 + 0] = m_run[mt];
-      pml[(mt * 16 + lr) * 2 + 1] = l_run[mt];
+      pml[(w * 16 + lr) * 2 + 0] = m_run;
+      pml[(w * 16 + lr) * 2 + 1] = l_run;
     }
   }
 }
 
-// One workgroup (hd threads) per query row: combine the wave partials.
+// One workgroup (hd threads) per query row: combine the key-range partials.
 template <int HD>
 __global__ void __launch_bounds__(HD)
 k_attn_merge(AttnArgs a) {
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
+  const int QPW = 16 * a.plan.waves;
   const int qr = blockIdx.x;
-  const int qg = qr / 64, ql = qr % 64;
-  const int NWS = a.plan.n_wave_splits;
-  const size_t base = ((size_t)bg * a.plan.n_qgroups + qg) * NWS;
+  const int qg = qr / QPW, ql = qr % QPW;
+  const int NS = a.plan.n_wave_splits;
+  const size_t base = ((size_t)bg * a.plan.n_qgroups + qg) * NS;
   float M = -INFINITY;
-  for (int s = 0; s < NWS; ++s) M = fmaxf(M, a.part_ml[((base + s) * 64 + ql) * 2]);
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, a.part_ml[((base + s) * 128 + ql) * 2]);
   float L = 0.f, acc = 0.f;
   const int d = threadIdx.x;
-  for (int s = 0; s < NWS; ++s) {
-    const float* ml = a.part_ml + ((base + s) * 64 + ql) * 2;
+  for (int s = 0; s < NS; ++s) {
+    const float* ml = a.part_ml + ((base + s) * 128 + ql) * 2;
     if (ml[0] == -INFINITY) continue;
     const float f = exp2f(ml[0] - M);
     L += ml[1] * f;
-    acc += a.part_o[((base + s) * 64 + ql) * HD + d] * f;
+    acc += a.part_o[((base + s) * 128 + ql) * HD + d] * f;
   }
   const int j = qr / G, hh = qr % G;
-  a.out[((size_t)(b * a.K + j) * a.Hq + g * G + hh) * HD + d] = f32_to_bf16(acc / L);
+  a.out[((size_t)(b * a.K + j) * a.Hq + g * G + hh) * HD + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
 AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx) {
   AttnPlan p;
   const int G = c.n_q_heads / c.n_kv_heads;
-  p.n_qgroups = (G * K + 63) / 64;
+  const int tiles = (G * K + 15) / 16;
+  p.waves = 1;
+  while (p.waves < tiles && p.waves < 8) p.waves *= 2;
+  p.n_qgroups = (G * K + 16 * p.waves - 1) / (16 * p.waves);
   const long groups = (long)B * c.n_kv_heads * p.n_qgroups;
-  const int ctx = max_ctx > 1 ? max_ctx : 1;
-  long nws = (4096 + groups - 1) / groups;
-  const long by_len = (ctx + 63) / 64;
-  if (nws > by_len) nws = by_len;
-  if (nws < 1) nws = 1;
-  nws = (nws + 3) / 4 * 4;
-  p.n_wave_splits = (int)nws;
-  long sl = (ctx + nws - 1) / nws;
-  p.split_len = (int)((sl + 31) / 32 * 32);
+  const long ctx = max_ctx > 1 ? max_ctx : 1;
+  const long by_len = (ctx + 255) / 256;       // at least 4 chunks of 64 keys per range
+  long ns = (256 + groups - 1) / groups;       // one workgroup per CU
+  if (ns > by_len) ns = by_len;
+  const long max_len = (long)(kMaxPagesLds - 2) * c.page_size - 64;
+  const long by_lds = (ctx + max_len - 1) / max_len;
+  if (ns < by_lds) ns = by_lds;
+  if (ns < 1) ns = 1;
+  p.n_wave_splits = (int)ns;
+  const long sl = (ctx + ns - 1) / ns;
+  p.split_len = (int)((sl + 63) / 64 * 64);
   return p;
 }
 
 size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx) {
   const AttnPlan p = attn_plan(c, B, K, max_ctx);
-  const size_t parts = (size_t)B * c.n_kv_heads * p.n_qgroups * p.n_wave_splits * 64;
+  const size_t parts = (size_t)B * c.n_kv_heads * p.n_qgroups * p.n_wave_splits * 128;
   return align_up(parts * c.head_dim * sizeof(float), 256) + align_up(parts * 2 * sizeof(float), 256);
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.plan.n_wave_splits / 4, a.plan.n_qgroups, a.B * a.Hkv);
-  if (a.hd == 128) hipLaunchKernelGGL(k_attention<128>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_attention<64>, grid, dim3(256), 0, s, a);
+template <int HD>
+static hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.plan.n_wave_splits, a.plan.n_qgroups, a.B * a.Hkv);
+  const size_t lds = (size_t)kStages * 2 * 64 * HD * 2 + kMaxPagesLds * sizeof(int);
+  switch (a.plan.waves) {
+    case 1: hipLaunchKernelGGL((k_attention<HD, 1>), grid, dim3(64), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attention<HD, 2>), grid, dim3(128), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attention<HD, 4>), grid, dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_attention<HD, 8>), grid, dim3(512), lds, s, a); break;
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  return a.hd == 128 ? launch_attention_hd<128>(a, s) : launch_attention_hd<64>(a, s);
+}
+
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
+  if (a.plan.n_wave_splits == 1) return hipSuccess;   // the attention kernel wrote `out`
   const int G = a.Hq / a.Hkv;
   const dim3 mgrid(G * a.K, a.B * a.Hkv);
   if (a.hd == 128) hipLaunchKernelGGL(k_attn_merge<128>, mgrid, dim3(128), 0, s, a);

@@ -342,8 +342,16 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tiled kernel when the output has enough 256 x 128 tiles to spread over the
+// chip; narrow outputs (the LoRA A products, N = r..3r) keep the skinny kernel,
+// whose 8-wave K split gives them enough workgroups.
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  if (tiled_ok(a)) return launch_gemm_tiled(a, s);
+  if (tiled_ok(a)) {
+    int n_tiles = 0;
+    for (int i = 0; i < a.n_seg; ++i) n_tiles += a.seg[i].n / big::BN;
+    const int m_tiles = (a.M + big::BM - 1) / big::BM;
+    if (m_tiles * n_tiles >= 64) return launch_gemm_tiled(a, s);
+  }
   return launch_gemm_skinny(a, s);
 }
 

@@ -79,7 +79,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // group of 64 query rows and writes a partial (max, sum, output) that the merge
 // kernel combines.
 struct AttnPlan {
-  int n_qgroups, n_wave_splits, split_len;
+  int waves;            // waves per workgroup (16 query rows each)
+  int n_qgroups;        // groups of 16*waves query rows
+  int n_wave_splits;    // key ranges per query group
+  int split_len;        // keys per range (multiple of 64; the last runs to the end)
 };
 AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx);
 size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx);

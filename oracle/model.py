@@ -91,15 +91,18 @@ def attention(q, cache_k, cache_v, key_limit, n_kv_heads):
     group = Hq // n_kv_heads
     out = np.zeros_like(q)
     scale = 1.0 / np.sqrt(hd)
-    for r in range(R):
-        lim = int(key_limit[r]) + 1
-        for h in range(Hq):
-            g = h // group
-            s = cache_k[:lim, g, :] @ q[r, h] * scale
-            s = s - s.max()
-            p = np.exp(s)
-            p = p / p.sum()
-            out[r, h] = p @ cache_v[:lim, g, :]
+    top = int(np.max(key_limit)) + 1
+    for g in range(n_kv_heads):
+        kg = np.ascontiguousarray(cache_k[:top, g, :])     # keys of kv head g
+        vg = np.ascontiguousarray(cache_v[:top, g, :])
+        for r in range(R):
+            lim = int(key_limit[r]) + 1
+            for h in range(g * group, (g + 1) * group):
+                s = kg[:lim] @ q[r, h] * scale
+                s = s - s.max()
+                p = np.exp(s)
+                p = p / p.sum()
+                out[r, h] = p @ vg[:lim]
     return out
 
 

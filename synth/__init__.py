@@ -32,6 +32,11 @@ QWEN3_8B = dict(n_layers=36, d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=
 # the tiny shape with a LoRA rank that fills whole 64-wide K slices
 TINY_R64 = dict(TINY, lora_rank=64, lora_alpha=128.0)
 
+# small model with the 8B shape's head layout (head_dim 128, 4 q heads per kv head)
+SMALL_GQA = dict(n_layers=2, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                 d_ffn=1024, vocab=1024, mask_id=1023, rms_eps=1e-6, rope_theta=1000000.0,
+                 lora_rank=64, lora_alpha=128.0)
+
 # enumeration vocabulary toy: vocab 8 (mask id 7)
 VOCAB8 = dict(n_layers=1, d_model=32, n_q_heads=2, n_kv_heads=1, head_dim=16,
               d_ffn=64, vocab=8, mask_id=7, rms_eps=1e-6, rope_theta=10000.0,
@@ -221,3 +226,46 @@ def fill_kv_device(k_pages, v_pages, seed, std=1.0):
         for which, t in ((0, k_pages), (1, v_pages)):
             gen.manual_seed(int(seed) * 1000003 + li * 2 + which)
             t[li].normal_(0.0, std, generator=gen)
+
+
+class LazyF64Layers:
+    """fp64 numpy view of bf16 layer tensors, converted on every access (keeps
+    host memory at one layer's worth for the 8B shape)."""
+
+    def __init__(self, layers):
+        self._layers = layers
+
+    def __len__(self):
+        return len(self._layers)
+
+    def __iter__(self):
+        for lw in self._layers:
+            yield _LazyLayer(lw)
+
+
+class _LazyLayer:
+    def __init__(self, lw):
+        self._lw = lw
+
+    def __getitem__(self, k):
+        v = self._lw[k]
+        if isinstance(v, dict):
+            return _LazyDict(v)
+        return v.to(torch.float64).numpy()
+
+
+class _LazyDict:
+    def __init__(self, d):
+        self._d = d
+
+    def get(self, k, default=None):
+        v = self._d.get(k)
+        return default if v is None else v.to(torch.float64).numpy()
+
+
+def to_f64_lazy(wts):
+    """Like ``to_f64`` but layers convert on access (large models)."""
+    return {"embed": wts["embed"].to(torch.float64).numpy(),
+            "lm_head": wts["lm_head"].to(torch.float64).numpy(),
+            "final_norm": wts["final_norm"].to(torch.float64).numpy(),
+            "layers": LazyF64Layers(wts["layers"])}

@@ -1,0 +1,100 @@
+"""Full-size parity on the Qwen3-8B shape (36 layers, d_model 4096, 32/8 heads
+x 128, SwiGLU 12288, vocab 151936, LoRA r128 alpha 256), on sampled outputs
+the oracle can compute: one draft and one verify pass (K = 16) of a sequence
+whose committed context is seeded synthetic K/V.
+
+* batch 1, context 1023 (the batch-1 workload);
+* batch 64, context 9216 (the launch configuration of the benchmark): every
+  sequence runs on the GPU, sequence 37 is recomputed by the oracle.
+
+All 2 x 16 x 151936 logits of the sampled sequence are compared (2e-2 abs +
+1e-2 rel), then the sampler is checked bit-exact on the oracle's fp32 logits."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import spec as ospec
+
+from gpu_util import assert_logits_close, gpu_or_fail, load_kv_logical, progress
+
+pytestmark = pytest.mark.gpu
+
+K = 16
+
+
+@pytest.fixture(scope="module")
+def big():
+    U = gpu_or_fail()
+    cfg = synth.QWEN3_8B
+    progress("8B: generating weights on the host")
+    wts = synth.make_weights(cfg, seed=0)
+    progress("8B: uploading")
+    model = U.Model(cfg, wts)
+    torch.cuda.synchronize()
+    return U, cfg, wts, synth.to_f64_lazy(wts), model
+
+
+def _run(big, B, ctx, b_check):
+    U, cfg, wts, w64, model = big
+    cap = ctx + 2 * K + 8
+    n_pages = B * ((cap + 15) // 16)
+    kv = U.PagedKV(cfg, B, cap, page_order=torch.randperm(
+        n_pages, generator=torch.Generator().manual_seed(ctx)))
+    if B > 1:
+        synth.fill_kv_device(kv.k_pages, kv.v_pages, seed=ctx)
+    k, v = synth.kv_values(cfg, ctx, seed=21, seq=b_check)
+    load_kv_logical(kv, b_check, k, v)
+    kv.kv_len.fill_(ctx)
+    toks = synth.random_tokens(ctx + 1, cfg["vocab"], 300, (B, ctx + 1))
+    seq = ospec.Sequence(cfg, toks[b_check], capacity=cap)
+    for li in range(cfg["n_layers"]):
+        seq.cache.k[li][:ctx] = k[li].double().numpy()
+        seq.cache.v[li][:ctx] = v[li].double().numpy()
+    seq.kv_len = ctx
+    del k, v
+    ws = U.alloc_workspace(U.workspace_bytes(model, B, K, cap))
+    V = cfg["vocab"]
+    zq = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
+    zp = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
+    d = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    anchor = torch.from_numpy(toks[:, -1].copy()).cuda()
+    U.draft_block(model, kv, anchor, K, cap, 1.0, 0, torch.zeros(B, dtype=torch.uint64).cuda(),
+                  zq, d, ws, status)
+    progress("8B b%d: GPU draft done; oracle draft pass" % B)
+    zq_ref = ospec.draft_logits(cfg, w64, seq, K)
+    zq_g = zq[b_check].cpu().numpy()
+    err_q = assert_logits_close(zq_g, zq_ref, "8B b%d draft logits" % B)
+    drafts = ospec.draft_sample(zq_ref.astype(np.float32), 1.0, ospec.PhiloxDraws(0, b_check, 0))
+    rows = np.array(d.cpu().numpy(), dtype=np.int32)     # other sequences: any tokens
+    rows[b_check] = drafts
+    U.verify_block(model, kv, torch.from_numpy(rows).cuda(), cap, 1, zp, ws, status)
+    progress("8B b%d: GPU verify done; oracle verify pass" % B)
+    zp_ref = ospec.verify_logits(cfg, w64, seq, drafts)
+    err_p = assert_logits_close(zp[b_check].cpu().numpy(), zp_ref, "8B b%d verify logits" % B)
+    assert (status.cpu().numpy() == 0).all()
+    # sampler, bit-exact on the oracle's own fp32 logits
+    zq32, zp32 = zq_ref.astype(np.float32), zp_ref.astype(np.float32)
+    a_ref, comm_ref, e_ref = ospec.spec_accept(zq32, zp32, drafts, 1.0,
+                                               ospec.PhiloxDraws(0, 0, 0))
+    a = torch.empty(1, dtype=torch.int32, device="cuda")
+    c = torch.empty((1, K + 1), dtype=torch.int32, device="cuda")
+    e = torch.empty(1, dtype=torch.int32, device="cuda")
+    U.spec_accept(torch.from_numpy(zq32[None]).cuda(), torch.from_numpy(zp32[None]).cuda(),
+                  torch.tensor([drafts], dtype=torch.int32, device="cuda"), 1.0, 0,
+                  torch.zeros(1, dtype=torch.uint64).cuda(), a, c, e,
+                  U.alloc_workspace(U.spec_accept_workspace_bytes(1, K)))
+    assert (int(a.item()), int(e.item())) == (a_ref, e_ref)
+    progress("8B b%d ctx %d: max logit error draft %.2e verify %.2e; a = %d" % (
+        B, ctx, err_q, err_p, a_ref))
+    del kv, ws, zq, zp
+    torch.cuda.empty_cache()
+
+
+def test_8b_batch1_context_1k(big):
+    _run(big, 1, 1023, 0)
+
+
+def test_8b_batch64_context_9216(big):
+    _run(big, 64, 9216, 37)
