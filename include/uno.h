@@ -62,7 +62,7 @@ enum {
 
 /* Model shape.  Supported: head_dim 64 or 128; n_q_heads a multiple of
  * n_kv_heads; d_model, d_ffn, n_q_heads*head_dim multiples of 64; page_size a
- * multiple of 16; lora_rank a multiple of 16 and <= 256; vocab a multiple of
+ * power of two >= 16; lora_rank a multiple of 16 and <= 256; vocab a multiple of
  * 16 and <= 2^20. */
 typedef struct uno_config {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, mask_id;

@@ -59,7 +59,7 @@ int check_config(const uno_config* c) {
   if (c->d_model % 64 || c->d_ffn % 64 || (c->n_q_heads * c->head_dim) % 64)
     return UNO_ERR_UNSUPPORTED;
   if (c->vocab % 16 || c->vocab > (1 << 20)) return UNO_ERR_UNSUPPORTED;
-  if (c->page_size % 16) return UNO_ERR_UNSUPPORTED;
+  if (c->page_size & (c->page_size - 1)) return UNO_ERR_UNSUPPORTED;   // power of two >= 16
   if (c->lora_mask & ~0x7Fu) return UNO_ERR_INVALID_ARG;
   if (c->lora_mask) {
     if (c->lora_rank < 16 || c->lora_rank % 16 || c->lora_rank > 256) return UNO_ERR_UNSUPPORTED;
@@ -86,7 +86,8 @@ struct PassWs {
   float* h;          // [R, D]
   uint16_t* xn;      // [R, max(D, F, Hq*hd)]
   float* qkv;        // [R, (Hq+2Hkv)*hd]
-  uint16_t* qb;      // [R, Hq*hd]
+  uint16_t* qb;      // [R, Hq*hd]  q (bf16 high part)
+  uint16_t* qlo;     // [R, Hq*hd]  q - high part (bf16)
   uint16_t* ao;      // [R, Hq*hd]
   float* gu;         // [R, 2F]
   uint16_t* act;     // [R, F]
@@ -117,6 +118,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.xn = reinterpret_cast<uint16_t*>(take(R * X * 2));
   w.qkv = reinterpret_cast<float*>(take(R * QKV * 4));
   w.qb = reinterpret_cast<uint16_t*>(take(R * QD * 2));
+  w.qlo = reinterpret_cast<uint16_t*>(take(R * QD * 2));
   w.ao = reinterpret_cast<uint16_t*>(take(R * QD * 2));
   w.gu = reinterpret_cast<float*>(take(R * 2 * F * 4));
   w.act = reinterpret_cast<uint16_t*>(take(R * F * 2));
@@ -195,16 +197,18 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
     }
     UNO_TRY(launch_rope_kv_write(c, W.qkv, W.cs, *kv, li, B, K, draft ? 0 : pos_offset, W.qb,
-                                 status, s));
+                                 W.qlo, status, s));
     {
       AttnArgs a = {};
       a.q = W.qb;
+      a.q_lo = W.qlo;
       a.k_layer = static_cast<const uint16_t*>(kv->k_pages) + (size_t)li * layer_elems;
       a.v_layer = static_cast<const uint16_t*>(kv->v_pages) + (size_t)li * layer_elems;
       a.page_table = kv->page_table; a.kv_len = kv->kv_len;
       a.max_pages = kv->max_pages_per_seq; a.n_pages = kv->n_pages;
       a.B = B; a.K = K; a.pos_offset = draft ? 0 : pos_offset; a.draft = draft ? 1 : 0;
       a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.ps = c.page_size; a.plan = plan;
+      a.ps_shift = __builtin_ctz((unsigned)c.page_size);
       a.part_o = W.part_o; a.part_ml = W.part_ml; a.out = W.ao; a.status = status;
       UNO_TRY(timed(UNO_TIME_ATTENTION, s, [&] { return launch_attention(a, s); }));
       UNO_TRY(launch_attn_merge(a, s));

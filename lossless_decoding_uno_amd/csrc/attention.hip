@@ -18,9 +18,11 @@
 // v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 channels from LDS, B = the wave's
 // Q held in registers), so each lane ends with 8 consecutive keys of one query
 // row; the key-to-MFMA-row order is permuted so that those 8 keys are
-// contiguous, which makes P (bf16) the A operand of O += P V with no data
-// exchange.  V pages are stored channel-major ([hd][page_size]) in HBM and in
-// LDS ([hd][64 keys]), so the B operand of P V is one 16-byte LDS read of 8
+// contiguous, which makes P the A operand of O += P V with no data exchange.
+// q and P enter their products as a high and a low bf16 part (two MFMAs each),
+// so the only bf16 rounding left in the attention is that of the cached K/V;
+// the extra MFMAs fit in the slack of this HBM-bound kernel.  V pages are
+// stored channel-major ([hd][page_size]) in HBM and in LDS ([hd][64 keys]), so the B operand of P V is one 16-byte LDS read of 8
 // keys of one channel.  Softmax is online (base 2).  With one key range per
 // row the kernel writes the normalised output; otherwise each workgroup writes
 // a partial (max, sum, O) and a merge kernel combines them.  Every KV byte is
@@ -106,7 +108,8 @@ k_attention(AttnArgs a) {
   int hi = (split == n_split - 1) ? kv_end : min(kv_end, lo + a.plan.split_len);
   // a range longer than the LDS page cache (only if max_ctx understated the
   // context) is cut short and flagged
-  const int hi_cap = (lo / a.ps + kMaxPagesLds - 1) * a.ps;
+  // (the last 64-key chunk may run 63 keys past hi; its pages must be cached too)
+  const int hi_cap = (((lo >> a.ps_shift) + kMaxPagesLds) << a.ps_shift) - 128;
   if (hi > hi_cap) {
     if (tid == 0 && a.status) atomicOr(a.status + b, UNO_DEV_CAPACITY);
     hi = hi_cap;
@@ -114,61 +117,82 @@ k_attention(AttnArgs a) {
   const int n_chunks = hi > lo ? (hi - lo + 63) / 64 : 0;
 
   // page ids of [lo, hi) -> LDS (-1 where outside the table or the pool)
-  const int p_lo = lo / a.ps;
-  const int n_pg = n_chunks > 0 ? (lo + n_chunks * 64 - 1) / a.ps - p_lo + 1 : 0;
+  const int psh = a.ps_shift, pmask = (1 << psh) - 1;
+  const int p_lo = lo >> psh;
+  const int n_pg = n_chunks > 0 ? ((lo + n_chunks * 64 - 1) >> psh) - p_lo + 1 : 0;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  int bad_page = 0;
+  int bad_page = 0, missing = 0;
   for (int i = tid; i < n_pg && i < kMaxPagesLds; i += NW * 64) {
     const int pi = p_lo + i;
     int page = pi < a.max_pages ? pt[pi] : -1;
     if (page >= a.n_pages) page = -1;
-    if (page < 0 && pi * a.ps < hi) bad_page = 1;
+    if (page < 0 && (pi << psh) < hi) bad_page = 1;
+    missing |= page < 0;
     pages[i] = page;
   }
+  // any page of the range missing (a short table, or the range's last chunk
+  // running past the table): chunks must then be checked one by one
+  const int any_missing = __syncthreads_or(missing);
 
   // this wave's 16 query rows: Q as the B operand of S^T = K Q^T
   const int qr = qbase + w * 16 + lr;
   const bool q_ok = qr < QR;
   const int qj = q_ok ? qr / G : 0, qh = q_ok ? qr % G : 0;
   const int lim = q_ok ? row_limit(qj, kvl, a.K, a.pos_offset, a.draft) : -1;
-  AFrag qf[DS];
+  AFrag qf[DS], qfl[DS];    // q = high + low bf16 parts (scores keep ~16 bits of q)
   {
-    const uint16_t* qp = a.q + ((size_t)(b * a.K + qj) * a.Hq + g * G + qh) * HD + lg * 8;
+    const size_t qo = ((size_t)(b * a.K + qj) * a.Hq + g * G + qh) * HD + lg * 8;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[ds].u = q_ok ? *reinterpret_cast<const uint4*>(qp + ds * 32) : make_uint4(0, 0, 0, 0);
+    for (int ds = 0; ds < DS; ++ds) {
+      qf[ds].u = q_ok ? *reinterpret_cast<const uint4*>(a.q + qo + ds * 32) : make_uint4(0, 0, 0, 0);
+      qfl[ds].u = q_ok ? *reinterpret_cast<const uint4*>(a.q_lo + qo + ds * 32) : make_uint4(0, 0, 0, 0);
+    }
   }
   // Q and the page list are complete before the first DMA, so that no wait for
   // them is left inside the chunk loop (where it would drain the DMA ring)
   wait_vmcnt<0>();
   __syncthreads();   // page list visible
 
-  const size_t head_stride = (size_t)a.ps * HD;   // elements of one (page, head) block
+  const size_t head_stride = (size_t)HD << psh;   // elements of one (page, head) block
+  const size_t page_stride = head_stride * a.Hkv;  // elements of one page (all heads)
+  // Per lane and DMA instruction, the key it copies (offset in the chunk) and
+  // its element offset inside the page are fixed; per chunk only the page id
+  // changes.  Instructions 0..NINSTR/2-1 of a chunk copy K, the rest V (a wave
+  // may own instructions of both kinds when the workgroup has one wave).
+  const uint16_t* kbase = a.k_layer + (size_t)g * head_stride;
+  const uint16_t* vbase = a.v_layer + (size_t)g * head_stride;
+  int koff[IW];     // key offset in the chunk, 0..63
+  int eoff[IW];     // element offset inside the (page, head) block
+#pragma unroll
+  for (int ii = 0; ii < IW; ++ii) {
+    const int ins = w * IW + ii;
+    if (ins < NINSTR / 2) {                      // K: 1024/KROW keys per instruction
+      const int key = ins * (1024 / KROW) + l / KCH;
+      const int ch = (l % KCH) ^ (key % KCH);
+      koff[ii] = key;
+      eoff[ii] = (key & pmask) * HD + ch * 8;
+    } else {                                     // V: 8 channels per instruction
+      const int d = (ins - NINSTR / 2) * 8 + l / 8;
+      const int kg8 = (l % 8) ^ (d & 7);
+      koff[ii] = kg8 * 8;
+      eoff[ii] = (d << psh) + ((kg8 * 8) & pmask);
+    }
+  }
   // issue the DMA of chunk c into stage c % kStages (this wave's IW instructions)
   auto issue = [&](int c) {
     const int k0 = lo + c * 64;
+    const int k0_in_page = (k0 & pmask) & ~63;    // nonzero only for pages > 64 keys
     unsigned char* K_ = lds + (c % kStages) * STAGE;
 #pragma unroll
     for (int ii = 0; ii < IW; ++ii) {
-      const int ins = w * IW + ii;                 // 0 .. NINSTR-1
-      const uint16_t* src = a.k_layer;             // safe default for invalid lanes
-      if (ins < NINSTR / 2) {                      // K: 1024/KROW keys per instruction
-        const int key = ins * (1024 / KROW) + l / KCH;
-        const int ch = (l % KCH) ^ (key % KCH);
-        const int kabs = k0 + key;
-        const int page = kabs < hi ? pages[kabs / a.ps - p_lo] : -1;
-        if (page >= 0)
-          src = a.k_layer + ((size_t)page * a.Hkv + g) * head_stride + (size_t)(kabs % a.ps) * HD +
-                ch * 8;
-      } else {                                     // V: 8 channels per instruction
-        const int d = (ins - NINSTR / 2) * 8 + l / 8;
-        const int kg8 = (l % 8) ^ (d & 7);
-        const int kabs = k0 + kg8 * 8;
-        const int page = kabs < hi ? pages[kabs / a.ps - p_lo] : -1;
-        if (page >= 0)
-          src = a.v_layer + ((size_t)page * a.Hkv + g) * head_stride + (size_t)d * a.ps +
-                (kabs % a.ps);
-      }
+      const int ins = w * IW + ii;
+      const bool is_k = ins < NINSTR / 2;
+      const int kabs = k0 + koff[ii];
+      const int pidx = (kabs >> psh) - p_lo;     // < n_pg for every key of the chunk
+      const int page = (pidx < n_pg && (!any_missing || kabs < hi)) ? pages[pidx] : -1;
+      const uint16_t* src = page >= 0 ? (is_k ? kbase : vbase) + (size_t)page * page_stride +
+                                            eoff[ii] + k0_in_page * (is_k ? HD : 1)
+                                      : a.k_layer;   // safe address; zeroed below
       lds_dma16(src, K_ + ins * 1024);
     }
   };
@@ -194,11 +218,13 @@ k_attention(AttnArgs a) {
     unsigned char* V_ = K_ + KBYTES;
     // keys past the range or on a missing page: zero their V (K is masked)
     bool clean = k0 + 64 <= hi;
-    for (int pp = 0; pp < 64 / a.ps && clean; ++pp) clean = pages[(k0 + pp * a.ps) / a.ps - p_lo] >= 0;
+    if (any_missing)
+      for (int pp = 0; pp < (64 >> psh) + 1 && clean; ++pp)
+        clean = pages[min((k0 + (pp << psh)) >> psh, (k0 + 63) >> psh) - p_lo] >= 0;
     if (!clean) {
       for (int e = tid; e < HD * 64; e += NW * 64) {
         const int d = e / 64, key = e % 64, kabs = k0 + key;
-        const bool ok = kabs < hi && pages[kabs / a.ps - p_lo] >= 0;
+        const bool ok = kabs < hi && pages[(kabs >> psh) - p_lo] >= 0;
         if (!ok) {
           const int kg8 = key / 8;
           *reinterpret_cast<uint16_t*>(V_ + d * 128 + ((kg8 ^ (d & 7)) << 4) + (key % 8) * 2) = 0;
@@ -220,6 +246,7 @@ k_attention(AttnArgs a) {
         AFrag kf;
         kf.u = *reinterpret_cast<const uint4*>(K_ + key * KROW + ((ch ^ (key % KCH)) << 4));
         s4[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qf[ds].v, s4[kt], 0, 0, 0);
+        s4[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qfl[ds].v, s4[kt], 0, 0, 0);
       }
     }
     // lane holds keys 32h + 8*lg + c (h = kt/2, c = 4*(kt%2) + i) of query row lr
@@ -236,34 +263,49 @@ k_attention(AttnArgs a) {
       }
     rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
     rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-    const float m_new = fmaxf(m_run, rmax);
+    // The reference point m_run moves only when a row's maximum exceeds it by
+    // more than 8 (in log2 units): weights then stay <= 2^8, and O and l are
+    // rescaled by exp2(old - new) only on those rare chunks (softmax is
+    // invariant to the reference point).  m_run starts at -inf, so the first
+    // chunk with a visible key sets it.
+    const bool move = rmax > m_run + 8.0f;
+    const float m_new = move ? rmax : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
     float rsum = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        p[h][cc] = exp2f(p[h][cc] - m_use);
+        p[h][cc] = __builtin_amdgcn_exp2f(p[h][cc] - m_use);
         rsum += p[h][cc];
       }
     rsum += __shfl_xor(rsum, 16, 64);
     rsum += __shfl_xor(rsum, 32, 64);
     l_run = l_run * alpha + rsum;
     m_run = m_new;
-    float al[4];
+    if (__any(move)) {
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
+        for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      AFrag pf;
+      // P = high + low bf16 parts, so the softmax weights keep ~16 bits
+      AFrag pf, pfl;
       uint32_t* pe = reinterpret_cast<uint32_t*>(&pf.u);
+      uint32_t* pl = reinterpret_cast<uint32_t*>(&pfl.u);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) pe[cc] = pack_bf16x2(p[h][2 * cc], p[h][2 * cc + 1]);
+      for (int cc = 0; cc < 4; ++cc) {
+        const float x0 = p[h][2 * cc], x1 = p[h][2 * cc + 1];
+        const uint32_t hi = pack_bf16x2(x0, x1);
+        pe[cc] = hi;
+        pl[cc] = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
+      }
       const int kg8 = 4 * h + lg;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -271,6 +313,7 @@ k_attention(AttnArgs a) {
         AFrag vf;
         vf.u = *reinterpret_cast<const uint4*>(V_ + d * 128 + ((kg8 ^ (d & 7)) << 4));
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.v, vf.v, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfl.v, vf.v, o[nt], 0, 0, 0);
       }
     }
   }

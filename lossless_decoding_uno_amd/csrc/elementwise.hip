@@ -119,7 +119,8 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
                 int Hq, int Hkv, int hd, int pos_offset, const int32_t* __restrict__ kv_len,
                 const int32_t* __restrict__ page_table, int max_pages, int64_t n_pages,
                 int ps, uint16_t* __restrict__ k_layer, uint16_t* __restrict__ v_layer,
-                uint16_t* __restrict__ q_out, int32_t* __restrict__ status) {
+                uint16_t* __restrict__ q_out, uint16_t* __restrict__ q_lo,
+                int32_t* __restrict__ status) {
   const int r = blockIdx.x;
   const int b = r / K, j = r % K;
   const int half = hd / 2;
@@ -147,9 +148,13 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
     const float y1 = x1 * a.x - x2 * a.y;
     const float y2 = x2 * a.x + x1 * a.y;
     if (head < Hq) {
-      uint16_t* q = q_out + (size_t)r * Hq * hd + head * hd;
-      q[i] = f32_to_bf16(y1);
-      q[i + half] = f32_to_bf16(y2);
+      // q = hi + lo, both bf16: the attention scores use both parts
+      const size_t o = (size_t)r * Hq * hd + head * hd;
+      const uint16_t h1 = f32_to_bf16(y1), h2 = f32_to_bf16(y2);
+      q_out[o + i] = h1;
+      q_out[o + i + half] = h2;
+      q_lo[o + i] = f32_to_bf16(y1 - bf16_to_f32(h1));
+      q_lo[o + i + half] = f32_to_bf16(y2 - bf16_to_f32(h2));
     } else if (page >= 0) {
       const int g = head - Hq;
       uint16_t* kp = k_layer + (((size_t)page * Hkv + g) * ps + slot) * hd;
@@ -168,14 +173,15 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
 
 hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
                                 const uno_kv& kv, int layer, int B, int K, int pos_offset,
-                                bf16_raw_t* q_out, int32_t* status, hipStream_t s) {
+                                bf16_raw_t* q_out, bf16_raw_t* q_lo, int32_t* status,
+                                hipStream_t s) {
   const size_t layer_elems =
       (size_t)kv.n_pages * c.n_kv_heads * c.page_size * c.head_dim;
   uint16_t* kl = static_cast<uint16_t*>(kv.k_pages) + (size_t)layer * layer_elems;
   uint16_t* vl = static_cast<uint16_t*>(kv.v_pages) + (size_t)layer * layer_elems;
   hipLaunchKernelGGL(k_rope_kv_write, dim3(B * K), dim3(256), 0, s, qkv, cs, K, c.n_q_heads,
                      c.n_kv_heads, c.head_dim, pos_offset, kv.kv_len, kv.page_table,
-                     kv.max_pages_per_seq, kv.n_pages, c.page_size, kl, vl, q_out, status);
+                     kv.max_pages_per_seq, kv.n_pages, c.page_size, kl, vl, q_out, q_lo, status);
   return hipGetLastError();
 }
 

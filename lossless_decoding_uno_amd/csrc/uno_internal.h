@@ -36,11 +36,13 @@ hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float
 // absolute positions kv_len[b] + pos_offset + j.
 hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
                              float theta, float2* cs, hipStream_t s);
-// RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]), q -> bf16
-// [R, Hq*hd], k/v -> paged cache at the rows' positions.
+// RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]); q -> two
+// bf16 planes [R, Hq*hd] (hi and the rounding remainder lo), k/v (bf16) ->
+// paged cache at the rows' positions.
 hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
                                 const uno_kv& kv, int layer, int B, int K, int pos_offset,
-                                bf16_raw_t* q_out, int32_t* status, hipStream_t s);
+                                bf16_raw_t* q_out, bf16_raw_t* q_lo, int32_t* status,
+                                hipStream_t s);
 // act = silu(g) * u, gu fp32 [R, 2F] (gate then up) -> bf16 [R, F]
 hipError_t launch_silu_mul(const float* gu, int R, int F, bf16_raw_t* act, hipStream_t s);
 hipError_t launch_kv_commit(int32_t* kv_len, const int32_t* accept_len, int B, int K,
@@ -87,7 +89,8 @@ struct AttnPlan {
 AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx);
 size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx);
 struct AttnArgs {
-  const uint16_t* q;          // [R, Hq, hd] bf16, post-RoPE
+  const uint16_t* q;          // [R, Hq, hd] bf16, post-RoPE (high part)
+  const uint16_t* q_lo;       // [R, Hq, hd] bf16, q - high part
   const uint16_t* k_layer;    // this layer's K pages
   const uint16_t* v_layer;    // this layer's V pages (transposed inside a page)
   const int32_t* page_table;
@@ -95,7 +98,7 @@ struct AttnArgs {
   int max_pages;
   int64_t n_pages;
   int B, K, pos_offset, draft;
-  int Hq, Hkv, hd, ps;
+  int Hq, Hkv, hd, ps, ps_shift;   // page size and its log2
   AttnPlan plan;
   float* part_o;              // [B*Hkv, n_qgroups, n_wave_splits, 64, hd]
   float* part_ml;             // [B*Hkv, n_qgroups, n_wave_splits, 64, 2]

@@ -25,6 +25,18 @@ Everything here is fp64 numpy on logical (unpacked) weight layouts:
   v [Hkv*hd, D], o [D, Hq*hd], gate [F, D], up [F, D], down [D, F];
   LoRA: lora_a[p] [r, in_p], lora_b[p] [out_p, r] for p in PROJ.
 
+Precision.  By default every step is fp64 (the exact reference).  With
+``act_round=bf16_round`` the forward additionally rounds, to bfloat16
+(round-to-nearest-even), the activations a bf16 matrix-core implementation
+must hand to its bf16 products and its bf16 KV cache: the normalised inputs of
+every linear, the LoRA intermediate s*g*(x A^T), k and v (the cache entries),
+the attention output and the SwiGLU product.  Queries and softmax weights stay
+exact: an implementation can keep them at about twice bf16 precision by
+splitting them into two bf16 parts.  The pages fix no
+precision; this mode is the plainest model of "the same computation with bf16
+activations" and serves the deep full-size checks, where exact-arithmetic
+deviations of bf16 activations compound with depth.
+
 Parity: logit VALUES are "parity unpinned" against the pages (none are printed).
 Structural pins in tests/test_oracle_model.py: LoRA linear == dense
 x (W + s B A)^T; B = 0 makes the LoRA linear the plain linear; the cached block
@@ -34,6 +46,18 @@ agree with independent torch CPU routines.
 import numpy as np
 
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def bf16_round(x):
+    """Round to the nearest bfloat16 (ties to even) and return fp64.
+
+    bfloat16 keeps the top 16 bits of an IEEE fp32; the fp64 input is first
+    rounded to fp32 (RNE), then the low 16 bits are rounded away with ties to
+    even.  Inputs are finite."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def rms_norm(h, gain, eps):
@@ -57,11 +81,17 @@ def rope(x, pos, theta):
     return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
 
 
-def lora_linear(x, w, a, b, scale, gate):
-    """y = x W^T + gate_row * scale * (x A^T) B^T; a/b None means no LoRA."""
+def lora_linear(x, w, a, b, scale, gate, act_round=None):
+    """y = x W^T + gate_row * scale * (x A^T) B^T; a/b None means no LoRA.
+
+    With ``act_round`` the intermediate gate*scale*(x A^T) is rounded before
+    its product with B (the low-rank path's second product)."""
     y = x @ w.T
     if a is not None and b is not None:
-        y = y + (gate[:, None] * scale) * ((x @ a.T) @ b.T)
+        t = (gate[:, None] * scale) * (x @ a.T)
+        if act_round is not None:
+            t = act_round(t)
+        y = y + t @ b.T
     return y
 
 
@@ -106,13 +136,15 @@ def attention(q, cache_k, cache_v, key_limit, n_kv_heads):
     return out
 
 
-def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True):
+def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=None):
     """One pass over a block of rows of ONE sequence.
 
     Writes the block's K/V (after RoPE) into ``cache`` at ``pos`` before the
     attention of each layer, then attends row r to cache keys 0..key_limit[r].
-    Returns fp64 logits [R, V].
+    Returns fp64 logits [R, V].  ``act_round`` (e.g. ``bf16_round``) selects the
+    bf16-activation mode described in the module header.
     """
+    rd = act_round if act_round is not None else (lambda v: v)
     ids = np.asarray(ids)
     pos = np.asarray(pos)
     gate = np.asarray(gate, dtype=np.float64)
@@ -125,21 +157,21 @@ def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True):
         def lin(x, p):
             a = lw["lora_a"].get(p) if lora else None
             b = lw["lora_b"].get(p) if lora else None
-            return lora_linear(x, lw[p], a, b, scale, gate)
+            return lora_linear(x, lw[p], a, b, scale, gate, act_round)
 
-        x = rms_norm(h, lw["attn_norm"], eps)
+        x = rd(rms_norm(h, lw["attn_norm"], eps))
         q = lin(x, "q").reshape(R, Hq, hd)
         k = lin(x, "k").reshape(R, Hkv, hd)
-        v = lin(x, "v").reshape(R, Hkv, hd)
+        v = rd(lin(x, "v").reshape(R, Hkv, hd))
         q = rope(q, pos, cfg["rope_theta"])
-        k = rope(k, pos, cfg["rope_theta"])
+        k = rd(rope(k, pos, cfg["rope_theta"]))
         cache.k[li][pos] = k
         cache.v[li][pos] = v
-        o = attention(q, cache.k[li], cache.v[li], key_limit, Hkv).reshape(R, Hq * hd)
+        o = rd(attention(q, cache.k[li], cache.v[li], key_limit, Hkv).reshape(R, Hq * hd))
         h = h + lin(o, "o")
-        x = rms_norm(h, lw["mlp_norm"], eps)
-        h = h + lin(silu(lin(x, "gate")) * lin(x, "up"), "down")
-    x = rms_norm(h, wts["final_norm"], eps)
+        x = rd(rms_norm(h, lw["mlp_norm"], eps))
+        h = h + lin(rd(silu(lin(x, "gate")) * lin(x, "up")), "down")
+    x = rd(rms_norm(h, wts["final_norm"], eps))
     return x @ wts["lm_head"].T
 
 

@@ -88,14 +88,14 @@ def prefill(cfg, wts, seq):
     seq.kv_len = n - 1
 
 
-def draft_logits(cfg, wts, seq, K):
+def draft_logits(cfg, wts, seq, K, act_round=None):
     """Draft pass: rows [anchor, mask x (K-1)], gate (0, 1, ..., 1). fp64 [K, V]."""
     n0 = seq.kv_len                       # position of the anchor
     rows = [seq.tokens[-1]] + [cfg["mask_id"]] * (K - 1)
     pos = n0 + np.arange(K)
     gate = np.array([0.0] + [1.0] * (K - 1))
     lim = np.array([n0] + [n0 + K - 1] * (K - 1))
-    return forward(cfg, wts, seq.cache, rows, pos, gate, lim)
+    return forward(cfg, wts, seq.cache, rows, pos, gate, lim, act_round=act_round)
 
 
 def draft_sample(zq32, inv_temp, draws):
@@ -104,11 +104,11 @@ def draft_sample(zq32, inv_temp, draws):
             for j in range(zq32.shape[0])]
 
 
-def verify_logits(cfg, wts, seq, rows, pos_offset=1):
+def verify_logits(cfg, wts, seq, rows, pos_offset=1, act_round=None):
     """Verify pass with AR weights, causal: row j at position kv_len+pos_offset+j."""
     K = len(rows)
     pos = seq.kv_len + pos_offset + np.arange(K)
-    return forward(cfg, wts, seq.cache, rows, pos, np.zeros(K), pos)
+    return forward(cfg, wts, seq.cache, rows, pos, np.zeros(K), pos, act_round=act_round)
 
 
 def spec_accept(zq32, zp32, drafts, inv_temp, draws, forced=None):

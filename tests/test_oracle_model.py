@@ -145,3 +145,24 @@ def test_lora_param_count_is_pages_figure():
     assert round(n / 1e9, 2) == facts["extra_params_8b_billions"]
     kv_bytes = cfg["n_layers"] * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * 2
     assert kv_bytes == 147_456
+
+
+def test_bf16_round_matches_torch_and_identity_mode(tiny):
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(20000) * 10 ** rng.uniform(-6, 6, 20000),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.0078125, 3.0e38, -2.5e-38]])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(om.bf16_round(x), ref)
+    # ties go to even: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert om.bf16_round(np.array([1.0 + 2 ** -8]))[0] == 1.0
+    assert om.bf16_round(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+    # the rounded mode changes the logits only by rounding-sized amounts
+    cfg, w = tiny
+    prompt = synth.prompt_ids(cfg, 10, 3)
+    s1 = spec.Sequence(cfg, prompt, capacity=32)
+    spec.prefill(cfg, w, s1)
+    s2 = s1.copy()
+    z = spec.draft_logits(cfg, w, s1, 4)
+    zr = spec.draft_logits(cfg, w, s2, 4, act_round=om.bf16_round)
+    err = np.abs(z - zr).max()
+    assert 0 < err < 0.05
