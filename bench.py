@@ -150,7 +150,7 @@ def probe_classes(U, W, i, torch):
     names = {U.TIME_ATTENTION: "attention", U.TIME_GEMM: "gemm", U.TIME_LORA_A: "lora_a",
              U.TIME_LM_HEAD: "lm_head", U.TIME_SAMPLER: "sampler"}
     for cls, name in names.items():
-        timer = U.KernelTimer(cls, 200)
+        timer = U.KernelTimer(cls, 400)
         kv_save = W.kv.kv_len.clone()
         step_save = W.step_ctr.clone()
         e_save = W.e.clone()

@@ -42,30 +42,6 @@ __device__ __forceinline__ int row_limit(int j, int kvl, int K, int pos_offset, 
   return kvl + pos_offset + j;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
-// Counts above the 6-bit field wait for more than needed (always safe).
-template <int N0>
-__device__ __forceinline__ void wait_vmcnt() {
-  constexpr int N = N0 < 63 ? N0 : 63;
-  static_assert(N >= 0, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// One 16-byte-per-lane DMA from global memory into LDS: lane i's bytes land at
-// lds_dst + 16*i (lds_dst wave-uniform).  Written as inline asm so that the
-// compiler does not serialise the ring of in-flight chunks with vmcnt(0)
-// waits; completion is awaited explicitly with wait_vmcnt + a barrier.  The
-// instruction has no destination register.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
-  const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst;
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(off);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0v), "v"(src)
-               : "memory", "m0");
-}
-
 constexpr int kStages = 4;         // KV chunks of 64 keys resident in LDS
 constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
 
@@ -161,8 +137,9 @@ k_attention(AttnArgs a) {
   // may own instructions of both kinds when the workgroup has one wave).
   const uint16_t* kbase = a.k_layer + (size_t)g * head_stride;
   const uint16_t* vbase = a.v_layer + (size_t)g * head_stride;
-  int koff[IW];     // key offset in the chunk, 0..63
-  int eoff[IW];     // element offset inside the (page, head) block
+  int koff[IW];                 // key offset in the chunk, 0..63
+  int pic[IW];                  // which of the chunk's pages holds that key
+  uint64_t gsrc[IW];            // source byte address with the page term left out
 #pragma unroll
   for (int ii = 0; ii < IW; ++ii) {
     const int ins = w * IW + ii;
@@ -170,30 +147,42 @@ k_attention(AttnArgs a) {
       const int key = ins * (1024 / KROW) + l / KCH;
       const int ch = (l % KCH) ^ (key % KCH);
       koff[ii] = key;
-      eoff[ii] = (key & pmask) * HD + ch * 8;
+      gsrc[ii] = (uint64_t)(uintptr_t)(kbase + (key & pmask) * HD + ch * 8);
     } else {                                     // V: 8 channels per instruction
       const int d = (ins - NINSTR / 2) * 8 + l / 8;
       const int kg8 = (l % 8) ^ (d & 7);
       koff[ii] = kg8 * 8;
-      eoff[ii] = (d << psh) + ((kg8 * 8) & pmask);
+      gsrc[ii] = (uint64_t)(uintptr_t)(vbase + (d << psh) + ((kg8 * 8) & pmask));
     }
+    pic[ii] = koff[ii] >> psh;                   // 0 when pages hold >= 64 keys
   }
+  const uint32_t page_bytes = (uint32_t)(page_stride * sizeof(uint16_t));
+  const uint64_t safe_src = (uint64_t)(uintptr_t)a.k_layer;   // any readable address
+  const uint32_t lds_base = lds_addr(lds) + w * IW * 1024;
   // issue the DMA of chunk c into stage c % kStages (this wave's IW instructions)
   auto issue = [&](int c) {
     const int k0 = lo + c * 64;
-    const int k0_in_page = (k0 & pmask) & ~63;    // nonzero only for pages > 64 keys
-    unsigned char* K_ = lds + (c % kStages) * STAGE;
+    const int pb = (k0 >> psh) - p_lo;           // first page of the chunk in the list
+    // bytes from a page's start to key k0 (nonzero only for pages > 64 keys)
+    const uint32_t in_page = (uint32_t)((k0 & pmask) & ~63);
+    int pgv[IW];
+#pragma unroll
+    for (int ii = 0; ii < IW; ++ii) pgv[ii] = pages[pb + pic[ii]];
+    if (any_missing) {
+#pragma unroll
+      for (int ii = 0; ii < IW; ++ii)
+        if (k0 + koff[ii] >= hi) pgv[ii] = -1;
+    }
+    const uint32_t stage = __builtin_amdgcn_readfirstlane(lds_base + (c % kStages) * STAGE);
 #pragma unroll
     for (int ii = 0; ii < IW; ++ii) {
-      const int ins = w * IW + ii;
-      const bool is_k = ins < NINSTR / 2;
-      const int kabs = k0 + koff[ii];
-      const int pidx = (kabs >> psh) - p_lo;     // < n_pg for every key of the chunk
-      const int page = (pidx < n_pg && (!any_missing || kabs < hi)) ? pages[pidx] : -1;
-      const uint16_t* src = page >= 0 ? (is_k ? kbase : vbase) + (size_t)page * page_stride +
-                                            eoff[ii] + k0_in_page * (is_k ? HD : 1)
-                                      : a.k_layer;   // safe address; zeroed below
-      lds_dma16(src, K_ + ins * 1024);
+      const bool is_k = w * IW + ii < NINSTR / 2;
+      const int page = pgv[ii];
+      const uint32_t pu = page < 0 ? 0u : (uint32_t)page;
+      uint64_t src = gsrc[ii] + (uint64_t)pu * page_bytes +
+                     (uint64_t)(in_page * (is_k ? HD * 2u : 2u));
+      src = page < 0 ? safe_src : src;           // zeroed below when used
+      lds_dma16((const void*)(uintptr_t)src, stage + ii * 1024);
     }
   };
 

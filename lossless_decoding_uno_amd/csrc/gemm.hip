@@ -170,20 +170,26 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s) {
 // Tiled kernel (many rows: batched decode blocks, prompt chunks).
 // Workgroup tile 256 x 128 (rows of X x columns of W), 4 waves in a 2 x 2
 // grid, each wave 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Both
-// operands are staged through LDS in 64-wide K slices, double buffered: the
-// global loads of slice s+1 are issued before the MFMAs of slice s and stored
-// to the other LDS buffer after them.  LDS rows are 128 bytes (8 chunks of 16
-// bytes) with the chunk index XOR-swizzled by the row, so the 16-byte fragment
-// reads of 32 consecutive rows spread over the banks.  The LoRA product runs
-// as r/64 extra K slices with T and B as operands.  Tiles are ordered so that
-// the workgroups sharing one W tile run on the same XCD (same L2).  Split-K
-// (grid.z) accumulates with fp32 atomics into the residual stream.
+// operands stream through LDS in 64-wide K slices by direct global -> LDS DMA
+// (global_load_lds_dwordx4, no staging registers), three slices resident, so
+// two slices are in flight while the MFMAs of the third run.  LDS rows are 128
+// bytes (8 chunks of 16 bytes) with the chunk index XOR-swizzled by the row,
+// applied by choosing which source chunk each DMA lane copies.  The LoRA
+// product runs as r/64 extra K slices with T and B as operands.  Tiles are
+// ordered so that the workgroups sharing one W tile run on the same XCD (same
+// L2).  Split-K (grid.z) accumulates with fp32 atomics into the residual
+// stream.
 // ============================================================================
 namespace big {
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kLdsA = BM * BK * 2;      // bytes per stage
 constexpr int kLdsB = BN * BK * 2;
+constexpr int kStage = kLdsA + kLdsB;
+constexpr int kStages = 3;
+constexpr int kInstr = kStage / 1024;   // 1 KB DMA instructions per slice
+constexpr int kIW = kInstr / 4;         // per wave
+constexpr int kInstrA = kLdsA / 1024;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return (row * 8 + (chunk ^ (row & 7))) * 16; }
 }  // namespace big
@@ -214,44 +220,35 @@ k_gemm_tiled(GemmArgs a, int m_tiles, int n_tiles, int splits) {
   const int kb0 = nk_base * z / splits, kb1 = nk_base * (z + 1) / splits;
   const int nk = (kb1 - kb0) + (z == splits - 1 ? nk_lora : 0);
 
-  // global load mapping: 8 threads per 128-byte row; A: 256 rows (8 per thread),
-  // B: 128 rows (4 per thread)
-  const int lrow = tid >> 3, lch = tid & 7;
-  uint4 ra[8], rb[4];
-  auto gload = [&](int s) {
+  // DMA lanes: instruction ins copies 8 rows (A rows 0..255, then B rows 0..127);
+  // lane l takes row 8*ins' + l/8 and writes physical chunk l%8, which holds
+  // logical chunk (l%8) ^ (row%8).  Row pointers exclude the K offset.
+  const uint16_t* pbase[kIW];
+  const uint16_t* plora[kIW];
+#pragma unroll
+  for (int ii = 0; ii < kIW; ++ii) {
+    const int ins = w * kIW + ii;
+    const bool is_a = ins < kInstrA;
+    const int row = (is_a ? ins : ins - kInstrA) * 8 + l / 8;
+    const int ch = (l % 8) ^ (row & 7);
+    if (is_a) {
+      const int m = m0 + row < a.M ? m0 + row : 0;   // rows past M: any valid row (discarded)
+      pbase[ii] = a.x + (size_t)m * a.ldx + ch * 8;
+      plora[ii] = a.t ? a.t + (size_t)m * a.ldt + sv.t_col + ch * 8 : a.x;
+    } else {
+      pbase[ii] = sv.w + (size_t)(n0 + row) * a.Kd + ch * 8;
+      plora[ii] = sv.lb ? sv.lb + (size_t)(n0 + row) * a.rank + ch * 8 : sv.w;
+    }
+  }
+  const uint32_t lds_base = lds_addr(lds) + w * kIW * 1024;
+  auto issue = [&](int s) {
     const int kk = kb0 + s;
     const bool lora = kk >= kb1;
-    const uint16_t* xa;
-    size_t lda;
-    const uint16_t* wb;
-    size_t ldb;
-    if (!lora) {
-      xa = a.x + (size_t)kk * BK; lda = a.ldx;
-      wb = sv.w + (size_t)kk * BK; ldb = a.Kd;
-    } else {
-      const int rs = kk - kb1;
-      xa = a.t + sv.t_col + (size_t)rs * BK; lda = a.ldt;
-      wb = sv.lb + (size_t)rs * BK; ldb = a.rank;
-    }
+    const int koff = (lora ? kk - kb1 : kk) * BK;
+    const uint32_t stage = __builtin_amdgcn_readfirstlane(lds_base + (s % kStages) * kStage);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = lrow + i * 32, m = m0 + row;
-      ra[i] = m < a.M ? *reinterpret_cast<const uint4*>(xa + (size_t)m * lda + lch * 8)
-                      : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = lrow + i * 32;
-      rb[i] = *reinterpret_cast<const uint4*>(wb + (size_t)(n0 + row) * ldb + lch * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* A = lds + buf * (kLdsA + kLdsB);
-    unsigned char* B = A + kLdsA;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(A + swz(lrow + i * 32, lch)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + swz(lrow + i * 32, lch)) = rb[i];
+    for (int ii = 0; ii < kIW; ++ii)
+      lds_dma16((lora ? plora[ii] : pbase[ii]) + koff, stage + ii * 1024);
   };
 
   f32x16 acc[4][2];
@@ -262,15 +259,15 @@ k_gemm_tiled(GemmArgs a, int m_tiles, int n_tiles, int splits) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue(s);
   for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) gload(s + 1);
-    const unsigned char* A = lds + buf * (kLdsA + kLdsB);
+    if (s + 1 < nk) wait_vmcnt<kIW>();        // slice s landed (s+1 may be in flight)
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (s + kStages - 1 < nk) issue(s + kStages - 1);   // into the stage read at s-1
+    const unsigned char* A = lds + (s % kStages) * kStage;
     const unsigned char* B = A + kLdsA;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -288,8 +285,6 @@ k_gemm_tiled(GemmArgs a, int m_tiles, int n_tiles, int splits) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i].v, fb[j].v, acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds rows (e/4)*8 + (l/32)*4 + e%4, column l%32 of each 32x32 tile
@@ -336,7 +331,7 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
     const int wgs = m_tiles * n_tiles;
     while (wgs * splits < 256 && splits < 4 && (a.Kd / big::BK) / (splits * 2) >= 8) splits *= 2;
   }
-  const size_t lds = 2 * (big::kLdsA + big::kLdsB);
+  const size_t lds = (size_t)big::kStages * big::kStage;
   hipLaunchKernelGGL(k_gemm_tiled, dim3(m_tiles * n_tiles, 1, splits), dim3(big::kThreads), lds,
                      s, a, m_tiles, n_tiles, splits);
   return hipGetLastError();

@@ -90,3 +90,33 @@ __device__ __forceinline__ u128 wave_inclusive_scan_u128(u128 v) {
   }
   return v;
 }
+
+// ---------------------------------------------------------------- LDS DMA
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+// Counts above the 6-bit field wait for more than needed (always safe).
+template <int N0>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int N = N0 < 63 ? N0 : 63;
+  static_assert(N >= 0, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane DMA from global memory into LDS: lane i's bytes land at
+// lds_dst + 16*i (lds_dst wave-uniform).  Written as inline asm so that the
+// compiler does not serialise the ring of in-flight chunks with vmcnt(0)
+// waits; completion is awaited explicitly with wait_vmcnt + a barrier.  The
+// instruction has no destination register.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_off) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(src)
+               : "memory", "m0");
+}
+
+// 32-bit LDS address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
