@@ -45,17 +45,21 @@ __device__ __forceinline__ int row_limit(int j, int kvl, int K, int pos_offset, 
 constexpr int kStages = 4;         // KV chunks of 64 keys resident in LDS
 constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
 
-// A workgroup of NW waves owns 16*NW query rows of one (sequence, kv head) --
-// wave w the rows 16w..16w+15 -- and one range of keys, walked in chunks of 64
-// keys.  Chunks stream HBM -> LDS with global_load_lds_dwordx4 (no registers),
+// A workgroup of RW x KH waves owns 16*RW query rows of one (sequence, kv
+// head) -- row group rg = w % RW the rows 16rg..16rg+15 -- and one range of
+// keys, walked in chunks of 64 keys; with KH = 2 the two waves of a row group
+// take one half (32 keys) of every chunk each, with their own online softmax,
+// and are merged through LDS at the end (twice the waves for the same LDS).  Chunks stream HBM -> LDS with global_load_lds_dwordx4 (no registers),
 // kStages deep, and every wave reads each chunk from LDS.  LDS layouts
 // (16-byte chunks XOR-swizzled; the swizzle is applied by choosing which
 // source address each lane loads, since lane i of a DMA writes 16*i):
 //   K: [64 keys][HD]  row = one key,      chunk index ^ (key % (HD/8))
 //   V: [HD][64 keys]  row = one channel,  key-group index ^ (channel % 8)
-template <int HD, int NW>
-__global__ void __launch_bounds__(NW * 64)
+template <int HD, int RW, int KH>
+__global__ void __launch_bounds__(RW * KH * 64)
 k_attention(AttnArgs a) {
+  constexpr int NW = RW * KH;             // waves per workgroup
+  constexpr int NH = 2 / KH;              // 32-key halves of a chunk per wave
   constexpr int DS = HD / 32;             // 32-channel MFMA steps of S
   constexpr int NT = HD / 16;             // 16-channel tiles of O
   constexpr int KROW = HD * 2;            // bytes per key row in LDS
@@ -70,10 +74,11 @@ k_attention(AttnArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int lr = l & 15, lg = l >> 4;
+  const int rg = w % RW, kh = w / RW;     // row group, key half
   const int bg = blockIdx.z, b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.K;
-  const int QPW = 16 * NW;                 // query rows per workgroup
+  const int QPW = 16 * RW;                 // query rows per workgroup
   const int qg = blockIdx.y, qbase = qg * QPW;
   const int split = blockIdx.x, n_split = a.plan.n_wave_splits;
   const int kvl = a.kv_len[b];
@@ -111,7 +116,7 @@ k_attention(AttnArgs a) {
   const int any_missing = __syncthreads_or(missing);
 
   // this wave's 16 query rows: Q as the B operand of S^T = K Q^T
-  const int qr = qbase + w * 16 + lr;
+  const int qr = qbase + rg * 16 + lr;
   const bool q_ok = qr < QR;
   const int qj = q_ok ? qr / G : 0, qh = q_ok ? qr % G : 0;
   const int lim = q_ok ? row_limit(qj, kvl, a.K, a.pos_offset, a.draft) : -1;
@@ -186,8 +191,9 @@ k_attention(AttnArgs a) {
     }
   };
 
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   float m_run = -INFINITY, l_run = 0.f;
+  // smallest row limit of the workgroup: chunks below it need no masking
+  const int lim_min = a.draft ? kvl : kvl + a.pos_offset + min(a.K - 1, qbase / G);
   f32x4 o[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -223,32 +229,43 @@ k_attention(AttnArgs a) {
     }
     if (c + kStages - 1 < n_chunks) issue(c + kStages - 1);
 
-    // S^T tiles: MFMA row rho of key tile kt is key 32*(kt/2) + 8*(rho/4) + 4*(kt%2) + rho%4
-    f32x4 s4[4];
+    // S^T tiles of this wave's halves h: MFMA row rho of tile t is key
+    // 32*h + 8*(rho/4) + 4*t + rho%4
+    f32x4 s4[2 * NH];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = 32 * (kt >> 1) + 8 * (lr >> 2) + 4 * (kt & 1) + (lr & 3);
-      s4[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const int ch = ds * 4 + lg;
-        AFrag kf;
-        kf.u = *reinterpret_cast<const uint4*>(K_ + key * KROW + ((ch ^ (key % KCH)) << 4));
-        s4[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qf[ds].v, s4[kt], 0, 0, 0);
-        s4[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qfl[ds].v, s4[kt], 0, 0, 0);
+      for (int t = 0; t < 2; ++t) {
+        const int h = kh * NH + hh;
+        const int key = 32 * h + 8 * (lr >> 2) + 4 * t + (lr & 3);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const int ch = ds * 4 + lg;
+          AFrag kf;
+          kf.u = *reinterpret_cast<const uint4*>(K_ + key * KROW + ((ch ^ (key % KCH)) << 4));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qf[ds].v, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qfl[ds].v, acc, 0, 0, 0);
+        }
+        s4[2 * hh + t] = acc;
       }
-    }
-    // lane holds keys 32h + 8*lg + c (h = kt/2, c = 4*(kt%2) + i) of query row lr
-    float p[2][8];
+    // lane holds keys 32h + 8*lg + c (c = 4t + i) of query row lr; scores are
+    // already in log2 units (q carries log2(e)/sqrt(hd))
+    float p[NH][8];
     float rmax = -INFINITY;
+    const bool all_visible = k0 + 63 <= lim_min && k0 + 64 <= hi;   // wave-uniform
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const int key = k0 + 32 * h + 8 * lg + cc;
-        const float v = s4[2 * h + (cc >> 2)][cc & 3] * scale_log2;
-        p[h][cc] = (key <= lim && key < hi) ? v : -INFINITY;
-        rmax = fmaxf(rmax, p[h][cc]);
+        const float v = s4[2 * hh + (cc >> 2)][cc & 3];
+        if (all_visible) {
+          p[hh][cc] = v;
+        } else {
+          const int key = k0 + 32 * (kh * NH + hh) + 8 * lg + cc;
+          p[hh][cc] = (key <= lim && key < hi) ? v : -INFINITY;
+        }
+        rmax = fmaxf(rmax, p[hh][cc]);
       }
     rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
     rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
@@ -263,11 +280,11 @@ k_attention(AttnArgs a) {
     const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
     float rsum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        p[h][cc] = __builtin_amdgcn_exp2f(p[h][cc] - m_use);
-        rsum += p[h][cc];
+        p[hh][cc] = __builtin_amdgcn_exp2f(p[hh][cc] - m_use);
+        rsum += p[hh][cc];
       }
     rsum += __shfl_xor(rsum, 16, 64);
     rsum += __shfl_xor(rsum, 32, 64);
@@ -283,19 +300,19 @@ k_attention(AttnArgs a) {
         for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int hh = 0; hh < NH; ++hh) {
       // P = high + low bf16 parts, so the softmax weights keep ~16 bits
       AFrag pf, pfl;
       uint32_t* pe = reinterpret_cast<uint32_t*>(&pf.u);
       uint32_t* pl = reinterpret_cast<uint32_t*>(&pfl.u);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const float x0 = p[h][2 * cc], x1 = p[h][2 * cc + 1];
+        const float x0 = p[hh][2 * cc], x1 = p[hh][2 * cc + 1];
         const uint32_t hi = pack_bf16x2(x0, x1);
         pe[cc] = hi;
         pl[cc] = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
       }
-      const int kg8 = 4 * h + lg;
+      const int kg8 = 4 * (kh * NH + hh) + lg;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int d = nt * 16 + lr;
@@ -308,12 +325,45 @@ k_attention(AttnArgs a) {
   }
   if (bad_page && a.status) atomicOr(a.status + b, UNO_DEV_BAD_PAGE);
 
-  // O rows of this lane: q = 4*lg + i of the wave's 16
+  if constexpr (KH == 2) {
+    // merge the two key halves of each row group: wave kh = 1 hands its
+    // (max, sum, O) to wave kh = 0 through LDS (the chunk stages are free now)
+    __syncthreads();
+    float* mo = reinterpret_cast<float*>(lds);            // [RW][16][HD]
+    float* mml = mo + RW * 16 * HD;                       // [RW][16][2]
+    if (kh == 1) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mo[(rg * 16 + 4 * lg + i) * HD + nt * 16 + lr] = o[nt][i];
+      if (lg == 0) {
+        mml[(rg * 16 + lr) * 2 + 0] = m_run;
+        mml[(rg * 16 + lr) * 2 + 1] = l_run;
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = mml[(rg * 16 + lr) * 2 + 0], l1 = mml[(rg * 16 + lr) * 2 + 1];
+    const float M = fmaxf(m_run, m1);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float f0 = __builtin_amdgcn_exp2f(m_run - M_use), f1 = __builtin_amdgcn_exp2f(m1 - M_use);
+    l_run = l_run * f0 + l1 * f1;
+    m_run = M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a0 = __shfl(f0, 4 * lg + i, 64), a1 = __shfl(f1, 4 * lg + i, 64);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        o[nt][i] = o[nt][i] * a0 + mo[(rg * 16 + 4 * lg + i) * HD + nt * 16 + lr] * a1;
+    }
+  }
+
+  // O rows of this lane: q = 4*lg + i of the row group's 16
   if (n_split == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float li = __shfl(l_run, 4 * lg + i, 64);
-      const int r = qbase + w * 16 + 4 * lg + i;
+      const int r = qbase + rg * 16 + 4 * lg + i;
       if (r >= QR) continue;
       const int j = r / G, hh = r % G;
       uint16_t* op = a.out + ((size_t)(b * a.K + j) * a.Hq + g * G + hh) * HD;
@@ -328,10 +378,10 @@ k_attention(AttnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) po[(size_t)(w * 16 + 4 * lg + i) * HD + nt * 16 + lr] = o[nt][i];
+      for (int i = 0; i < 4; ++i) po[(size_t)(rg * 16 + 4 * lg + i) * HD + nt * 16 + lr] = o[nt][i];
     if (lg == 0) {
-      pml[(w * 16 + lr) * 2 + 0] = m_run;
-      pml[(w * 16 + lr) * 2 + 1] = l_run;
+      pml[(rg * 16 + lr) * 2 + 0] = m_run;
+      pml[(rg * 16 + lr) * 2 + 1] = l_run;
     }
   }
 }
@@ -342,7 +392,7 @@ __global__ void __launch_bounds__(HD)
 k_attn_merge(AttnArgs a) {
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int QPW = 16 * a.plan.waves;
+  const int QPW = 16 * a.plan.waves;      // query rows per workgroup
   const int qr = blockIdx.x;
   const int qg = qr / QPW, ql = qr % QPW;
   const int NS = a.plan.n_wave_splits;
@@ -368,6 +418,7 @@ AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx) {
   const int tiles = (G * K + 15) / 16;
   p.waves = 1;
   while (p.waves < tiles && p.waves < 8) p.waves *= 2;
+  p.key_halves = p.waves <= 4 ? 2 : 1;
   p.n_qgroups = (G * K + 16 * p.waves - 1) / (16 * p.waves);
   const long groups = (long)B * c.n_kv_heads * p.n_qgroups;
   const long ctx = max_ctx > 1 ? max_ctx : 1;
@@ -394,11 +445,13 @@ template <int HD>
 static hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.plan.n_wave_splits, a.plan.n_qgroups, a.B * a.Hkv);
   const size_t lds = (size_t)kStages * 2 * 64 * HD * 2 + kMaxPagesLds * sizeof(int);
-  switch (a.plan.waves) {
-    case 1: hipLaunchKernelGGL((k_attention<HD, 1>), grid, dim3(64), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attention<HD, 2>), grid, dim3(128), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attention<HD, 4>), grid, dim3(256), lds, s, a); break;
-    default: hipLaunchKernelGGL((k_attention<HD, 8>), grid, dim3(512), lds, s, a); break;
+  const int kh = a.plan.key_halves;
+  const dim3 block(64 * a.plan.waves * kh);
+  switch (a.plan.waves * 10 + kh) {
+    case 12: hipLaunchKernelGGL((k_attention<HD, 1, 2>), grid, block, lds, s, a); break;
+    case 22: hipLaunchKernelGGL((k_attention<HD, 2, 2>), grid, block, lds, s, a); break;
+    case 42: hipLaunchKernelGGL((k_attention<HD, 4, 2>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_attention<HD, 8, 1>), grid, block, lds, s, a); break;
   }
   return hipGetLastError();
 }

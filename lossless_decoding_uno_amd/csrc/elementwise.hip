@@ -112,8 +112,8 @@ hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset
 
 // ------------------------------------------------------------ RoPE + KV write
 // qkv row layout: [q heads | k heads | v heads], each head hd wide, fp32.
-// q -> bf16 [R, Hq*hd] (rotated); k (rotated) -> K page [slot][hd];
-// v -> V page transposed [hd][slot].
+// q (rotated, times log2(e)/sqrt(hd)) -> hi + lo bf16 [R, Hq*hd];
+// k (rotated) -> K page [slot][hd]; v -> V page transposed [hd][slot].
 __global__ void __launch_bounds__(256)
 k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, int K,
                 int Hq, int Hkv, int hd, int pos_offset, const int32_t* __restrict__ kv_len,
@@ -125,6 +125,7 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
   const int b = r / K, j = r % K;
   const int half = hd / 2;
   const int width = (Hq + 2 * Hkv) * hd;
+  const float q_scale = 1.4426950408889634f / sqrtf((float)hd);
   const float* row = qkv + (size_t)r * width;
   const float2* c = cs + (size_t)r * half;
   const int pos = kv_len[b] + pos_offset + j;
@@ -148,13 +149,15 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
     const float y1 = x1 * a.x - x2 * a.y;
     const float y2 = x2 * a.x + x1 * a.y;
     if (head < Hq) {
-      // q = hi + lo, both bf16: the attention scores use both parts
+      // q * log2(e)/sqrt(hd) (the attention works in base 2) as hi + lo bf16
+      // parts: the scores use both
       const size_t o = (size_t)r * Hq * hd + head * hd;
-      const uint16_t h1 = f32_to_bf16(y1), h2 = f32_to_bf16(y2);
+      const float z1 = y1 * q_scale, z2 = y2 * q_scale;
+      const uint16_t h1 = f32_to_bf16(z1), h2 = f32_to_bf16(z2);
       q_out[o + i] = h1;
       q_out[o + i + half] = h2;
-      q_lo[o + i] = f32_to_bf16(y1 - bf16_to_f32(h1));
-      q_lo[o + i + half] = f32_to_bf16(y2 - bf16_to_f32(h2));
+      q_lo[o + i] = f32_to_bf16(z1 - bf16_to_f32(h1));
+      q_lo[o + i + half] = f32_to_bf16(z2 - bf16_to_f32(h2));
     } else if (page >= 0) {
       const int g = head - Hq;
       uint16_t* kp = k_layer + (((size_t)page * Hkv + g) * ps + slot) * hd;

@@ -14,14 +14,15 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
-// round-to-nearest-even (inputs are finite in this library)
+// round-to-nearest-even conversions; on gfx950 these lower to the hardware
+// v_cvt_pk_bf16_f32 (inputs are finite in this library)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------- wave helpers

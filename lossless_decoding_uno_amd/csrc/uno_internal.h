@@ -36,9 +36,9 @@ hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float
 // absolute positions kv_len[b] + pos_offset + j.
 hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
                              float theta, float2* cs, hipStream_t s);
-// RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]); q -> two
-// bf16 planes [R, Hq*hd] (hi and the rounding remainder lo), k/v (bf16) ->
-// paged cache at the rows' positions.
+// RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]); q, scaled
+// by log2(e)/sqrt(hd), -> two bf16 planes [R, Hq*hd] (hi and the rounding
+// remainder lo), k/v (bf16) -> paged cache at the rows' positions.
 hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
                                 const uno_kv& kv, int layer, int B, int K, int pos_offset,
                                 bf16_raw_t* q_out, bf16_raw_t* q_lo, int32_t* status,
@@ -81,7 +81,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // group of 64 query rows and writes a partial (max, sum, output) that the merge
 // kernel combines.
 struct AttnPlan {
-  int waves;            // waves per workgroup (16 query rows each)
+  int waves;            // row groups per workgroup (16 query rows each)
+  int key_halves;       // waves per row group (each takes half of every chunk)
   int n_qgroups;        // groups of 16*waves query rows
   int n_wave_splits;    // key ranges per query group
   int split_len;        // keys per range (multiple of 64; the last runs to the end)
@@ -89,8 +90,8 @@ struct AttnPlan {
 AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx);
 size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx);
 struct AttnArgs {
-  const uint16_t* q;          // [R, Hq, hd] bf16, post-RoPE (high part)
-  const uint16_t* q_lo;       // [R, Hq, hd] bf16, q - high part
+  const uint16_t* q;          // [R, Hq, hd] bf16, q * log2(e)/sqrt(hd) (high part)
+  const uint16_t* q_lo;       // [R, Hq, hd] bf16, remainder of that
   const uint16_t* k_layer;    // this layer's K pages
   const uint16_t* v_layer;    // this layer's V pages (transposed inside a page)
   const int32_t* page_table;
