@@ -95,6 +95,8 @@ struct PassWs {
   float2* cs;        // [R, hd/2]
   float* part_o;
   float* part_ml;
+  float* gemm_part;      // split-K partial tiles (passes of 128 rows or more)
+  size_t gemm_part_floats;
   size_t total;
 };
 
@@ -126,6 +128,8 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.cs = reinterpret_cast<float2*>(take(R * (c.head_dim / 2) * sizeof(float2)));
   w.part_o = reinterpret_cast<float*>(take(parts * c.head_dim * 4));
   w.part_ml = reinterpret_cast<float*>(take(parts * 2 * 4));
+  w.gemm_part_floats = R >= 128 ? kGemmPartFloats : 0;
+  w.gemm_part = reinterpret_cast<float*>(take(w.gemm_part_floats * 4));
   w.total = off;
   return w;
 }
@@ -166,8 +170,14 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
   const size_t layer_elems = (size_t)kv->n_pages * Hkv * c.page_size * hd;
 
-  auto lora_t = [&](const bf16_raw_t* x, int ldx, int Kd, const void* const* a_ptrs, int n_a) {
+  auto scratch_args = [&] {
     GemmArgs g = {};
+    g.part = W.gemm_part_floats ? W.gemm_part : nullptr;
+    g.part_floats = W.gemm_part_floats;
+    return g;
+  };
+  auto lora_t = [&](const bf16_raw_t* x, int ldx, int Kd, const void* const* a_ptrs, int n_a) {
+    GemmArgs g = scratch_args();
     g.x = x; g.M = R; g.Kd = Kd; g.ldx = ldx;
     for (int i = 0; i < n_a; ++i) g.seg[i] = GemmSeg{bp(a_ptrs[i]), r, nullptr, 0};
     g.n_seg = n_a;
@@ -186,7 +196,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(lora_t(W.xn, D, D, a3, 3));
     }
     {
-      GemmArgs g = {};
+      GemmArgs g = scratch_args();
       g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
       g.seg[0] = GemmSeg{bp(L.wq), QD, lq ? bp(L.lora_b[P_Q]) : nullptr, 0};
       g.seg[1] = GemmSeg{bp(L.wk), KD, lq ? bp(L.lora_b[P_K]) : nullptr, r};
@@ -218,7 +228,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(lora_t(W.ao, QD, QD, a1, 1));
     }
     {
-      GemmArgs g = {};
+      GemmArgs g = scratch_args();
       g.x = W.ao; g.M = R; g.Kd = QD; g.ldx = QD;
       g.seg[0] = GemmSeg{bp(L.wo), D, lo ? bp(L.lora_b[P_O]) : nullptr, 0};
       g.n_seg = 1;
@@ -233,7 +243,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(lora_t(W.xn, D, D, a2, 2));
     }
     {
-      GemmArgs g = {};
+      GemmArgs g = scratch_args();
       g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
       g.seg[0] = GemmSeg{bp(L.wgate), F, lg ? bp(L.lora_b[P_GATE]) : nullptr, 0};
       g.seg[1] = GemmSeg{bp(L.wup), F, lg ? bp(L.lora_b[P_UP]) : nullptr, r};
@@ -248,7 +258,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(lora_t(W.act, F, F, a1, 1));
     }
     {
-      GemmArgs g = {};
+      GemmArgs g = scratch_args();
       g.x = W.act; g.M = R; g.Kd = F; g.ldx = F;
       g.seg[0] = GemmSeg{bp(L.wdown), D, ld ? bp(L.lora_b[P_DOWN]) : nullptr, 0};
       g.n_seg = 1;
@@ -259,7 +269,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   }
   if (logits) {
     UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(w->final_norm), R, D, c.rms_eps, W.xn, s));
-    GemmArgs g = {};
+    GemmArgs g = scratch_args();
     g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
     g.seg[0] = GemmSeg{bp(w->lm_head), c.vocab, nullptr, 0};
     g.n_seg = 1;

@@ -42,6 +42,15 @@ __device__ __forceinline__ int row_limit(int j, int kvl, int K, int pos_offset, 
   return kvl + pos_offset + j;
 }
 
+// LDS swizzles (XOR on the 16-byte chunk index of a row).  A 16-byte LDS read
+// serves 16 lanes per cycle from 64 banks (256 bytes), so the 16 rows one read
+// touches must land in distinct bank groups:
+//  * K rows (one key, HD*2 bytes): the 16 keys an S tile reads are
+//    8a + 4t + b (a, b in 0..3), so the swizzle is b + 4a;
+//  * V rows (one channel, 128 bytes, two per bank window): (channel / 2) % 8.
+__device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
 constexpr int kStages = 4;         // KV chunks of 64 keys resident in LDS
 constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
 
@@ -53,8 +62,8 @@ constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
 // kStages deep, and every wave reads each chunk from LDS.  LDS layouts
 // (16-byte chunks XOR-swizzled; the swizzle is applied by choosing which
 // source address each lane loads, since lane i of a DMA writes 16*i):
-//   K: [64 keys][HD]  row = one key,      chunk index ^ (key % (HD/8))
-//   V: [HD][64 keys]  row = one channel,  key-group index ^ (channel % 8)
+//   K: [64 keys][HD]  row = one key,      chunk index ^ kswz(key) % (HD/8)
+//   V: [HD][64 keys]  row = one channel,  key-group index ^ vswz(channel)
 template <int HD, int RW, int KH>
 __global__ void __launch_bounds__(RW * KH * 64)
 k_attention(AttnArgs a) {
@@ -150,12 +159,12 @@ k_attention(AttnArgs a) {
     const int ins = w * IW + ii;
     if (ins < NINSTR / 2) {                      // K: 1024/KROW keys per instruction
       const int key = ins * (1024 / KROW) + l / KCH;
-      const int ch = (l % KCH) ^ (key % KCH);
+      const int ch = (l % KCH) ^ (kswz(key) & (KCH - 1));
       koff[ii] = key;
       gsrc[ii] = (uint64_t)(uintptr_t)(kbase + (key & pmask) * HD + ch * 8);
     } else {                                     // V: 8 channels per instruction
       const int d = (ins - NINSTR / 2) * 8 + l / 8;
-      const int kg8 = (l % 8) ^ (d & 7);
+      const int kg8 = (l % 8) ^ vswz(d);
       koff[ii] = kg8 * 8;
       gsrc[ii] = (uint64_t)(uintptr_t)(vbase + (d << psh) + ((kg8 * 8) & pmask));
     }
@@ -222,7 +231,7 @@ k_attention(AttnArgs a) {
         const bool ok = kabs < hi && pages[(kabs >> psh) - p_lo] >= 0;
         if (!ok) {
           const int kg8 = key / 8;
-          *reinterpret_cast<uint16_t*>(V_ + d * 128 + ((kg8 ^ (d & 7)) << 4) + (key % 8) * 2) = 0;
+          *reinterpret_cast<uint16_t*>(V_ + d * 128 + ((kg8 ^ vswz(d)) << 4) + (key % 8) * 2) = 0;
         }
       }
       __syncthreads();
@@ -243,7 +252,8 @@ k_attention(AttnArgs a) {
         for (int ds = 0; ds < DS; ++ds) {
           const int ch = ds * 4 + lg;
           AFrag kf;
-          kf.u = *reinterpret_cast<const uint4*>(K_ + key * KROW + ((ch ^ (key % KCH)) << 4));
+          kf.u = *reinterpret_cast<const uint4*>(K_ + key * KROW +
+                                                 ((ch ^ (kswz(key) & (KCH - 1))) << 4));
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qf[ds].v, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qfl[ds].v, acc, 0, 0, 0);
         }
@@ -317,7 +327,7 @@ k_attention(AttnArgs a) {
       for (int nt = 0; nt < NT; ++nt) {
         const int d = nt * 16 + lr;
         AFrag vf;
-        vf.u = *reinterpret_cast<const uint4*>(V_ + d * 128 + ((kg8 ^ (d & 7)) << 4));
+        vf.u = *reinterpret_cast<const uint4*>(V_ + d * 128 + ((kg8 ^ vswz(d)) << 4));
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.v, vf.v, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfl.v, vf.v, o[nt], 0, 0, 0);
       }

@@ -36,6 +36,7 @@ struct SegView {
   int t_col;
   int col_base;
   int n0;
+  int n;        // columns of the segment
 };
 
 __device__ __forceinline__ SegView pick_segment(const GemmArgs& a, int tile) {
@@ -44,13 +45,16 @@ __device__ __forceinline__ SegView pick_segment(const GemmArgs& a, int tile) {
   int t0 = a.seg[0].n >> 4, t1 = a.seg[1].n >> 4;
   if (a.n_seg == 1 || tile < t0) {
     v.w = a.seg[0].w; v.lb = a.seg[0].lora_b; v.t_col = a.seg[0].t_col; v.n0 = tile * 16;
+    v.n = a.seg[0].n;
   } else if (a.n_seg == 2 || tile < t0 + t1) {
     base = a.seg[0].n;
     v.w = a.seg[1].w; v.lb = a.seg[1].lora_b; v.t_col = a.seg[1].t_col; v.n0 = (tile - t0) * 16;
+    v.n = a.seg[1].n;
   } else {
     base = a.seg[0].n + a.seg[1].n;
     v.w = a.seg[2].w; v.lb = a.seg[2].lora_b; v.t_col = a.seg[2].t_col;
     v.n0 = (tile - t0 - t1) * 16;
+    v.n = a.seg[2].n;
   }
   v.col_base = base;
   return v;
@@ -168,184 +172,359 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s) {
 
 // ============================================================================
 // Tiled kernel (many rows: batched decode blocks, prompt chunks).
-// Workgroup tile 256 x 128 (rows of X x columns of W), 4 waves in a 2 x 2
-// grid, each wave 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.  Both
-// operands stream through LDS in 64-wide K slices by direct global -> LDS DMA
-// (global_load_lds_dwordx4, no staging registers), three slices resident, so
-// two slices are in flight while the MFMAs of the third run.  LDS rows are 128
-// bytes (8 chunks of 16 bytes) with the chunk index XOR-swizzled by the row,
-// applied by choosing which source chunk each DMA lane copies.  The LoRA
-// product runs as r/64 extra K slices with T and B as operands.  Tiles are
-// ordered so that the workgroups sharing one W tile run on the same XCD (same
-// L2).  Split-K (grid.z) accumulates with fp32 atomics into the residual
-// stream.
+// Workgroup tile BM x BN (rows of X x columns of W), WM x WN waves, each wave
+// (BM/WM) x (BN/WN) as 32 x 32 tiles of v_mfma_f32_32x32x16_bf16.  Both
+// operands stream through LDS in 32-wide K slices by direct global -> LDS DMA
+// (global_load_lds_dwordx4), S slices resident: S-1 are in flight while the
+// MFMAs of one run.  LDS rows are 64 bytes (4 chunks of 16 bytes), the chunk
+// index XOR-ed with (row / 4) % 4 so that the 16 lanes served together hit 16
+// distinct 16-byte bank groups; the DMA applies the swizzle by choosing which
+// source chunk each lane copies.  Each half-slice's fragments are read while
+// the MFMAs of the other half issue.  The LoRA product runs as r/32 extra K
+// slices with T and B as operands.  Configurations:
+//   L  256 x 256, 8 waves, 4 stages (128 KB LDS): one workgroup per CU
+//   M  256 x 128, 4 waves, 3 stages (72 KB): two workgroups per CU
+//   S  128 x 128, 4 waves, 4 stages (64 KB): two workgroups per CU
+// Two resident workgroups cover each other's barrier waits, prologue and
+// epilogue.
+//
+// Split-K (too few tiles for the chip): every split writes its fp32 partial
+// tile to scratch and a second kernel sums the splits in order (run-to-run
+// identical) and applies the epilogue.
 // ============================================================================
 namespace big {
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int kThreads = 256;
-constexpr int kLdsA = BM * BK * 2;      // bytes per stage
-constexpr int kLdsB = BN * BK * 2;
-constexpr int kStage = kLdsA + kLdsB;
-constexpr int kStages = 3;
-constexpr int kInstr = kStage / 1024;   // 1 KB DMA instructions per slice
-constexpr int kIW = kInstr / 4;         // per wave
-constexpr int kInstrA = kLdsA / 1024;
+constexpr int BK = 32;
+template <int BM_, int BN_, int WM_, int WN_, int S_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int kWaves = WM * WN, kThreads = kWaves * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
+  static constexpr int TI = TM / 32, TJ = TN / 32;   // MFMA tiles per wave
+  static constexpr int kLdsA = BM * BK * 2, kLdsB = BN * BK * 2, kStage = kLdsA + kLdsB;
+  static constexpr int kInstr = kStage / 1024;       // 1 KB DMA instructions per slice
+  static constexpr int kIW = kInstr / kWaves;        // per wave
+  static constexpr int kInstrA = kLdsA / 1024;
+  static constexpr int kLds = S * kStage;
+  static constexpr int kTileFloats = BM * BN;
+  static_assert(kInstr % kWaves == 0, "DMA instructions must split evenly over the waves");
+};
+using CfgL = Cfg<256, 256, 2, 4, 4>;
+using CfgM = Cfg<256, 128, 2, 2, 3>;
+using CfgS = Cfg<128, 128, 2, 2, 4>;
+__device__ __forceinline__ int swz_f(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ swz_f(row)) << 4); }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (row * 8 + (chunk ^ (row & 7))) * 16; }
+// Work item -> (m tile, split, n tile).  Consecutive workgroups go round-robin
+// over the 8 XCDs; each XCD gets a contiguous range of items (m tile fastest,
+// then the split, then the n tile) so the workgroups sharing W columns share
+// an L2.
+struct Item {
+  int mt, z, nt;
+};
+__device__ __forceinline__ Item item_of(int id, int m_tiles, int splits, int nwg) {
+  const int xcd = id & 7, q = nwg >> 3, r8 = nwg & 7;
+  const int lin = xcd * q + (xcd < r8 ? xcd : r8) + (id >> 3);
+  Item it;
+  it.mt = lin % m_tiles;
+  const int rest = lin / m_tiles;
+  it.z = rest % splits;
+  it.nt = rest / splits;
+  return it;
+}
 }  // namespace big
 
-__global__ void __launch_bounds__(big::kThreads)
-k_gemm_tiled(GemmArgs a, int m_tiles, int n_tiles, int splits) {
+__device__ __forceinline__ void store_out(const GemmArgs& a, int m, int n, float v) {
+  const size_t o = (size_t)m * a.ldo + n;
+  switch (a.epi) {
+    case EPI_STORE_F32: static_cast<float*>(a.out)[o] = v; break;
+    case EPI_ADD_F32: static_cast<float*>(a.out)[o] += v; break;
+    case EPI_STORE_BF16: static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v); break;
+    default: {
+      const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
+      static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(g * v);
+    }
+  }
+}
+
+// two waves per SIMD in every configuration (at most 256 VGPRs per wave)
+template <class C>
+__global__ void __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits) {
   using namespace big;
+  constexpr int TI = C::TI, TJ = C::TJ, IW = C::kIW, S = C::S;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / C::WN, wn = w % C::WN;
 
-  // XCD-aware order: linear id -> (xcd, slot); tiles of one N column stay together
-  const int nwg = m_tiles * n_tiles;
-  const int id = blockIdx.x;
-  const int per_xcd = (nwg + 7) / 8;
-  int lin = (id % 8) * per_xcd + id / 8;
-  if (nwg % 8 != 0) lin = id;             // keep it simple when the grid is ragged
-  const int mt = lin % m_tiles, nt = lin / m_tiles;
-  if (nt >= n_tiles) return;
-  const int m0 = mt * BM;
-  const SegView sv = pick_segment(a, nt * (BN / 16));
+  const Item it = item_of(blockIdx.x, m_tiles, splits, m_tiles * n_tiles * splits);
+  const int m0 = it.mt * C::BM, z = it.z;
+  const SegView sv = pick_segment(a, it.nt * (C::BN / 16));
   const int n0 = sv.n0;
 
-  // K slices of this split
+  // K slices of this split (LoRA slices after the last split's base slices)
   const int nk_base = a.Kd / BK;
   const int nk_lora = (a.t && sv.lb) ? a.rank / BK : 0;
-  const int z = blockIdx.z;
   const int kb0 = nk_base * z / splits, kb1 = nk_base * (z + 1) / splits;
   const int nk = (kb1 - kb0) + (z == splits - 1 ? nk_lora : 0);
 
-  // DMA lanes: instruction ins copies 8 rows (A rows 0..255, then B rows 0..127);
-  // lane l takes row 8*ins' + l/8 and writes physical chunk l%8, which holds
-  // logical chunk (l%8) ^ (row%8).  Row pointers exclude the K offset.
-  const uint16_t* pbase[kIW];
-  const uint16_t* plora[kIW];
+  // DMA lanes: instruction ins copies 16 rows (A rows, then B rows); lane l
+  // fills row 16*ins' + l/4, physical chunk l%4, which holds logical chunk
+  // (l%4) ^ swz_f(row).  Rows past M / past the segment re-read a valid row;
+  // their results are discarded.
+  const uint16_t* pbase[IW];
+  const uint16_t* plora[IW];
 #pragma unroll
-  for (int ii = 0; ii < kIW; ++ii) {
-    const int ins = w * kIW + ii;
-    const bool is_a = ins < kInstrA;
-    const int row = (is_a ? ins : ins - kInstrA) * 8 + l / 8;
-    const int ch = (l % 8) ^ (row & 7);
+  for (int ii = 0; ii < IW; ++ii) {
+    const int ins = w * IW + ii;
+    const bool is_a = ins < C::kInstrA;
+    const int row = (is_a ? ins : ins - C::kInstrA) * 16 + (l >> 2);
+    const int ch = (l & 3) ^ swz_f(row);
     if (is_a) {
-      const int m = m0 + row < a.M ? m0 + row : 0;   // rows past M: any valid row (discarded)
+      const int m = m0 + row < a.M ? m0 + row : 0;
       pbase[ii] = a.x + (size_t)m * a.ldx + ch * 8;
       plora[ii] = a.t ? a.t + (size_t)m * a.ldt + sv.t_col + ch * 8 : a.x;
     } else {
-      pbase[ii] = sv.w + (size_t)(n0 + row) * a.Kd + ch * 8;
-      plora[ii] = sv.lb ? sv.lb + (size_t)(n0 + row) * a.rank + ch * 8 : sv.w;
+      const int n = n0 + row < sv.n ? n0 + row : sv.n - 1;
+      pbase[ii] = sv.w + (size_t)n * a.Kd + ch * 8;
+      plora[ii] = sv.lb ? sv.lb + (size_t)n * a.rank + ch * 8 : sv.w;
     }
   }
-  const uint32_t lds_base = lds_addr(lds) + w * kIW * 1024;
-  auto issue = [&](int s) {
+  const uint32_t lds_base = lds_addr(lds) + w * IW * 1024;
+  auto issue = [&](int s, int stage) {
     const int kk = kb0 + s;
     const bool lora = kk >= kb1;
     const int koff = (lora ? kk - kb1 : kk) * BK;
-    const uint32_t stage = __builtin_amdgcn_readfirstlane(lds_base + (s % kStages) * kStage);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage * C::kStage);
 #pragma unroll
-    for (int ii = 0; ii < kIW; ++ii)
-      lds_dma16((lora ? plora[ii] : pbase[ii]) + koff, stage + ii * 1024);
+    for (int ii = 0; ii < IW; ++ii)
+      lds_dma16((lora ? plora[ii] : pbase[ii]) + koff, dst + ii * 1024);
+  };
+  // slice s has landed once at most `ahead` later slices of this wave are in flight
+  auto wait_slice = [&](int ahead) {
+    if (S > 3 && ahead >= 3) wait_vmcnt<3 * IW>();
+    else if (ahead >= 2) wait_vmcnt<2 * IW>();
+    else if (ahead == 1) wait_vmcnt<IW>();
+    else wait_vmcnt<0>();
   };
 
-  f32x16 acc[4][2];
+  Frag fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+  auto read = [&](int stage, int kk, Frag (&fa)[TI], Frag (&fb)[TJ]) {
+    const unsigned char* A = lds + stage * C::kStage;
+    const unsigned char* B = A + C::kLdsA;
+    const int ch = 2 * kk + (l >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
+      fa[i].u = *reinterpret_cast<const uint4*>(A + swz(wm * C::TM + i * 32 + (l & 31), ch));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
+      fb[j].u = *reinterpret_cast<const uint4*>(B + swz(wn * C::TN + j * 32 + (l & 31), ch));
+  };
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto mma = [&](const Frag (&fa)[TI], const Frag (&fb)[TJ]) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i].v, fb[j].v, acc[i][j], 0, 0, 0);
+  };
 
+  if (nk > 0) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s);
-  for (int s = 0; s < nk; ++s) {
-    if (s + 1 < nk) wait_vmcnt<kIW>();        // slice s landed (s+1 may be in flight)
-    else wait_vmcnt<0>();
+    for (int s = 0; s < S; ++s)
+      if (s < nk) issue(s, s);
+    wait_slice(nk - 1 < S - 1 ? nk - 1 : S - 1);
     __syncthreads();
-    if (s + kStages - 1 < nk) issue(s + kStages - 1);   // into the stage read at s-1
-    const unsigned char* A = lds + (s % kStages) * kStage;
-    const unsigned char* B = A + kLdsA;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = 2 * kk + (l >> 5);
-      Frag fa[4], fb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i].u = *reinterpret_cast<const uint4*>(A + swz(wm * 128 + i * 32 + (l & 31), ch));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j].u = *reinterpret_cast<const uint4*>(B + swz(wn * 64 + j * 32 + (l & 31), ch));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i].v, fb[j].v, acc[i][j], 0, 0, 0);
+    // The scheduling fences keep each half-slice's fragment reads ahead of
+    // the MFMAs of the other half (left alone, the compiler sinks the reads
+    // next to their use and the LDS latency is exposed).
+    int st = 0;                       // stage of slice s
+    read(st, 0, fa0, fb0);
+    int s = 0;
+    for (; s < nk - 1; ++s) {
+      read(st, 1, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      // slices s+1 .. min(s+S-1, nk-1) are in flight; s+1 must have landed
+      const int last = s + S - 1 < nk - 1 ? s + S - 1 : nk - 1;
+      wait_slice(last - (s + 1));
+      __syncthreads();   // every wave is done with stage st (and has s+1)
+      const int nst = st + 1 == S ? 0 : st + 1;
+      read(nst, 0, fa0, fb0);
+      if (s + S < nk) issue(s + S, st);
+      st = nst;
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    read(st, 1, fa1, fb1);
+    mma(fa0, fb0);
+    mma(fa1, fb1);
+  }
+
+  if (splits > 1) {
+    // partial tile, layout [wave][i][j][e/4][lane] of float4
+    const int tile = it.nt * m_tiles + it.mt;
+    float4* dst = reinterpret_cast<float4*>(
+        a.part + ((size_t)z * m_tiles * n_tiles + tile) * C::kTileFloats);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          dst[(((w * TI + i) * TJ + j) * 4 + e4) * 64 + l] =
+              make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                          acc[i][j][4 * e4 + 3]);
+    return;
   }
 
   // epilogue: lane holds rows (e/4)*8 + (l/32)*4 + e%4, column l%32 of each 32x32 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < TJ; ++j) {
+    const int nl = n0 + wn * C::TN + j * 32 + (l & 31);
+    if (nl >= sv.n) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
-        if (m >= a.M) continue;
-        const int n = sv.col_base + n0 + wn * 64 + j * 32 + (l & 31);
-        const size_t o = (size_t)m * a.ldo + n;
-        const float v = acc[i][j][e];
-        switch (a.epi) {
-          case EPI_STORE_F32: static_cast<float*>(a.out)[o] = v; break;
-          case EPI_ADD_F32:
-            if (splits > 1) atomicAdd(static_cast<float*>(a.out) + o, v);
-            else static_cast<float*>(a.out)[o] += v;
-            break;
-          case EPI_STORE_BF16: static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v); break;
-          default: {
-            const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
-            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(g * v);
-          }
-        }
+        const int m = m0 + wm * C::TM + i * 32 + (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
+        if (m < a.M) store_out(a, m, sv.col_base + nl, acc[i][j][e]);
       }
+  }
 }
 
-static bool tiled_ok(const GemmArgs& a) {
-  if (a.M < 128 || a.Kd % big::BK) return false;
-  for (int i = 0; i < a.n_seg; ++i)
-    if (a.seg[i].n % big::BN) return false;
-  if (a.t && a.rank % big::BK) return false;
+// Sum the split-K partial tiles in split order and apply the epilogue; one
+// thread per float4 of a partial tile (4 rows of one column).
+template <class C>
+__global__ void __launch_bounds__(256)
+k_gemm_splitk_reduce(GemmArgs a, int m_tiles, int n_tiles, int splits) {
+  constexpr int Q = C::kTileFloats / 4;        // float4 per tile
+  const int tiles = m_tiles * n_tiles;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= tiles * Q) return;
+  const int tile = g / Q, q = g % Q;
+  const int mt = tile % m_tiles, nt = tile / m_tiles;
+  const float4* src = reinterpret_cast<const float4*>(a.part);
+  float4 t = src[(size_t)tile * Q + q];
+  for (int z = 1; z < splits; ++z) {
+    const float4 u = src[((size_t)z * tiles + tile) * Q + q];
+    t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+  }
+  // q = (((w * TI + i) * TJ + j) * 4 + e4) * 64 + l
+  const int l = q & 63;
+  int r = q >> 6;
+  const int e4 = r & 3;
+  r >>= 2;
+  const int j = r % C::TJ;
+  r /= C::TJ;
+  const int i = r % C::TI, w = r / C::TI;
+  const int wm = w / C::WN, wn = w % C::WN;
+  const SegView sv = pick_segment(a, nt * (C::BN / 16));
+  const int nl = sv.n0 + wn * C::TN + j * 32 + (l & 31);
+  if (nl >= sv.n) return;
+  const int mb = mt * C::BM + wm * C::TM + i * 32 + e4 * 8 + (l >> 5) * 4;
+  const float v[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (mb + c < a.M) store_out(a, mb + c, sv.col_base + nl, v[c]);
+}
+
+// Shapes the tiled kernel takes with column tile bn: K and the LoRA rank in
+// whole 32-wide slices, 16-byte aligned rows, every segment but a single one
+// a whole number of tiles (a single segment may end in a partial tile).
+static bool big_ok(const GemmArgs& a, int bn) {
+  if (a.Kd % big::BK || a.ldx % 8) return false;
+  if (a.t && (a.rank % big::BK || a.ldt % 8)) return false;
+  if (a.n_seg > 1)
+    for (int i = 0; i < a.n_seg; ++i)
+      if (a.seg[i].n % bn) return false;
   return true;
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) {
-  int n_tiles = 0;
-  for (int i = 0; i < a.n_seg; ++i) n_tiles += a.seg[i].n / big::BN;
-  const int m_tiles = (a.M + big::BM - 1) / big::BM;
-  int splits = 1;
-  if (a.epi == EPI_ADD_F32) {
-    const int wgs = m_tiles * n_tiles;
-    while (wgs * splits < 256 && splits < 4 && (a.Kd / big::BK) / (splits * 2) >= 8) splits *= 2;
+enum BigCfg { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
+struct BigPlan {
+  int cfg, m_tiles, n_tiles, splits;
+  double cost_us;
+};
+struct CfgInfo {
+  int bm, bn, per_cu;   // tile, workgroups resident per CU
+  double rate1, rate2;  // sustained bf16 TFLOP/s per CU with 1 / 2 of them resident
+};
+// Rates measured on MI355X for 1024-row passes of the Qwen3-8B shapes.
+static const CfgInfo kCfgInfo[3] = {
+    {256, 256, 1, 4.0, 4.0}, {256, 128, 2, 3.0, 4.3}, {128, 128, 2, 1.9, 3.4}};
+constexpr double kL2BytesPerUs = 12e6;     // L2 -> CU operand traffic the chip sustains
+constexpr double kPartBytesPerUs = 5e6;    // split-K partial tiles, written and read back
+
+// Pick the tile configuration and the K split from a cost model: rounds of
+// resident workgroups times the time one workgroup's K range takes at the
+// CU's sustained rate (bounded below by the L2 operand traffic), plus the
+// split-K partial tiles and the reduction launch.
+static BigPlan plan_big(const GemmArgs& a) {
+  BigPlan best = {-1, 0, 0, 0, 1e30};
+  const int nk = a.Kd / big::BK + (a.t ? a.rank / big::BK : 0);
+  for (int c = 0; c < 3; ++c) {
+    const CfgInfo& ci = kCfgInfo[c];
+    if (!big_ok(a, ci.bn)) continue;
+    const int m_tiles = (a.M + ci.bm - 1) / ci.bm;
+    int n_tiles = 0;
+    for (int i = 0; i < a.n_seg; ++i) n_tiles += (a.seg[i].n + ci.bn - 1) / ci.bn;
+    const int tiles = m_tiles * n_tiles;
+    const double slice_flop = 2.0 * ci.bm * ci.bn * big::BK;
+    const double slice_bytes = (ci.bm + ci.bn) * big::BK * 2.0;
+    for (int sp = 1; sp <= 16; ++sp) {
+      if (sp > 1 && a.Kd / big::BK / sp < 4) break;
+      const size_t part = (size_t)tiles * sp * ci.bm * ci.bn;
+      if (sp > 1 && (!a.part || part > a.part_floats)) break;
+      const int units = tiles * sp;
+      const int occ = units > 256 && ci.per_cu > 1 ? 2 : 1;
+      const int rounds = (units + 256 * occ - 1) / (256 * occ);
+      const double rate = (occ == 2 ? ci.rate2 : ci.rate1) / occ * 1e6;   // flop/us per WG
+      const int k_per = (nk + sp - 1) / sp;
+      double cost = rounds * k_per * slice_flop / rate;
+      const double l2 = (double)units * k_per * slice_bytes / kL2BytesPerUs;
+      if (l2 > cost) cost = l2;
+      cost += 2.0;
+      if (sp > 1) cost += (double)part * 4 * 2 / kPartBytesPerUs + 3.0;
+      if (cost < best.cost_us) best = BigPlan{c, m_tiles, n_tiles, sp, cost};
+    }
   }
-  const size_t lds = (size_t)big::kStages * big::kStage;
-  hipLaunchKernelGGL(k_gemm_tiled, dim3(m_tiles * n_tiles, 1, splits), dim3(big::kThreads), lds,
-                     s, a, m_tiles, n_tiles, splits);
+  return best;
+}
+
+template <class C>
+static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_gemm_big<C>, dim3(p.m_tiles * p.n_tiles * p.splits), dim3(C::kThreads),
+                     C::kLds, s, a, p.m_tiles, p.n_tiles, p.splits);
+  if (p.splits > 1) {
+    const int n = p.m_tiles * p.n_tiles * (C::kTileFloats / 4);
+    hipLaunchKernelGGL(k_gemm_splitk_reduce<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
+                       p.m_tiles, p.n_tiles, p.splits);
+  }
   return hipGetLastError();
 }
 
-// Tiled kernel when the output has enough 256 x 128 tiles to spread over the
-// chip; narrow outputs (the LoRA A products, N = r..3r) keep the skinny kernel,
-// whose 8-wave K split gives them enough workgroups.
+static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
+  switch (p.cfg) {
+    case CFG_L: return launch_big_cfg<big::CfgL>(a, p, s);
+    case CFG_M: return launch_big_cfg<big::CfgM>(a, p, s);
+    default: return launch_big_cfg<big::CfgS>(a, p, s);
+  }
+}
+
+// The tiled kernel for many rows; decode-sized row counts keep the skinny
+// kernel, which streams W once with the rows held in registers.
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  if (tiled_ok(a)) {
-    int n_tiles = 0;
-    for (int i = 0; i < a.n_seg; ++i) n_tiles += a.seg[i].n / big::BN;
-    const int m_tiles = (a.M + big::BM - 1) / big::BM;
-    if (m_tiles * n_tiles >= 64) return launch_gemm_tiled(a, s);
+  if (a.M >= 128) {
+    const BigPlan p = plan_big(a);
+    if (p.cfg >= 0) return launch_big(a, p, s);
   }
   return launch_gemm_skinny(a, s);
 }

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/uno.h"
+#include "uno.h"
 
 namespace uno {
 
@@ -70,7 +70,12 @@ struct GemmArgs {
   // EPI_LORA_T: out[m, n] = bf16(scale * gate(m) * acc); gate(m) = (m % K != 0)
   float scale;
   int rows_per_seq;
+  // split-K scratch (workspace) for fp32 partial tiles; null: no split
+  float* part;
+  size_t part_floats;
 };
+// split-K scratch carved per pass of 128 rows or more
+constexpr size_t kGemmPartFloats = size_t(16) << 20;   // 64 MB
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
