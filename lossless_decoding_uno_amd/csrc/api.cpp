@@ -128,7 +128,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.cs = reinterpret_cast<float2*>(take(R * (c.head_dim / 2) * sizeof(float2)));
   w.part_o = reinterpret_cast<float*>(take(parts * c.head_dim * 4));
   w.part_ml = reinterpret_cast<float*>(take(parts * 2 * 4));
-  w.gemm_part_floats = R >= 128 ? kGemmPartFloats : 0;
+  w.gemm_part_floats = R >= 128 ? kGemmPartFloats : kGemmPartFloatsSkinny;
   w.gemm_part = reinterpret_cast<float*>(take(w.gemm_part_floats * 4));
   w.total = off;
   return w;
@@ -172,7 +172,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
 
   auto scratch_args = [&] {
     GemmArgs g = {};
-    g.part = W.gemm_part_floats ? W.gemm_part : nullptr;
+    g.part = W.gemm_part;
     g.part_floats = W.gemm_part_floats;
     return g;
   };

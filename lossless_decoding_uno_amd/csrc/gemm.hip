@@ -7,15 +7,15 @@
 // verification; picx.dev summary, "Architecture"; paperglide reader, "Sampler
 // Extensions").
 //
-// Skinny kernel (decode rows, M <= 64 per workgroup): one workgroup owns a
-// 16-column tile of W and 16..64 rows of X; its 8 waves split the K dimension
+// Skinny kernel (decode rows, M <= 64 per workgroup): one workgroup owns
+// 16..64 columns of W and 16..64 rows of X; its 8 waves split the K dimension
 // (wave w takes the 32-wide K steps w, w+8, ...), so every weight byte is read
-// from HBM once per tile and the 8 waves' loads cover 512 contiguous bytes of
-// each of the 16 weight rows at a time.  Each wave issues
-// v_mfma_f32_16x16x32_bf16 (A = 16 rows of X, B = 16 columns of W^T); the eight
-// partial 16x16 tiles are summed in LDS in a fixed order (run-to-run identical)
-// and the epilogue stores, accumulates into the fp32 residual stream, or forms
-// the gated, scaled LoRA input T.
+// from HBM once and the 8 waves' loads cover 512 contiguous bytes of each
+// weight row at a time.  Each wave issues v_mfma_f32_16x16x32_bf16 (A = 16
+// rows of X, B = 16 columns of W^T); the eight partial tiles are summed in LDS
+// in a fixed order and the epilogue stores, accumulates into the fp32 residual
+// stream, or forms the gated, scaled LoRA input T.  Narrow outputs split K over
+// workgroups; a second kernel sums the splits in order (run-to-run identical).
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -60,18 +60,40 @@ __device__ __forceinline__ SegView pick_segment(const GemmArgs& a, int tile) {
   return v;
 }
 
+__device__ __forceinline__ void store_out(const GemmArgs& a, int m, int n, float v) {
+  const size_t o = (size_t)m * a.ldo + n;
+  switch (a.epi) {
+    case EPI_STORE_F32: static_cast<float*>(a.out)[o] = v; break;
+    case EPI_ADD_F32: static_cast<float*>(a.out)[o] += v; break;
+    case EPI_STORE_BF16: static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v); break;
+    default: {
+      const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
+      static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(g * v);
+    }
+  }
+}
+
 constexpr int kSkWaves = 8;
 
-template <int MT>
+// MT: 16-row tiles of X per workgroup; NT: 16-column tiles of W per
+// workgroup (MT * NT <= 4).  grid = (column groups, row groups, K splits).
+template <int MT, int NT>
 __global__ void __launch_bounds__(kSkWaves * 64)
 k_gemm_skinny(GemmArgs a) {
-  __shared__ f32x4 red[kSkWaves * MT * 64];
+  __shared__ f32x4 red[kSkWaves * MT * NT * 64];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int rr = l & 15, kg = l >> 4;
-  const SegView sv = pick_segment(a, blockIdx.x);
+  const SegView sv = pick_segment(a, blockIdx.x * NT);
   const int m0 = blockIdx.y * MT * 16;
+  const int splits = gridDim.z, zs = blockIdx.z;
 
-  const uint16_t* wrow = sv.w + (size_t)(sv.n0 + rr) * a.Kd + kg * 8;
+  // W rows of the NT column tiles (rows past the segment re-read its last row)
+  const uint16_t* wrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = sv.n0 + t * 16 + rr;
+    wrow[t] = sv.w + (size_t)(n < sv.n ? n : sv.n - 1) * a.Kd + kg * 8;
+  }
   const uint16_t* xrow[MT];
   bool xok[MT];
 #pragma unroll
@@ -80,95 +102,172 @@ k_gemm_skinny(GemmArgs a) {
     xok[mt] = m < a.M;
     xrow[mt] = a.x + (size_t)(xok[mt] ? m : 0) * a.ldx + kg * 8;
   }
-  f32x4 acc[MT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int n_steps = a.Kd >> 5;
-  int s = w;
-  // main loop, 4 K-steps in flight per wave
-  for (; s + 3 * kSkWaves < n_steps; s += 4 * kSkWaves) {
-    Frag bw[4];
-    Frag ax[4][MT];
+  // this split's 32-wide K steps; wave w takes ks0 + w, ks0 + w + 8, ...
+  const int n_all = a.Kd >> 5;
+  const int ks0 = n_all * zs / splits, ks1 = n_all * (zs + 1) / splits;
+  constexpr int UN = 4;   // K steps in flight per wave
+  int s = ks0 + w;
+  for (; s + (UN - 1) * kSkWaves < ks1; s += UN * kSkWaves) {
+    Frag bw[UN][NT];
+    Frag ax[UN][MT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bw[u].u = ldg16(wrow + (s + u * kSkWaves) * 32);
+    for (int u = 0; u < UN; ++u)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16(wrow[t] + (s + u * kSkWaves) * 32);
+#pragma unroll
+    for (int u = 0; u < UN; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         ax[u][mt].u = xok[mt] ? ldg16(xrow[mt] + (s + u * kSkWaves) * 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < UN; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][mt].v, bw[u].v, acc[mt], 0, 0, 0);
-  }
-  for (; s < n_steps; s += kSkWaves) {
-    Frag bw, ax;
-    bw.u = ldg16(wrow + s * 32);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      ax.u = xok[mt] ? ldg16(xrow[mt] + s * 32) : make_uint4(0, 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax.v, bw.v, acc[mt], 0, 0, 0);
-    }
+        for (int t = 0; t < NT; ++t)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][mt].v, bw[u][t].v, acc[mt][t], 0, 0, 0);
   }
-  // fused LoRA: T [M, r] (already gated and scaled) times B [n, r]^T
-  if (a.t && sv.lb) {
+  for (; s < ks1; s += kSkWaves) {
+    Frag bw[NT], ax[MT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bw[t].u = ldg16(wrow[t] + s * 32);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ax[mt].u = xok[mt] ? ldg16(xrow[mt] + s * 32) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[mt].v, bw[t].v, acc[mt][t], 0, 0, 0);
+  }
+  // fused LoRA (last split): T [M, r] (already gated and scaled) times B [n, r]^T
+  if (a.t && sv.lb && zs == splits - 1) {
     // rank 16 fills half of a 32-wide step: lanes past the rank feed zeros
     const int r_steps = (a.rank + 31) >> 5;
-    const uint16_t* brow = sv.lb + (size_t)(sv.n0 + rr) * a.rank + kg * 8;
     for (int rs = w; rs < r_steps; rs += kSkWaves) {
       const bool kin = rs * 32 + kg * 8 < a.rank;
-      Frag bw, ax;
-      bw.u = kin ? ldg16(brow + rs * 32) : make_uint4(0, 0, 0, 0);
+      Frag bw[NT], ax[MT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = sv.n0 + t * 16 + rr;
+        const uint16_t* brow = sv.lb + (size_t)(n < sv.n ? n : sv.n - 1) * a.rank + kg * 8;
+        bw[t].u = kin ? ldg16(brow + rs * 32) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = m0 + mt * 16 + rr;
-        ax.u = (kin && m < a.M) ? ldg16(a.t + (size_t)m * a.ldt + sv.t_col + rs * 32 + kg * 8)
-                                : make_uint4(0, 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax.v, bw.v, acc[mt], 0, 0, 0);
+        ax[mt].u = (kin && m < a.M) ? ldg16(a.t + (size_t)m * a.ldt + sv.t_col + rs * 32 + kg * 8)
+                                    : make_uint4(0, 0, 0, 0);
       }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[mt].v, bw[t].v, acc[mt][t], 0, 0, 0);
     }
   }
+  // the eight waves' partial tiles are summed in a fixed order
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[(w * MT + mt) * 64 + l] = acc[mt];
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[((w * MT + mt) * NT + t) * 64 + l] = acc[mt][t];
   __syncthreads();
   const float* redf = reinterpret_cast<const float*>(red);
-  for (int e = threadIdx.x; e < MT * 256; e += kSkWaves * 64) {
-    const int mt = e >> 8, rem = e & 255, ln = rem >> 2, i = rem & 3;
+  constexpr int kTile = MT * NT * 256;   // outputs of this workgroup
+  float* part = splits > 1
+      ? a.part + ((size_t)zs * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x) * kTile
+      : nullptr;
+  for (int e = threadIdx.x; e < kTile; e += kSkWaves * 64) {
+    const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kSkWaves; ++ww) v += redf[((ww * MT + mt) * 64 + ln) * 4 + i];
-    const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
-    if (m >= a.M) continue;
-    const int n = sv.col_base + sv.n0 + (ln & 15);
-    const size_t o = (size_t)m * a.ldo + n;
-    switch (a.epi) {
-      case EPI_STORE_F32: static_cast<float*>(a.out)[o] = v; break;
-      case EPI_ADD_F32: static_cast<float*>(a.out)[o] += v; break;
-      case EPI_STORE_BF16: static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v); break;
-      default: {
-        const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
-        static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(g * v);
-      }
+    for (int ww = 0; ww < kSkWaves; ++ww) v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + i];
+    if (part) {
+      part[e] = v;
+      continue;
     }
+    const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
+    const int nl = sv.n0 + t * 16 + (ln & 15);
+    if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
+  }
+}
+
+// Sum the skinny kernel's split-K partials in split order and apply the
+// epilogue; one thread per output of a workgroup tile.
+template <int MT, int NT>
+__global__ void __launch_bounds__(256)
+k_gemm_skinny_reduce(GemmArgs a, int gx, int gy, int splits) {
+  constexpr int kTile = MT * NT * 256;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= gx * gy * kTile) return;
+  const int wg = g / kTile, e = g % kTile;
+  const int bx = wg % gx, by = wg / gx;
+  float v = a.part[(size_t)wg * kTile + e];
+  for (int z = 1; z < splits; ++z) v += a.part[((size_t)z * gx * gy + wg) * kTile + e];
+  const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
+  const SegView sv = pick_segment(a, bx * NT);
+  const int m = by * MT * 16 + mt * 16 + 4 * (ln >> 4) + i;
+  const int nl = sv.n0 + t * 16 + (ln & 15);
+  if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
+}
+
+struct SkinnyPlan {
+  int mt, nt, gx, gy, splits;
+};
+
+// Column tiles per workgroup: as many as keep >= 128 workgroups (fewer
+// re-reads of X); K splits until about 512 workgroups are in flight.
+static SkinnyPlan plan_skinny(const GemmArgs& a) {
+  SkinnyPlan p;
+  p.mt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+  p.gy = a.M <= 32 ? 1 : (a.M + 63) / 64;
+  int tiles16 = 0;
+  for (int i = 0; i < a.n_seg; ++i) tiles16 += (a.seg[i].n + 15) / 16;
+  p.nt = 1;
+  for (int nt = 4 / p.mt; nt > 1; nt /= 2) {
+    bool ok = true;
+    if (a.n_seg > 1)
+      for (int i = 0; i < a.n_seg; ++i) ok = ok && a.seg[i].n % (16 * nt) == 0;
+    if (ok && (tiles16 + nt - 1) / nt * p.gy >= 128) { p.nt = nt; break; }
+  }
+  p.gx = (tiles16 + p.nt - 1) / p.nt;
+  const int steps = a.Kd >> 5;
+  const size_t tile = (size_t)p.mt * p.nt * 256;
+  p.splits = 1;
+  if (a.part)
+    while (p.gx * p.gy * p.splits < 512 && steps / (p.splits * 2) >= kSkWaves &&
+           (size_t)p.gx * p.gy * p.splits * 2 * tile <= a.part_floats)
+      p.splits *= 2;
+  return p;
+}
+
+template <int MT, int NT>
+static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
+  if (p.splits > 1) {
+    const int n = p.gx * p.gy * MT * NT * 256;
+    hipLaunchKernelGGL((k_gemm_skinny_reduce<MT, NT>), dim3((n + 255) / 256), dim3(256), 0, s, a,
+                       p.gx, p.gy, p.splits);
   }
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s) {
-  int tiles = 0;
-  for (int i = 0; i < a.n_seg; ++i) tiles += a.seg[i].n / 16;
-  const dim3 block(kSkWaves * 64);
-  if (a.M <= 16) {
-    hipLaunchKernelGGL(k_gemm_skinny<1>, dim3(tiles, 1), block, 0, s, a);
-  } else if (a.M <= 32) {
-    hipLaunchKernelGGL(k_gemm_skinny<2>, dim3(tiles, 1), block, 0, s, a);
-  } else {
-    hipLaunchKernelGGL(k_gemm_skinny<4>, dim3(tiles, (a.M + 63) / 64), block, 0, s, a);
+  const SkinnyPlan p = plan_skinny(a);
+  switch (p.mt * 8 + p.nt) {
+    case 8 + 4: launch_sk<1, 4>(a, p, s); break;
+    case 8 + 2: launch_sk<1, 2>(a, p, s); break;
+    case 8 + 1: launch_sk<1, 1>(a, p, s); break;
+    case 16 + 2: launch_sk<2, 2>(a, p, s); break;
+    case 16 + 1: launch_sk<2, 1>(a, p, s); break;
+    default: launch_sk<4, 1>(a, p, s); break;
   }
   return hipGetLastError();
 }
-
 
 // ============================================================================
 // Tiled kernel (many rows: batched decode blocks, prompt chunks).
@@ -233,18 +332,6 @@ __device__ __forceinline__ Item item_of(int id, int m_tiles, int splits, int nwg
 }
 }  // namespace big
 
-__device__ __forceinline__ void store_out(const GemmArgs& a, int m, int n, float v) {
-  const size_t o = (size_t)m * a.ldo + n;
-  switch (a.epi) {
-    case EPI_STORE_F32: static_cast<float*>(a.out)[o] = v; break;
-    case EPI_ADD_F32: static_cast<float*>(a.out)[o] += v; break;
-    case EPI_STORE_BF16: static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v); break;
-    default: {
-      const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
-      static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(g * v);
-    }
-  }
-}
 
 // two waves per SIMD in every configuration (at most 256 VGPRs per wave)
 template <class C>
