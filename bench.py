@@ -11,11 +11,20 @@ drafts a ~ U{0..16} per sequence (staggered, exercising ragged commit and
 rollback); accepted tokens per step = sum_b (a_b + 1).  KV content and weights
 are seeded synthetic data.
 
-Prints one JSON line.  `roofline` covers the kernel class that takes the most
-time per step (found in an untimed probe step), timed with HIP events that the
-library records around each of its launches inside the timed region.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Prints one JSON line.  `roofline` covers the single kernel that takes the most
+time per step (block attention at this workload; the per-class totals come from
+an untimed probe step), timed with HIP events that the library records around
+each of its launches inside the timed region: achieved = the algorithmic bytes
+of those launches (every cached K/V entry the block's rows may see, read once,
+plus q in and the output out) / their summed duration.  `traffic` is the HBM
+traffic per launch that rocprofv3 counters measured for the same kernel source
+(FETCH_SIZE + WRITE_SIZE, scaled by the factor the same counters give for a
+plain copy of known size, `--calibrate-copy`), or null when the kernel source
+has changed since.  `roofline_gemm` is the MFMA fraction of the projection
+GEMMs of both passes (flops / their probe-step time).  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
 """
+import hashlib
 import argparse
 import json
 import os
@@ -30,6 +39,22 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
+# HBM traffic of the attention kernel from rocprofv3 counters (see the
+# attention profile summary under profiles/): mean FETCH_SIZE and WRITE_SIZE per
+# dispatch, scaled by the copy calibration factor, for the kernel source with
+# this digest.
+ATTN_TRAFFIC = None
+ATTN_SOURCES = ["lossless_decoding_uno_amd/csrc/attention.hip",
+                "lossless_decoding_uno_amd/csrc/uno_device.h"]
+
+
+def attn_source_digest():
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -41,6 +66,8 @@ def parse():
     ap.add_argument("--K", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (counter calibration)")
     return ap.parse_args()
 
 
@@ -114,6 +141,52 @@ def gemm_flops_per_pass(cfg, R, draft):
     return 2.0 * R * per_layer * cfg["n_layers"]
 
 
+def measured_ceilings(torch):
+    """Streaming ceilings measured on this GPU with library kernels: a 2 GiB read
+    (torch sum) and a 1 GiB copy (read + write bytes)."""
+    x = torch.ones((1 << 31) // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(2):
+        x.sum()
+        y.copy_(x[: y.numel()])
+    torch.cuda.synchronize()
+    best_r, best_c = 1e9, 1e9
+    for _ in range(5):
+        ev[0].record(); x.sum(); ev[1].record()
+        ev[2].record(); y.copy_(x[: y.numel()]); ev[3].record()
+        torch.cuda.synchronize()
+        best_r = min(best_r, ev[0].elapsed_time(ev[1]))
+        best_c = min(best_c, ev[2].elapsed_time(ev[3]))
+    del x, y
+    torch.cuda.empty_cache()
+    return {"read_GBps": round((1 << 31) / (best_r / 1e3) / 1e9, 1),
+            "copy_GBps": round(2 * (1 << 30) / (best_c / 1e3) / 1e9, 1)}
+
+
+def library_gemm_reference(torch, cfg, R):
+    """ms per step that torch.matmul (hipBLASLt) takes for the same four
+    projection shapes (both passes, no LoRA), for comparison."""
+    total = 0.0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for name in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"):
+        N, Kd, _ = proj_shape(cfg, name)
+        x = torch.randn(R, Kd, device="cuda", dtype=torch.bfloat16)
+        w = torch.randn(N, Kd, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(x, w.t())
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(10):
+            torch.matmul(x, w.t())
+        ev[1].record()
+        torch.cuda.synchronize()
+        total += ev[0].elapsed_time(ev[1]) / 10
+        del x, w
+    torch.cuda.empty_cache()
+    return round(total * 2 * cfg["n_layers"], 3)
+
+
 def run_timed(W, steps, warmup, torch, timer=None):
     for i in range(warmup):
         W.step(i)
@@ -144,13 +217,22 @@ def run_timed(W, steps, warmup, torch, timer=None):
     return ms, wall, tokens, used, attn_bytes, kv0
 
 
+CLASSES = ["attention", "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "lora_a", "lm_head",
+           "sampler"]
+
+
+def class_ids(U):
+    return {"attention": U.TIME_ATTENTION, "gemm_qkv": U.TIME_GEMM_QKV, "gemm_o": U.TIME_GEMM_O,
+            "gemm_gate_up": U.TIME_GEMM_GATE_UP, "gemm_down": U.TIME_GEMM_DOWN,
+            "lora_a": U.TIME_LORA_A, "lm_head": U.TIME_LM_HEAD, "sampler": U.TIME_SAMPLER}
+
+
 def probe_classes(U, W, i, torch):
-    """Untimed: total ms per kernel class over one step (one class per rerun)."""
+    """Untimed: total ms per kernel launch site over one step (one class per rerun)."""
     totals = {}
-    names = {U.TIME_ATTENTION: "attention", U.TIME_GEMM: "gemm", U.TIME_LORA_A: "lora_a",
-             U.TIME_LM_HEAD: "lm_head", U.TIME_SAMPLER: "sampler"}
-    for cls, name in names.items():
-        timer = U.KernelTimer(cls, 400)
+    ids = class_ids(U)
+    for name in CLASSES:
+        timer = U.KernelTimer(ids[name], 400)
         kv_save = W.kv.kv_len.clone()
         step_save = W.step_ctr.clone()
         e_save = W.e.clone()
@@ -168,6 +250,24 @@ def probe_classes(U, W, i, torch):
     return totals
 
 
+def proj_shape(cfg, name):
+    """(output columns N, reduction length Kd, output bytes per element) of a projection."""
+    D, F = cfg["d_model"], cfg["d_ffn"]
+    qd = cfg["n_q_heads"] * cfg["head_dim"]
+    kd = cfg["n_kv_heads"] * cfg["head_dim"]
+    return {"gemm_qkv": (qd + 2 * kd, D, 4), "gemm_o": (D, qd, 8), "gemm_gate_up": (2 * F, D, 4),
+            "gemm_down": (D, F, 8), "lm_head": (cfg["vocab"], D, 4)}[name]
+
+
+def gemm_launch_work(cfg, name, R, draft):
+    """Algorithmic (flops, bytes) of one launch: every weight (and, drafting, LoRA B
+    and the LoRA input T) read once, X read once, the output written (and read,
+    for the residual adds)."""
+    N, Kd, ob = proj_shape(cfg, name)
+    r = cfg["lora_rank"] if (draft and name != "lm_head") else 0
+    flops = 2.0 * R * N * (Kd + r)
+    byts = 2.0 * N * (Kd + r) + 2.0 * R * (Kd + r) + ob * R * N
+    return flops, byts
 def cpu_baseline(K, ctx, forced_mean_tokens):
     """The oracle (fp64 model, exact-integer sampler) on one sequence of the
     workload: a whole step (best of two) with 1 and with 5 layers of the 8B
@@ -215,6 +315,16 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
     import lossless_decoding_uno_amd as U
     import synth
     U.load_library()
@@ -235,37 +345,63 @@ def main():
     W.step_ctr.copy_(torch.zeros(args.batch, dtype=torch.uint64))
     classes = probe_classes(U, W, 0, torch)
     log("class ms per step: %s" % json.dumps({k: round(v, 3) for k, v in classes.items()}))
-    dominant = max(classes, key=classes.get)
-    cls_id = {"attention": U.TIME_ATTENTION, "gemm": U.TIME_GEMM, "lora_a": U.TIME_LORA_A,
-              "lm_head": U.TIME_LM_HEAD, "sampler": U.TIME_SAMPLER}[dominant]
-    n_launch = {"attention": 2 * cfg["n_layers"], "gemm": 8 * cfg["n_layers"],
-                "lora_a": 4 * cfg["n_layers"], "lm_head": 2, "sampler": 2}[dominant]
-    timer = U.KernelTimer(cls_id, n_launch * args.steps)
-    log("timed region: %d steps after %d warmup (dominant class: %s)" % (args.steps, args.warmup,
-                                                                       dominant))
+    dominant = max(CLASSES, key=lambda k: classes[k])
+    L = cfg["n_layers"]
+    per_step = {"attention": 2 * L, "gemm_qkv": 2 * L, "gemm_o": 2 * L, "gemm_gate_up": 2 * L,
+                "gemm_down": 2 * L, "lora_a": 4 * L, "lm_head": 2, "sampler": 2}[dominant]
+    timer = U.KernelTimer(class_ids(U)[dominant], per_step * args.steps)
+    log("timed region: %d steps after %d warmup (dominant kernel: %s)" % (args.steps, args.warmup,
+                                                                        dominant))
     ms, wall, tokens, used, attn_bytes, kv0 = run_timed(W, args.steps, args.warmup, torch, timer)
     durs = np.array(timer.durations_ms(used))
     timer.close()
     ms_step = ms / args.steps
     value = tokens / (ms / 1e3)
     R = args.batch * K
+    avg_us = round(float(durs.mean()) * 1e3, 2)
     if dominant == "attention":
         achieved = float(np.sum(attn_bytes[:used])) / (durs.sum() / 1e3) / 1e9
+        traffic = None
+        if ATTN_TRAFFIC is not None and ATTN_TRAFFIC["source"] == attn_source_digest():
+            traffic = ATTN_TRAFFIC["bytes_per_launch"]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_attention<128>", "launches": int(used),
-                "avg_launch_us": round(float(durs.mean()) * 1e3, 2)}
-    elif dominant == "gemm":
-        fl = (gemm_flops_per_pass(cfg, R, True) + gemm_flops_per_pass(cfg, R, False)) * args.steps
-        achieved = fl / (durs.sum() / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "k_gemm (4 projections per layer, both passes)", "launches": int(used),
-                "avg_launch_us": round(float(durs.mean()) * 1e3, 2)}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_attention (block attention, split-KV partials)", "launches": int(used),
+                "avg_launch_us": avg_us,
+                "algorithmic_bytes_per_launch": round(float(np.mean(attn_bytes[:used])))}
+    elif dominant.startswith("gemm") or dominant == "lm_head":
+        # launches alternate draft pass (L layers) / verify pass (L layers) per step
+        work = [gemm_launch_work(cfg, dominant, R, (k // (per_step // 2)) % 2 == 0)
+                for k in range(used)]
+        fl = sum(w[0] for w in work)
+        by = sum(w[1] for w in work)
+        t = durs.sum() / 1e3
+        if fl / by > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            roof = {"bound": "mfma", "achieved": round(fl / t / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        else:
+            roof = {"bound": "hbm", "achieved": round(by / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+        roof.update({"traffic": None, "kernel": "k_gemm (%s)" % dominant, "launches": int(used),
+                     "avg_launch_us": avg_us})
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": dominant, "launches": int(used),
-                "avg_launch_us": round(float(durs.mean()) * 1e3, 2)}
+                "avg_launch_us": avg_us}
+    ceil = measured_ceilings(torch)
+    if roof["unit"] == "GB/s" and roof["achieved"] is not None:
+        roof["frac_of_measured_read"] = round(roof["achieved"] / ceil["read_GBps"], 4)
+    # MFMA fraction of the projection GEMMs (both passes) from the probe step
+    gemm_ms = sum(classes[k] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"))
+    gfl = gemm_flops_per_pass(cfg, R, True) + gemm_flops_per_pass(cfg, R, False)
+    vfl = gemm_flops_per_pass(cfg, R, False)
+    roof_gemm = {"bound": "mfma", "achieved": round(gfl / (gemm_ms / 1e3) / 1e12, 1),
+                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(gfl / (gemm_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "ms_per_step": round(gemm_ms, 3), "flop_per_step": gfl,
+                 "verify_flop_per_step": vfl,
+                 "kernel": "k_gemm: q|k|v, o, gate|up, down projections of both passes",
+                 "torch_matmul_ms_per_step": library_gemm_reference(torch, cfg, R)}
     out = {"metric": "accepted tokens/s/GPU (Qwen3-8B shape, Psi-Spec draft+verify step)",
            "value": round(value, 1), "unit": "accepted tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
@@ -275,6 +411,8 @@ def main():
                args.batch, args.ctx, K, K), "global_batch": args.batch, "seq_len": args.ctx,
                "block_K": K, "parallelism": "none (1 GPU)"},
            "roofline": roof,
+           "roofline_gemm": roof_gemm,
+           "measured_ceilings": ceil,
            "kernel_class_ms_per_step": {k: round(v, 3) for k, v in classes.items()},
            "forward_passes_per_s": round(2 * args.steps / (ms / 1e3), 2),
            "wall_s_timed": round(wall, 3)}

@@ -206,7 +206,13 @@ enum {
                              gate|up, down), LoRA B fused when drafting       */
   UNO_TIME_LORA_A = 3,    /* the LoRA A products (x A^T, gated and scaled)    */
   UNO_TIME_LM_HEAD = 4,   /* the final vocabulary projection                  */
-  UNO_TIME_SAMPLER = 5    /* draft sampling and the accept / resample kernels */
+  UNO_TIME_SAMPLER = 5,   /* draft sampling and the accept / resample kernels */
+  /* one projection of every layer (also counted in UNO_TIME_GEMM); a launch
+   * is the GEMM plus, when K is split, its ordered reduction kernel         */
+  UNO_TIME_GEMM_QKV = 6,
+  UNO_TIME_GEMM_O = 7,
+  UNO_TIME_GEMM_GATE_UP = 8,
+  UNO_TIME_GEMM_DOWN = 9
 };
 int uno_set_timing_events(int kernel_class, void *const *start, void *const *stop, int n);
 int uno_timing_events_used(void);

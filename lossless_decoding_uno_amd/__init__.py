@@ -29,6 +29,7 @@ EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_verify_block", "uno_dr
            "uno_last_hip_error")
 
 TIME_ATTENTION, TIME_GEMM, TIME_LORA_A, TIME_LM_HEAD, TIME_SAMPLER = 1, 2, 3, 4, 5
+TIME_GEMM_QKV, TIME_GEMM_O, TIME_GEMM_GATE_UP, TIME_GEMM_DOWN = 6, 7, 8, 9
 
 
 class UnoConfig(ctypes.Structure):

@@ -28,9 +28,11 @@ struct TimingHook {
 };
 TimingHook g_hook;
 
+// Records events around `launch` when the armed class is `cls` or `cls2`
+// (a projection GEMM belongs to UNO_TIME_GEMM and to its own class).
 template <class F>
-hipError_t timed(int cls, hipStream_t s, F&& launch) {
-  const bool on = g_hook.cls == cls && g_hook.count < g_hook.n;
+hipError_t timed(int cls, hipStream_t s, F&& launch, int cls2 = -1) {
+  const bool on = (g_hook.cls == cls || g_hook.cls == cls2) && g_hook.count < g_hook.n;
   if (on) hipEventRecord(g_hook.start[g_hook.count], s);
   const hipError_t e = launch();
   if (on) hipEventRecord(g_hook.stop[g_hook.count++], s);
@@ -204,7 +206,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 3;
       g.t = lq ? W.t : nullptr; g.ldt = 3 * r; g.rank = r;
       g.epi = EPI_STORE_F32; g.out = W.qkv; g.ldo = QKV;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_QKV));
     }
     UNO_TRY(launch_rope_kv_write(c, W.qkv, W.cs, *kv, li, B, K, draft ? 0 : pos_offset, W.qb,
                                  W.qlo, status, s));
@@ -234,7 +236,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 1;
       g.t = lo ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_O));
     }
     // ---- MLP block
     UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.mlp_norm), R, D, c.rms_eps, W.xn, s));
@@ -250,7 +252,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 2;
       g.t = lg ? W.t : nullptr; g.ldt = 2 * r; g.rank = r;
       g.epi = EPI_STORE_F32; g.out = W.gu; g.ldo = 2 * F;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_GATE_UP));
     }
     UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
     if (ld) {
@@ -264,7 +266,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 1;
       g.t = ld ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }));
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_DOWN));
     }
   }
   if (logits) {
@@ -380,7 +382,7 @@ int uno_set_timing_events(int kernel_class, void* const* start, void* const* sto
     g_hook = TimingHook();
     return UNO_OK;
   }
-  if (kernel_class < 0 || kernel_class > UNO_TIME_SAMPLER || !start || !stop || n < 1)
+  if (kernel_class < 0 || kernel_class > UNO_TIME_GEMM_DOWN || !start || !stop || n < 1)
     return UNO_ERR_INVALID_ARG;
   g_hook.cls = kernel_class;
   g_hook.start = reinterpret_cast<hipEvent_t*>(const_cast<void**>(start));

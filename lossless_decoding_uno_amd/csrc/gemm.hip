@@ -303,9 +303,12 @@ struct Cfg {
   static constexpr int kInstr = kStage / 1024;       // 1 KB DMA instructions per slice
   static constexpr int kIW = kInstr / kWaves;        // per wave
   static constexpr int kInstrA = kLdsA / 1024;
+  static constexpr int kIA = kInstrA / kWaves;       // A instructions per wave (first)
+  static constexpr int kIB = kIW - kIA;              // then B instructions
   static constexpr int kLds = S * kStage;
   static constexpr int kTileFloats = BM * BN;
-  static_assert(kInstr % kWaves == 0, "DMA instructions must split evenly over the waves");
+  static_assert(kInstr % kWaves == 0 && kInstrA % kWaves == 0,
+                "DMA instructions of A and of B must split evenly over the waves");
 };
 using CfgL = Cfg<256, 256, 2, 4, 4>;
 using CfgM = Cfg<256, 128, 2, 2, 3>;
@@ -354,37 +357,55 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits) {
   const int kb0 = nk_base * z / splits, kb1 = nk_base * (z + 1) / splits;
   const int nk = (kb1 - kb0) + (z == splits - 1 ? nk_lora : 0);
 
-  // DMA lanes: instruction ins copies 16 rows (A rows, then B rows); lane l
-  // fills row 16*ins' + l/4, physical chunk l%4, which holds logical chunk
-  // (l%4) ^ swz_f(row).  Rows past M / past the segment re-read a valid row;
-  // their results are discarded.
-  const uint16_t* pbase[IW];
-  const uint16_t* plora[IW];
+  // DMA: every wave issues kIA instructions of A rows, then kIB of B rows,
+  // each 16 rows x 64 bytes; lane l fills row 16*i + l/4 (i the instruction's
+  // index among all A or all B instructions), physical chunk l%4, which holds
+  // logical chunk (l%4) ^ swz_f(row).  Rows past M / past the segment re-read
+  // a valid row; their results are discarded.  Buffer loads with per-lane byte
+  // offsets fixed here and the slice's K offset as the scalar offset; the
+  // resources span exactly the operands, so no load leaves them.
+  constexpr int IA = C::kIA, IB = C::kIB;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const i32x4 rs_x = make_rsrc(a.x, (uint32_t)((size_t)a.M * a.ldx * 2));
+  const i32x4 rs_w = make_rsrc(sv.w, (uint32_t)((size_t)sv.n * a.Kd * 2));
+  const i32x4 rs_t = a.t ? make_rsrc(a.t, (uint32_t)((size_t)a.M * a.ldt * 2)) : rs_x;
+  const i32x4 rs_lb = sv.lb ? make_rsrc(sv.lb, (uint32_t)((size_t)sv.n * a.rank * 2)) : rs_w;
+  uint32_t vb[IW], vl[IW];
 #pragma unroll
   for (int ii = 0; ii < IW; ++ii) {
-    const int ins = w * IW + ii;
-    const bool is_a = ins < C::kInstrA;
-    const int row = (is_a ? ins : ins - C::kInstrA) * 16 + (l >> 2);
+    const bool is_a = ii < IA;
+    const int row = (is_a ? wu * IA + ii : wu * IB + ii - IA) * 16 + (l >> 2);
     const int ch = (l & 3) ^ swz_f(row);
     if (is_a) {
       const int m = m0 + row < a.M ? m0 + row : 0;
-      pbase[ii] = a.x + (size_t)m * a.ldx + ch * 8;
-      plora[ii] = a.t ? a.t + (size_t)m * a.ldt + sv.t_col + ch * 8 : a.x;
+      vb[ii] = (uint32_t)(((size_t)m * a.ldx + ch * 8) * 2);
+      vl[ii] = (uint32_t)(((size_t)m * a.ldt + sv.t_col + ch * 8) * 2);
     } else {
       const int n = n0 + row < sv.n ? n0 + row : sv.n - 1;
-      pbase[ii] = sv.w + (size_t)n * a.Kd + ch * 8;
-      plora[ii] = sv.lb ? sv.lb + (size_t)n * a.rank + ch * 8 : sv.w;
+      vb[ii] = (uint32_t)(((size_t)n * a.Kd + ch * 8) * 2);
+      vl[ii] = (uint32_t)(((size_t)n * a.rank + ch * 8) * 2);
     }
   }
-  const uint32_t lds_base = lds_addr(lds) + w * IW * 1024;
+  const uint32_t lds0 = lds_addr(lds);
+  const uint32_t dst_a = lds0 + wu * IA * 1024, dst_b = lds0 + C::kLdsA + wu * IB * 1024;
   auto issue = [&](int s, int stage) {
     const int kk = kb0 + s;
-    const bool lora = kk >= kb1;
-    const int koff = (lora ? kk - kb1 : kk) * BK;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage * C::kStage);
+    const uint32_t so = stage * C::kStage;
+    if (kk < kb1) {
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(kk * BK * 2);
 #pragma unroll
-    for (int ii = 0; ii < IW; ++ii)
-      lds_dma16((lora ? plora[ii] : pbase[ii]) + koff, dst + ii * 1024);
+      for (int ii = 0; ii < IW; ++ii) {
+        if (ii < IA) lds_dma16_buf(rs_x, vb[ii], soff, dst_a + so + ii * 1024);
+        else lds_dma16_buf(rs_w, vb[ii], soff, dst_b + so + (ii - IA) * 1024);
+      }
+    } else {
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((kk - kb1) * BK * 2);
+#pragma unroll
+      for (int ii = 0; ii < IW; ++ii) {
+        if (ii < IA) lds_dma16_buf(rs_t, vl[ii], soff, dst_a + so + ii * 1024);
+        else lds_dma16_buf(rs_lb, vl[ii], soff, dst_b + so + (ii - IA) * 1024);
+      }
+    }
   };
   // slice s has landed once at most `ahead` later slices of this wave are in flight
   auto wait_slice = [&](int ahead) {
@@ -529,6 +550,11 @@ k_gemm_splitk_reduce(GemmArgs a, int m_tiles, int n_tiles, int splits) {
 static bool big_ok(const GemmArgs& a, int bn) {
   if (a.Kd % big::BK || a.ldx % 8) return false;
   if (a.t && (a.rank % big::BK || a.ldt % 8)) return false;
+  // buffer offsets are 32-bit: every operand under 2 GiB
+  const size_t lim = size_t(1) << 31;
+  if ((size_t)a.M * a.ldx * 2 >= lim || (a.t && (size_t)a.M * a.ldt * 2 >= lim)) return false;
+  for (int i = 0; i < a.n_seg; ++i)
+    if ((size_t)a.seg[i].n * a.Kd * 2 >= lim) return false;
   if (a.n_seg > 1)
     for (int i = 0; i < a.n_seg; ++i)
       if (a.seg[i].n % bn) return false;

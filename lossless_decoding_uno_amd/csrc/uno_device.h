@@ -117,6 +117,26 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_off) {
 }
 
 // 32-bit LDS address of a pointer into __shared__ memory
+// Buffer resource (raw, stride 0) over `bytes` bytes at `base`; loads past
+// the end return zero instead of faulting.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t base = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(base & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(base >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+// 16 bytes per lane from rsrc + voff + soff into LDS at lds_off + 16 * lane
+// (buffer_load_dwordx4 with the LDS bit; counted by vmcnt).
+__device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                              uint32_t lds_off) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
