@@ -287,9 +287,11 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s) {
 // Two resident workgroups cover each other's barrier waits, prologue and
 // epilogue.
 //
-// Split-K (too few tiles for the chip): every split writes its fp32 partial
-// tile to scratch and a second kernel sums the splits in order (run-to-run
-// identical) and applies the epilogue.
+// Split-K: whole rounds of tiles run unsplit; the tiles left over for a last,
+// partly filled round (or all tiles, when there are too few for the chip) are
+// split over K.  Every split writes its fp32 partial tile to scratch and a
+// second kernel sums the splits in order (run-to-run identical) and applies
+// the epilogue.
 // ============================================================================
 namespace big {
 constexpr int BK = 32;
@@ -339,23 +341,33 @@ __device__ __forceinline__ Item item_of(int id, int m_tiles, int splits, int nwg
 // two waves per SIMD in every configuration (at most 256 VGPRs per wave)
 template <class C>
 __global__ void __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits) {
+k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
   using namespace big;
   constexpr int TI = C::TI, TJ = C::TJ, IW = C::kIW, S = C::S;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wm = w / C::WN, wn = w % C::WN;
 
-  const Item it = item_of(blockIdx.x, m_tiles, splits, m_tiles * n_tiles * splits);
-  const int m0 = it.mt * C::BM, z = it.z;
-  const SegView sv = pick_segment(a, it.nt * (C::BN / 16));
+  // Tiles [0, n_full) run whole, one workgroup each (XCD-aware order); the
+  // remaining tiles are split `splits` ways over K to fill the last round.
+  int mt, nt, z, sp;
+  if ((int)blockIdx.x < n_full) {
+    const Item it = item_of(blockIdx.x, m_tiles, 1, n_full);
+    mt = it.mt; nt = it.nt; z = 0; sp = 1;
+  } else {
+    const int j = blockIdx.x - n_full;
+    const int tile = n_full + j / splits;
+    mt = tile % m_tiles; nt = tile / m_tiles; z = j % splits; sp = splits;
+  }
+  const int m0 = mt * C::BM;
+  const SegView sv = pick_segment(a, nt * (C::BN / 16));
   const int n0 = sv.n0;
 
   // K slices of this split (LoRA slices after the last split's base slices)
   const int nk_base = a.Kd / BK;
   const int nk_lora = (a.t && sv.lb) ? a.rank / BK : 0;
-  const int kb0 = nk_base * z / splits, kb1 = nk_base * (z + 1) / splits;
-  const int nk = (kb1 - kb0) + (z == splits - 1 ? nk_lora : 0);
+  const int kb0 = nk_base * z / sp, kb1 = nk_base * (z + 1) / sp;
+  const int nk = (kb1 - kb0) + (z == sp - 1 ? nk_lora : 0);
 
   // DMA: every wave issues kIA instructions of A rows, then kIB of B rows,
   // each 16 rows x 64 bytes; lane l fills row 16*i + l/4 (i the instruction's
@@ -454,19 +466,33 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits) {
     int st = 0;                       // stage of slice s
     read(st, 0, fa0, fb0);
     int s = 0;
+    // steady state: slices s+1 .. s+S-1 are in flight, s+1 must have landed,
+    // and slice s+S refills the stage just read
+    for (; s < nk - S; ++s) {
+      read(st, 1, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(S - 2) * IW>();
+      __syncthreads();   // every wave is done with stage st (and has s+1)
+      const int nst = st + 1 == S ? 0 : st + 1;
+      read(nst, 0, fa0, fb0);
+      issue(s + S, st);
+      st = nst;
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // tail: nothing left to issue; wait for everything in flight
     for (; s < nk - 1; ++s) {
       read(st, 1, fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
       mma(fa0, fb0);
       __builtin_amdgcn_sched_barrier(0);
-      // slices s+1 .. min(s+S-1, nk-1) are in flight; s+1 must have landed
-      const int last = s + S - 1 < nk - 1 ? s + S - 1 : nk - 1;
-      wait_slice(last - (s + 1));
-      __syncthreads();   // every wave is done with stage st (and has s+1)
-      const int nst = st + 1 == S ? 0 : st + 1;
-      read(nst, 0, fa0, fb0);
-      if (s + S < nk) issue(s + S, st);
-      st = nst;
+      wait_vmcnt<0>();
+      __syncthreads();
+      st = st + 1 == S ? 0 : st + 1;
+      read(st, 0, fa0, fb0);
       __builtin_amdgcn_sched_barrier(0);
       mma(fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
@@ -476,11 +502,12 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits) {
     mma(fa1, fb1);
   }
 
-  if (splits > 1) {
+  if (sp > 1) {
     // partial tile, layout [wave][i][j][e/4][lane] of float4
-    const int tile = it.nt * m_tiles + it.mt;
+    const int rem = m_tiles * n_tiles - n_full;
+    const int tile = nt * m_tiles + mt - n_full;
     float4* dst = reinterpret_cast<float4*>(
-        a.part + ((size_t)z * m_tiles * n_tiles + tile) * C::kTileFloats);
+        a.part + ((size_t)z * rem + tile) * C::kTileFloats);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -512,17 +539,18 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits) {
 // thread per float4 of a partial tile (4 rows of one column).
 template <class C>
 __global__ void __launch_bounds__(256)
-k_gemm_splitk_reduce(GemmArgs a, int m_tiles, int n_tiles, int splits) {
+k_gemm_splitk_reduce(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
   constexpr int Q = C::kTileFloats / 4;        // float4 per tile
-  const int tiles = m_tiles * n_tiles;
+  const int rem = m_tiles * n_tiles - n_full;  // the split tiles n_full, n_full + 1, ...
   const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= tiles * Q) return;
-  const int tile = g / Q, q = g % Q;
+  if (g >= rem * Q) return;
+  const int tr = g / Q, q = g % Q;
+  const int tile = n_full + tr;
   const int mt = tile % m_tiles, nt = tile / m_tiles;
   const float4* src = reinterpret_cast<const float4*>(a.part);
-  float4 t = src[(size_t)tile * Q + q];
+  float4 t = src[(size_t)tr * Q + q];
   for (int z = 1; z < splits; ++z) {
-    const float4 u = src[((size_t)z * tiles + tile) * Q + q];
+    const float4 u = src[((size_t)z * rem + tr) * Q + q];
     t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
   }
   // q = (((w * TI + i) * TJ + j) * 4 + e4) * 64 + l
@@ -564,6 +592,7 @@ static bool big_ok(const GemmArgs& a, int bn) {
 enum BigCfg { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
 struct BigPlan {
   int cfg, m_tiles, n_tiles, splits;
+  int n_full;          // tiles run whole; the rest are split `splits` ways
   double cost_us;
 };
 struct CfgInfo {
@@ -572,16 +601,16 @@ struct CfgInfo {
 };
 // Rates measured on MI355X for 1024-row passes of the Qwen3-8B shapes.
 static const CfgInfo kCfgInfo[3] = {
-    {256, 256, 1, 4.0, 4.0}, {256, 128, 2, 3.0, 4.3}, {128, 128, 2, 1.9, 3.4}};
-constexpr double kL2BytesPerUs = 12e6;     // L2 -> CU operand traffic the chip sustains
-constexpr double kPartBytesPerUs = 5e6;    // split-K partial tiles, written and read back
+    {256, 256, 1, 4.8, 4.8}, {256, 128, 2, 3.6, 4.5}, {128, 128, 2, 1.9, 3.6}};
+constexpr double kL2BytesPerUs = 30e6;     // L2 -> CU operand traffic the chip sustains
+constexpr double kPartBytesPerUs = 10e6;   // split-K partial tiles, written and read back (mostly in the 256 MB last-level cache)
 
 // Pick the tile configuration and the K split from a cost model: rounds of
 // resident workgroups times the time one workgroup's K range takes at the
 // CU's sustained rate (bounded below by the L2 operand traffic), plus the
 // split-K partial tiles and the reduction launch.
 static BigPlan plan_big(const GemmArgs& a) {
-  BigPlan best = {-1, 0, 0, 0, 1e30};
+  BigPlan best = {-1, 0, 0, 0, 0, 1e30};
   const int nk = a.Kd / big::BK + (a.t ? a.rank / big::BK : 0);
   for (int c = 0; c < 3; ++c) {
     const CfgInfo& ci = kCfgInfo[c];
@@ -592,21 +621,29 @@ static BigPlan plan_big(const GemmArgs& a) {
     const int tiles = m_tiles * n_tiles;
     const double slice_flop = 2.0 * ci.bm * ci.bn * big::BK;
     const double slice_bytes = (ci.bm + ci.bn) * big::BK * 2.0;
+    const int slots_max = 256 * ci.per_cu;
     for (int sp = 1; sp <= 16; ++sp) {
       if (sp > 1 && a.Kd / big::BK / sp < 4) break;
-      const size_t part = (size_t)tiles * sp * ci.bm * ci.bn;
+      // whole rounds of tiles stay unsplit; the remainder is split
+      const int n_full = sp == 1 ? tiles : (tiles / slots_max) * slots_max;
+      const int rem = tiles - n_full;
+      if (sp > 1 && rem == 0) break;
+      const size_t part = (size_t)rem * sp * ci.bm * ci.bn;
       if (sp > 1 && (!a.part || part > a.part_floats)) break;
-      const int units = tiles * sp;
-      const int occ = units > 256 && ci.per_cu > 1 ? 2 : 1;
-      const int rounds = (units + 256 * occ - 1) / (256 * occ);
+      const int items = n_full + rem * sp;
+      const int occ = items > 256 && ci.per_cu > 1 ? 2 : 1;
+      const int slots = 256 * occ;
       const double rate = (occ == 2 ? ci.rate2 : ci.rate1) / occ * 1e6;   // flop/us per WG
-      const int k_per = (nk + sp - 1) / sp;
-      double cost = rounds * k_per * slice_flop / rate;
-      const double l2 = (double)units * k_per * slice_bytes / kL2BytesPerUs;
+      const int k_rem = (nk + sp - 1) / sp;
+      // rounds of whole tiles, then rounds of split items
+      const int r_full = n_full / slots, left = n_full % slots;
+      const int r_rem = (left + rem * sp + slots - 1) / slots;
+      double cost = (r_full * nk + r_rem * (left ? nk : k_rem)) * slice_flop / rate;
+      const double l2 = ((double)n_full * nk + (double)rem * sp * k_rem) * slice_bytes / kL2BytesPerUs;
       if (l2 > cost) cost = l2;
       cost += 2.0;
       if (sp > 1) cost += (double)part * 4 * 2 / kPartBytesPerUs + 3.0;
-      if (cost < best.cost_us) best = BigPlan{c, m_tiles, n_tiles, sp, cost};
+      if (cost < best.cost_us) best = BigPlan{c, m_tiles, n_tiles, sp, n_full, cost};
     }
   }
   return best;
@@ -614,12 +651,13 @@ static BigPlan plan_big(const GemmArgs& a) {
 
 template <class C>
 static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_big<C>, dim3(p.m_tiles * p.n_tiles * p.splits), dim3(C::kThreads),
-                     C::kLds, s, a, p.m_tiles, p.n_tiles, p.splits);
+  const int rem = p.m_tiles * p.n_tiles - p.n_full;
+  hipLaunchKernelGGL(k_gemm_big<C>, dim3(p.n_full + rem * p.splits), dim3(C::kThreads), C::kLds,
+                     s, a, p.m_tiles, p.n_tiles, p.splits, p.n_full);
   if (p.splits > 1) {
-    const int n = p.m_tiles * p.n_tiles * (C::kTileFloats / 4);
+    const int n = rem * (C::kTileFloats / 4);
     hipLaunchKernelGGL(k_gemm_splitk_reduce<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
-                       p.m_tiles, p.n_tiles, p.splits);
+                       p.m_tiles, p.n_tiles, p.splits, p.n_full);
   }
   return hipGetLastError();
 }

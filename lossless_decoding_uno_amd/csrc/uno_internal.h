@@ -74,9 +74,9 @@ struct GemmArgs {
   float* part;
   size_t part_floats;
 };
-// split-K scratch carved per pass: 64 MB for passes of 128 rows or more
+// split-K scratch carved per pass: 128 MB for passes of 128 rows or more
 // (tiled kernel), 4 MB below (skinny kernel)
-constexpr size_t kGemmPartFloats = size_t(16) << 20;
+constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
