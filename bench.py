@@ -69,6 +69,11 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--generate", type=int, default=0, metavar="N",
+                    help="end-to-end mode: prefill a --prompt-token prompt per sequence, then "
+                         "generate N tokens with natural acceptance (pages on demand)")
+    ap.add_argument("--prompt", type=int, default=1024)
+    ap.add_argument("--prior", type=int, default=0, help="draft noise prior: 0 mask, 1 uniform")
     return ap.parse_args()
 
 
@@ -308,6 +313,45 @@ def cpu_baseline(K, ctx, forced_mean_tokens):
                        % (ctx, K, times[1], times[5], t36, forced_mean_tokens))}
 
 
+def generate_mode(args, U, synth, torch, cfg):
+    """Chunked prefill of random prompts, then continuous Psi-Spec steps with
+    natural acceptance until every sequence has args.generate new tokens."""
+    from lossless_decoding_uno_amd.generate import Generator
+    K = args.K
+    log("generating weights on the GPU")
+    model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))
+    max_ctx = args.prompt + args.generate + 3 * K + 8
+    g = Generator(model, args.batch, K, max_ctx, seed=0, prefill_chunk=512)
+    prompts = synth.prompt_ids(cfg, args.prompt, 1, batch=args.batch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.prefill(prompts)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    log("prefill done in %.2f s; generating %d tokens" % (t_prefill, args.generate))
+    t0 = time.perf_counter()
+    last = t0
+    while min(len(o) for o in g.out) < args.generate:
+        g.step()
+        if time.perf_counter() - last > 30:
+            last = time.perf_counter()
+            log("%d steps, %d tokens" % (g.steps, min(len(o) for o in g.out)))
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t0
+    st = g.stats()
+    toks = sum(len(o) for o in g.out)
+    out = {"metric": "generated tokens/s (natural acceptance, end to end)",
+           "value": round(toks / t_gen, 1), "unit": "tokens/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic (random-init weights, uniform random prompts)",
+           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d" % (
+               args.batch, args.prompt, args.generate, K, args.prior)},
+           "steps": st["steps"], "TPF": round(st["TPF"], 3), "AL": round(st["AL"], 3),
+           "ms_per_step": round(1e3 * t_gen / st["steps"], 3),
+           "prefill_s": round(t_prefill, 3), "pages_in_use": st["pages_in_use"]}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -330,7 +374,9 @@ def main():
     import synth
     U.load_library()
     assert torch.cuda.is_available(), "no GPU"
-    cfg = synth.QWEN3_8B
+    cfg = dict(synth.QWEN3_8B, noise_prior=args.prior)
+    if args.generate:
+        return generate_mode(args, U, synth, torch, cfg)
     K = args.K
     log("generating weights on the GPU")
     model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))

@@ -74,6 +74,16 @@ typedef struct uno_config {
                          3 o, 4 gate, 5 up, 6 down.  q,k,v must agree, and
                          gate,up must agree.                                  */
   int32_t page_size;  /* tokens per KV page (16)                              */
+  int32_t noise_prior; /* noise tokens of a draft block (paperglide reader,
+                          "The Psi-Speculative Sampler": the block is the
+                          anchor plus K-1 tokens drawn from the diffusion
+                          prior; "Supplementary Details": a masked model's
+                          prior is the mask token, a uniform-state model's is
+                          uniform over the vocabulary).
+                          0: mask_id at every noise position;
+                          1: uniform token ids, floor(w * vocab / 2^64) with w
+                             word 0 of Philox4x64-10 at counter (3, j, b,
+                             step[b]), key (seed, 0), for draft row j >= 1.  */
 } uno_config;
 
 /* One layer's weights [dev].  Base weights are bf16 [out, in] (row-major,
@@ -117,8 +127,9 @@ size_t uno_workspace_bytes(const uno_config *cfg, int batch, int K, int max_ctx)
 
 /* Draft block (paperglide reader, "The Psi-Speculative Sampler" and "Sampler
  * Extensions"; picx.dev summary, "Architecture").
- * Rows of sequence b: [anchor[b], mask_id x (K-1)] at positions kv_len[b] ..
- * kv_len[b]+K-1.  Row 0 runs with the AR weights and attends causally (keys
+ * Rows of sequence b: [anchor[b], noise x (K-1)] at positions kv_len[b] ..
+ * kv_len[b]+K-1, the noise tokens being mask_id or uniform Philox draws as
+ * cfg->noise_prior says.  Row 0 runs with the AR weights and attends causally (keys
  * <= kv_len[b]); rows 1..K-1 add the LoRA term (scale lora_scale) and attend to
  * every key up to kv_len[b]+K-1.  The pass writes the rows' K/V into the cache
  * at those positions (the anchor's entry is final; the mask rows' are scratch)
@@ -127,6 +138,7 @@ size_t uno_workspace_bytes(const uno_config *cfg, int batch, int K, int max_ctx)
  *   draft_logits  [dev] fp32 [batch, K, V]   q_1..q_K (untempered logits)
  *   draft_tokens  [dev] int32 [batch, K]     d_j+1 ~ q_j+1 at temperature 1/inv_temp
  *   step          [dev] uint64 [batch]       Philox step counter per sequence
+ *                                            (draft sampling; uniform noise)
  *   status        [dev] int32 [batch] or NULL
  *   ws/ws_bytes   [dev] workspace of uno_workspace_bytes(cfg, batch, K, max_ctx)
  * 1 <= K <= 64, batch >= 1, inv_temp > 0 and finite. */

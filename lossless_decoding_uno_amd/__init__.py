@@ -39,7 +39,8 @@ class UnoConfig(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("mask_id", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("lora_rank", ctypes.c_int32), ("lora_scale", ctypes.c_float),
-                ("lora_mask", ctypes.c_uint32), ("page_size", ctypes.c_int32)]
+                ("lora_mask", ctypes.c_uint32), ("page_size", ctypes.c_int32),
+                ("noise_prior", ctypes.c_int32)]
 
 
 class UnoLayerWeights(ctypes.Structure):
@@ -139,7 +140,7 @@ def make_config(cfg, page_size=16, lora=True):
                      int(cfg["n_kv_heads"]), int(cfg["head_dim"]), int(cfg["d_ffn"]),
                      int(cfg["vocab"]), int(cfg["mask_id"]), float(cfg["rms_eps"]),
                      float(cfg["rope_theta"]), r, float(cfg["lora_alpha"]) / r,
-                     0x7F if lora else 0, int(page_size))
+                     0x7F if lora else 0, int(page_size), int(cfg.get("noise_prior", 0)))
 
 
 class Model:
@@ -193,12 +194,16 @@ class PagedKV:
     of the pool is used (any assignment of distinct pages works)."""
 
     def __init__(self, cfg, batch, capacity, page_size=16, device="cuda", page_order=None,
-                 extra_pages=0):
+                 extra_pages=0, n_pages=None):
+        """``n_pages`` sets the pool size directly (pages then handed out on
+        demand, e.g. by ``generate.PagePool``; the table starts at page 0)."""
         self.cfg = cfg
         self.batch = batch
         self.page_size = page_size
         self.max_pages = (capacity + page_size - 1) // page_size
-        self.n_pages = batch * self.max_pages + extra_pages
+        self.n_pages = batch * self.max_pages + extra_pages if n_pages is None else int(n_pages)
+        if n_pages is not None:
+            page_order = torch.zeros(batch * self.max_pages, dtype=torch.int64)
         L, H, hd = cfg["n_layers"], cfg["n_kv_heads"], cfg["head_dim"]
         dev = torch.device(device)
         self.k_pages = torch.zeros((L, self.n_pages, H, page_size, hd), dtype=torch.bfloat16,

@@ -63,6 +63,7 @@ int check_config(const uno_config* c) {
   if (c->vocab % 16 || c->vocab > (1 << 20)) return UNO_ERR_UNSUPPORTED;
   if (c->page_size & (c->page_size - 1)) return UNO_ERR_UNSUPPORTED;   // power of two >= 16
   if (c->lora_mask & ~0x7Fu) return UNO_ERR_INVALID_ARG;
+  if (c->noise_prior != 0 && c->noise_prior != 1) return UNO_ERR_INVALID_ARG;
   if (c->lora_mask) {
     if (c->lora_rank < 16 || c->lora_rank % 16 || c->lora_rank > 256) return UNO_ERR_UNSUPPORTED;
     const bool q = bit(*c, P_Q), k = bit(*c, P_K), v = bit(*c, P_V);
@@ -155,7 +156,8 @@ const bf16_raw_t* bp(const void* p) { return static_cast<const bf16_raw_t*>(p); 
 // One forward pass of B*K rows (draft when `anchor` != null, verify otherwise).
 int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const int32_t* anchor,
              const int32_t* rows, int B, int K, int max_ctx, int pos_offset, bool lora,
-             float* logits, int32_t* status, void* ws, hipStream_t s) {
+             uint64_t seed, const uint64_t* step, float* logits, int32_t* status, void* ws,
+             hipStream_t s) {
   const PassWs W = carve(c, B, K, max_ctx, ws);
   const int R = B * K;
   const int D = c.d_model, F = c.d_ffn, hd = c.head_dim;
@@ -166,7 +168,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   hipError_t e;
 #define UNO_TRY(x) do { e = (x); if (e != hipSuccess) return hip_fail(e); } while (0)
 
-  UNO_TRY(launch_embed(c, bp(w->embed), anchor, rows, B, K, W.h, status, s));
+  UNO_TRY(launch_embed(c, bp(w->embed), anchor, rows, B, K, seed, step, W.h, status, s));
   UNO_TRY(launch_rope_table(kv->kv_len, B, K, draft ? 0 : pos_offset, hd / 2, c.rope_theta,
                             W.cs, s));
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
@@ -305,8 +307,8 @@ int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* k
   if ((rc = check_layers(*cfg, w, true))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = run_pass(*cfg, w, kv, anchor, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
-                draft_logits, status, ws, s);
+  rc = run_pass(*cfg, w, kv, anchor, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0, seed,
+                step, draft_logits, status, ws, s);
   if (rc) return rc;
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
     return launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed, step,
@@ -327,7 +329,7 @@ int uno_verify_block(const uno_config* cfg, const uno_weights* w, const uno_kv* 
   if ((rc = check_kv(*cfg, kv, K, pos_offset))) return rc;
   if ((rc = check_layers(*cfg, w, false))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
-  return run_pass(*cfg, w, kv, nullptr, rows, batch, K, max_ctx, pos_offset, false,
+  return run_pass(*cfg, w, kv, nullptr, rows, batch, K, max_ctx, pos_offset, false, 0, nullptr,
                   verify_logits, status, ws, static_cast<hipStream_t>(stream));
 }
 

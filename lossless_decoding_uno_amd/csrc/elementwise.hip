@@ -15,14 +15,28 @@ namespace uno {
 
 // ------------------------------------------------------------ embedding
 // One workgroup per row r = b*K + j.  Draft mode (anchor != null): id =
-// anchor[b] for j == 0, mask_id otherwise.  Verify mode: id = rows[r].
+// anchor[b] for j == 0; the noise rows j >= 1 hold mask_id (noise_prior 0) or
+// a uniform token floor(w * V / 2^64), w = Philox word 0 at counter
+// (3, j, b, step[b]) under key (seed, 0) (noise_prior 1).  Verify mode: id =
+// rows[r].
 __global__ void __launch_bounds__(256)
 k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
-        const int32_t* __restrict__ rows, int K, int D, int V, int mask_id,
-        float* __restrict__ h, int32_t* __restrict__ status) {
+        const int32_t* __restrict__ rows, int K, int D, int V, int mask_id, int noise_prior,
+        uint64_t seed, const uint64_t* __restrict__ step, float* __restrict__ h,
+        int32_t* __restrict__ status) {
   const int r = blockIdx.x;
   const int b = r / K, j = r % K;
-  int id = anchor ? (j == 0 ? anchor[b] : mask_id) : rows[r];
+  int id;
+  if (!anchor) {
+    id = rows[r];
+  } else if (j == 0) {
+    id = anchor[b];
+  } else if (noise_prior == 0) {
+    id = mask_id;
+  } else {
+    const uint64_t w = philox_word0(3, j, b, step ? step[b] : 0, seed, 0);
+    id = (int)__umul64hi(w, (uint64_t)V);
+  }
   const bool bad = id < 0 || id >= V;
   if (bad) {
     if (threadIdx.x == 0 && status) atomicOr(status + b, UNO_DEV_BAD_TOKEN);
@@ -44,10 +58,10 @@ k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
 }
 
 hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
-                        const int32_t* rows, int B, int K, float* h, int32_t* status,
-                        hipStream_t s) {
+                        const int32_t* rows, int B, int K, uint64_t seed, const uint64_t* step,
+                        float* h, int32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(k_embed, dim3(B * K), dim3(256), 0, s, embed, anchor, rows, K, c.d_model,
-                     c.vocab, c.mask_id, h, status);
+                     c.vocab, c.mask_id, c.noise_prior, seed, step, h, status);
   return hipGetLastError();
 }
 

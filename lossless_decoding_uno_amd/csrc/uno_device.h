@@ -117,6 +117,26 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_off) {
 }
 
 // 32-bit LDS address of a pointer into __shared__ memory
+// Word 0 of Philox4x64-10 (Salmon et al., SC'11: the 4x64 bijection with 10
+// rounds) for counter (c0, c1, c2, c3) and key (k0, k1).  One round maps the
+// counter to (hi(M1 c2)^c1^k0, lo(M1 c2), hi(M0 c0)^c3^k1, lo(M0 c0)); the key
+// is bumped by the Weyl constants (W0, W1) between rounds.  Every random
+// decision of the decode step is one counter: (slot, row j, sequence b, step).
+__device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                 uint64_t c3, uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
+    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return c0;
+}
+
 // Buffer resource (raw, stride 0) over `bytes` bytes at `base`; loads past
 // the end return zero instead of faulting.
 typedef int i32x4 __attribute__((ext_vector_type(4)));

@@ -26,9 +26,11 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
 // ---------------------------------------------------------------- elementwise / small ops
 // Block rows: draft (anchor + mask ids) or given rows; gathers embeddings into
 // the fp32 residual stream h [R, D]; also writes ids [R].
+// Draft rows (anchor != null) draw uniform noise tokens from (seed, step) when
+// c.noise_prior == 1.
 hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
-                        const int32_t* rows, int B, int K, float* h, int32_t* status,
-                        hipStream_t s);
+                        const int32_t* rows, int B, int K, uint64_t seed, const uint64_t* step,
+                        float* h, int32_t* status, hipStream_t s);
 // RMSNorm of fp32 rows into bf16 rows.
 hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
                           bf16_raw_t* out, hipStream_t s);

@@ -1,0 +1,158 @@
+"""End-to-end generation over the decode step: prompt prefill in chunks, then
+continuous Psi-Spec steps with natural (or forced) acceptance, KV pages handed
+out on demand from one pool.
+
+The four library calls do all the device work; this module only orders them,
+keeps the page table and reads back the committed tokens.  Tokens per forward
+pass (TPF) follow the pages' definition: output tokens per forward pass, where
+one step runs two passes (draft and verify) and commits a + 1 tokens, so
+1 <= TPF <= (K + 1) / 2 (paperglide reader, "The Uno Framework"); AL is the mean
+number of tokens a step commits.
+"""
+import numpy as np
+import torch
+
+from . import (PagedKV, alloc_workspace, draft_block, kv_commit, spec_accept,
+               spec_accept_workspace_bytes, verify_block, workspace_bytes)
+
+
+class PagePool:
+    """Host-side allocator of the KV pages of one PagedKV pool.
+
+    Sequence b owns the pages listed in row b of the page table, in position
+    order; ``ensure(b, n)`` appends free pages until the sequence can hold n
+    positions, ``release(b)`` returns them.  ``sync()`` copies the rows that
+    changed to the device table (call it before a pass that reads them)."""
+
+    def __init__(self, kv):
+        self.kv = kv
+        self.ps = kv.page_size
+        self.free = list(range(kv.n_pages - 1, -1, -1))    # pop() hands out 0, 1, ...
+        self.owned = [[] for _ in range(kv.batch)]
+        self.table = np.zeros((kv.batch, kv.max_pages), dtype=np.int32)
+        self.dirty = False
+
+    def ensure(self, b, n_positions):
+        need = (n_positions + self.ps - 1) // self.ps
+        if need > self.kv.max_pages:
+            raise RuntimeError("sequence %d needs %d pages, the table holds %d"
+                               % (b, need, self.kv.max_pages))
+        while len(self.owned[b]) < need:
+            if not self.free:
+                raise RuntimeError("KV page pool exhausted")
+            p = self.free.pop()
+            self.table[b, len(self.owned[b])] = p
+            self.owned[b].append(p)
+            self.dirty = True
+
+    def release(self, b):
+        self.free.extend(reversed(self.owned[b]))
+        self.owned[b] = []
+        self.table[b, :] = 0
+        self.dirty = True
+
+    def pages_in_use(self):
+        return sum(len(o) for o in self.owned)
+
+    def sync(self):
+        if self.dirty:
+            self.kv.page_table.copy_(torch.from_numpy(self.table))
+            self.dirty = False
+
+
+class Generator:
+    """Batch of B sequences with equal-length prompts.
+
+        g = Generator(model, B, K, max_ctx, n_pages)
+        g.prefill(prompts)            # int array [B, P]
+        tokens = g.generate(n_new)    # list of B token lists
+    """
+
+    def __init__(self, model, batch, K, max_ctx, n_pages=None, inv_temp=1.0, seed=0,
+                 prefill_chunk=512, page_size=16, device="cuda"):
+        self.model, self.B, self.K = model, batch, K
+        self.cfg = model.cfg
+        self.inv_temp, self.seed = float(inv_temp), int(seed)
+        self.chunk = int(prefill_chunk)
+        self.max_ctx = int(max_ctx)
+        max_pages = (self.max_ctx + page_size - 1) // page_size
+        self.kv = PagedKV(self.cfg, batch, self.max_ctx, page_size=page_size, device=device,
+                          n_pages=n_pages or batch * max_pages)
+        self.pool = PagePool(self.kv)
+        V = self.cfg["vocab"]
+        rows = max(K, self.chunk)
+        self.ws = alloc_workspace(max(workspace_bytes(model, batch, K, self.max_ctx),
+                                      workspace_bytes(model, batch, rows, self.max_ctx)))
+        self.aws = alloc_workspace(spec_accept_workspace_bytes(batch, K))
+        self.zq = torch.empty((batch, K, V), dtype=torch.float32, device=device)
+        self.zp = torch.empty((batch, K, V), dtype=torch.float32, device=device)
+        self.d = torch.empty((batch, K), dtype=torch.int32, device=device)
+        self.a = torch.empty(batch, dtype=torch.int32, device=device)
+        self.c = torch.empty((batch, K + 1), dtype=torch.int32, device=device)
+        self.e = torch.empty(batch, dtype=torch.int32, device=device)
+        self.step_ctr = torch.zeros(batch, dtype=torch.uint64).to(device)
+        self.status = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.kv_len = np.zeros(batch, dtype=np.int64)          # host mirror
+        self.out = [[] for _ in range(batch)]
+        self.steps = 0
+        self.committed_per_step = []
+
+    # -- prefill: verify passes over the prompt (AR weights, causal), in chunks
+    def prefill(self, prompts):
+        prompts = np.asarray(prompts, dtype=np.int32)
+        assert prompts.shape[0] == self.B and prompts.shape[1] >= 2
+        body = prompts[:, :-1]                  # the last prompt token is the first anchor
+        dev = self.kv.kv_len.device
+        for s in range(0, body.shape[1], self.chunk):
+            rows = body[:, s: s + self.chunk]
+            n = rows.shape[1]
+            for b in range(self.B):
+                self.pool.ensure(b, int(self.kv_len[b]) + n)
+            self.pool.sync()
+            verify_block(self.model, self.kv, torch.from_numpy(np.ascontiguousarray(rows)).to(dev),
+                         self.max_ctx, 0, None, self.ws, self.status)
+            kv_commit(self.kv, torch.full((self.B,), n - 1, dtype=torch.int32, device=dev), n)
+            self.kv_len += n
+        self.e.copy_(torch.from_numpy(prompts[:, -1].copy()))
+        self._check_status()
+
+    # -- one Psi-Spec step (natural acceptance unless `forced` [B] is given)
+    def step(self, forced=None):
+        K = self.K
+        for b in range(self.B):
+            # draft writes kv_len .. kv_len+K-1, verify kv_len+1 .. kv_len+K
+            self.pool.ensure(b, int(self.kv_len[b]) + K + 1)
+        self.pool.sync()
+        draft_block(self.model, self.kv, self.e, K, self.max_ctx, self.inv_temp, self.seed,
+                    self.step_ctr, self.zq, self.d, self.ws, self.status)
+        verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws,
+                     self.status)
+        spec_accept(self.zq, self.zp, self.d, self.inv_temp, self.seed, self.step_ctr, self.a,
+                    self.c, self.e, self.aws, status=self.status, forced_accept=forced)
+        kv_commit(self.kv, self.a, K, self.step_ctr, self.status)
+        a = self.a.cpu().numpy().astype(np.int64)
+        c = self.c.cpu().numpy()
+        for b in range(self.B):
+            self.out[b].extend(int(t) for t in c[b, : a[b] + 1])
+        self.kv_len += a + 1
+        self.steps += 1
+        self.committed_per_step.append(a + 1)
+        return a
+
+    def generate(self, n_new, forced=None):
+        while min(len(o) for o in self.out) < n_new:
+            self.step(None if forced is None else forced[self.steps])
+        self._check_status()
+        return [o[:n_new] for o in self.out]
+
+    def stats(self):
+        per = np.array(self.committed_per_step, dtype=np.float64)   # [steps, B]
+        return {"steps": self.steps,
+                "AL": float(per.mean()) if per.size else 0.0,
+                "TPF": float(per.mean() / 2.0) if per.size else 0.0,
+                "pages_in_use": self.pool.pages_in_use()}
+
+    def _check_status(self):
+        st = self.status.cpu().numpy()
+        if np.any(st):
+            raise RuntimeError("device status flags %s" % st.tolist())

@@ -29,6 +29,7 @@ PHILOX_W1 = 0xBB67AE8584CAA73B   # sqrt(3) - 1
 SLOT_DRAFT = 0     # draft token j+1 is drawn with j
 SLOT_ACCEPT = 1    # accept test of draft i uses j = i - 1
 SLOT_EXTRA = 2     # residual / bonus token uses j = a
+SLOT_NOISE = 3     # uniform-prior noise token of draft row j >= 1
 
 
 def philox4x64_10(counter, key):
@@ -49,6 +50,12 @@ def philox4x64_10(counter, key):
 def uniform24(seed, slot, j, b, step):
     """24-bit uniform integer U in [0, 2^24) for one decision."""
     return philox4x64_10((slot, j, b, step), (seed, 0))[0] >> 40
+
+
+def noise_id(seed, j, b, step, vocab):
+    """Uniform noise token of draft row j for a uniform-state prior:
+    floor(w * vocab / 2^64), w = word 0 at counter (SLOT_NOISE, j, b, step)."""
+    return (philox4x64_10((SLOT_NOISE, j, b, step), (seed, 0))[0] * int(vocab)) >> 64
 
 
 # ---- vectorised form (numpy uint64), used for large batches of draws ----

@@ -40,7 +40,7 @@ import numpy as np
 
 from . import canonical as cn
 from .model import KVCache, forward
-from .philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, uniform24
+from .philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, noise_id, uniform24
 
 
 class PhiloxDraws:
@@ -51,6 +51,9 @@ class PhiloxDraws:
 
     def u(self, slot, j):
         return uniform24(self.seed, slot, j, self.b, self.step)
+
+    def noise(self, j, vocab):
+        return noise_id(self.seed, j, self.b, self.step, vocab)
 
     def categorical(self, slot, j, weights):
         return cn.categorical(weights, self.u(slot, j))
@@ -88,10 +91,20 @@ def prefill(cfg, wts, seq):
     seq.kv_len = n - 1
 
 
-def draft_logits(cfg, wts, seq, K, act_round=None):
-    """Draft pass: rows [anchor, mask x (K-1)], gate (0, 1, ..., 1). fp64 [K, V]."""
+def draft_logits(cfg, wts, seq, K, act_round=None, draws=None):
+    """Draft pass: rows [anchor, noise x (K-1)], gate (0, 1, ..., 1). fp64 [K, V].
+
+    The noisy block is the anchor followed by K-1 tokens from the diffusion
+    prior (paperglide reader, "The Psi-Speculative Sampler"): the mask token
+    for a masked model, or uniform tokens for a uniform-state model
+    ("Supplementary Details"), chosen by cfg["noise_prior"] (0 / 1); uniform
+    tokens come from ``draws.noise(j, V)``."""
     n0 = seq.kv_len                       # position of the anchor
-    rows = [seq.tokens[-1]] + [cfg["mask_id"]] * (K - 1)
+    if cfg.get("noise_prior", 0) == 1:
+        noise = [draws.noise(j, cfg["vocab"]) for j in range(1, K)]
+    else:
+        noise = [cfg["mask_id"]] * (K - 1)
+    rows = [seq.tokens[-1]] + noise
     pos = n0 + np.arange(K)
     gate = np.array([0.0] + [1.0] * (K - 1))
     lim = np.array([n0] + [n0 + K - 1] * (K - 1))
@@ -165,7 +178,7 @@ def step(cfg, wts, seq, K, inv_temp, draws, forced=None):
     Returns a dict with the logits (fp64 and the fp32 copies the sampler saw),
     drafts, a, committed tokens and the extra token.
     """
-    zq = draft_logits(cfg, wts, seq, K)
+    zq = draft_logits(cfg, wts, seq, K, draws=draws)
     zq32 = zq.astype(np.float32)
     drafts = draft_sample(zq32, inv_temp, draws)
     zp = verify_logits(cfg, wts, seq, drafts)

@@ -66,6 +66,10 @@ def test_entry_points_reject_bad_arguments_on_the_host():
     bad = U.make_config(dict(synth.TINY, head_dim=48))
     assert lib.uno_verify_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
                                 64, 1, fake, None, fake, 1 << 20, None) == 2
+    # unknown noise prior
+    bad = U.make_config(dict(synth.TINY, noise_prior=2))
+    assert lib.uno_verify_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
+                                64, 1, fake, None, fake, 1 << 20, None) == 1
     # verify: empty kv struct
     assert lib.uno_verify_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
                                 64, 1, fake, None, fake, 1 << 30, None) == 1

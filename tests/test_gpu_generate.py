@@ -1,0 +1,70 @@
+"""End-to-end generation with natural acceptance (chunked prefill, continuous
+steps, KV pages handed out on demand) on the tiny model.
+
+At every step the oracle replays the step on the same committed state: the
+GPU's draft and verify logits must lie within the logit tolerance of the
+oracle's, and the oracle sampler fed the GPU's own fp32 logits and the same
+Philox counters must take exactly the GPU's decisions (draft tokens, accept
+length, committed tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import spec as ospec
+
+from gpu_util import assert_logits_close, gpu_or_fail, progress
+
+pytestmark = pytest.mark.gpu
+
+SEED = 11
+
+
+@pytest.mark.parametrize("prior", [0, 1])
+def test_natural_generation_matches_oracle_step_by_step(prior):
+    U = gpu_or_fail()
+    from lossless_decoding_uno_amd.generate import Generator
+    cfg = dict(synth.TINY, noise_prior=prior)
+    wts = synth.make_weights(cfg, 0)
+    w64 = synth.to_f64(wts)
+    model = U.Model(cfg, wts)
+    B, K, P, n_new = 2, 4, 32, 40
+    prompts = np.stack([synth.prompt_ids(cfg, P, 5 + b) for b in range(B)])
+    max_ctx = P + n_new + 3 * K + 8
+    # a pool smaller than B full-length tables: pages come on demand
+    g = Generator(model, B, K, max_ctx, n_pages=(max_ctx // 16 + 2) * B - 1, seed=SEED,
+                  prefill_chunk=7)
+    g.prefill(prompts)
+    seqs = []
+    for b in range(B):
+        s = ospec.Sequence(cfg, list(prompts[b]), capacity=max_ctx)
+        ospec.prefill(cfg, w64, s)
+        assert s.kv_len == int(g.kv_len[b]) == P - 1
+        seqs.append(s)
+    worst = 0.0
+    while min(len(o) for o in g.out) < n_new:
+        a_g = g.step()
+        zq, zp = g.zq.cpu().numpy(), g.zp.cpu().numpy()
+        d, c = g.d.cpu().numpy(), g.c.cpu().numpy()
+        for b in range(B):
+            s = seqs[b]
+            draws = ospec.PhiloxDraws(SEED, b, s.step)
+            zq_o = ospec.draft_logits(cfg, w64, s, K, draws=draws)
+            worst = max(worst, assert_logits_close(zq[b], zq_o, "draft b%d step %d" % (b, s.step)))
+            drafts = ospec.draft_sample(zq[b], 1.0, draws)
+            np.testing.assert_array_equal(d[b], drafts)
+            zp_o = ospec.verify_logits(cfg, w64, s, drafts)
+            worst = max(worst, assert_logits_close(zp[b], zp_o, "verify b%d step %d" % (b, s.step)))
+            a, committed, extra = ospec.spec_accept(zq[b], zp[b], drafts, 1.0, draws)
+            assert a == a_g[b] and a >= 1
+            np.testing.assert_array_equal(c[b, : a + 1], committed)
+            ospec.commit(s, a, committed)
+            assert s.kv_len == int(g.kv_len[b])
+    st = g.stats()
+    assert 1.0 <= st["TPF"] <= (K + 1) / 2.0
+    assert g.pool.pages_in_use() <= g.kv.n_pages
+    assert int(g.status.abs().sum().item()) == 0
+    for b in range(B):
+        assert g.out[b] == seqs[b].tokens[P:]
+    progress("natural generation (prior %d): %d steps, TPF %.2f, AL %.2f, worst logit err %.2e"
+             % (prior, st["steps"], st["TPF"], st["AL"], worst))

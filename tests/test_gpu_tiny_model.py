@@ -87,8 +87,20 @@ def _prefill_gpu(U, model, kv, prompt, ws, max_ctx):
 
 def test_tiny_model_teacher_forced_generation(setup):
     U, cfg, wts, w64, model = setup
+    _teacher_forced(U, cfg, w64, model, N_NEW)
+
+
+def test_tiny_model_uniform_prior_generation(setup):
+    """Uniform-state prior: the draft block's noise tokens are uniform Philox
+    draws (slot 3) on the GPU and in the oracle alike."""
+    U, cfg, wts, w64, _ = setup
+    cfg_u = dict(cfg, noise_prior=1)
+    _teacher_forced(U, cfg_u, w64, U.Model(cfg_u, wts), 32)
+
+
+def _teacher_forced(U, cfg, w64, model, n_new):
     prompt = synth.prompt_ids(cfg, 32, 1)
-    cap = len(prompt) + N_NEW + 2 * K + 8
+    cap = len(prompt) + n_new + 2 * K + 8
     max_ctx = cap
     kv = U.PagedKV(cfg, 1, cap, page_order=torch.randperm(
         (cap + 15) // 16 + 3, generator=torch.Generator().manual_seed(3)), extra_pages=3)
@@ -118,13 +130,13 @@ def test_tiny_model_teacher_forced_generation(setup):
     aws = U.alloc_workspace(U.spec_accept_workspace_bytes(1, K))
     n_dec = n_skip = 0
     worst = 0.0
-    while len(seq.tokens) - len(prompt) < N_NEW:
+    while len(seq.tokens) - len(prompt) < n_new:
         st = seq.step
         anchor = torch.tensor([seq.tokens[-1]], dtype=torch.int32, device=dev)
         U.draft_block(model, kv, anchor, K, max_ctx, 1.0, SEED, step_g, zq_g, d_g, ws, status)
-        zq = ospec.draft_logits(cfg, w64, seq, K)
-        zq32 = zq.astype(np.float32)
         draws = ospec.PhiloxDraws(SEED, 0, st)
+        zq = ospec.draft_logits(cfg, w64, seq, K, draws=draws)
+        zq32 = zq.astype(np.float32)
         drafts = ospec.draft_sample(zq32, 1.0, draws)
         zq_gpu = zq_g.cpu().numpy()[0]
         worst = max(worst, assert_logits_close(zq_gpu, zq, "draft logits step %d" % st))

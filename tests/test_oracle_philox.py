@@ -2,7 +2,8 @@
 import numpy as np
 import pytest
 
-from oracle.philox import philox4x64_10, philox4x64_10_np, uniform24, uniform24_np
+from oracle.philox import (SLOT_NOISE, noise_id, philox4x64_10, philox4x64_10_np, uniform24,
+                           uniform24_np)
 
 MASK = (1 << 64) - 1
 
@@ -51,3 +52,19 @@ def test_uniform24_range_and_spread():
     # a fair 24-bit uniform: mean 2^23 within 5 sigma
     sigma = 2**24 / np.sqrt(12) / np.sqrt(u.size)
     assert abs(u.astype(np.float64).mean() - 2**23) < 5 * sigma
+
+
+def test_noise_id_is_word0_times_vocab_over_2_64():
+    """Uniform-prior noise tokens: floor(w * V / 2^64) of numpy's own word 0."""
+    for (j, b, step, V) in [(1, 0, 0, 512), (15, 63, 1234, 151936), (7, 3, 99, 8)]:
+        w = _numpy_words([SLOT_NOISE, j, b, step], [5, 0])[0]
+        assert noise_id(5, j, b, step, V) == (w * V) >> 64
+
+
+def test_noise_id_uniform_chi_square():
+    from scipy import stats
+    V = 64
+    ids = [noise_id(0, j, b, s, V) for j in range(1, 16) for b in range(32) for s in range(20)]
+    assert min(ids) >= 0 and max(ids) < V
+    counts = np.bincount(ids, minlength=V)
+    assert stats.chisquare(counts).pvalue > 0.01

@@ -24,7 +24,7 @@ import synth
 from oracle import canonical as cn
 from oracle import model as om
 from oracle import spec
-from oracle.philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, uniform24_np
+from oracle.philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, noise_id, uniform24_np
 
 TWO24 = 1 << 24
 
@@ -59,6 +59,11 @@ class _EnumDraws:
             self.i += 1
             return d
         raise _Branch(dist_fn())
+
+    def noise(self, j, vocab):
+        # uniform-prior noise tokens: a fixed Philox realisation (losslessness
+        # must hold for any draft distribution, hence for any noise)
+        return noise_id(7, j, 0, 0, vocab)
 
     def categorical(self, slot, j, weights):
         def dist():
@@ -163,6 +168,18 @@ def test_exact_enumeration_one_step_lossless(toy, K):
     if K >= 2:
         # some rejections happen, so the check covers the residual branch
         assert any(len(c) < K + 1 for c in dist)
+
+
+@pytest.mark.parametrize("K", [2, 3])
+def test_exact_enumeration_uniform_prior(toy, K):
+    """Uniform-state prior: the block's noise tokens are uniform Philox draws
+    instead of the mask id (paperglide reader, "Lossless Psi-Spec decoding for
+    USDMs"); the committed prefix is still exactly p_AR."""
+    cfg, w = toy
+    cfg = dict(cfg, noise_prior=1)
+    noise = [noise_id(7, j, 0, 0, cfg["vocab"]) for j in range(1, K)]
+    assert any(t != cfg["mask_id"] for t in noise)
+    _check_one_step(cfg, w, [1, 5, 2, 6, 0], K, 1.0)
 
 
 def test_exact_enumeration_temperature(toy):
