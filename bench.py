@@ -74,6 +74,7 @@ def parse():
                          "generate N tokens with natural acceptance (pages on demand)")
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--prior", type=int, default=0, help="draft noise prior: 0 mask, 1 uniform")
+    ap.add_argument("--passes", type=int, default=1, help="draft passes per step (generate mode)")
     return ap.parse_args()
 
 
@@ -321,7 +322,7 @@ def generate_mode(args, U, synth, torch, cfg):
     log("generating weights on the GPU")
     model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))
     max_ctx = args.prompt + args.generate + 3 * K + 8
-    g = Generator(model, args.batch, K, max_ctx, seed=0, prefill_chunk=512)
+    g = Generator(model, args.batch, K, max_ctx, seed=0, prefill_chunk=512, n_passes=args.passes)
     prompts = synth.prompt_ids(cfg, args.prompt, 1, batch=args.batch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -344,8 +345,8 @@ def generate_mode(args, U, synth, torch, cfg):
            "value": round(toks / t_gen, 1), "unit": "tokens/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "bf16",
            "data": "synthetic (random-init weights, uniform random prompts)",
-           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d" % (
-               args.batch, args.prompt, args.generate, K, args.prior)},
+           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d passes%d" % (
+               args.batch, args.prompt, args.generate, K, args.prior, args.passes)},
            "steps": st["steps"], "TPF": round(st["TPF"], 3), "AL": round(st["AL"], 3),
            "ms_per_step": round(1e3 * t_gen / st["steps"], 3),
            "prefill_s": round(t_prefill, 3), "pages_in_use": st["pages_in_use"]}

@@ -148,6 +148,26 @@ int uno_draft_block(const uno_config *cfg, const uno_weights *w, const uno_kv *k
                     float *draft_logits, int32_t *draft_tokens, int32_t *status,
                     void *ws, size_t ws_bytes, void *stream);
 
+/* One draft pass of a multi-pass draft (paperglide reader, "Supplementary
+ * Details": Psi-samplers refine a block over several denoising steps, and
+ * sample quality grows with the number of steps).  Same as uno_draft_block,
+ * except that
+ *   block        [dev] int32 [batch, K] or NULL: when given, draft rows
+ *                1..K-1 of sequence b hold block[b*K + 0 .. K-2] (the tokens
+ *                d_1..d_{K-1} the previous pass sampled) instead of the
+ *                prior's noise; it may alias draft_tokens (it is read before
+ *                draft_tokens is written);
+ *   sample_slot  Philox slot of this pass's draft sampling: 0 for the pass
+ *                whose drafts go to verification (as uno_draft_block), 4 + i
+ *                for intermediate pass i (4 <= sample_slot <= 63).
+ * Only the final pass's logits and tokens enter uno_spec_accept, so the
+ * decode stays lossless for any number of passes. */
+int uno_draft_block_from(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
+                         const int32_t *anchor, const int32_t *block, int batch, int K,
+                         int max_ctx, float inv_temp, uint64_t seed, const uint64_t *step,
+                         int sample_slot, float *draft_logits, int32_t *draft_tokens,
+                         int32_t *status, void *ws, size_t ws_bytes, void *stream);
+
 /* Verify block (picx.dev summary, "Architecture": verification uses the AR
  * weights only).  Rows of sequence b: rows[b, 0..K-1] at positions
  * kv_len[b] + pos_offset + j, causal (row j sees keys <= its own position),

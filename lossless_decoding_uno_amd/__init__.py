@@ -23,7 +23,8 @@ STATUS_NAMES = {1: "invalid argument", 2: "unsupported shape", 3: "page table to
                 4: "workspace too small", 5: "HIP launch failure"}
 DEV_CAPACITY, DEV_BAD_TOKEN, DEV_BAD_PAGE, DEV_NONFINITE, DEV_BAD_ACCEPT = 1, 2, 4, 8, 16
 
-EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_verify_block", "uno_draft_sample",
+EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_draft_block_from", "uno_verify_block",
+           "uno_draft_sample",
            "uno_spec_accept_workspace_bytes", "uno_spec_accept", "uno_kv_commit",
            "uno_set_timing_events", "uno_timing_events_used", "uno_status_string",
            "uno_last_hip_error")
@@ -78,6 +79,8 @@ def load_library():
     lib.uno_workspace_bytes.argtypes = [P, I, I, I]
     lib.uno_draft_block.restype = I
     lib.uno_draft_block.argtypes = [P, P, P, P, I, I, I, F, U64, P, P, P, P, P, SZ, P]
+    lib.uno_draft_block_from.restype = I
+    lib.uno_draft_block_from.argtypes = [P, P, P, P, P, I, I, I, F, U64, P, I, P, P, P, P, SZ, P]
     lib.uno_verify_block.restype = I
     lib.uno_verify_block.argtypes = [P, P, P, P, I, I, I, I, P, P, P, SZ, P]
     lib.uno_draft_sample.restype = I
@@ -247,6 +250,37 @@ def draft_block(model, kv, anchor, K, max_ctx, inv_temp, seed, step, draft_logit
                                ctypes.byref(kv.struct), _ptr(anchor), B, K, max_ctx,
                                float(inv_temp), int(seed), _ptr(step), _ptr(draft_logits),
                                _ptr(draft_tokens), _ptr(status), _ptr(ws), ws.numel(), _stream()))
+
+
+def draft_block_from(model, kv, anchor, block, K, max_ctx, inv_temp, seed, step, sample_slot,
+                     draft_logits, draft_tokens, ws, status=None):
+    """uno_draft_block_from: one pass of a multi-pass draft; block [B, K] int32
+    (rows 1..K-1 take block[:, :K-1]) or None; sample_slot 0 or 4 + pass."""
+    lib = load_library()
+    B = anchor.shape[0]
+    V = model.cfg["vocab"]
+    _need(anchor, torch.int32, (B,), "anchor")
+    if block is not None:
+        _need(block, torch.int32, (B, K), "block")
+    _need(step, torch.uint64, (B,), "step")
+    _need(draft_logits, torch.float32, (B, K, V), "draft_logits")
+    _need(draft_tokens, torch.int32, (B, K), "draft_tokens")
+    _check(lib.uno_draft_block_from(ctypes.byref(model.config), ctypes.byref(model.weights),
+                                    ctypes.byref(kv.struct), _ptr(anchor), _ptr(block), B, K,
+                                    max_ctx, float(inv_temp), int(seed), _ptr(step),
+                                    int(sample_slot), _ptr(draft_logits), _ptr(draft_tokens),
+                                    _ptr(status), _ptr(ws), ws.numel(), _stream()))
+
+
+def draft_passes(model, kv, anchor, K, max_ctx, inv_temp, seed, step, n_passes, draft_logits,
+                 draft_tokens, ws, status=None):
+    """n_passes draft passes: pass i > 0 reads the tokens pass i-1 sampled (slot
+    4 + (i-1)); the last pass samples with slot 0 and leaves the logits and
+    tokens that verification uses."""
+    for i in range(n_passes):
+        draft_block_from(model, kv, anchor, draft_tokens if i else None, K, max_ctx, inv_temp,
+                         seed, step, 0 if i == n_passes - 1 else 4 + i, draft_logits,
+                         draft_tokens, ws, status)
 
 
 def verify_block(model, kv, rows, max_ctx, pos_offset, verify_logits, ws, status=None):

@@ -155,7 +155,8 @@ const bf16_raw_t* bp(const void* p) { return static_cast<const bf16_raw_t*>(p); 
 
 // One forward pass of B*K rows (draft when `anchor` != null, verify otherwise).
 int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const int32_t* anchor,
-             const int32_t* rows, int B, int K, int max_ctx, int pos_offset, bool lora,
+             const int32_t* block, const int32_t* rows, int B, int K, int max_ctx, int pos_offset,
+             bool lora,
              uint64_t seed, const uint64_t* step, float* logits, int32_t* status, void* ws,
              hipStream_t s) {
   const PassWs W = carve(c, B, K, max_ctx, ws);
@@ -168,7 +169,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   hipError_t e;
 #define UNO_TRY(x) do { e = (x); if (e != hipSuccess) return hip_fail(e); } while (0)
 
-  UNO_TRY(launch_embed(c, bp(w->embed), anchor, rows, B, K, seed, step, W.h, status, s));
+  UNO_TRY(launch_embed(c, bp(w->embed), anchor, block, rows, B, K, seed, step, W.h, status, s));
   UNO_TRY(launch_rope_table(kv->kv_len, B, K, draft ? 0 : pos_offset, hd / 2, c.rope_theta,
                             W.cs, s));
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
@@ -293,28 +294,38 @@ size_t uno_workspace_bytes(const uno_config* cfg, int batch, int K, int max_ctx)
   return carve(*cfg, batch, K, max_ctx, nullptr).total;
 }
 
-int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
-                    const int32_t* anchor, int batch, int K, int max_ctx, float inv_temp,
-                    uint64_t seed, const uint64_t* step, float* draft_logits,
-                    int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
-                    void* stream) {
+int uno_draft_block_from(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
+                         const int32_t* anchor, const int32_t* block, int batch, int K,
+                         int max_ctx, float inv_temp, uint64_t seed, const uint64_t* step,
+                         int sample_slot, float* draft_logits, int32_t* draft_tokens,
+                         int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || K < 1 || K > 64 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
   if (!anchor || !step || !draft_logits || !draft_tokens || !ws) return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
+  if (sample_slot != 0 && (sample_slot < 4 || sample_slot > 63)) return UNO_ERR_INVALID_ARG;
   if ((rc = check_kv(*cfg, kv, K, 0))) return rc;
   if ((rc = check_layers(*cfg, w, true))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = run_pass(*cfg, w, kv, anchor, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0, seed,
-                step, draft_logits, status, ws, s);
+  rc = run_pass(*cfg, w, kv, anchor, block, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
+                seed, step, draft_logits, status, ws, s);
   if (rc) return rc;
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
-    return launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed, step,
-                               draft_tokens, status, s);
+    return launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed, sample_slot,
+                               step, draft_tokens, status, s);
   });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
+                    const int32_t* anchor, int batch, int K, int max_ctx, float inv_temp,
+                    uint64_t seed, const uint64_t* step, float* draft_logits,
+                    int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return uno_draft_block_from(cfg, w, kv, anchor, nullptr, batch, K, max_ctx, inv_temp, seed,
+                              step, 0, draft_logits, draft_tokens, status, ws, ws_bytes, stream);
 }
 
 int uno_verify_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
@@ -329,8 +340,8 @@ int uno_verify_block(const uno_config* cfg, const uno_weights* w, const uno_kv* 
   if ((rc = check_kv(*cfg, kv, K, pos_offset))) return rc;
   if ((rc = check_layers(*cfg, w, false))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
-  return run_pass(*cfg, w, kv, nullptr, rows, batch, K, max_ctx, pos_offset, false, 0, nullptr,
-                  verify_logits, status, ws, static_cast<hipStream_t>(stream));
+  return run_pass(*cfg, w, kv, nullptr, nullptr, rows, batch, K, max_ctx, pos_offset, false, 0,
+                  nullptr, verify_logits, status, ws, static_cast<hipStream_t>(stream));
 }
 
 int uno_draft_sample(const float* logits, int batch, int K, int vocab, float inv_temp,
@@ -339,7 +350,7 @@ int uno_draft_sample(const float* logits, int batch, int K, int vocab, float inv
   if (!logits || !step || !tokens) return UNO_ERR_INVALID_ARG;
   if (batch < 1 || K < 1 || vocab < 1 || vocab > (1 << 20)) return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
-  const hipError_t e = launch_draft_sample(logits, batch, K, vocab, inv_temp, seed, step, tokens,
+  const hipError_t e = launch_draft_sample(logits, batch, K, vocab, inv_temp, seed, 0, step, tokens,
                                            status, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }

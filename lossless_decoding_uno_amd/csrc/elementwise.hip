@@ -15,13 +15,14 @@ namespace uno {
 
 // ------------------------------------------------------------ embedding
 // One workgroup per row r = b*K + j.  Draft mode (anchor != null): id =
-// anchor[b] for j == 0; the noise rows j >= 1 hold mask_id (noise_prior 0) or
-// a uniform token floor(w * V / 2^64), w = Philox word 0 at counter
-// (3, j, b, step[b]) under key (seed, 0) (noise_prior 1).  Verify mode: id =
-// rows[r].
+// anchor[b] for j == 0; the rows j >= 1 hold block[b*K + j-1] in a later draft
+// pass, else the prior's noise: mask_id (noise_prior 0) or a uniform token
+// floor(w * V / 2^64), w = Philox word 0 at counter (3, j, b, step[b]) under
+// key (seed, 0) (noise_prior 1).  Verify mode: id = rows[r].
 __global__ void __launch_bounds__(256)
 k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
-        const int32_t* __restrict__ rows, int K, int D, int V, int mask_id, int noise_prior,
+        const int32_t* __restrict__ block, const int32_t* __restrict__ rows, int K, int D, int V,
+        int mask_id, int noise_prior,
         uint64_t seed, const uint64_t* __restrict__ step, float* __restrict__ h,
         int32_t* __restrict__ status) {
   const int r = blockIdx.x;
@@ -31,6 +32,8 @@ k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
     id = rows[r];
   } else if (j == 0) {
     id = anchor[b];
+  } else if (block) {
+    id = block[b * K + j - 1];
   } else if (noise_prior == 0) {
     id = mask_id;
   } else {
@@ -58,10 +61,10 @@ k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
 }
 
 hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
-                        const int32_t* rows, int B, int K, uint64_t seed, const uint64_t* step,
-                        float* h, int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3(B * K), dim3(256), 0, s, embed, anchor, rows, K, c.d_model,
-                     c.vocab, c.mask_id, c.noise_prior, seed, step, h, status);
+                        const int32_t* block, const int32_t* rows, int B, int K, uint64_t seed,
+                        const uint64_t* step, float* h, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(B * K), dim3(256), 0, s, embed, anchor, block, rows, K,
+                     c.d_model, c.vocab, c.mask_id, c.noise_prior, seed, step, h, status);
   return hipGetLastError();
 }
 

@@ -239,10 +239,12 @@ __device__ __forceinline__ void flag(int32_t* status, int b, int32_t f) {
 }
 
 // ------------------------------------------------------------ kernels
-// One workgroup per draft row (b, j): d = categorical(W(row), U(slot 0, j, b, step[b])).
+// One workgroup per draft row (b, j): d = categorical(W(row), U(slot, j, b, step[b]));
+// slot 0 for the drafts that go to verification, 4 + i for the samples of an
+// intermediate draft pass i.
 __global__ void __launch_bounds__(kThreads)
 k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, uint64_t seed,
-               const uint64_t* __restrict__ step, int32_t* __restrict__ tokens,
+               int slot, const uint64_t* __restrict__ step, int32_t* __restrict__ tokens,
                int32_t* __restrict__ status) {
   extern __shared__ u128 tiles[];
   __shared__ RowShared sh;
@@ -257,7 +259,7 @@ k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, u
   }
   PlainWeights wf{row, m, inv_temp};
   const u128 S = block_weight_sum(wf, V, tiles, sh);
-  const uint32_t U = uniform24(seed, 0, j, b, step[b]);
+  const uint32_t U = uniform24(seed, slot, j, b, step[b]);
   const int v = block_find(wf, V, tiles, scaled_target(U, S), sh);
   if (threadIdx.x == 0) tokens[row_id] = v;
 }
@@ -396,10 +398,10 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
 static size_t tile_lds_bytes(int V) { return (size_t)((V + kTile - 1) / kTile) * sizeof(u128); }
 
 hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
-                               uint64_t seed, const uint64_t* step, int32_t* tokens,
+                               uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
                                int32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(k_draft_sample, dim3(B * K), dim3(kThreads), tile_lds_bytes(V), s, logits,
-                     K, V, inv_temp, seed, step, tokens, status);
+                     K, V, inv_temp, seed, slot, step, tokens, status);
   return hipGetLastError();
 }
 

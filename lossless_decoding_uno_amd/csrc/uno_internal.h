@@ -15,7 +15,7 @@ static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; 
 
 // ---------------------------------------------------------------- sampler
 hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
-                               uint64_t seed, const uint64_t* step, int32_t* tokens,
+                               uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
                                int32_t* status, hipStream_t s);
 size_t spec_accept_ws_bytes(int B, int K);
 hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* drafts, int B,
@@ -26,11 +26,12 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
 // ---------------------------------------------------------------- elementwise / small ops
 // Block rows: draft (anchor + mask ids) or given rows; gathers embeddings into
 // the fp32 residual stream h [R, D]; also writes ids [R].
-// Draft rows (anchor != null) draw uniform noise tokens from (seed, step) when
-// c.noise_prior == 1.
+// Draft rows (anchor != null): rows j >= 1 take block[b*K + j-1] when block is
+// given (a later draft pass), else the prior's noise: mask_id, or uniform
+// tokens from (seed, step) when c.noise_prior == 1.
 hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
-                        const int32_t* rows, int B, int K, uint64_t seed, const uint64_t* step,
-                        float* h, int32_t* status, hipStream_t s);
+                        const int32_t* block, const int32_t* rows, int B, int K, uint64_t seed,
+                        const uint64_t* step, float* h, int32_t* status, hipStream_t s);
 // RMSNorm of fp32 rows into bf16 rows.
 hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
                           bf16_raw_t* out, hipStream_t s);

@@ -7,12 +7,13 @@ keeps the page table and reads back the committed tokens.  Tokens per forward
 pass (TPF) follow the pages' definition: output tokens per forward pass, where
 one step runs two passes (draft and verify) and commits a + 1 tokens, so
 1 <= TPF <= (K + 1) / 2 (paperglide reader, "The Uno Framework"); AL is the mean
-number of tokens a step commits.
+number of tokens a step commits.  With n draft passes per step (multi-pass
+drafting) a step runs n + 1 passes; ``stats`` reports TPF over all of them.
 """
 import numpy as np
 import torch
 
-from . import (PagedKV, alloc_workspace, draft_block, kv_commit, spec_accept,
+from . import (PagedKV, alloc_workspace, draft_passes, kv_commit, spec_accept,
                spec_accept_workspace_bytes, verify_block, workspace_bytes)
 
 
@@ -69,8 +70,9 @@ class Generator:
     """
 
     def __init__(self, model, batch, K, max_ctx, n_pages=None, inv_temp=1.0, seed=0,
-                 prefill_chunk=512, page_size=16, device="cuda"):
+                 prefill_chunk=512, page_size=16, device="cuda", n_passes=1):
         self.model, self.B, self.K = model, batch, K
+        self.n_passes = int(n_passes)      # draft passes per step (multi-pass drafting)
         self.cfg = model.cfg
         self.inv_temp, self.seed = float(inv_temp), int(seed)
         self.chunk = int(prefill_chunk)
@@ -123,8 +125,8 @@ class Generator:
             # draft writes kv_len .. kv_len+K-1, verify kv_len+1 .. kv_len+K
             self.pool.ensure(b, int(self.kv_len[b]) + K + 1)
         self.pool.sync()
-        draft_block(self.model, self.kv, self.e, K, self.max_ctx, self.inv_temp, self.seed,
-                    self.step_ctr, self.zq, self.d, self.ws, self.status)
+        draft_passes(self.model, self.kv, self.e, K, self.max_ctx, self.inv_temp, self.seed,
+                     self.step_ctr, self.n_passes, self.zq, self.d, self.ws, self.status)
         verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws,
                      self.status)
         spec_accept(self.zq, self.zp, self.d, self.inv_temp, self.seed, self.step_ctr, self.a,
@@ -149,7 +151,7 @@ class Generator:
         per = np.array(self.committed_per_step, dtype=np.float64)   # [steps, B]
         return {"steps": self.steps,
                 "AL": float(per.mean()) if per.size else 0.0,
-                "TPF": float(per.mean() / 2.0) if per.size else 0.0,
+                "TPF": float(per.mean() / (self.n_passes + 1)) if per.size else 0.0,
                 "pages_in_use": self.pool.pages_in_use()}
 
     def _check_status(self):

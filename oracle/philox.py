@@ -30,6 +30,7 @@ SLOT_DRAFT = 0     # draft token j+1 is drawn with j
 SLOT_ACCEPT = 1    # accept test of draft i uses j = i - 1
 SLOT_EXTRA = 2     # residual / bonus token uses j = a
 SLOT_NOISE = 3     # uniform-prior noise token of draft row j >= 1
+SLOT_PASS = 4      # sample j of intermediate draft pass i uses slot SLOT_PASS + i
 
 
 def philox4x64_10(counter, key):

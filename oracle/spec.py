@@ -40,7 +40,7 @@ import numpy as np
 
 from . import canonical as cn
 from .model import KVCache, forward
-from .philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, noise_id, uniform24
+from .philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, SLOT_PASS, noise_id, uniform24
 
 
 class PhiloxDraws:
@@ -91,16 +91,19 @@ def prefill(cfg, wts, seq):
     seq.kv_len = n - 1
 
 
-def draft_logits(cfg, wts, seq, K, act_round=None, draws=None):
+def draft_logits(cfg, wts, seq, K, act_round=None, draws=None, block=None):
     """Draft pass: rows [anchor, noise x (K-1)], gate (0, 1, ..., 1). fp64 [K, V].
 
     The noisy block is the anchor followed by K-1 tokens from the diffusion
     prior (paperglide reader, "The Psi-Speculative Sampler"): the mask token
     for a masked model, or uniform tokens for a uniform-state model
     ("Supplementary Details"), chosen by cfg["noise_prior"] (0 / 1); uniform
-    tokens come from ``draws.noise(j, V)``."""
+    tokens come from ``draws.noise(j, V)``.  A later pass of a multi-pass draft
+    passes ``block``: rows 1..K-1 then hold block[0..K-2]."""
     n0 = seq.kv_len                       # position of the anchor
-    if cfg.get("noise_prior", 0) == 1:
+    if block is not None:
+        noise = [int(t) for t in block[: K - 1]]
+    elif cfg.get("noise_prior", 0) == 1:
         noise = [draws.noise(j, cfg["vocab"]) for j in range(1, K)]
     else:
         noise = [cfg["mask_id"]] * (K - 1)
@@ -111,10 +114,27 @@ def draft_logits(cfg, wts, seq, K, act_round=None, draws=None):
     return forward(cfg, wts, seq.cache, rows, pos, gate, lim, act_round=act_round)
 
 
-def draft_sample(zq32, inv_temp, draws):
+def draft_sample(zq32, inv_temp, draws, slot=SLOT_DRAFT):
     """d_{j+1} ~ q_{j+1} for each draft row j (fp32 logits [K, V])."""
-    return [draws.categorical(SLOT_DRAFT, j, cn.row_weights(zq32[j], inv_temp)[0])
+    return [draws.categorical(slot, j, cn.row_weights(zq32[j], inv_temp)[0])
             for j in range(zq32.shape[0])]
+
+
+def draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws):
+    """Multi-pass draft (paperglide reader, "Supplementary Details": a
+    Psi-sampler refines the block over several denoising steps).  Pass i
+    re-runs the draft block with rows 1..K-1 holding the tokens pass i-1
+    sampled (intermediate samples use Philox slot SLOT_PASS + i); the last pass
+    samples the drafts with SLOT_DRAFT.  Returns (zq fp64, zq fp32, drafts) of
+    the last pass: only those enter the accept test, so any number of passes
+    keeps the decode lossless."""
+    block = None
+    for i in range(n_passes):
+        zq = draft_logits(cfg, wts, seq, K, draws=draws, block=block)
+        zq32 = zq.astype(np.float32)
+        last = i == n_passes - 1
+        block = draft_sample(zq32, inv_temp, draws, SLOT_DRAFT if last else SLOT_PASS + i)
+    return zq, zq32, block
 
 
 def verify_logits(cfg, wts, seq, rows, pos_offset=1, act_round=None):
@@ -172,15 +192,14 @@ def commit(seq, a, committed):
     seq.step += 1
 
 
-def step(cfg, wts, seq, K, inv_temp, draws, forced=None):
-    """One full draft -> sample -> verify -> accept -> commit step.
+def step(cfg, wts, seq, K, inv_temp, draws, forced=None, n_passes=1):
+    """One full draft (n_passes passes) -> sample -> verify -> accept -> commit
+    step.
 
     Returns a dict with the logits (fp64 and the fp32 copies the sampler saw),
     drafts, a, committed tokens and the extra token.
     """
-    zq = draft_logits(cfg, wts, seq, K, draws=draws)
-    zq32 = zq.astype(np.float32)
-    drafts = draft_sample(zq32, inv_temp, draws)
+    zq, zq32, drafts = draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws)
     zp = verify_logits(cfg, wts, seq, drafts)
     zp32 = zp.astype(np.float32)
     a, committed, extra = spec_accept(zq32, zp32, drafts, inv_temp, draws, forced)

@@ -302,3 +302,57 @@ def test_many_rows_tiled_gemm_matches_oracle(B, K_blk, prompt_len):
         assert_logits_close(zq_c[b], ospec.draft_logits(cfg, w64, s, K_blk), "draft seq %d" % b)
         assert_logits_close(zp_c[b], ospec.verify_logits(cfg, w64, s, list(rows[b])),
                             "verify seq %d" % b)
+
+
+def test_multi_pass_draft_matches_oracle(setup):
+    """Multi-pass draft, pass by pass: pass 1 samples its block with Philox
+    slot 4, pass 2 re-runs the draft with rows 1..K-1 holding those tokens and
+    samples the drafts with slot 0.  Each pass's logits must match the oracle's
+    on the same block, and its tokens must be exactly the oracle sampler's on
+    the GPU's own logits; then verification and the accept step as usual."""
+    U, cfg, wts, w64, model = setup
+    prompt = synth.prompt_ids(cfg, 24, 9)
+    cap = len(prompt) + 4 * (K + 1) + 8
+    kv = U.PagedKV(cfg, 1, cap)
+    ws = U.alloc_workspace(max(U.workspace_bytes(model, 1, K, cap),
+                               U.workspace_bytes(model, 1, len(prompt), cap)))
+    _prefill_gpu(U, model, kv, prompt, ws, cap)
+    seq = ospec.Sequence(cfg, prompt, capacity=cap)
+    ospec.prefill(cfg, w64, seq)
+    dev = "cuda"
+    V = cfg["vocab"]
+    zq_g = torch.empty((1, K, V), dtype=torch.float32, device=dev)
+    zp_g = torch.empty((1, K, V), dtype=torch.float32, device=dev)
+    d_g = torch.empty((1, K), dtype=torch.int32, device=dev)
+    a_g = torch.empty(1, dtype=torch.int32, device=dev)
+    c_g = torch.empty((1, K + 1), dtype=torch.int32, device=dev)
+    e_g = torch.empty(1, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    step_g = torch.zeros(1, dtype=torch.uint64).to(dev)
+    aws = U.alloc_workspace(U.spec_accept_workspace_bytes(1, K))
+    for _ in range(4):
+        draws = ospec.PhiloxDraws(SEED, 0, seq.step)
+        anchor = torch.tensor([seq.tokens[-1]], dtype=torch.int32, device=dev)
+        block = None
+        for p, slot in enumerate((4, 0)):
+            U.draft_block_from(model, kv, anchor, d_g if p else None, K, cap, 1.0, SEED, step_g,
+                               slot, zq_g, d_g, ws, status)
+            zq = ospec.draft_logits(cfg, w64, seq, K, draws=draws, block=block)
+            zq_gpu = zq_g.cpu().numpy()[0]
+            assert_logits_close(zq_gpu, zq, "pass %d step %d" % (p, seq.step))
+            toks = ospec.draft_sample(zq_gpu, 1.0, draws, slot)
+            np.testing.assert_array_equal(d_g.cpu().numpy()[0], toks)
+            block = toks
+        drafts = block
+        rows = torch.tensor([drafts], dtype=torch.int32, device=dev)
+        U.verify_block(model, kv, rows, cap, 1, zp_g, ws, status)
+        zp = ospec.verify_logits(cfg, w64, seq, drafts)
+        zp_gpu = zp_g.cpu().numpy()[0]
+        assert_logits_close(zp_gpu, zp, "verify step %d" % seq.step)
+        a, committed, extra = ospec.spec_accept(zq_gpu, zp_gpu, drafts, 1.0, draws)
+        U.spec_accept(zq_g, zp_g, rows, 1.0, SEED, step_g, a_g, c_g, e_g, aws, status=status)
+        assert int(a_g.item()) == a
+        np.testing.assert_array_equal(c_g.cpu().numpy()[0][: a + 1], committed)
+        U.kv_commit(kv, a_g, K, step_g, status)
+        ospec.commit(seq, a, committed)
+    assert int(status.item()) == 0

@@ -24,7 +24,8 @@ import synth
 from oracle import canonical as cn
 from oracle import model as om
 from oracle import spec
-from oracle.philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, noise_id, uniform24_np
+from oracle.philox import (SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, SLOT_PASS, noise_id,
+                           uniform24_np)
 
 TWO24 = 1 << 24
 
@@ -86,15 +87,30 @@ class _EnumDraws:
         return self._take(dist)
 
 
-def _enumerate_step(cfg, w, seq, K, inv_t):
-    """{committed tuple: probability} of one step from ``seq`` (exact)."""
+class _FixedPassDraws(_EnumDraws):
+    """Enumerates the final pass; the intermediate passes' samples are fixed."""
+
+    def __init__(self, path, fixed):
+        super().__init__(path)
+        self.fixed = fixed          # {(slot, j): token}
+
+    def categorical(self, slot, j, weights):
+        if slot >= SLOT_PASS:
+            return self.fixed[(slot, j)]
+        return super().categorical(slot, j, weights)
+
+
+def _enumerate_step(cfg, w, seq, K, inv_t, n_passes=1, fixed=None):
+    """{committed tuple: probability} of one step from ``seq`` (exact; with
+    ``fixed`` the intermediate draft passes' samples are held fixed)."""
     out = {}
     stack = [([], Fraction(1))]
     while stack:
         path, prob = stack.pop()
         s = seq.copy()
+        draws = _EnumDraws(path) if fixed is None else _FixedPassDraws(path, fixed)
         try:
-            r = spec.step(cfg, w, s, K, inv_t, _EnumDraws(path))
+            r = spec.step(cfg, w, s, K, inv_t, draws, n_passes=n_passes)
         except _Branch as br:
             for dec, p in br.dist.items():
                 stack.append((path + [dec], prob * p))
@@ -121,10 +137,10 @@ def toy():
     return cfg, synth.to_f64(wts)
 
 
-def _check_one_step(cfg, w, prompt, K, inv_t):
+def _check_one_step(cfg, w, prompt, K, inv_t, n_passes=1, fixed=None):
     seq = spec.Sequence(cfg, prompt, capacity=len(prompt) + 2 * K + 4)
     spec.prefill(cfg, w, seq)
-    dist = _enumerate_step(cfg, w, seq, K, inv_t)
+    dist = _enumerate_step(cfg, w, seq, K, inv_t, n_passes, fixed)
     assert abs(sum(dist.values()) - 1) == 0
     for c in dist:
         assert 2 <= len(c) <= K + 1          # tokens per step within [2, K+1]
@@ -180,6 +196,31 @@ def test_exact_enumeration_uniform_prior(toy, K):
     noise = [noise_id(7, j, 0, 0, cfg["vocab"]) for j in range(1, K)]
     assert any(t != cfg["mask_id"] for t in noise)
     _check_one_step(cfg, w, [1, 5, 2, 6, 0], K, 1.0)
+
+
+@pytest.mark.parametrize("fixed", [{(4, 0): 0, (4, 1): 5}, {(4, 0): 6, (4, 1): 6},
+                                   {(4, 0): 2, (4, 1): 7, (5, 0): 1, (5, 1): 3}])
+def test_exact_enumeration_multi_pass_draft(toy, fixed):
+    """Several draft passes, each feeding its samples back into the block.
+    Conditional on any outcome of the intermediate passes the final pass is an
+    ordinary draft, so the committed prefix must be exactly p_AR for every such
+    outcome (enumerated exactly over the final pass and the accept draws)."""
+    cfg, w = toy
+    n_passes = 1 + max(slot for slot, _ in fixed) - 3
+    _check_one_step(cfg, w, [3, 1, 4], 2, 1.0, n_passes, fixed)
+
+
+def test_multi_pass_changes_the_draft(toy):
+    """A second pass conditions the draft on the first pass's tokens: its q
+    differs from the one-pass q (otherwise the extra passes would be void)."""
+    cfg, w = toy
+    seq = spec.Sequence(cfg, [3, 1, 4, 1, 5], capacity=20)
+    spec.prefill(cfg, w, seq)
+    draws = spec.PhiloxDraws(0, 0, 0)
+    z1 = spec.draft_logits(cfg, w, seq, 3, draws=draws)
+    z2, _, _ = spec.draft_passes(cfg, w, seq, 3, 2, 1.0, draws)
+    assert np.array_equal(z1[0], z2[0])             # row 0 is the AR row in every pass
+    assert np.abs(z1[1:] - z2[1:]).max() > 1e-6
 
 
 def test_exact_enumeration_temperature(toy):
