@@ -65,6 +65,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--ctx", type=int, default=9216)
     ap.add_argument("--K", type=int, default=16)
+    ap.add_argument("--temp", type=float, default=1.0, help="sampling temperature")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -85,8 +86,9 @@ def log(msg):
 class Workload:
     """Device state of one (batch, context, K) decode workload."""
 
-    def __init__(self, U, torch, synth, model, cfg, B, ctx, K, n_steps, seed):
+    def __init__(self, U, torch, synth, model, cfg, B, ctx, K, n_steps, seed, temp=1.0):
         self.U, self.torch = U, torch
+        self.inv_t = float(np.float32(1.0 / temp))
         self.B, self.ctx, self.K = B, ctx, K
         self.cfg = cfg
         dev = "cuda"
@@ -115,10 +117,10 @@ class Workload:
 
     def step(self, i):
         U = self.U
-        U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, 1.0, 0, self.step_ctr,
+        U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, self.inv_t, 0, self.step_ctr,
                       self.zq, self.d, self.ws)
         U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws)
-        U.spec_accept(self.zq, self.zp, self.d, 1.0, 0, self.step_ctr, self.a, self.c, self.e,
+        U.spec_accept(self.zq, self.zp, self.d, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e,
                       self.aws, forced_accept=self.forced[i])
         U.kv_commit(self.kv, self.a, self.K, self.step_ctr)
 
@@ -384,7 +386,8 @@ def main():
     torch.cuda.synchronize()
     n_steps = args.warmup + args.steps + 1
     log("allocating KV for batch %d context %d" % (args.batch, args.ctx))
-    W = Workload(U, torch, synth, model, cfg, args.batch, args.ctx, K, n_steps, seed=1)
+    W = Workload(U, torch, synth, model, cfg, args.batch, args.ctx, K, n_steps, seed=1,
+                 temp=args.temp)
     torch.cuda.synchronize()
     log("probe step (per-kernel-class times)")
     W.step(0)
@@ -455,9 +458,10 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded random-init weights and KV, forced accept lengths)",
-           "config": {"workload": "qwen3-8b-shape b%d ctx%d K%d forced a~U{0..%d}" % (
-               args.batch, args.ctx, K, K), "global_batch": args.batch, "seq_len": args.ctx,
-               "block_K": K, "parallelism": "none (1 GPU)"},
+           "config": {"workload": "qwen3-8b-shape b%d ctx%d K%d T%g forced a~U{0..%d}" % (
+               args.batch, args.ctx, K, args.temp, K), "global_batch": args.batch,
+               "seq_len": args.ctx, "block_K": K, "temperature": args.temp,
+               "parallelism": "none (1 GPU)"},
            "roofline": roof,
            "roofline_gemm": roof_gemm,
            "measured_ceilings": ceil,

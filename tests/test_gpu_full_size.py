@@ -60,7 +60,7 @@ def _check(gpu, bf, exact, elementwise, what):
     return float(d_gpu.max())
 
 
-def _run(big, B, ctx, b_check, elementwise=False):
+def _run(big, B, ctx, b_check, elementwise=False, K=K, inv_t=1.0):
     U, cfg, wts, w64, model = big
     cap = ctx + 2 * K + 8
     n_pages = B * ((cap + 15) // 16)
@@ -106,13 +106,13 @@ def _run(big, B, ctx, b_check, elementwise=False):
     assert (status.cpu().numpy() == 0).all()
     # sampler, bit-exact on the oracle's own fp32 logits
     zq32, zp32 = zq_ref.astype(np.float32), zp_ref.astype(np.float32)
-    a_ref, comm_ref, e_ref = ospec.spec_accept(zq32, zp32, drafts, 1.0,
+    a_ref, comm_ref, e_ref = ospec.spec_accept(zq32, zp32, drafts, inv_t,
                                                ospec.PhiloxDraws(0, 0, 0))
     a = torch.empty(1, dtype=torch.int32, device="cuda")
     c = torch.empty((1, K + 1), dtype=torch.int32, device="cuda")
     e = torch.empty(1, dtype=torch.int32, device="cuda")
     U.spec_accept(torch.from_numpy(zq32[None]).cuda(), torch.from_numpy(zp32[None]).cuda(),
-                  torch.tensor([drafts], dtype=torch.int32, device="cuda"), 1.0, 0,
+                  torch.tensor([drafts], dtype=torch.int32, device="cuda"), inv_t, 0,
                   torch.zeros(1, dtype=torch.uint64).cuda(), a, c, e,
                   U.alloc_workspace(U.spec_accept_workspace_bytes(1, K)))
     assert (int(a.item()), int(e.item())) == (a_ref, e_ref)
@@ -132,6 +132,12 @@ def big1():
 
 def test_8b_width_one_layer_elementwise(big1):
     _run(big1, 1, 1023, 0, elementwise=True)
+
+
+def test_8b_width_one_layer_batch16_context_32768_k32(big1):
+    """Long-context rollout shape (batch 16, context 32768, K = 32) at 8B width,
+    one layer, elementwise; the sampler at temperature 0.7."""
+    _run(big1, 16, 32768, 5, elementwise=True, K=32, inv_t=float(np.float32(1 / 0.7)))
 
 
 def test_8b_batch1_context_1k(big):
