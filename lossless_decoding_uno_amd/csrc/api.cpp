@@ -139,6 +139,9 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
 
 int check_layers(const uno_config& c, const uno_weights* w, bool lora) {
   if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->layers) return UNO_ERR_INVALID_ARG;
+  // set when a residual projection's split-K reduction also wrote the RMSNorm
+  // of the updated rows into W.xn (the stand-alone norm is then skipped)
+  bool normed = false;
   for (int li = 0; li < c.n_layers; ++li) {
     const uno_layer_weights& L = w->layers[li];
     if (!L.attn_norm || !L.mlp_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.wgate || !L.wup ||
@@ -190,12 +193,16 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
     return timed(UNO_TIME_LORA_A, s, [&] { return launch_gemm(g, s); });
   };
 
+  // set when a residual projection's split-K reduction also wrote the RMSNorm
+  // of the updated rows into W.xn (the stand-alone norm is then skipped)
+  bool normed = false;
   for (int li = 0; li < c.n_layers; ++li) {
     const uno_layer_weights& L = w->layers[li];
     const bool lq = r && bit(c, P_Q), lo = r && bit(c, P_O), lg = r && bit(c, P_GATE),
                ld = r && bit(c, P_DOWN);
     // ---- attention block
-    UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.attn_norm), R, D, c.rms_eps, W.xn, s));
+    if (!normed)
+      UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.attn_norm), R, D, c.rms_eps, W.xn, s));
     if (lq) {
       const void* a3[3] = {L.lora_a[P_Q], L.lora_a[P_K], L.lora_a[P_V]};
       UNO_TRY(lora_t(W.xn, D, D, a3, 3));
@@ -239,10 +246,12 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 1;
       g.t = lo ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_O));
+      g.norm_gain = static_cast<const float*>(L.mlp_norm); g.norm_out = W.xn; g.norm_eps = c.rms_eps;
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, &normed); }, UNO_TIME_GEMM_O));
     }
     // ---- MLP block
-    UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.mlp_norm), R, D, c.rms_eps, W.xn, s));
+    if (!normed)
+      UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.mlp_norm), R, D, c.rms_eps, W.xn, s));
     if (lg) {
       const void* a2[2] = {L.lora_a[P_GATE], L.lora_a[P_UP]};
       UNO_TRY(lora_t(W.xn, D, D, a2, 2));
@@ -269,11 +278,16 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 1;
       g.t = ld ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_DOWN));
+      const void* next_norm = li + 1 < c.n_layers ? w->layers[li + 1].attn_norm
+                              : logits             ? w->final_norm
+                                                   : nullptr;
+      g.norm_gain = static_cast<const float*>(next_norm); g.norm_out = W.xn; g.norm_eps = c.rms_eps;
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, &normed); }, UNO_TIME_GEMM_DOWN));
     }
   }
   if (logits) {
-    UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(w->final_norm), R, D, c.rms_eps, W.xn, s));
+    if (!normed)
+      UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(w->final_norm), R, D, c.rms_eps, W.xn, s));
     GemmArgs g = scratch_args();
     g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
     g.seg[0] = GemmSeg{bp(w->lm_head), c.vocab, nullptr, 0};

@@ -216,6 +216,65 @@ k_gemm_skinny_reduce(GemmArgs a, int gx, int gy, int splits) {
   if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
 }
 
+// Split-K reduction of a residual-add projection over whole rows, fused with
+// the RMSNorm that follows it: one workgroup per row m sums each column's
+// splits in split order, adds the sum into the residual row (a.out), and
+// writes bf16(h * rsqrt(mean(h^2) + eps) * gain) to a.norm_out.  The per-thread
+// column pattern (4 consecutive columns, 1024 apart) and the reduction order of
+// the sum of squares are those of the stand-alone RMSNorm kernel.
+template <int MT, int NT>
+__global__ void __launch_bounds__(256)
+k_gemm_skinny_reduce_norm(GemmArgs a, int gx, int gy, int splits) {
+  constexpr int kTile = MT * NT * 256;
+  constexpr int kMaxIt = 8;                    // D <= 8192
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int D = a.seg[0].n;
+  float* h = static_cast<float*>(a.out) + (size_t)m * a.ldo;
+  const int by = m / (MT * 16), mt = (m % (MT * 16)) / 16, mr = m % 16;
+  const int ebase = mt * NT * 256 + (mr >> 2) * 64 + (mr & 3);
+  float4 hv[kMaxIt];
+  float ss = 0.f;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int i = threadIdx.x * 4 + it * 1024;
+    if (i >= D) break;
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int n = i + c;
+      const int bx = n / (16 * NT), t = (n >> 4) % NT;
+      const size_t e = ebase + t * 256 + (n & 15) * 4;
+      const size_t wg = (size_t)by * gx + bx;
+      float sum = a.part[wg * kTile + e];
+      for (int z = 1; z < splits; ++z) sum += a.part[((size_t)z * gx * gy + wg) * kTile + e];
+      v[c] = sum;
+    }
+    float4 x = *reinterpret_cast<const float4*>(h + i);
+    x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
+    *reinterpret_cast<float4*>(h + i) = x;
+    hv[it] = x;
+    ss += (x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
+  }
+  ss = wave_sum(ss);
+  if (lane_id() == 0) red[threadIdx.x / UNO_WAVE] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)D + a.norm_eps);
+  uint16_t* o = a.norm_out + (size_t)m * D;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int i = threadIdx.x * 4 + it * 1024;
+    if (i >= D) break;
+    const float4 g = *reinterpret_cast<const float4*>(a.norm_gain + i);
+    const float4 x = hv[it];
+    uint2 pk;
+    pk.x = pack_bf16x2(x.x * inv * g.x, x.y * inv * g.y);
+    pk.y = pack_bf16x2(x.z * inv * g.z, x.w * inv * g.w);
+    *reinterpret_cast<uint2*>(o + i) = pk;
+  }
+}
+
 struct SkinnyPlan {
   int mt, nt, gx, gy, splits;
 };
@@ -246,18 +305,30 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   return p;
 }
 
+// the fused reduce + RMSNorm applies to split residual adds over whole rows
+static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
+  return p.splits > 1 && a.norm_gain && a.norm_out && a.epi == EPI_ADD_F32 && a.n_seg == 1 &&
+         a.seg[0].n == a.ldo && a.ldo % 4 == 0 && a.ldo <= 8192;
+}
+
 template <int MT, int NT>
 static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
   if (p.splits > 1) {
+    if (fuse_norm(a, p)) {
+      hipLaunchKernelGGL((k_gemm_skinny_reduce_norm<MT, NT>), dim3(a.M), dim3(256), 0, s, a,
+                         p.gx, p.gy, p.splits);
+      return;
+    }
     const int n = p.gx * p.gy * MT * NT * 256;
     hipLaunchKernelGGL((k_gemm_skinny_reduce<MT, NT>), dim3((n + 255) / 256), dim3(256), 0, s, a,
                        p.gx, p.gy, p.splits);
   }
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed) {
   const SkinnyPlan p = plan_skinny(a);
+  if (normed) *normed = fuse_norm(a, p);
   switch (p.mt * 8 + p.nt) {
     case 8 + 4: launch_sk<1, 4>(a, p, s); break;
     case 8 + 2: launch_sk<1, 2>(a, p, s); break;
@@ -672,12 +743,13 @@ static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s)
 
 // The tiled kernel for many rows; decode-sized row counts keep the skinny
 // kernel, which streams W once with the rows held in registers.
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed) {
+  if (normed) *normed = false;
   if (a.M >= 128) {
     const BigPlan p = plan_big(a);
     if (p.cfg >= 0) return launch_big(a, p, s);
   }
-  return launch_gemm_skinny(a, s);
+  return launch_gemm_skinny(a, s, normed);
 }
 
 }  // namespace uno

@@ -76,12 +76,18 @@ struct GemmArgs {
   // split-K scratch (workspace) for fp32 partial tiles; null: no split
   float* part;
   size_t part_floats;
+  // optional RMSNorm of the updated rows (EPI_ADD_F32 over whole rows only):
+  // norm_out[m] = bf16(out[m] * rsqrt(mean(out[m]^2) + norm_eps) * norm_gain);
+  // launch_gemm reports through *normed whether it did this
+  const float* norm_gain;
+  uint16_t* norm_out;
+  float norm_eps;
 };
 // split-K scratch carved per pass: 128 MB for passes of 128 rows or more
 // (tiled kernel), 4 MB below (skinny kernel)
 constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr);
 
 // ---------------------------------------------------------------- attention
 // Block attention of a pass over the paged cache.  Query rows of sequence b
