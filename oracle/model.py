@@ -112,8 +112,10 @@ class KVCache:
         return c
 
 
-def attention(q, cache_k, cache_v, key_limit, n_kv_heads):
-    """Per row r and q head h: softmax over keys 0..key_limit[r] of the cache.
+def attention(q, cache_k, cache_v, key_limit, n_kv_heads, key_sets=None):
+    """Per row r and q head h: softmax over keys 0..key_limit[r] of the cache,
+    or over the cache slots listed in key_sets[r] when ``key_sets`` is given
+    (a token tree's rows see the context and their own ancestors only).
 
     q [R, Hq, hd]; cache_k/v [cap, Hkv, hd]; returns [R, Hq, hd].
     """
@@ -121,28 +123,37 @@ def attention(q, cache_k, cache_v, key_limit, n_kv_heads):
     group = Hq // n_kv_heads
     out = np.zeros_like(q)
     scale = 1.0 / np.sqrt(hd)
-    top = int(np.max(key_limit)) + 1
+    if key_sets is None:
+        keys = [np.arange(int(key_limit[r]) + 1) for r in range(R)]
+    else:
+        keys = [np.asarray(sorted(int(k) for k in key_sets[r])) for r in range(R)]
+    top = max(int(k.max()) for k in keys) + 1
     for g in range(n_kv_heads):
         kg = np.ascontiguousarray(cache_k[:top, g, :])     # keys of kv head g
         vg = np.ascontiguousarray(cache_v[:top, g, :])
         for r in range(R):
-            lim = int(key_limit[r]) + 1
+            idx = keys[r]
             for h in range(g * group, (g + 1) * group):
-                s = kg[:lim] @ q[r, h] * scale
+                s = kg[idx] @ q[r, h] * scale
                 s = s - s.max()
                 p = np.exp(s)
                 p = p / p.sum()
-                out[r, h] = p @ vg[:lim]
+                out[r, h] = p @ vg[idx]
     return out
 
 
-def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=None):
+def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=None,
+            slots=None, key_sets=None):
     """One pass over a block of rows of ONE sequence.
 
     Writes the block's K/V (after RoPE) into ``cache`` at ``pos`` before the
     attention of each layer, then attends row r to cache keys 0..key_limit[r].
     Returns fp64 logits [R, V].  ``act_round`` (e.g. ``bf16_round``) selects the
     bf16-activation mode described in the module header.
+
+    A token tree's rows sit at positions (RoPE) that differ from the cache
+    slots holding their K/V: ``slots`` then gives the slots, and ``key_sets``
+    the slots each row attends to (``key_limit`` is then unused).
     """
     rd = act_round if act_round is not None else (lambda v: v)
     ids = np.asarray(ids)
@@ -152,6 +163,7 @@ def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=Non
     eps = cfg["rms_eps"]
     scale = cfg["lora_alpha"] / cfg["lora_rank"]
     R = len(ids)
+    slots = pos if slots is None else np.asarray(slots)
     h = wts["embed"][ids].astype(np.float64)
     for li, lw in enumerate(wts["layers"]):
         def lin(x, p):
@@ -165,9 +177,10 @@ def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=Non
         v = rd(lin(x, "v").reshape(R, Hkv, hd))
         q = rope(q, pos, cfg["rope_theta"])
         k = rd(rope(k, pos, cfg["rope_theta"]))
-        cache.k[li][pos] = k
-        cache.v[li][pos] = v
-        o = rd(attention(q, cache.k[li], cache.v[li], key_limit, Hkv).reshape(R, Hq * hd))
+        cache.k[li][slots] = k
+        cache.v[li][slots] = v
+        o = rd(attention(q, cache.k[li], cache.v[li], key_limit, Hkv, key_sets)
+               .reshape(R, Hq * hd))
         h = h + lin(o, "o")
         x = rd(rms_norm(h, lw["mlp_norm"], eps))
         h = h + lin(rd(silu(lin(x, "gate")) * lin(x, "up")), "down")
