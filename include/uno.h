@@ -30,7 +30,9 @@
  * - Shapes: R = batch * K rows per pass; V = vocab.  All matrices are row-major.
  * - Tokens are int32.  Random draws use Philox4x64-10 with key (seed, 0) and
  *   counter (slot, j, b, step[b]); the uniform is the top 24 bits of word 0.
- *   Slots: 0 draft token j+1; 1 accept test of draft j+1; 2 extra token (j = a).
+ *   Slots: 0 draft token j+1; 1 accept test of draft j+1; 2 extra token (j = a;
+ *   a tree node at depth d draws with j = d + 1); 3 uniform-prior noise of
+ *   draft row j; 4 + i samples of intermediate draft pass i.
  */
 #ifndef UNO_H
 #define UNO_H
@@ -223,6 +225,84 @@ int uno_spec_accept(const float *draft_logits, const float *verify_logits,
  * accept_len outside [0, K] sets UNO_DEV_BAD_ACCEPT and leaves kv_len[b]. */
 int uno_kv_commit(const uno_kv *kv, const int32_t *accept_len, int batch, int K,
                   uint64_t *step, int32_t *status, void *stream);
+
+/* ---------------------------------------------------------------- tree sampler
+ * The per-request variant of the step (picx.dev summary, "Psi-Speculative
+ * Sampler", tree sampler; paperglide reader, "The Psi-Speculative Sampler",
+ * worked example and step list; "Empirical Results", parameters (B, K, V)).
+ * With the block length K here (the pages' B), topk (their K) and n_keep (their
+ * V): one draft pass (uno_draft_block; only its token d_1 of row 0 is used) ->
+ * uno_tree_build -> uno_verify_tree -> uno_tree_accept -> uno_tree_commit.
+ * The pages leave the arithmetic and the multi-candidate accept rule open; the
+ * readings implemented:
+ *  - top-k of a drafted row: the k largest fp32 logits, equal values by id;
+ *  - candidates: d_1 followed by one top-k token of each drafted row 1..K-1;
+ *    score = sum over rows of rint(fp32(z[token] - z[top-1]) * 2^20) (floored
+ *    at -2^40) in exact int64, which ranks like the joint log-probability at
+ *    any temperature; ties by the rank tuples, lexicographically; the best
+ *    n_keep are kept;
+ *  - tree: node 0 = d_1; the kept candidates, best first, add their new
+ *    prefixes as nodes, by depth.  A sequence always has N = uno_tree_rows()
+ *    node rows; rows n >= n_nodes[b] repeat d_1 at depth 0 and are inert;
+ *  - walk (lossless): at node u draw x from the verify row of u (integer
+ *    sampler, Philox slot 2, j = depth(u) + 1); move to the child holding x,
+ *    else stop.  a = nodes walked (d_1 included); the step commits their
+ *    tokens and x.  Every token is an exact AR draw, so the output law is the
+ *    AR model's. */
+
+/* Node rows per sequence, N = 1 + n_keep * (K - 1); 0 if the shape is out of
+ * range (2 <= K <= 32, 1 <= topk <= 8, 1 <= n_keep <= min(64, topk^(K-1))). */
+int uno_tree_rows(int K, int topk, int n_keep);
+
+/* Workspace for uno_tree_build (per-row top-k ids and score terms). */
+size_t uno_tree_workspace_bytes(int batch, int K, int topk);
+
+/* Tree of one step per sequence from the draft pass's outputs.
+ *   draft_logits [dev] fp32 [batch, K, V]; draft_tokens [dev] int32 [batch, K]
+ *   (only column 0, d_1, is read)
+ *   node_tokens, node_parent, node_depth [dev] int32 [batch, N]
+ *   node_anc  [dev] uint32 [batch, N, (N+31)/32]: bit m of row n set iff node m
+ *             is n or an ancestor of n
+ *   n_nodes   [dev] int32 [batch]
+ * A non-finite drafted row sets UNO_DEV_NONFINITE and gives token -1 (the
+ * verify pass then flags UNO_DEV_BAD_TOKEN). */
+int uno_tree_build(const float *draft_logits, const int32_t *draft_tokens, int batch, int K,
+                   int vocab, int topk, int n_keep, int32_t *node_tokens,
+                   int32_t *node_parent, int32_t *node_depth, uint32_t *node_anc,
+                   int32_t *n_nodes, int32_t *status, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* Tree-masked verify pass (AR weights) over the node rows, n_rows = N.  Node n
+ * sits at position kv_len[b] + 1 + depth(n); its K/V go to slot
+ * kv_len[b] + 1 + n; it attends to slots <= kv_len[b] (context and anchor) and
+ * to the slots of its ancestors and itself.  verify_logits [dev] fp32
+ * [batch, N, V] (rows past n_nodes are inert).  ws: uno_workspace_bytes(cfg,
+ * batch, N, max_ctx); the page table must cover kv_len + 1 + N slots. */
+int uno_verify_tree(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
+                    const int32_t *node_tokens, const int32_t *node_depth,
+                    const uint32_t *node_anc, int batch, int n_rows, int max_ctx,
+                    float *verify_logits, int32_t *status, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Accept walk.  node_sample [dev] int32 [batch, N]: the draw of every node
+ * (-1 past n_nodes); accept_len [dev] int32 [batch] (a >= 1); committed [dev]
+ * int32 [batch, K+1] (the a walked tokens, then x, then -1); extra_token [dev]
+ * int32 [batch] (x, the next anchor); path [dev] int32 [batch, K] (node at
+ * each depth, then -1).  A non-finite verify row sets UNO_DEV_NONFINITE, a = 0
+ * and committed = -1. */
+int uno_tree_accept(const float *verify_logits, const int32_t *node_tokens,
+                    const int32_t *node_parent, const int32_t *node_depth,
+                    const int32_t *n_nodes, int batch, int K, int n_rows, int vocab,
+                    float inv_temp, uint64_t seed, const uint64_t *step,
+                    int32_t *node_sample, int32_t *accept_len, int32_t *committed,
+                    int32_t *extra_token, int32_t *path, int32_t *status, void *stream);
+
+/* Commit of a tree step: the K/V of path[b, d] (every layer) move from slot
+ * kv_len + 1 + path[b, d] to kv_len + 1 + d for d = 1..a-1, then kv_len[b] +=
+ * 1 + a and step[b] += 1 (as uno_kv_commit). */
+int uno_tree_commit(const uno_config *cfg, const uno_kv *kv, const int32_t *path,
+                    const int32_t *accept_len, int batch, int K, uint64_t *step,
+                    int32_t *status, void *stream);
 
 /* Measurement hook (not part of the decode path; for benchmarks and
  * profilers).  While set, every launch of one kernel class made by the entry

@@ -26,6 +26,8 @@ DEV_CAPACITY, DEV_BAD_TOKEN, DEV_BAD_PAGE, DEV_NONFINITE, DEV_BAD_ACCEPT = 1, 2,
 EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_draft_block_from", "uno_verify_block",
            "uno_draft_sample",
            "uno_spec_accept_workspace_bytes", "uno_spec_accept", "uno_kv_commit",
+           "uno_tree_rows", "uno_tree_workspace_bytes", "uno_tree_build", "uno_verify_tree",
+           "uno_tree_accept", "uno_tree_commit",
            "uno_set_timing_events", "uno_timing_events_used", "uno_status_string",
            "uno_last_hip_error")
 
@@ -91,6 +93,18 @@ def load_library():
     lib.uno_spec_accept.argtypes = [P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P, SZ, P]
     lib.uno_kv_commit.restype = I
     lib.uno_kv_commit.argtypes = [P, P, I, I, P, P, P]
+    lib.uno_tree_rows.restype = I
+    lib.uno_tree_rows.argtypes = [I, I, I]
+    lib.uno_tree_workspace_bytes.restype = SZ
+    lib.uno_tree_workspace_bytes.argtypes = [I, I, I]
+    lib.uno_tree_build.restype = I
+    lib.uno_tree_build.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P, SZ, P]
+    lib.uno_verify_tree.restype = I
+    lib.uno_verify_tree.argtypes = [P, P, P, P, P, P, I, I, I, P, P, P, SZ, P]
+    lib.uno_tree_accept.restype = I
+    lib.uno_tree_accept.argtypes = [P, P, P, P, P, I, I, I, I, F, U64, P, P, P, P, P, P, P, P]
+    lib.uno_tree_commit.restype = I
+    lib.uno_tree_commit.argtypes = [P, P, P, P, I, I, P, P, P]
     lib.uno_status_string.restype = ctypes.c_char_p
     lib.uno_status_string.argtypes = [I]
     lib.uno_last_hip_error.restype = ctypes.c_char_p
@@ -333,6 +347,86 @@ def kv_commit(kv, accept_len, K, step=None, status=None):
         _need(step, torch.uint64, (B,), "step")
     _check(lib.uno_kv_commit(ctypes.byref(kv.struct), _ptr(accept_len), B, K, _ptr(step),
                              _ptr(status), _stream()))
+
+
+# ---------------------------------------------------------------- tree sampler
+def tree_rows(K, topk, n_keep):
+    """Node rows per sequence (1 + n_keep * (K - 1)); 0 for an unsupported shape."""
+    return int(load_library().uno_tree_rows(K, topk, n_keep))
+
+
+class TreeBuffers:
+    """Device buffers of one tree step for B sequences (block length K)."""
+
+    def __init__(self, B, K, topk, n_keep, vocab, device="cuda"):
+        N = tree_rows(K, topk, n_keep)
+        if not N:
+            raise ValueError("unsupported tree shape K=%d topk=%d n_keep=%d" % (K, topk, n_keep))
+        self.B, self.K, self.topk, self.n_keep, self.N = B, K, topk, n_keep, N
+        W = (N + 31) // 32
+        i32 = dict(dtype=torch.int32, device=device)
+        self.tokens = torch.empty((B, N), **i32)
+        self.parent = torch.empty((B, N), **i32)
+        self.depth = torch.empty((B, N), **i32)
+        self.anc = torch.empty((B, N, W), dtype=torch.uint32, device=device)
+        self.n_nodes = torch.empty(B, **i32)
+        self.sample = torch.empty((B, N), **i32)
+        self.path = torch.empty((B, K), **i32)
+        self.ws = alloc_workspace(load_library().uno_tree_workspace_bytes(B, K, topk), device)
+
+
+def tree_build(draft_logits, draft_tokens, tb, status=None):
+    """uno_tree_build: the best tb.n_keep candidates of the drafted rows and
+    their prefix tree, into tb."""
+    lib = load_library()
+    B, K, V = draft_logits.shape
+    _need(draft_logits, torch.float32, (tb.B, tb.K, V), "draft_logits")
+    _need(draft_tokens, torch.int32, (B, K), "draft_tokens")
+    _check(lib.uno_tree_build(_ptr(draft_logits), _ptr(draft_tokens), B, K, V, tb.topk,
+                              tb.n_keep, _ptr(tb.tokens), _ptr(tb.parent), _ptr(tb.depth),
+                              _ptr(tb.anc), _ptr(tb.n_nodes), _ptr(status), _ptr(tb.ws),
+                              tb.ws.numel(), _stream()))
+
+
+def verify_tree(model, kv, tb, max_ctx, verify_logits, ws, status=None):
+    """uno_verify_tree: verify_logits [B, N, V] fp32 over the node rows of tb."""
+    lib = load_library()
+    if verify_logits is not None:
+        _need(verify_logits, torch.float32, (tb.B, tb.N, model.cfg["vocab"]), "verify_logits")
+    _check(lib.uno_verify_tree(ctypes.byref(model.config), ctypes.byref(model.weights),
+                               ctypes.byref(kv.struct), _ptr(tb.tokens), _ptr(tb.depth),
+                               _ptr(tb.anc), tb.B, tb.N, max_ctx, _ptr(verify_logits),
+                               _ptr(status), _ptr(ws), ws.numel(), _stream()))
+
+
+def tree_accept(verify_logits, tb, inv_temp, seed, step, accept_len, committed, extra_token,
+                status=None):
+    """uno_tree_accept: per-node draws (tb.sample), the walk, a / committed /
+    extra token, and the walked path (tb.path)."""
+    lib = load_library()
+    B, N, V = verify_logits.shape
+    _need(verify_logits, torch.float32, (tb.B, tb.N, V), "verify_logits")
+    _need(step, torch.uint64, (B,), "step")
+    _need(accept_len, torch.int32, (B,), "accept_len")
+    _need(committed, torch.int32, (B, tb.K + 1), "committed")
+    _need(extra_token, torch.int32, (B,), "extra_token")
+    _check(lib.uno_tree_accept(_ptr(verify_logits), _ptr(tb.tokens), _ptr(tb.parent),
+                               _ptr(tb.depth), _ptr(tb.n_nodes), B, tb.K, N, V, float(inv_temp),
+                               int(seed), _ptr(step), _ptr(tb.sample), _ptr(accept_len),
+                               _ptr(committed), _ptr(extra_token), _ptr(tb.path), _ptr(status),
+                               _stream()))
+
+
+def tree_commit(model, kv, tb, accept_len, step=None, status=None):
+    """uno_tree_commit: move the walked path's K/V into place, then advance
+    kv_len (and step)."""
+    lib = load_library()
+    _need(accept_len, torch.int32, (tb.B,), "accept_len")
+    if step is not None:
+        _need(step, torch.uint64, (tb.B,), "step")
+    _check(lib.uno_tree_commit(ctypes.byref(model.config), ctypes.byref(kv.struct),
+                               _ptr(tb.path), _ptr(accept_len), tb.B, tb.K, _ptr(step),
+                               _ptr(status), _stream()))
 
 
 class KernelTimer:

@@ -3,8 +3,9 @@
     python -m lossless_decoding_uno_amd.build      # or build() from Python
 
 Every source is compiled for gfx950 only, with packed fp32 arithmetic switched
-off; the sampler file is additionally compiled without floating-point
-contraction (its integer weights come from separately rounded fp32 ops).
+off; the sampler and tree files are additionally compiled without
+floating-point contraction (their integer weights and scores come from
+separately rounded fp32 ops).
 """
 import concurrent.futures as cf
 import os
@@ -18,11 +19,11 @@ OUT = os.path.join(HERE, "libuno.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "sampler.hip", "elementwise.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["api.cpp", "sampler.hip", "elementwise.hip", "gemm.hip", "attention.hip", "tree.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC]
-PER_FILE = {"sampler.hip": ["-ffp-contract=off"]}
+PER_FILE = {"sampler.hip": ["-ffp-contract=off"], "tree.hip": ["-ffp-contract=off"]}
 
 
 def _compile(src):

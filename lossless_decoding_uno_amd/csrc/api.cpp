@@ -157,11 +157,14 @@ int check_layers(const uno_config& c, const uno_weights* w, bool lora) {
 const bf16_raw_t* bp(const void* p) { return static_cast<const bf16_raw_t*>(p); }
 
 // One forward pass of B*K rows (draft when `anchor` != null, verify otherwise).
+// A token tree's verify pass passes tree_depth [B*K] (RoPE positions) and
+// tree_anc [B*K, (K+31)/32] (attention mask); both null otherwise.
 int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const int32_t* anchor,
              const int32_t* block, const int32_t* rows, int B, int K, int max_ctx, int pos_offset,
              bool lora,
              uint64_t seed, const uint64_t* step, float* logits, int32_t* status, void* ws,
-             hipStream_t s) {
+             hipStream_t s, const int32_t* tree_depth = nullptr,
+             const uint32_t* tree_anc = nullptr) {
   const PassWs W = carve(c, B, K, max_ctx, ws);
   const int R = B * K;
   const int D = c.d_model, F = c.d_ffn, hd = c.head_dim;
@@ -174,7 +177,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
 
   UNO_TRY(launch_embed(c, bp(w->embed), anchor, block, rows, B, K, seed, step, W.h, status, s));
   UNO_TRY(launch_rope_table(kv->kv_len, B, K, draft ? 0 : pos_offset, hd / 2, c.rope_theta,
-                            W.cs, s));
+                            tree_depth, W.cs, s));
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
   const size_t layer_elems = (size_t)kv->n_pages * Hkv * c.page_size * hd;
 
@@ -229,6 +232,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       a.page_table = kv->page_table; a.kv_len = kv->kv_len;
       a.max_pages = kv->max_pages_per_seq; a.n_pages = kv->n_pages;
       a.B = B; a.K = K; a.pos_offset = draft ? 0 : pos_offset; a.draft = draft ? 1 : 0;
+      a.tree_anc = tree_anc; a.anc_words = (K + 31) / 32;
       a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.ps = c.page_size; a.plan = plan;
       a.ps_shift = __builtin_ctz((unsigned)c.page_size);
       a.part_o = W.part_o; a.part_ml = W.part_ml; a.out = W.ao; a.status = status;
@@ -401,6 +405,96 @@ int uno_kv_commit(const uno_kv* kv, const int32_t* accept_len, int batch, int K,
   if (batch < 1 || K < 0) return UNO_ERR_INVALID_ARG;
   const hipError_t e = launch_kv_commit(kv->kv_len, accept_len, batch, K, step, status,
                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+// ---------------------------------------------------------------- tree sampler
+int uno_tree_rows(int K, int topk, int n_keep) {
+  if (K < 2 || K > 32 || topk < 1 || topk > 8 || n_keep < 1 || n_keep > 64) return 0;
+  // n_keep <= topk^(K-1)
+  long long cands = 1;
+  for (int i = 0; i < K - 1 && cands < n_keep; ++i) cands *= topk;
+  if (cands < n_keep) return 0;
+  return 1 + n_keep * (K - 1);
+}
+
+size_t uno_tree_workspace_bytes(int batch, int K, int topk) {
+  if (batch < 1 || K < 2 || K > 32 || topk < 1 || topk > 8) return 0;
+  return tree_ws_bytes(batch, K, topk);
+}
+
+int uno_tree_build(const float* draft_logits, const int32_t* draft_tokens, int batch, int K,
+                   int vocab, int topk, int n_keep, int32_t* node_tokens, int32_t* node_parent,
+                   int32_t* node_depth, uint32_t* node_anc, int32_t* n_nodes, int32_t* status,
+                   void* ws, size_t ws_bytes, void* stream) {
+  const int N = uno_tree_rows(K, topk, n_keep);
+  if (!N || batch < 1 || vocab < 16 || vocab > (1 << 20)) return UNO_ERR_INVALID_ARG;
+  if (!draft_logits || !draft_tokens || !node_tokens || !node_parent || !node_depth ||
+      !node_anc || !n_nodes || !ws)
+    return UNO_ERR_INVALID_ARG;
+  if (ws_bytes < tree_ws_bytes(batch, K, topk)) return UNO_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
+    return launch_tree_build(draft_logits, draft_tokens, batch, K, vocab, topk, n_keep, N,
+                             node_tokens, node_parent, node_depth, node_anc, n_nodes, status, ws,
+                             s);
+  });
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+int uno_verify_tree(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
+                    const int32_t* node_tokens, const int32_t* node_depth,
+                    const uint32_t* node_anc, int batch, int n_rows, int max_ctx,
+                    float* verify_logits, int32_t* status, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || n_rows < 2 || n_rows > 4096 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
+  if (!node_tokens || !node_depth || !node_anc || !ws) return UNO_ERR_INVALID_ARG;
+  if ((rc = check_kv(*cfg, kv, n_rows, 1))) return rc;
+  if ((rc = check_layers(*cfg, w, false))) return rc;
+  if (ws_bytes < carve(*cfg, batch, n_rows, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
+  return run_pass(*cfg, w, kv, nullptr, nullptr, node_tokens, batch, n_rows, max_ctx, 1, false, 0,
+                  nullptr, verify_logits, status, ws, static_cast<hipStream_t>(stream),
+                  node_depth, node_anc);
+}
+
+int uno_tree_accept(const float* verify_logits, const int32_t* node_tokens,
+                    const int32_t* node_parent, const int32_t* node_depth,
+                    const int32_t* n_nodes, int batch, int K, int n_rows, int vocab,
+                    float inv_temp, uint64_t seed, const uint64_t* step, int32_t* node_sample,
+                    int32_t* accept_len, int32_t* committed, int32_t* extra_token,
+                    int32_t* path, int32_t* status, void* stream) {
+  if (!verify_logits || !node_tokens || !node_parent || !node_depth || !n_nodes || !step ||
+      !node_sample || !accept_len || !committed || !extra_token || !path)
+    return UNO_ERR_INVALID_ARG;
+  if (batch < 1 || K < 2 || K > 32 || n_rows < K || n_rows > 4096 || vocab < 16 ||
+      vocab > (1 << 20))
+    return UNO_ERR_INVALID_ARG;
+  if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
+    hipError_t r = launch_tree_sample(verify_logits, batch, n_rows, vocab, inv_temp, seed, step,
+                                      node_depth, n_nodes, node_sample, status, s);
+    if (r != hipSuccess) return r;
+    return launch_tree_walk(node_tokens, node_parent, n_nodes, node_sample, batch, K, n_rows,
+                            accept_len, committed, extra_token, path, status, s);
+  });
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
+int uno_tree_commit(const uno_config* cfg, const uno_kv* kv, const int32_t* path,
+                    const int32_t* accept_len, int batch, int K, uint64_t* step, int32_t* status,
+                    void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!kv || !kv->kv_len || !kv->k_pages || !kv->v_pages || !kv->page_table || !path ||
+      !accept_len)
+    return UNO_ERR_INVALID_ARG;
+  if (batch < 1 || K < 2 || K > 32) return UNO_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_tree_commit(*cfg, *kv, path, accept_len, batch, K, status, s);
+  if (e == hipSuccess) e = launch_kv_commit(kv->kv_len, accept_len, batch, K, step, status, s);
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 

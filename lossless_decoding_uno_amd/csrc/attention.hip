@@ -8,6 +8,9 @@
 // Masks (per query row j of a sequence whose cache holds kv_len positions):
 //   draft : j == 0 sees keys <= kv_len; j >= 1 sees keys <= kv_len + K - 1
 //   verify: row j sees keys <= kv_len + pos_offset + j (causal)
+//   tree  : verify rows are the nodes of a token tree (node j at slot
+//           kv_len + 1 + j); row j sees keys <= kv_len and the slots of its
+//           ancestors and itself (a bit row per node)
 //
 // Kernel shape.  A workgroup of 4 waves owns up to 64 query rows of one
 // (sequence, kv head) -- GQA heads times block rows, wave w the rows
@@ -129,6 +132,8 @@ k_attention(AttnArgs a) {
   const bool q_ok = qr < QR;
   const int qj = q_ok ? qr / G : 0, qh = q_ok ? qr % G : 0;
   const int lim = q_ok ? row_limit(qj, kvl, a.K, a.pos_offset, a.draft) : -1;
+  // token tree: keys past the context also need this row's ancestor bit
+  const uint32_t* anc_row = a.tree_anc ? a.tree_anc + ((size_t)b * a.K + qj) * a.anc_words : nullptr;
   AFrag qf[DS], qfl[DS];    // q = high + low bf16 parts (scores keep ~16 bits of q)
   {
     const size_t qo = ((size_t)(b * a.K + qj) * a.Hq + g * G + qh) * HD + lg * 8;
@@ -202,7 +207,7 @@ k_attention(AttnArgs a) {
 
   float m_run = -INFINITY, l_run = 0.f;
   // smallest row limit of the workgroup: chunks below it need no masking
-  const int lim_min = a.draft ? kvl : kvl + a.pos_offset + min(a.K - 1, qbase / G);
+  const int lim_min = (a.draft || a.tree_anc) ? kvl : kvl + a.pos_offset + min(a.K - 1, qbase / G);
   f32x4 o[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -273,7 +278,12 @@ k_attention(AttnArgs a) {
           p[hh][cc] = v;
         } else {
           const int key = k0 + 32 * (kh * NH + hh) + 8 * lg + cc;
-          p[hh][cc] = (key <= lim && key < hi) ? v : -INFINITY;
+          bool vis = key <= lim && key < hi;
+          if (vis && anc_row && key > kvl) {
+            const int node = key - kvl - 1;        // < K: key <= lim = kvl + 1 + qj
+            vis = (anc_row[node >> 5] >> (node & 31)) & 1u;
+          }
+          p[hh][cc] = vis ? v : -INFINITY;
         }
         rmax = fmaxf(rmax, p[hh][cc]);
       }

@@ -106,12 +106,14 @@ hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float
 
 // ------------------------------------------------------------ rotary table
 // cs[r, i] = (cos, sin)(pos_r * theta^(-2i/hd)), angle in fp64 so that large
-// positions keep full fp32 accuracy.
+// positions keep full fp32 accuracy.  pos_r = kv_len + pos_offset + j, or
+// + depth[r] for a token tree's rows (their slot stays kv_len + pos_offset + j).
 __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_offset, int half,
-                             double log_theta, float2* __restrict__ cs) {
+                             double log_theta, const int32_t* __restrict__ depth,
+                             float2* __restrict__ cs) {
   const int r = blockIdx.x;
   const int b = r / K, j = r % K;
-  const double pos = (double)(kv_len[b] + pos_offset + j);
+  const double pos = (double)(kv_len[b] + pos_offset + (depth ? depth[r] : j));
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     const double inv_freq = exp(-log_theta * (2.0 * i) / (2.0 * half));
     double sn, cn;
@@ -121,9 +123,9 @@ __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_
 }
 
 hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
-                             float theta, float2* cs, hipStream_t s) {
+                             float theta, const int32_t* depth, float2* cs, hipStream_t s) {
   hipLaunchKernelGGL(k_rope_table, dim3(B * K), dim3(64), 0, s, kv_len, K, pos_offset, half,
-                     log((double)theta), cs);
+                     log((double)theta), depth, cs);
   return hipGetLastError();
 }
 

@@ -241,15 +241,22 @@ __device__ __forceinline__ void flag(int32_t* status, int b, int32_t f) {
 // ------------------------------------------------------------ kernels
 // One workgroup per draft row (b, j): d = categorical(W(row), U(slot, j, b, step[b]));
 // slot 0 for the drafts that go to verification, 4 + i for the samples of an
-// intermediate draft pass i.
+// intermediate draft pass i.  Token-tree rows (row_j != null) draw with
+// j = row_j[row] + j_add, and rows at or past n_valid[b] are skipped (-1).
 __global__ void __launch_bounds__(kThreads)
 k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, uint64_t seed,
                int slot, const uint64_t* __restrict__ step, int32_t* __restrict__ tokens,
-               int32_t* __restrict__ status) {
+               int32_t* __restrict__ status, const int32_t* __restrict__ row_j, int j_add,
+               const int32_t* __restrict__ n_valid) {
   extern __shared__ u128 tiles[];
   __shared__ RowShared sh;
   const int row_id = blockIdx.x;
-  const int b = row_id / K, j = row_id % K;
+  const int b = row_id / K;
+  if (n_valid && row_id % K >= n_valid[b]) {
+    if (threadIdx.x == 0) tokens[row_id] = -1;
+    return;
+  }
+  const int j = row_j ? row_j[row_id] + j_add : row_id % K;
   Row row{logits + (size_t)row_id * V, V, (V & 3) == 0};
   bool bad = false;
   const float m = block_row_max(row, sh, &bad);
@@ -401,7 +408,16 @@ hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float i
                                uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
                                int32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(k_draft_sample, dim3(B * K), dim3(kThreads), tile_lds_bytes(V), s, logits,
-                     K, V, inv_temp, seed, slot, step, tokens, status);
+                     K, V, inv_temp, seed, slot, step, tokens, status, nullptr, 0, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float inv_temp,
+                              uint64_t seed, const uint64_t* step, const int32_t* node_depth,
+                              const int32_t* n_nodes, int32_t* samples, int32_t* status,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_draft_sample, dim3(B * N), dim3(kThreads), tile_lds_bytes(V), s, logits,
+                     N, V, inv_temp, seed, 2, step, samples, status, node_depth, 1, n_nodes);
   return hipGetLastError();
 }
 

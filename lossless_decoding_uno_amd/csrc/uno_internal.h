@@ -17,6 +17,13 @@ static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; 
 hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
                                uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
                                int32_t* status, hipStream_t s);
+// Per-node draws of a token tree's verify rows [B, N]: row (b, n) draws from
+// its own logits with Philox slot 2, j = node_depth + 1; rows n >= n_nodes[b]
+// get -1.
+hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float inv_temp,
+                              uint64_t seed, const uint64_t* step, const int32_t* node_depth,
+                              const int32_t* n_nodes, int32_t* samples, int32_t* status,
+                              hipStream_t s);
 size_t spec_accept_ws_bytes(int B, int K);
 hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* drafts, int B,
                               int K, int V, float inv_temp, uint64_t seed, const uint64_t* step,
@@ -36,9 +43,10 @@ hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int3
 hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
                           bf16_raw_t* out, hipStream_t s);
 // cos/sin table [R, head_dim/2] (fp32, angles evaluated in fp64) for the rows'
-// absolute positions kv_len[b] + pos_offset + j.
+// absolute positions kv_len[b] + pos_offset + j, or kv_len[b] + pos_offset +
+// depth[r] for the rows of a token tree (depth != null).
 hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
-                             float theta, float2* cs, hipStream_t s);
+                             float theta, const int32_t* depth, float2* cs, hipStream_t s);
 // RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]); q, scaled
 // by log2(e)/sqrt(hd), -> two bf16 planes [R, Hq*hd] (hi and the rounding
 // remainder lo), k/v (bf16) -> paged cache at the rows' positions.
@@ -50,6 +58,28 @@ hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const flo
 hipError_t launch_silu_mul(const float* gu, int R, int F, bf16_raw_t* act, hipStream_t s);
 hipError_t launch_kv_commit(int32_t* kv_len, const int32_t* accept_len, int B, int K,
                             uint64_t* step, int32_t* status, hipStream_t s);
+
+// ---------------------------------------------------------------- tree sampler
+// Workspace of launch_tree_build (top-k tokens and integer score deltas).
+size_t tree_ws_bytes(int B, int K, int topk);
+// Top-k of the drafted rows 1..K-1 of zq [B, K, V], the best n_keep
+// candidates and their prefix tree: node_tokens/parent/depth [B, N],
+// node_anc [B, N, (N+31)/32] (ancestor-or-self bits), n_nodes [B].
+hipError_t launch_tree_build(const float* zq, const int32_t* draft_tokens, int B, int K, int V,
+                             int topk, int n_keep, int N, int32_t* node_tokens,
+                             int32_t* node_parent, int32_t* node_depth, uint32_t* node_anc,
+                             int32_t* n_nodes, int32_t* status, void* ws, hipStream_t s);
+// Walk of the per-node draws: accept_len [B], committed [B, K+1] (-1 padded),
+// extra_token [B], path [B, K] (node at each depth, -1 padded).
+hipError_t launch_tree_walk(const int32_t* node_tokens, const int32_t* node_parent,
+                            const int32_t* n_nodes, const int32_t* samples, int B, int K, int N,
+                            int32_t* accept_len, int32_t* committed, int32_t* extra_token,
+                            int32_t* path, int32_t* status, hipStream_t s);
+// Moves the walked nodes' K/V (every layer) to slots kv_len+1 .. kv_len+a-1;
+// kv_len itself is advanced by launch_kv_commit afterwards.
+hipError_t launch_tree_commit(const uno_config& c, const uno_kv& kv, const int32_t* path,
+                              const int32_t* accept_len, int B, int K, int32_t* status,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM
 // Y[m, n] = sum_k X[m, k] W[n, k]  (+ LoRA)  for up to 3 column segments.
@@ -115,6 +145,10 @@ struct AttnArgs {
   int max_pages;
   int64_t n_pages;
   int B, K, pos_offset, draft;
+  // token tree (verify): row j also needs bit (key - kv_len - 1) of its
+  // ancestor-or-self row tree_anc[(b*K + j)*anc_words ..] for keys past kv_len
+  const uint32_t* tree_anc;
+  int anc_words;
   int Hq, Hkv, hd, ps, ps_shift;   // page size and its log2
   AttnPlan plan;
   float* part_o;              // [B*Hkv, n_qgroups, n_wave_splits, 64, hd]

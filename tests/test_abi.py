@@ -74,3 +74,40 @@ def test_entry_points_reject_bad_arguments_on_the_host():
     assert lib.uno_verify_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
                                 64, 1, fake, None, fake, 1 << 30, None) == 1
     assert lib.uno_kv_commit(None, fake, 1, 4, None, None, None) == 1
+
+
+def test_tree_entry_points_shape_rules_and_host_validation():
+    import lossless_decoding_uno_amd as U
+    lib = U.load_library()
+    # N = 1 + n_keep (K - 1); n_keep <= min(64, topk^(K-1)); 2 <= K <= 32; topk <= 8
+    assert lib.uno_tree_rows(16, 2, 8) == 1 + 8 * 15
+    assert lib.uno_tree_rows(3, 2, 4) == 9
+    assert lib.uno_tree_rows(3, 2, 5) == 0          # only 4 candidates
+    assert lib.uno_tree_rows(2, 1, 1) == 2
+    assert lib.uno_tree_rows(1, 2, 1) == 0
+    assert lib.uno_tree_rows(33, 2, 1) == 0
+    assert lib.uno_tree_rows(16, 9, 1) == 0
+    assert lib.uno_tree_rows(16, 2, 65) == 0
+    assert lib.uno_tree_rows(32, 8, 64) == 1 + 64 * 31
+    assert lib.uno_tree_workspace_bytes(4, 16, 4) >= 4 * 15 * 4 * 12
+    assert lib.uno_tree_workspace_bytes(4, 1, 4) == 0
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    cfg = U.make_config(synth.TINY)
+    w, kv = U.UnoWeights(), U.UnoKV()
+    # unsupported tree shape
+    assert lib.uno_tree_build(fake, fake, 1, 3, 512, 2, 5, fake, fake, fake, fake, fake, None,
+                              fake, 1 << 20, None) == 1
+    # workspace too small
+    assert lib.uno_tree_build(fake, fake, 1, 3, 512, 2, 4, fake, fake, fake, fake, fake, None,
+                              fake, 8, None) == 4
+    # null node arrays, empty kv struct
+    assert lib.uno_verify_tree(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), None, fake,
+                               fake, 1, 9, 64, fake, None, fake, 1 << 30, None) == 1
+    assert lib.uno_verify_tree(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, fake,
+                               fake, 1, 9, 64, fake, None, fake, 1 << 30, None) == 1
+    # bad temperature, rows fewer than the block
+    assert lib.uno_tree_accept(fake, fake, fake, fake, fake, 1, 3, 9, 512, 0.0, 0, fake, fake,
+                               fake, fake, fake, fake, None, None) == 1
+    assert lib.uno_tree_accept(fake, fake, fake, fake, fake, 1, 16, 9, 512, 1.0, 0, fake, fake,
+                               fake, fake, fake, fake, None, None) == 1
+    assert lib.uno_tree_commit(ctypes.byref(cfg), None, fake, fake, 1, 3, None, None, None) == 1
