@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--prior", type=int, default=0, help="draft noise prior: 0 mask, 1 uniform")
     ap.add_argument("--passes", type=int, default=1, help="draft passes per step (generate mode)")
+    ap.add_argument("--tree", type=str, default="", metavar="TOPK,NKEEP",
+                    help="tree-sampler mode: steps of draft -> tree build (top-TOPK per drafted "
+                         "position, best NKEEP candidates) -> tree verify -> walk -> commit, "
+                         "natural acceptance (prints its own JSON line)")
     return ap.parse_args()
 
 
@@ -355,6 +359,100 @@ def generate_mode(args, U, synth, torch, cfg):
     print(json.dumps(out), flush=True)
 
 
+class TreeWorkload:
+    """Device state of a tree-sampler workload (batch, context, block K, topk, n_keep)."""
+
+    def __init__(self, U, torch, synth, model, cfg, B, ctx, K, topk, n_keep, n_steps, seed,
+                 temp=1.0):
+        self.U, self.torch, self.cfg, self.model = U, torch, cfg, model
+        self.inv_t = float(np.float32(1.0 / temp))
+        self.B, self.ctx, self.K = B, ctx, K
+        V = cfg["vocab"]
+        dev = "cuda"
+        self.tb = U.TreeBuffers(B, K, topk, n_keep, V)
+        N = self.tb.N
+        self.capacity = ctx + n_steps * (K + 1) + N + 2
+        perm = torch.randperm(B * ((self.capacity + 15) // 16),
+                              generator=torch.Generator().manual_seed(seed))
+        self.kv = U.PagedKV(cfg, B, self.capacity, page_order=perm)
+        synth.fill_kv_device(self.kv.k_pages, self.kv.v_pages, seed)
+        self.kv.kv_len.fill_(ctx)
+        self.max_ctx = self.capacity
+        self.ws = U.alloc_workspace(max(U.workspace_bytes(model, B, K, self.max_ctx),
+                                        U.workspace_bytes(model, B, N, self.max_ctx)))
+        self.zq = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+        self.zp = torch.empty((B, N, V), dtype=torch.float32, device=dev)
+        self.d = torch.empty((B, K), dtype=torch.int32, device=dev)
+        self.a = torch.empty(B, dtype=torch.int32, device=dev)
+        self.c = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        self.e = torch.from_numpy(synth.prompt_ids(cfg, B, seed)).to(dev)
+        self.step_ctr = torch.zeros(B, dtype=torch.uint64).to(dev)
+
+    def step(self, i):
+        U = self.U
+        U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, self.inv_t, 0,
+                      self.step_ctr, self.zq, self.d, self.ws)
+        U.tree_build(self.zq, self.d, self.tb)
+        U.verify_tree(self.model, self.kv, self.tb, self.max_ctx, self.zp, self.ws)
+        U.tree_accept(self.zp, self.tb, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e)
+        U.tree_commit(self.model, self.kv, self.tb, self.a, self.step_ctr)
+
+
+def tree_mode(args, U, synth, torch, cfg):
+    """Steps of the tree sampler with natural acceptance; tokens per step are
+    read from the growth of kv_len after the timed region (1 + a per
+    sequence and step)."""
+    topk, n_keep = (int(x) for x in args.tree.split(","))
+    K = args.K
+    log("generating weights on the GPU")
+    model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))
+    W = TreeWorkload(U, torch, synth, model, cfg, args.batch, args.ctx, K, topk, n_keep,
+                     args.warmup + args.steps + 1, seed=1, temp=args.temp)
+    log("tree rows per sequence: %d; probe step" % W.tb.N)
+    W.step(0)
+    torch.cuda.synchronize()
+    classes = probe_classes(U, W, 0, torch)
+    log("class ms per step: %s" % json.dumps({k: round(v, 3) for k, v in classes.items()}))
+    for i in range(args.warmup):
+        W.step(i)
+    torch.cuda.synchronize()
+    kv0 = W.kv.kv_len.cpu().numpy().astype(np.int64)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        W.step(args.warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    tokens = int(np.sum(W.kv.kv_len.cpu().numpy().astype(np.int64) - kv0))
+    # projection GEMMs of both passes against HBM: every weight read once per pass
+    L = cfg["n_layers"]
+    gemm_ms = sum(classes[k] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"))
+    wbytes = 0.0
+    for name in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"):
+        wbytes += L * (gemm_launch_work(cfg, name, args.batch * K, True)[1] +
+                       gemm_launch_work(cfg, name, args.batch * W.tb.N, False)[1])
+    out = {"metric": "accepted tokens/s/GPU (Qwen3-8B shape, Psi-Spec tree sampler step, "
+                     "natural acceptance)",
+           "value": round(tokens / (ms / 1e3), 1), "unit": "accepted tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 3),
+           "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic (seeded random-init weights and KV; natural acceptance of a "
+                   "random model, so acceptance is near its floor)",
+           "config": {"workload": "qwen3-8b-shape b%d ctx%d K%d tree topk%d keep%d T%g natural"
+                      % (args.batch, args.ctx, K, topk, n_keep, args.temp),
+                      "tree_rows": W.tb.N},
+           "AL": round(tokens / (args.steps * args.batch), 3),
+           "roofline_gemm": {"bound": "hbm", "achieved": round(wbytes / (gemm_ms / 1e3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(wbytes / (gemm_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "kernel": "k_gemm: projections of the draft and tree-verify passes",
+                             "ms_per_step": round(gemm_ms, 3)},
+           "kernel_class_ms_per_step": {k: round(v, 3) for k, v in classes.items()}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -380,6 +478,8 @@ def main():
     cfg = dict(synth.QWEN3_8B, noise_prior=args.prior)
     if args.generate:
         return generate_mode(args, U, synth, torch, cfg)
+    if args.tree:
+        return tree_mode(args, U, synth, torch, cfg)
     K = args.K
     log("generating weights on the GPU")
     model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))

@@ -98,7 +98,7 @@ struct PassWs {
   float2* cs;        // [R, hd/2]
   float* part_o;
   float* part_ml;
-  float* gemm_part;      // split-K partial tiles (passes of 128 rows or more)
+  float* gemm_part;      // split-K partial tiles (passes of more than 64 rows)
   size_t gemm_part_floats;
   size_t total;
 };
@@ -131,7 +131,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.cs = reinterpret_cast<float2*>(take(R * (c.head_dim / 2) * sizeof(float2)));
   w.part_o = reinterpret_cast<float*>(take(parts * c.head_dim * 4));
   w.part_ml = reinterpret_cast<float*>(take(parts * 2 * 4));
-  w.gemm_part_floats = R >= 128 ? kGemmPartFloats : kGemmPartFloatsSkinny;
+  w.gemm_part_floats = R > 64 ? kGemmPartFloats : kGemmPartFloatsSkinny;
   w.gemm_part = reinterpret_cast<float*>(take(w.gemm_part_floats * 4));
   w.total = off;
   return w;

@@ -741,11 +741,12 @@ static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s)
   }
 }
 
-// The tiled kernel for many rows; decode-sized row counts keep the skinny
-// kernel, which streams W once with the rows held in registers.
+// The tiled kernel for more than 64 rows (one 128-row tile streams W once);
+// decode-sized row counts keep the skinny kernel, which streams W once with
+// the rows held in registers (past 64 rows it would stream W once per 64).
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed) {
   if (normed) *normed = false;
-  if (a.M >= 128) {
+  if (a.M > 64) {
     const BigPlan p = plan_big(a);
     if (p.cfg >= 0) return launch_big(a, p, s);
   }

@@ -113,8 +113,8 @@ struct GemmArgs {
   uint16_t* norm_out;
   float norm_eps;
 };
-// split-K scratch carved per pass: 128 MB for passes of 128 rows or more
-// (tiled kernel), 4 MB below (skinny kernel)
+// split-K scratch carved per pass: 128 MB for passes of more than 64 rows
+// (tiled kernel), 4 MB for up to 64 (skinny kernel)
 constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr);

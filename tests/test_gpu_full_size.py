@@ -146,3 +146,71 @@ def test_8b_batch1_context_1k(big):
 
 def test_8b_batch64_context_9216(big):
     _run(big, 64, 9216, 37)
+
+
+def test_8b_width_one_layer_tree_sampler(big1):
+    """Tree sampler at 8B width (one layer), batch 2, context 1023, K = 16,
+    top-2 per drafted position, 8 kept candidates (121 node rows per
+    sequence): the tree built from the GPU's draft logits equals the oracle's
+    tree on the same fp32 logits; every node's verify logits (121 x 151936)
+    agree elementwise with the oracle's bf16-activation forward over the
+    tree; the draws and the walk equal the oracle's on the GPU's logits."""
+    from oracle import canonical as cn
+    from oracle import tree as ot
+    U, cfg, wts, w64, model = big1
+    B, ctx, b_check, topk, n_keep = 2, 1023, 1, 2, 8
+    N = U.tree_rows(K, topk, n_keep)
+    cap = ctx + N + K + 8
+    kv = U.PagedKV(cfg, B, cap, page_order=torch.randperm(
+        B * ((cap + 15) // 16), generator=torch.Generator().manual_seed(7)))
+    synth.fill_kv_device(kv.k_pages, kv.v_pages, seed=8)
+    k, v = synth.kv_values(cfg, ctx, seed=22, seq=b_check)
+    load_kv_logical(kv, b_check, k, v)
+    kv.kv_len.fill_(ctx)
+    toks = synth.random_tokens(ctx + 1, cfg["vocab"], 301, (B, ctx + 1))
+    seq = ospec.Sequence(cfg, toks[b_check], capacity=cap)
+    seq.cache.k[0][:ctx] = k[0].double().numpy()
+    seq.cache.v[0][:ctx] = v[0].double().numpy()
+    seq.kv_len = ctx
+    V = cfg["vocab"]
+    ws = U.alloc_workspace(max(U.workspace_bytes(model, B, K, cap),
+                               U.workspace_bytes(model, B, N, cap)))
+    zq = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
+    zp = torch.empty((B, N, V), dtype=torch.float32, device="cuda")
+    d = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    a = torch.empty(B, dtype=torch.int32, device="cuda")
+    c = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    e = torch.empty(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    step = torch.zeros(B, dtype=torch.uint64).cuda()
+    tb = U.TreeBuffers(B, K, topk, n_keep, V)
+    anchor = torch.from_numpy(toks[:, -1].copy()).cuda()
+    U.draft_block(model, kv, anchor, K, cap, 1.0, 0, step, zq, d, ws, status)
+    U.tree_build(zq, d, tb, status)
+    U.verify_tree(model, kv, tb, cap, zp, ws, status)
+    U.tree_accept(zp, tb, 1.0, 0, step, a, c, e, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    progress("8B L1 tree: GPU step done; oracle draft and tree verify (bf16 activations)")
+    zq_g = zq[b_check].cpu().numpy()
+    assert_logits_close(zq_g, ospec.draft_logits(cfg, w64, seq, K, act_round=bf16_round),
+                        "8B L1 tree draft logits")
+    u_d1 = ospec.PhiloxDraws(0, b_check, 0).u(0, 0)
+    d1 = cn.categorical(cn.row_weights(zq_g[0], 1.0)[0], u_d1)
+    assert int(d[b_check, 0]) == d1
+    tree = ot.build_tree(zq_g, d1, topk, n_keep)
+    assert int(tb.n_nodes[b_check]) == tree.n_nodes
+    np.testing.assert_array_equal(tb.tokens[b_check].cpu().numpy(), tree.tokens)
+    np.testing.assert_array_equal(tb.parent[b_check].cpu().numpy(), tree.parent)
+    zp_ref = ot.tree_verify_logits(cfg, w64, seq, tree, act_round=bf16_round)
+    zp_g = zp[b_check].cpu().numpy()
+    err = assert_logits_close(zp_g[: tree.n_nodes], zp_ref, "8B L1 tree verify logits")
+    a_ref, comm_ref, e_ref, path_ref = ot.tree_accept(tree, zp_g, 1.0,
+                                                      ospec.PhiloxDraws(0, b_check, 0))
+    assert int(a[b_check]) == a_ref and int(e[b_check]) == e_ref
+    np.testing.assert_array_equal(tb.path[b_check].cpu().numpy(),
+                                  path_ref + [-1] * (K - len(path_ref)))
+    progress("8B L1 tree: %d nodes, max verify logit error %.2e, a = %d"
+             % (tree.n_nodes, err, a_ref))
+    del kv, ws, zq, zp
+    torch.cuda.empty_cache()
