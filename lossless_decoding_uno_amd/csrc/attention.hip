@@ -67,7 +67,8 @@ constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
 // source address each lane loads, since lane i of a DMA writes 16*i):
 //   K: [64 keys][HD]  row = one key,      chunk index ^ kswz(key) % (HD/8)
 //   V: [HD][64 keys]  row = one channel,  key-group index ^ vswz(channel)
-template <int HD, int RW, int KH>
+// TREE: the rows are a token tree's nodes (ancestor-bit mask past the context).
+template <int HD, int RW, int KH, bool TREE>
 __global__ void __launch_bounds__(RW * KH * 64)
 k_attention(AttnArgs a) {
   constexpr int NW = RW * KH;             // waves per workgroup
@@ -133,7 +134,7 @@ k_attention(AttnArgs a) {
   const int qj = q_ok ? qr / G : 0, qh = q_ok ? qr % G : 0;
   const int lim = q_ok ? row_limit(qj, kvl, a.K, a.pos_offset, a.draft) : -1;
   // token tree: keys past the context also need this row's ancestor bit
-  const uint32_t* anc_row = a.tree_anc ? a.tree_anc + ((size_t)b * a.K + qj) * a.anc_words : nullptr;
+  const uint32_t* anc_row = TREE ? a.tree_anc + ((size_t)b * a.K + qj) * a.anc_words : nullptr;
   AFrag qf[DS], qfl[DS];    // q = high + low bf16 parts (scores keep ~16 bits of q)
   {
     const size_t qo = ((size_t)(b * a.K + qj) * a.Hq + g * G + qh) * HD + lg * 8;
@@ -207,7 +208,7 @@ k_attention(AttnArgs a) {
 
   float m_run = -INFINITY, l_run = 0.f;
   // smallest row limit of the workgroup: chunks below it need no masking
-  const int lim_min = (a.draft || a.tree_anc) ? kvl : kvl + a.pos_offset + min(a.K - 1, qbase / G);
+  const int lim_min = (a.draft || TREE) ? kvl : kvl + a.pos_offset + min(a.K - 1, qbase / G);
   f32x4 o[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -279,7 +280,7 @@ k_attention(AttnArgs a) {
         } else {
           const int key = k0 + 32 * (kh * NH + hh) + 8 * lg + cc;
           bool vis = key <= lim && key < hi;
-          if (vis && anc_row && key > kvl) {
+          if (TREE && vis && key > kvl) {
             const int node = key - kvl - 1;        // < K: key <= lim = kvl + 1 + qj
             vis = (anc_row[node >> 5] >> (node & 31)) & 1u;
           }
@@ -461,23 +462,25 @@ size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx) {
   return align_up(parts * c.head_dim * sizeof(float), 256) + align_up(parts * 2 * sizeof(float), 256);
 }
 
-template <int HD>
+template <int HD, bool TREE>
 static hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.plan.n_wave_splits, a.plan.n_qgroups, a.B * a.Hkv);
   const size_t lds = (size_t)kStages * 2 * 64 * HD * 2 + kMaxPagesLds * sizeof(int);
   const int kh = a.plan.key_halves;
   const dim3 block(64 * a.plan.waves * kh);
   switch (a.plan.waves * 10 + kh) {
-    case 12: hipLaunchKernelGGL((k_attention<HD, 1, 2>), grid, block, lds, s, a); break;
-    case 22: hipLaunchKernelGGL((k_attention<HD, 2, 2>), grid, block, lds, s, a); break;
-    case 42: hipLaunchKernelGGL((k_attention<HD, 4, 2>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_attention<HD, 8, 1>), grid, block, lds, s, a); break;
+    case 12: hipLaunchKernelGGL((k_attention<HD, 1, 2, TREE>), grid, block, lds, s, a); break;
+    case 22: hipLaunchKernelGGL((k_attention<HD, 2, 2, TREE>), grid, block, lds, s, a); break;
+    case 42: hipLaunchKernelGGL((k_attention<HD, 4, 2, TREE>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_attention<HD, 8, 1, TREE>), grid, block, lds, s, a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  return a.hd == 128 ? launch_attention_hd<128>(a, s) : launch_attention_hd<64>(a, s);
+  if (a.tree_anc)
+    return a.hd == 128 ? launch_attention_hd<128, true>(a, s) : launch_attention_hd<64, true>(a, s);
+  return a.hd == 128 ? launch_attention_hd<128, false>(a, s) : launch_attention_hd<64, false>(a, s);
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
