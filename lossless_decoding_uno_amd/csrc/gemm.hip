@@ -217,17 +217,20 @@ k_gemm_skinny_reduce(GemmArgs a, int gx, int gy, int splits) {
 }
 
 // Split-K reduction of a residual-add projection over whole rows, fused with
-// the RMSNorm that follows it: one workgroup per row m sums each column's
-// splits in split order, adds the sum into the residual row (a.out), and
-// writes bf16(h * rsqrt(mean(h^2) + eps) * gain) to a.norm_out.  The per-thread
-// column pattern (4 consecutive columns, 1024 apart) and the reduction order of
-// the sum of squares are those of the stand-alone RMSNorm kernel.
+// the RMSNorm that follows it: one workgroup (16 waves) per row m sums each
+// column's splits in split order, adds the sum into the residual row (a.out),
+// and writes bf16(h * rsqrt(mean(h^2) + eps) * gain) to a.norm_out.  Thread t
+// owns the columns 4t..4t+3 (+ 4096); the sum of squares is reduced in a fixed
+// order.
+constexpr int kRedNormThreads = 1024;
 template <int MT, int NT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRedNormThreads)
 k_gemm_skinny_reduce_norm(GemmArgs a, int gx, int gy, int splits) {
   constexpr int kTile = MT * NT * 256;
-  constexpr int kMaxIt = 8;                    // D <= 8192
-  __shared__ float red[4];
+  constexpr int kStep = kRedNormThreads * 4;
+  constexpr int kMaxIt = 2;                    // D <= 8192
+  constexpr int kW = kRedNormThreads / UNO_WAVE;
+  __shared__ float red[kW];
   const int m = blockIdx.x;
   const int D = a.seg[0].n;
   float* h = static_cast<float*>(a.out) + (size_t)m * a.ldo;
@@ -237,7 +240,7 @@ k_gemm_skinny_reduce_norm(GemmArgs a, int gx, int gy, int splits) {
   float ss = 0.f;
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
-    const int i = threadIdx.x * 4 + it * 1024;
+    const int i = threadIdx.x * 4 + it * kStep;
     if (i >= D) break;
     float v[4];
 #pragma unroll
@@ -259,12 +262,14 @@ k_gemm_skinny_reduce_norm(GemmArgs a, int gx, int gy, int splits) {
   ss = wave_sum(ss);
   if (lane_id() == 0) red[threadIdx.x / UNO_WAVE] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.f;
+#pragma unroll
+  for (int q = 0; q < kW; ++q) tot += red[q];
   const float inv = 1.0f / sqrtf(tot / (float)D + a.norm_eps);
   uint16_t* o = a.norm_out + (size_t)m * D;
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
-    const int i = threadIdx.x * 4 + it * 1024;
+    const int i = threadIdx.x * 4 + it * kStep;
     if (i >= D) break;
     const float4 g = *reinterpret_cast<const float4*>(a.norm_gain + i);
     const float4 x = hv[it];
@@ -316,8 +321,8 @@ static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
   if (p.splits > 1) {
     if (fuse_norm(a, p)) {
-      hipLaunchKernelGGL((k_gemm_skinny_reduce_norm<MT, NT>), dim3(a.M), dim3(256), 0, s, a,
-                         p.gx, p.gy, p.splits);
+      hipLaunchKernelGGL((k_gemm_skinny_reduce_norm<MT, NT>), dim3(a.M), dim3(kRedNormThreads), 0,
+                         s, a, p.gx, p.gy, p.splits);
       return;
     }
     const int n = p.gx * p.gy * MT * NT * 256;
