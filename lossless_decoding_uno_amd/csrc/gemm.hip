@@ -108,23 +108,28 @@ k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this split's 32-wide K steps; wave w takes ks0 + w, ks0 + w + 8, ...
+  // this split's 32-wide K steps.  One row tile (MT = 1): wave w takes blocks
+  // of UN consecutive steps (ks0 + UN*w, then every 8th block), so each of its
+  // W rows is read in 256-byte runs; more row tiles: wave w takes the steps
+  // ks0 + w, ks0 + w + 8, ... (even split of short ranges over the waves).
   const int n_all = a.Kd >> 5;
   const int ks0 = n_all * zs / splits, ks1 = n_all * (zs + 1) / splits;
   constexpr int UN = 4;   // K steps in flight per wave
-  int s = ks0 + w;
-  for (; s + (UN - 1) * kSkWaves < ks1; s += UN * kSkWaves) {
+  constexpr bool kBlk = MT == 1;
+  constexpr int kUS = kBlk ? 1 : kSkWaves;          // step distance inside a group
+  int s = ks0 + (kBlk ? w * UN : w);
+  for (; s + (UN - 1) * kUS < ks1; s += UN * kSkWaves) {
     Frag bw[UN][NT];
     Frag ax[UN][MT];
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16(wrow[t] + (s + u * kSkWaves) * 32);
+      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16(wrow[t] + (s + u * kUS) * 32);
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        ax[u][mt].u = xok[mt] ? ldg16(xrow[mt] + (s + u * kSkWaves) * 32) : make_uint4(0, 0, 0, 0);
+        ax[u][mt].u = xok[mt] ? ldg16(xrow[mt] + (s + u * kUS) * 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
@@ -133,7 +138,8 @@ k_gemm_skinny(GemmArgs a) {
         for (int t = 0; t < NT; ++t)
           acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][mt].v, bw[u][t].v, acc[mt][t], 0, 0, 0);
   }
-  for (; s < ks1; s += kSkWaves) {
+  // the rest: the wave's partial block (blocked), or its remaining steps
+  for (; s < ks1; s += kBlk ? 1 : kSkWaves) {
     Frag bw[NT], ax[MT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) bw[t].u = ldg16(wrow[t] + s * 32);
