@@ -327,8 +327,11 @@ def generate_mode(args, U, synth, torch, cfg):
     K = args.K
     log("generating weights on the GPU")
     model = U.Model(cfg, synth.make_weights_device(cfg, seed=0))
-    max_ctx = args.prompt + args.generate + 3 * K + 8
-    g = Generator(model, args.batch, K, max_ctx, seed=0, prefill_chunk=512, n_passes=args.passes)
+    tree = tuple(int(x) for x in args.tree.split(",")) if args.tree else None
+    extra = U.tree_rows(K, *tree) if tree else K
+    max_ctx = args.prompt + args.generate + 2 * K + extra + 8
+    g = Generator(model, args.batch, K, max_ctx, seed=0, prefill_chunk=512, n_passes=args.passes,
+                  tree=tree)
     prompts = synth.prompt_ids(cfg, args.prompt, 1, batch=args.batch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -351,8 +354,9 @@ def generate_mode(args, U, synth, torch, cfg):
            "value": round(toks / t_gen, 1), "unit": "tokens/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "bf16",
            "data": "synthetic (random-init weights, uniform random prompts)",
-           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d passes%d" % (
-               args.batch, args.prompt, args.generate, K, args.prior, args.passes)},
+           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d passes%d%s" % (
+               args.batch, args.prompt, args.generate, K, args.prior, args.passes,
+               " tree topk%d keep%d" % tree if tree else "")},
            "steps": st["steps"], "TPF": round(st["TPF"], 3), "AL": round(st["AL"], 3),
            "ms_per_step": round(1e3 * t_gen / st["steps"], 3),
            "prefill_s": round(t_prefill, 3), "pages_in_use": st["pages_in_use"]}
@@ -476,7 +480,7 @@ def main():
     U.load_library()
     assert torch.cuda.is_available(), "no GPU"
     cfg = dict(synth.QWEN3_8B, noise_prior=args.prior)
-    if args.generate:
+    if args.generate:                       # with --tree: end-to-end with the tree sampler
         return generate_mode(args, U, synth, torch, cfg)
     if args.tree:
         return tree_mode(args, U, synth, torch, cfg)

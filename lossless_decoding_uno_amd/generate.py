@@ -9,12 +9,17 @@ one step runs two passes (draft and verify) and commits a + 1 tokens, so
 1 <= TPF <= (K + 1) / 2 (paperglide reader, "The Uno Framework"); AL is the mean
 number of tokens a step commits.  With n draft passes per step (multi-pass
 drafting) a step runs n + 1 passes; ``stats`` reports TPF over all of them.
+With ``tree=(topk, n_keep)`` each step uses the tree sampler instead of the
+linear one: the last draft pass's logits give the prefix tree of the best
+n_keep candidates, one tree-masked verify pass scores every node, and the walk
+commits the longest accepted path plus one token.
 """
 import numpy as np
 import torch
 
-from . import (PagedKV, alloc_workspace, draft_passes, kv_commit, spec_accept,
-               spec_accept_workspace_bytes, verify_block, workspace_bytes)
+from . import (PagedKV, TreeBuffers, alloc_workspace, draft_passes, kv_commit, spec_accept,
+               spec_accept_workspace_bytes, tree_accept, tree_build, tree_commit, verify_block,
+               verify_tree, workspace_bytes)
 
 
 class PagePool:
@@ -70,7 +75,7 @@ class Generator:
     """
 
     def __init__(self, model, batch, K, max_ctx, n_pages=None, inv_temp=1.0, seed=0,
-                 prefill_chunk=512, page_size=16, device="cuda", n_passes=1):
+                 prefill_chunk=512, page_size=16, device="cuda", n_passes=1, tree=None):
         self.model, self.B, self.K = model, batch, K
         self.n_passes = int(n_passes)      # draft passes per step (multi-pass drafting)
         self.cfg = model.cfg
@@ -82,12 +87,14 @@ class Generator:
                           n_pages=n_pages or batch * max_pages)
         self.pool = PagePool(self.kv)
         V = self.cfg["vocab"]
-        rows = max(K, self.chunk)
+        self.tb = TreeBuffers(batch, K, tree[0], tree[1], V, device) if tree else None
+        self.n_rows = self.tb.N if tree else K          # verify rows per sequence
+        rows = max(self.n_rows, self.chunk)
         self.ws = alloc_workspace(max(workspace_bytes(model, batch, K, self.max_ctx),
                                       workspace_bytes(model, batch, rows, self.max_ctx)))
         self.aws = alloc_workspace(spec_accept_workspace_bytes(batch, K))
         self.zq = torch.empty((batch, K, V), dtype=torch.float32, device=device)
-        self.zp = torch.empty((batch, K, V), dtype=torch.float32, device=device)
+        self.zp = torch.empty((batch, self.n_rows, V), dtype=torch.float32, device=device)
         self.d = torch.empty((batch, K), dtype=torch.int32, device=device)
         self.a = torch.empty(batch, dtype=torch.int32, device=device)
         self.c = torch.empty((batch, K + 1), dtype=torch.int32, device=device)
@@ -122,16 +129,26 @@ class Generator:
     def step(self, forced=None):
         K = self.K
         for b in range(self.B):
-            # draft writes kv_len .. kv_len+K-1, verify kv_len+1 .. kv_len+K
-            self.pool.ensure(b, int(self.kv_len[b]) + K + 1)
+            # draft writes kv_len .. kv_len+K-1, verify kv_len+1 .. kv_len+rows
+            self.pool.ensure(b, int(self.kv_len[b]) + self.n_rows + 1)
         self.pool.sync()
         draft_passes(self.model, self.kv, self.e, K, self.max_ctx, self.inv_temp, self.seed,
                      self.step_ctr, self.n_passes, self.zq, self.d, self.ws, self.status)
-        verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws,
-                     self.status)
-        spec_accept(self.zq, self.zp, self.d, self.inv_temp, self.seed, self.step_ctr, self.a,
-                    self.c, self.e, self.aws, status=self.status, forced_accept=forced)
-        kv_commit(self.kv, self.a, K, self.step_ctr, self.status)
+        if self.tb is not None:
+            if forced is not None:
+                raise ValueError("forced accept lengths apply to the linear sampler only")
+            tree_build(self.zq, self.d, self.tb, self.status)
+            verify_tree(self.model, self.kv, self.tb, self.max_ctx, self.zp, self.ws, self.status)
+            tree_accept(self.zp, self.tb, self.inv_temp, self.seed, self.step_ctr, self.a, self.c,
+                        self.e, self.status)
+            tree_commit(self.model, self.kv, self.tb, self.a, self.step_ctr, self.status)
+        else:
+            verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws,
+                         self.status)
+            spec_accept(self.zq, self.zp, self.d, self.inv_temp, self.seed, self.step_ctr,
+                        self.a, self.c, self.e, self.aws, status=self.status,
+                        forced_accept=forced)
+            kv_commit(self.kv, self.a, K, self.step_ctr, self.status)
         a = self.a.cpu().numpy().astype(np.int64)
         c = self.c.cpu().numpy()
         for b in range(self.B):

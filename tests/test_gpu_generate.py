@@ -68,3 +68,73 @@ def test_natural_generation_matches_oracle_step_by_step(prior):
         assert g.out[b] == seqs[b].tokens[P:]
     progress("natural generation (prior %d): %d steps, TPF %.2f, AL %.2f, worst logit err %.2e"
              % (prior, st["steps"], st["TPF"], st["AL"], worst))
+
+
+def test_tree_generation_matches_oracle_step_by_step():
+    """The generator with the tree sampler (top-4 per drafted position, 6
+    kept candidates, K = 5) on a vocab-32 tiny model whose LM head is scaled
+    by 4 (sharper laws, so walks go deep): chunked prefill, pages on demand;
+    every step's tree equals the oracle's tree on the GPU's draft logits,
+    every node's verify logits (divided by the head scale) lie within the
+    tolerance of the oracle's bf16-activation forward, and the walk (accept
+    length, committed tokens, path) equals the oracle's on the GPU's logits.
+    The outputs equal the oracle's committed tokens."""
+    U = gpu_or_fail()
+    from lossless_decoding_uno_amd.generate import Generator
+    from oracle import canonical as cn
+    from oracle import model as om
+    from oracle import tree as ot
+    from gpu_util import u24
+    cfg = dict(synth.TINY, vocab=32, mask_id=31)
+    wts = synth.make_weights(cfg, 2)
+    hs = 4.0
+    wts["lm_head"] = (wts["lm_head"].float() * hs).to(torch.bfloat16)
+    w64 = synth.to_f64(wts)
+    model = U.Model(cfg, wts)
+    B, K, P, n_new, topk, n_keep = 2, 5, 24, 40, 4, 6
+    N = U.tree_rows(K, topk, n_keep)
+    prompts = np.stack([synth.prompt_ids(cfg, P, 40 + b) for b in range(B)])
+    max_ctx = P + n_new + 2 * K + N + 8
+    g = Generator(model, B, K, max_ctx, n_pages=(max_ctx // 16 + 2) * B - 1, seed=SEED,
+                  prefill_chunk=9, tree=(topk, n_keep))
+    g.prefill(prompts)
+    seqs = []
+    for b in range(B):
+        s = ospec.Sequence(cfg, list(prompts[b]), capacity=max_ctx)
+        ospec.prefill(cfg, w64, s)
+        for li in range(cfg["n_layers"]):
+            s.cache.k[li][:] = om.bf16_round(s.cache.k[li])
+            s.cache.v[li][:] = om.bf16_round(s.cache.v[li])
+        seqs.append(s)
+    worst, moves = 0.0, 0
+    while min(len(o) for o in g.out) < n_new:
+        a_g = g.step()
+        zq, zp = g.zq.cpu().numpy(), g.zp.cpu().numpy()
+        c, path_g = g.c.cpu().numpy(), g.tb.path.cpu().numpy()
+        for b in range(B):
+            s = seqs[b]
+            zq_o = ospec.draft_logits(cfg, w64, s, K, act_round=om.bf16_round)
+            worst = max(worst, assert_logits_close(zq[b] / hs, zq_o / hs,
+                                                   "tree draft b%d step %d" % (b, s.step)))
+            d1 = cn.categorical(cn.row_weights(zq[b, 0], 1.0)[0], u24(SEED, 0, 0, b, s.step))
+            tree = ot.build_tree(zq[b], d1, topk, n_keep)
+            np.testing.assert_array_equal(g.tb.tokens[b].cpu().numpy(), tree.tokens)
+            np.testing.assert_array_equal(g.tb.parent[b].cpu().numpy(), tree.parent)
+            zp_o = ot.tree_verify_logits(cfg, w64, s, tree, act_round=om.bf16_round)
+            worst = max(worst, assert_logits_close(zp[b, : tree.n_nodes] / hs, zp_o / hs,
+                                                   "tree verify b%d step %d" % (b, s.step)))
+            a, committed, extra, path = ot.tree_accept(tree, zp[b], 1.0,
+                                                       ospec.PhiloxDraws(SEED, b, s.step))
+            assert a == a_g[b] and a >= 1
+            np.testing.assert_array_equal(c[b, : a + 1], committed)
+            np.testing.assert_array_equal(path_g[b, :a], path)
+            moves += sum(1 for dd in range(1, a) if path[dd] != dd)
+            ot.tree_commit(s, path, a, committed)
+            assert s.kv_len == int(g.kv_len[b])
+    st = g.stats()
+    assert int(g.status.abs().sum().item()) == 0
+    for b in range(B):
+        assert g.out[b] == seqs[b].tokens[P:]
+    progress("tree generation: %d steps, TPF %.2f, AL %.2f, %d K/V moves, worst logit err %.2e"
+             % (st["steps"], st["TPF"], st["AL"], moves, worst))
+    assert 2.0 <= st["AL"] <= K + 1
