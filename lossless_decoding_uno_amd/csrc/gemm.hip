@@ -363,7 +363,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed) {
 // source chunk each lane copies.  Each half-slice's fragments are read while
 // the MFMAs of the other half issue.  The LoRA product runs as r/32 extra K
 // slices with T and B as operands.  Configurations:
-//   L  256 x 256, 8 waves, 4 stages (128 KB LDS): one workgroup per CU
+//   L  256 x 256, 8 waves, 5 stages (160 KB LDS): one workgroup per CU
 //   M  256 x 128, 4 waves, 3 stages (72 KB): two workgroups per CU
 //   S  128 x 128, 4 waves, 4 stages (64 KB): two workgroups per CU
 // Two resident workgroups cover each other's barrier waits, prologue and
@@ -394,7 +394,7 @@ struct Cfg {
   static_assert(kInstr % kWaves == 0 && kInstrA % kWaves == 0,
                 "DMA instructions of A and of B must split evenly over the waves");
 };
-using CfgL = Cfg<256, 256, 2, 4, 4>;
+using CfgL = Cfg<256, 256, 2, 4, 5>;
 using CfgM = Cfg<256, 128, 2, 2, 3>;
 using CfgS = Cfg<128, 128, 2, 2, 4>;
 __device__ __forceinline__ int swz_f(int row) { return (row >> 2) & 3; }
