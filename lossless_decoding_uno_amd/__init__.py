@@ -184,13 +184,26 @@ class Model:
         if n != cfg["n_layers"]:
             raise ValueError("weights hold %d layers, config %d" % (n, cfg["n_layers"]))
         self._table = (UnoLayerWeights * n)()
+        def up_pair(a, b, dtype):
+            # gate and up stored back to back: the library then fuses SwiGLU
+            # into the gate|up product (any placement works, this one is faster)
+            both = torch.cat([a.to(device=dev, dtype=dtype), b.to(device=dev, dtype=dtype)])
+            return both[: a.shape[0]], both[a.shape[0]:]
+
         for li, lw in enumerate(weights["layers"]):
             d = {"attn_norm": up(lw["attn_norm"], torch.float32),
                  "mlp_norm": up(lw["mlp_norm"], torch.float32)}
             for p in PROJ:
-                d[p] = up(lw[p], torch.bfloat16)
+                if p not in ("gate", "up"):
+                    d[p] = up(lw[p], torch.bfloat16)
+            d["gate"], d["up"] = up_pair(lw["gate"], lw["up"], torch.bfloat16)
             d["lora_a"] = {p: up(t, torch.bfloat16) for p, t in lw.get("lora_a", {}).items()}
-            d["lora_b"] = {p: up(t, torch.bfloat16) for p, t in lw.get("lora_b", {}).items()}
+            d["lora_b"] = {p: up(t, torch.bfloat16) for p, t in lw.get("lora_b", {}).items()
+                           if p not in ("gate", "up")}
+            lb = lw.get("lora_b", {})
+            if "gate" in lb and "up" in lb:
+                d["lora_b"]["gate"], d["lora_b"]["up"] = up_pair(lb["gate"], lb["up"],
+                                                                 torch.bfloat16)
             self.layers.append(d)
             e = self._table[li]
             e.attn_norm, e.mlp_norm = d["attn_norm"].data_ptr(), d["mlp_norm"].data_ptr()

@@ -261,16 +261,28 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(lora_t(W.xn, D, D, a2, 2));
     }
     {
+      // gate and up rows stored back to back (and their LoRA B factors too):
+      // the tiled kernel pairs them and writes silu(gate) * up directly
+      const char* wg = static_cast<const char*>(L.wgate);
+      const bool adjacent =
+          static_cast<const char*>(L.wup) == wg + (size_t)F * D * 2 &&
+          (!lg || static_cast<const char*>(L.lora_b[P_UP]) ==
+                      static_cast<const char*>(L.lora_b[P_GATE]) + (size_t)F * r * 2);
       GemmArgs g = scratch_args();
       g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
-      g.seg[0] = GemmSeg{bp(L.wgate), F, lg ? bp(L.lora_b[P_GATE]) : nullptr, 0};
-      g.seg[1] = GemmSeg{bp(L.wup), F, lg ? bp(L.lora_b[P_UP]) : nullptr, r};
-      g.n_seg = 2;
       g.t = lg ? W.t : nullptr; g.ldt = 2 * r; g.rank = r;
-      g.epi = EPI_STORE_F32; g.out = W.gu; g.ldo = 2 * F;
+      g.seg[0] = GemmSeg{bp(L.wgate), F, lg ? bp(L.lora_b[P_GATE]) : nullptr, 0};
+      g.n_seg = 1;
+      g.epi = EPI_SWIGLU; g.out = W.act; g.ldo = F;
+      const bool fused = adjacent && gemm_swiglu_ok(g);
+      if (!fused) {
+        g.seg[1] = GemmSeg{bp(L.wup), F, lg ? bp(L.lora_b[P_UP]) : nullptr, r};
+        g.n_seg = 2;
+        g.epi = EPI_STORE_F32; g.out = W.gu; g.ldo = 2 * F;
+      }
       UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_GATE_UP));
+      if (!fused) UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
     }
-    UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
     if (ld) {
       const void* a1[1] = {L.lora_a[P_DOWN]};
       UNO_TRY(lora_t(W.act, F, F, a1, 1));

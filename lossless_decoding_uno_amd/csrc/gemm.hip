@@ -442,12 +442,18 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
     mt = tile % m_tiles; nt = tile / m_tiles; z = j % splits; sp = splits;
   }
   const int m0 = mt * C::BM;
-  const SegView sv = pick_segment(a, nt * (C::BN / 16));
-  const int n0 = sv.n0;
+  // SwiGLU pairs: tile nt covers act columns [nt*BN/2, (nt+1)*BN/2); its
+  // rows 0..BN/2-1 are those gate rows, rows BN/2..BN-1 the same up rows
+  const bool pair = a.epi == EPI_SWIGLU;
+  constexpr int HALF = C::BN / 2;
+  const SegView sv = pick_segment(a, pair ? 0 : nt * (C::BN / 16));
+  const int n0 = pair ? nt * HALF : sv.n0;
+  const int wrows = pair ? 2 * sv.n : sv.n;        // rows the W / LoRA B resources span
 
   // K slices of this split (LoRA slices after the last split's base slices)
   const int nk_base = a.Kd / BK;
-  const int nk_lora = (a.t && sv.lb) ? a.rank / BK : 0;
+  const int nk_r = (a.t && sv.lb) ? a.rank / BK : 0;
+  const int nk_lora = pair ? 2 * nk_r : nk_r;   // pairs: [T_gate | T_up] against [B_g, 0 | 0, B_u]
   const int kb0 = nk_base * z / sp, kb1 = nk_base * (z + 1) / sp;
   const int nk = (kb1 - kb0) + (z == sp - 1 ? nk_lora : 0);
 
@@ -461,9 +467,10 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
   constexpr int IA = C::kIA, IB = C::kIB;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const i32x4 rs_x = make_rsrc(a.x, (uint32_t)((size_t)a.M * a.ldx * 2));
-  const i32x4 rs_w = make_rsrc(sv.w, (uint32_t)((size_t)sv.n * a.Kd * 2));
+  const i32x4 rs_w = make_rsrc(sv.w, (uint32_t)((size_t)wrows * a.Kd * 2));
   const i32x4 rs_t = a.t ? make_rsrc(a.t, (uint32_t)((size_t)a.M * a.ldt * 2)) : rs_x;
-  const i32x4 rs_lb = sv.lb ? make_rsrc(sv.lb, (uint32_t)((size_t)sv.n * a.rank * 2)) : rs_w;
+  const uint32_t lb_bytes = (uint32_t)((size_t)wrows * a.rank * 2);
+  const i32x4 rs_lb = sv.lb ? make_rsrc(sv.lb, lb_bytes) : rs_w;
   uint32_t vb[IW], vl[IW];
 #pragma unroll
   for (int ii = 0; ii < IW; ++ii) {
@@ -475,11 +482,16 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
       vb[ii] = (uint32_t)(((size_t)m * a.ldx + ch * 8) * 2);
       vl[ii] = (uint32_t)(((size_t)m * a.ldt + sv.t_col + ch * 8) * 2);
     } else {
-      const int n = n0 + row < sv.n ? n0 + row : sv.n - 1;
+      int n;
+      if (pair) n = row < HALF ? n0 + row : sv.n + n0 + row - HALF;
+      else n = n0 + row < sv.n ? n0 + row : sv.n - 1;
       vb[ii] = (uint32_t)(((size_t)n * a.Kd + ch * 8) * 2);
       vl[ii] = (uint32_t)(((size_t)n * a.rank + ch * 8) * 2);
     }
   }
+  // SwiGLU pairs, LoRA slices q < nk_r feed T_gate, the rest T_up: the other
+  // half's B rows read past the end of their resource, which returns zeros
+  const int b_up0 = pair ? (HALF / 16 - wu * IB + IA) : 0x7fffffff;  // first up instruction
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t dst_a = lds0 + wu * IA * 1024, dst_b = lds0 + C::kLdsA + wu * IB * 1024;
   auto issue = [&](int s, int stage) {
@@ -493,11 +505,18 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
         else lds_dma16_buf(rs_w, vb[ii], soff, dst_b + so + (ii - IA) * 1024);
       }
     } else {
-      const uint32_t soff = __builtin_amdgcn_readfirstlane((kk - kb1) * BK * 2);
+      const int q = kk - kb1;
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(q * BK * 2);
+      // pairs: gate rows take slices q < nk_r, up rows q >= nk_r (at q - nk_r)
+      const uint32_t soff_g = __builtin_amdgcn_readfirstlane(q < nk_r ? q * BK * 2 : lb_bytes);
+      const uint32_t soff_u =
+          __builtin_amdgcn_readfirstlane(q >= nk_r ? (q - nk_r) * BK * 2 : lb_bytes);
 #pragma unroll
       for (int ii = 0; ii < IW; ++ii) {
         if (ii < IA) lds_dma16_buf(rs_t, vl[ii], soff, dst_a + so + ii * 1024);
-        else lds_dma16_buf(rs_lb, vl[ii], soff, dst_b + so + (ii - IA) * 1024);
+        else if (!pair) lds_dma16_buf(rs_lb, vl[ii], soff, dst_b + so + (ii - IA) * 1024);
+        else lds_dma16_buf(rs_lb, vl[ii], ii < b_up0 ? soff_g : soff_u,
+                           dst_b + so + (ii - IA) * 1024);
       }
     }
   };
@@ -602,6 +621,41 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
     return;
   }
 
+  if (pair) {
+    // the up waves (wn >= WN/2) hand their tile to the gate waves through LDS
+    // (same fragment layout), which write bf16(silu(g) * u)
+    constexpr int HW = C::WN / 2, NF = TI * TJ * 16;
+    __syncthreads();                                   // stages no longer read
+    float* xch = reinterpret_cast<float*>(lds);
+    const int slot = wm * HW + (wn % HW);
+    if (wn >= HW) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xch[((slot * NF) + (i * TJ + j) * 16 + e) * 64 + l] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (wn < HW) {
+      uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int c = n0 + wn * C::TN + j * 32 + (l & 31);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = m0 + wm * C::TM + i * 32 + (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
+            const float g = acc[i][j][e];
+            const float u = xch[((slot * NF) + (i * TJ + j) * 16 + e) * 64 + l];
+            if (m < a.M) out[(size_t)m * a.ldo + c] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+          }
+      }
+    }
+    return;
+  }
+
   // epilogue: lane holds rows (e/4)*8 + (l/32)*4 + e%4, column l%32 of each 32x32 tile
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
@@ -663,6 +717,9 @@ static bool big_ok(const GemmArgs& a, int bn) {
   // buffer offsets are 32-bit: every operand under 2 GiB
   const size_t lim = size_t(1) << 31;
   if ((size_t)a.M * a.ldx * 2 >= lim || (a.t && (size_t)a.M * a.ldt * 2 >= lim)) return false;
+  if (a.epi == EPI_SWIGLU)   // one segment of F gate rows followed by F up rows
+    return a.n_seg == 1 && a.seg[0].n % (bn / 2) == 0 &&
+           (size_t)2 * a.seg[0].n * a.Kd * 2 < lim;
   for (int i = 0; i < a.n_seg; ++i)
     if ((size_t)a.seg[i].n * a.Kd * 2 >= lim) return false;
   if (a.n_seg > 1)
@@ -693,13 +750,14 @@ constexpr double kPartBytesPerUs = 10e6;   // split-K partial tiles, written and
 // split-K partial tiles and the reduction launch.
 static BigPlan plan_big(const GemmArgs& a) {
   BigPlan best = {-1, 0, 0, 0, 0, 1e30};
-  const int nk = a.Kd / big::BK + (a.t ? a.rank / big::BK : 0);
+  const int pair = a.epi == EPI_SWIGLU ? 2 : 1;
+  const int nk = a.Kd / big::BK + (a.t ? pair * a.rank / big::BK : 0);
   for (int c = 0; c < 3; ++c) {
     const CfgInfo& ci = kCfgInfo[c];
     if (!big_ok(a, ci.bn)) continue;
     const int m_tiles = (a.M + ci.bm - 1) / ci.bm;
     int n_tiles = 0;
-    for (int i = 0; i < a.n_seg; ++i) n_tiles += (a.seg[i].n + ci.bn - 1) / ci.bn;
+    for (int i = 0; i < a.n_seg; ++i) n_tiles += (pair * a.seg[i].n + ci.bn - 1) / ci.bn;
     const int tiles = m_tiles * n_tiles;
     const double slice_flop = 2.0 * ci.bm * ci.bn * big::BK;
     const double slice_bytes = (ci.bm + ci.bn) * big::BK * 2.0;
@@ -731,12 +789,61 @@ static BigPlan plan_big(const GemmArgs& a) {
   return best;
 }
 
+// Split-K reduction of an EPI_SWIGLU product: one thread per float4 (four
+// rows of one column) of a gate wave's partial tile; the matching float4 of
+// its up partner sits WN/2 waves on.  Splits are summed in order, then
+// bf16(silu(g) * u) is stored.
+template <class C>
+__global__ void __launch_bounds__(256)
+k_gemm_splitk_reduce_swiglu(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
+  constexpr int Q = C::kTileFloats / 4, QH = Q / 2, HW = C::WN / 2;
+  const int rem = m_tiles * n_tiles - n_full;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= rem * QH) return;
+  const int tr = g / QH;
+  int r = g % QH;
+  const int l = r & 63;
+  r >>= 6;
+  const int e4 = r & 3;
+  r >>= 2;
+  const int j = r % C::TJ;
+  r /= C::TJ;
+  const int i = r % C::TI;
+  r /= C::TI;
+  const int wg = r % HW, wm = r / HW;
+  const int w = wm * C::WN + wg;
+  const int q = (((w * C::TI + i) * C::TJ + j) * 4 + e4) * 64 + l;
+  const int qu = ((((w + HW) * C::TI + i) * C::TJ + j) * 4 + e4) * 64 + l;
+  const float4* src = reinterpret_cast<const float4*>(a.part);
+  float4 gs = src[(size_t)tr * Q + q], us = src[(size_t)tr * Q + qu];
+  for (int z = 1; z < splits; ++z) {
+    const float4 gz = src[((size_t)z * rem + tr) * Q + q];
+    const float4 uz = src[((size_t)z * rem + tr) * Q + qu];
+    gs.x += gz.x; gs.y += gz.y; gs.z += gz.z; gs.w += gz.w;
+    us.x += uz.x; us.y += uz.y; us.z += uz.z; us.w += uz.w;
+  }
+  const int tile = n_full + tr;
+  const int mt = tile % m_tiles, nt = tile / m_tiles;
+  const int c = nt * (C::BN / 2) + wg * C::TN + j * 32 + (l & 31);
+  const int mb = mt * C::BM + wm * C::TM + i * 32 + e4 * 8 + (l >> 5) * 4;
+  const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (mb + k < a.M)
+      out[(size_t)(mb + k) * a.ldo + c] = f32_to_bf16(gv[k] / (1.0f + __expf(-gv[k])) * uv[k]);
+}
+
 template <class C>
 static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
   const int rem = p.m_tiles * p.n_tiles - p.n_full;
   hipLaunchKernelGGL(k_gemm_big<C>, dim3(p.n_full + rem * p.splits), dim3(C::kThreads), C::kLds,
                      s, a, p.m_tiles, p.n_tiles, p.splits, p.n_full);
-  if (p.splits > 1) {
+  if (p.splits > 1 && a.epi == EPI_SWIGLU) {
+    const int n = rem * (C::kTileFloats / 8);
+    hipLaunchKernelGGL(k_gemm_splitk_reduce_swiglu<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
+                       p.m_tiles, p.n_tiles, p.splits, p.n_full);
+  } else if (p.splits > 1) {
     const int n = rem * (C::kTileFloats / 4);
     hipLaunchKernelGGL(k_gemm_splitk_reduce<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
                        p.m_tiles, p.n_tiles, p.splits, p.n_full);
@@ -755,8 +862,13 @@ static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s)
 // The tiled kernel for more than 64 rows (one 128-row tile streams W once);
 // decode-sized row counts keep the skinny kernel, which streams W once with
 // the rows held in registers (past 64 rows it would stream W once per 64).
+bool gemm_swiglu_ok(const GemmArgs& a) {
+  return a.epi == EPI_SWIGLU && a.M > 64 && plan_big(a).cfg >= 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed) {
   if (normed) *normed = false;
+  if (a.epi == EPI_SWIGLU && !gemm_swiglu_ok(a)) return hipErrorInvalidValue;
   if (a.M > 64) {
     const BigPlan p = plan_big(a);
     if (p.cfg >= 0) return launch_big(a, p, s);

@@ -89,7 +89,12 @@ struct GemmSeg {
   const bf16_raw_t* lora_b; // [n, r] bf16 or null
   int t_col;                // first column of this segment's LoRA input in T
 };
-enum GemmEpilogue { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_BF16 = 2, EPI_LORA_T = 3 };
+// EPI_SWIGLU (tiled kernel only, gemm_swiglu_ok): gate|up projection with the
+// SwiGLU product fused: seg[0].w holds the gate rows [F, Kd] immediately
+// followed by the up rows [F, Kd] (seg[0].n = F), seg[0].lora_b likewise
+// [2F, r]; T = [T_gate | T_up] (ldt = 2r); out[m, c] = bf16(silu(g) * u) [M, F].
+enum GemmEpilogue { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_STORE_BF16 = 2, EPI_LORA_T = 3,
+                    EPI_SWIGLU = 4 };
 struct GemmArgs {
   const bf16_raw_t* x;   // [M, Kd] bf16, row stride ldx
   int M, Kd, ldx;
@@ -118,6 +123,8 @@ struct GemmArgs {
 constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr);
+// whether launch_gemm can run this EPI_SWIGLU product (the tiled kernel takes it)
+bool gemm_swiglu_ok(const GemmArgs& a);
 
 // ---------------------------------------------------------------- attention
 // Block attention of a pass over the paged cache.  Query rows of sequence b
