@@ -161,7 +161,9 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
   }
   // rotation pairs of q and k heads
   const int n_pairs = (Hq + Hkv) * half;
-  for (int t = threadIdx.x; t < n_pairs; t += blockDim.x) {
+  // a row's work is spread over gridDim.y workgroups (short passes have few rows)
+  const int t0 = blockIdx.y * blockDim.x + threadIdx.x, tstep = blockDim.x * gridDim.y;
+  for (int t = t0; t < n_pairs; t += tstep) {
     const int head = t / half, i = t % half;
     const float x1 = row[head * hd + i], x2 = row[head * hd + i + half];
     const float2 a = c[i];
@@ -185,7 +187,7 @@ k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, in
     }
   }
   if (page >= 0) {
-    for (int t = threadIdx.x; t < Hkv * hd; t += blockDim.x) {
+    for (int t = t0; t < Hkv * hd; t += tstep) {
       const int g = t / hd, d = t % hd;
       const float v = row[(Hq + Hkv) * hd + t];
       v_layer[(((size_t)page * Hkv + g) * hd + d) * ps + slot] = f32_to_bf16(v);
@@ -201,7 +203,8 @@ hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const flo
       (size_t)kv.n_pages * c.n_kv_heads * c.page_size * c.head_dim;
   uint16_t* kl = static_cast<uint16_t*>(kv.k_pages) + (size_t)layer * layer_elems;
   uint16_t* vl = static_cast<uint16_t*>(kv.v_pages) + (size_t)layer * layer_elems;
-  hipLaunchKernelGGL(k_rope_kv_write, dim3(B * K), dim3(256), 0, s, qkv, cs, K, c.n_q_heads,
+  const int R = B * K, split = R >= 256 ? 1 : R >= 64 ? 2 : 4;
+  hipLaunchKernelGGL(k_rope_kv_write, dim3(R, split), dim3(256), 0, s, qkv, cs, K, c.n_q_heads,
                      c.n_kv_heads, c.head_dim, pos_offset, kv.kv_len, kv.page_table,
                      kv.max_pages_per_seq, kv.n_pages, c.page_size, kl, vl, q_out, q_lo, status);
   return hipGetLastError();
