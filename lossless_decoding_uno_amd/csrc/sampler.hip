@@ -15,8 +15,9 @@
 // rounded fp32 op: contraction into FMA is switched off in this file.
 //
 // Layout: logits are fp32 rows of V entries; row (b, j) of a [B, K, V] tensor
-// starts at (b*K + j)*V.  Each row is handled by one 256-thread workgroup
-// (4 waves of 64); rows are streamed with 16-byte loads when V % 4 == 0.
+// starts at (b*K + j)*V.  Each row is handled by one workgroup of 4 waves (16
+// when there are fewer than 512 rows); rows are streamed with 16-byte loads
+// when V % 4 == 0.
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -85,24 +86,26 @@ struct Row {
   }
 };
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / UNO_WAVE;
 constexpr int kTile = UNO_WAVE * 4;  // entries per wave tile
 
+// TH: threads per workgroup (one workgroup per row): 256, or 1024 when there
+// are too few rows to fill the chip with 256-thread workgroups.
+template <int TH>
 struct RowShared {
-  float red_f[kWaves];
-  int red_i[kWaves];
-  u128 red_u[kWaves];
+  float red_f[TH / UNO_WAVE];
+  int red_i[TH / UNO_WAVE];
+  u128 red_u[TH / UNO_WAVE];
   u128 found_before;
   int found_tile;
   int result;
 };
 
 // Block-wide max of a row; sets *nonfinite if any entry is NaN/Inf.
-__device__ float block_row_max(const Row& row, RowShared& sh, bool* nonfinite) {
+template <int TH>
+__device__ float block_row_max(const Row& row, RowShared<TH>& sh, bool* nonfinite) {
   float m = -INFINITY;
   int bad = 0;
-  for (int e0 = threadIdx.x * 4; e0 < row.V; e0 += kThreads * 4) {
+  for (int e0 = threadIdx.x * 4; e0 < row.V; e0 += TH * 4) {
     float v[4];
     bool ok[4];
     row.load4(e0, v, ok);
@@ -120,7 +123,7 @@ __device__ float block_row_max(const Row& row, RowShared& sh, bool* nonfinite) {
   __syncthreads();
   float r = sh.red_f[0];
   int rb = sh.red_i[0];
-  for (int i = 1; i < kWaves; ++i) { r = fmaxf(r, sh.red_f[i]); rb |= sh.red_i[i]; }
+  for (int i = 1; i < (TH / UNO_WAVE); ++i) { r = fmaxf(r, sh.red_f[i]); rb |= sh.red_i[i]; }
   __syncthreads();
   *nonfinite = rb != 0;
   return r;
@@ -161,12 +164,12 @@ struct ResidualWeights {  // max(0, Wp Sq - Wq Sp) of a row pair
 };
 
 // Sum of all weights; tile sums (kTile entries each) go to `tiles` (LDS).
-template <class WF>
-__device__ u128 block_weight_sum(const WF& wf, int V, u128* tiles, RowShared& sh) {
+template <int TH, class WF>
+__device__ u128 block_weight_sum(const WF& wf, int V, u128* tiles, RowShared<TH>& sh) {
   const int w = threadIdx.x / UNO_WAVE, l = lane_id();
   const int n_tiles = (V + kTile - 1) / kTile;
   u128 acc = u128_make(0, 0);
-  for (int t = w; t < n_tiles; t += kWaves) {
+  for (int t = w; t < n_tiles; t += (TH / UNO_WAVE)) {
     u128 v[4];
     wf.get4(t * kTile + l * 4, v);
     u128 s = u128_add(u128_add(v[0], v[1]), u128_add(v[2], v[3]));
@@ -177,15 +180,15 @@ __device__ u128 block_weight_sum(const WF& wf, int V, u128* tiles, RowShared& sh
   if (l == 0) sh.red_u[w] = acc;
   __syncthreads();
   u128 tot = sh.red_u[0];
-  for (int i = 1; i < kWaves; ++i) tot = u128_add(tot, sh.red_u[i]);
+  for (int i = 1; i < (TH / UNO_WAVE); ++i) tot = u128_add(tot, sh.red_u[i]);
   __syncthreads();
   return tot;
 }
 
 // Smallest entry whose running weight sum exceeds `t` (t < total).  Needs the
 // tile sums from block_weight_sum.  Every thread returns the index.
-template <class WF>
-__device__ int block_find(const WF& wf, int V, const u128* tiles, u128 t, RowShared& sh) {
+template <int TH, class WF>
+__device__ int block_find(const WF& wf, int V, const u128* tiles, u128 t, RowShared<TH>& sh) {
   const int w = threadIdx.x / UNO_WAVE, l = lane_id();
   const int n_tiles = (V + kTile - 1) / kTile;
   if (w == 0) {
@@ -243,13 +246,14 @@ __device__ __forceinline__ void flag(int32_t* status, int b, int32_t f) {
 // slot 0 for the drafts that go to verification, 4 + i for the samples of an
 // intermediate draft pass i.  Token-tree rows (row_j != null) draw with
 // j = row_j[row] + j_add, and rows at or past n_valid[b] are skipped (-1).
-__global__ void __launch_bounds__(kThreads)
+template <int TH>
+__global__ void __launch_bounds__(TH)
 k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, uint64_t seed,
                int slot, const uint64_t* __restrict__ step, int32_t* __restrict__ tokens,
                int32_t* __restrict__ status, const int32_t* __restrict__ row_j, int j_add,
                const int32_t* __restrict__ n_valid) {
   extern __shared__ u128 tiles[];
-  __shared__ RowShared sh;
+  __shared__ RowShared<TH> sh;
   const int row_id = blockIdx.x;
   const int b = row_id / K;
   if (n_valid && row_id % K >= n_valid[b]) {
@@ -273,11 +277,12 @@ k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, u
 
 // One workgroup per row of the concatenated [draft rows; verify rows]:
 // row maximum and exact weight sum (fits 64 bits: V <= 2^20, W <= 2^31).
-__global__ void __launch_bounds__(kThreads)
+template <int TH>
+__global__ void __launch_bounds__(TH)
 k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, int V,
             int n_rows_each, float inv_temp, float* __restrict__ m_out,
             uint64_t* __restrict__ s_out, int32_t* __restrict__ status) {
-  __shared__ RowShared sh;
+  __shared__ RowShared<TH> sh;
   const int r = blockIdx.x;
   const bool is_p = r >= n_rows_each;
   const int rr = is_p ? r - n_rows_each : r;
@@ -286,7 +291,7 @@ k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, i
   const float m = block_row_max(row, sh, &bad);
   uint64_t acc = 0;
   if (!bad) {
-    for (int e0 = threadIdx.x * 4; e0 < V; e0 += kThreads * 4) {
+    for (int e0 = threadIdx.x * 4; e0 < V; e0 += TH * 4) {
       float v[4];
       bool ok[4];
       row.load4(e0, v, ok);
@@ -301,7 +306,7 @@ k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, i
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t tot = 0;
-    for (int i = 0; i < kWaves; ++i) tot += sh.red_u[i].lo;
+    for (int i = 0; i < (TH / UNO_WAVE); ++i) tot += sh.red_u[i].lo;
     m_out[r] = m;
     s_out[r] = bad ? 0ull : tot;
     if (bad) flag(status, rr / K, UNO_DEV_NONFINITE);
@@ -309,7 +314,8 @@ k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, i
 }
 
 // One workgroup per sequence: accept tests, a, extra token, outputs.
-__global__ void __launch_bounds__(kThreads)
+template <int TH>
+__global__ void __launch_bounds__(TH)
 k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
               const int32_t* __restrict__ drafts, int K, int V, float inv_temp,
               uint64_t seed, const uint64_t* __restrict__ step,
@@ -318,7 +324,7 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
               int32_t* __restrict__ accept_len, int32_t* __restrict__ committed,
               int32_t* __restrict__ extra_token, int32_t* __restrict__ status) {
   extern __shared__ u128 tiles[];
-  __shared__ RowShared sh;
+  __shared__ RowShared<TH> sh;
   __shared__ int s_a;
   __shared__ int s_err;
   const int b = blockIdx.x;
@@ -362,7 +368,7 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
   __syncthreads();
   const int a = s_a;
   if (s_err) {
-    for (int j = threadIdx.x; j <= K; j += kThreads) committed[b * (K + 1) + j] = -1;
+    for (int j = threadIdx.x; j <= K; j += TH) committed[b * (K + 1) + j] = -1;
     if (threadIdx.x == 0) { accept_len[b] = 0; extra_token[b] = -1; }
     return;
   }
@@ -392,7 +398,7 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
     const uint32_t U = uniform24(seed, 2, K, b, st);
     e = block_find(pw, V, tiles, scaled_target(U, u128_make(sp[K - 1], 0)), sh);
   }
-  for (int j = threadIdx.x; j <= K; j += kThreads) {
+  for (int j = threadIdx.x; j <= K; j += TH) {
     int v = -1;
     if (j < a) v = drafts[b * K + j];
     else if (j == a) v = e;
@@ -404,11 +410,20 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
 // ------------------------------------------------------------ launchers
 static size_t tile_lds_bytes(int V) { return (size_t)((V + kTile - 1) / kTile) * sizeof(u128); }
 
+// 1024-thread workgroups when the rows would not fill the chip with 256
+static bool wide_rows(int rows) { return rows < 512; }
+
 hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
                                uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
                                int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_draft_sample, dim3(B * K), dim3(kThreads), tile_lds_bytes(V), s, logits,
-                     K, V, inv_temp, seed, slot, step, tokens, status, nullptr, 0, nullptr);
+  if (wide_rows(B * K))
+    hipLaunchKernelGGL(k_draft_sample<1024>, dim3(B * K), dim3(1024), tile_lds_bytes(V), s,
+                       logits, K, V, inv_temp, seed, slot, step, tokens, status, nullptr, 0,
+                       nullptr);
+  else
+    hipLaunchKernelGGL(k_draft_sample<256>, dim3(B * K), dim3(256), tile_lds_bytes(V), s,
+                       logits, K, V, inv_temp, seed, slot, step, tokens, status, nullptr, 0,
+                       nullptr);
   return hipGetLastError();
 }
 
@@ -416,8 +431,14 @@ hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float in
                               uint64_t seed, const uint64_t* step, const int32_t* node_depth,
                               const int32_t* n_nodes, int32_t* samples, int32_t* status,
                               hipStream_t s) {
-  hipLaunchKernelGGL(k_draft_sample, dim3(B * N), dim3(kThreads), tile_lds_bytes(V), s, logits,
-                     N, V, inv_temp, seed, 2, step, samples, status, node_depth, 1, n_nodes);
+  if (wide_rows(B * N))
+    hipLaunchKernelGGL(k_draft_sample<1024>, dim3(B * N), dim3(1024), tile_lds_bytes(V), s,
+                       logits, N, V, inv_temp, seed, 2, step, samples, status, node_depth, 1,
+                       n_nodes);
+  else
+    hipLaunchKernelGGL(k_draft_sample<256>, dim3(B * N), dim3(256), tile_lds_bytes(V), s,
+                       logits, N, V, inv_temp, seed, 2, step, samples, status, node_depth, 1,
+                       n_nodes);
   return hipGetLastError();
 }
 
@@ -434,13 +455,22 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
   float* m_all = static_cast<float*>(ws);
   uint64_t* s_all = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                                 align_up(2 * (size_t)n_each * sizeof(float), 256));
-  hipLaunchKernelGGL(k_row_stats, dim3(2 * n_each), dim3(kThreads), 0, s, zq, zp, K, V, n_each,
-                     inv_temp, m_all, s_all, status);
+  if (wide_rows(2 * n_each))
+    hipLaunchKernelGGL(k_row_stats<1024>, dim3(2 * n_each), dim3(1024), 0, s, zq, zp, K, V,
+                       n_each, inv_temp, m_all, s_all, status);
+  else
+    hipLaunchKernelGGL(k_row_stats<256>, dim3(2 * n_each), dim3(256), 0, s, zq, zp, K, V,
+                       n_each, inv_temp, m_all, s_all, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_spec_accept, dim3(B), dim3(kThreads), tile_lds_bytes(V), s, zq, zp, drafts,
-                     K, V, inv_temp, seed, step, forced, m_all, s_all, n_each, accept_len,
-                     committed, extra_token, status);
+  if (B <= 16)   // one workgroup per sequence: wide only for a handful of sequences
+    hipLaunchKernelGGL(k_spec_accept<1024>, dim3(B), dim3(1024), tile_lds_bytes(V), s, zq, zp,
+                       drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
+                       accept_len, committed, extra_token, status);
+  else
+    hipLaunchKernelGGL(k_spec_accept<256>, dim3(B), dim3(256), tile_lds_bytes(V), s, zq, zp,
+                       drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
+                       accept_len, committed, extra_token, status);
   return hipGetLastError();
 }
 
