@@ -96,6 +96,7 @@ struct PassWs {
   uint16_t* act;     // [R, F]
   uint16_t* t;       // [R, 3r]
   float2* cs;        // [R, hd/2]
+  int2* row_page;    // [R] K/V page and slot of each row
   float* part_o;
   float* part_ml;
   float* gemm_part;      // split-K partial tiles (passes of more than 64 rows)
@@ -129,6 +130,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.act = reinterpret_cast<uint16_t*>(take(R * F * 2));
   w.t = reinterpret_cast<uint16_t*>(take(R * 3 * r * 2));
   w.cs = reinterpret_cast<float2*>(take(R * (c.head_dim / 2) * sizeof(float2)));
+  w.row_page = reinterpret_cast<int2*>(take(R * sizeof(int2)));
   w.part_o = reinterpret_cast<float*>(take(parts * c.head_dim * 4));
   w.part_ml = reinterpret_cast<float*>(take(parts * 2 * 4));
   w.gemm_part_floats = R > 64 ? kGemmPartFloats : kGemmPartFloatsSkinny;
@@ -176,8 +178,8 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
 #define UNO_TRY(x) do { e = (x); if (e != hipSuccess) return hip_fail(e); } while (0)
 
   UNO_TRY(launch_embed(c, bp(w->embed), anchor, block, rows, B, K, seed, step, W.h, status, s));
-  UNO_TRY(launch_rope_table(kv->kv_len, B, K, draft ? 0 : pos_offset, hd / 2, c.rope_theta,
-                            tree_depth, W.cs, s));
+  UNO_TRY(launch_rope_table(c, *kv, B, K, draft ? 0 : pos_offset, tree_depth, W.cs, W.row_page,
+                            status, s));
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
   const size_t layer_elems = (size_t)kv->n_pages * Hkv * c.page_size * hd;
 
@@ -219,10 +221,14 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.n_seg = 3;
       g.t = lq ? W.t : nullptr; g.ldt = 3 * r; g.rank = r;
       g.epi = EPI_STORE_F32; g.out = W.qkv; g.ldo = QKV;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_QKV));
+      // a split product applies RoPE and writes q and the K/V pages in its reduction
+      g.rope_fuse = 1;
+      g.rope = make_rope_args(c, W.cs, W.row_page, *kv, li, K, W.qb, W.qlo);
+      bool roped = false;
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, nullptr, &roped); },
+                    UNO_TIME_GEMM_QKV));
+      if (!roped) UNO_TRY(launch_rope_kv_write(W.qkv, g.rope, R, s));
     }
-    UNO_TRY(launch_rope_kv_write(c, W.qkv, W.cs, *kv, li, B, K, draft ? 0 : pos_offset, W.qb,
-                                 W.qlo, status, s));
     {
       AttnArgs a = {};
       a.q = W.qb;

@@ -10,6 +10,7 @@
 // Implications").
 #include "uno_device.h"
 #include "uno_internal.h"
+#include "rope_store.h"
 
 namespace uno {
 
@@ -110,7 +111,9 @@ hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float
 // + depth[r] for a token tree's rows (their slot stays kv_len + pos_offset + j).
 __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_offset, int half,
                              double log_theta, const int32_t* __restrict__ depth,
-                             float2* __restrict__ cs) {
+                             float2* __restrict__ cs, const int32_t* __restrict__ page_table,
+                             int max_pages, int64_t n_pages, int ps, int2* __restrict__ row_page,
+                             int32_t* __restrict__ status) {
   const int r = blockIdx.x;
   const int b = r / K, j = r % K;
   const double pos = (double)(kv_len[b] + pos_offset + (depth ? depth[r] : j));
@@ -120,93 +123,75 @@ __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_
     sincos(pos * inv_freq, &sn, &cn);
     cs[(size_t)r * half + i] = make_float2((float)cn, (float)sn);
   }
+  // the row's K/V slot (kv_len + pos_offset + j) and its page, for every layer
+  if (threadIdx.x == 0) {
+    const int slot_pos = kv_len[b] + pos_offset + j;
+    const int pidx = slot_pos / ps;
+    int page = -1;
+    if (slot_pos >= 0 && pidx < max_pages) {
+      page = page_table[(size_t)b * max_pages + pidx];
+      if (page < 0 || page >= n_pages) {
+        if (status) atomicOr(status + b, UNO_DEV_BAD_PAGE);
+        page = -1;
+      }
+    } else if (status) {
+      atomicOr(status + b, UNO_DEV_CAPACITY);
+    }
+    row_page[r] = make_int2(page, slot_pos % ps);
+  }
 }
 
-hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
-                             float theta, const int32_t* depth, float2* cs, hipStream_t s) {
-  hipLaunchKernelGGL(k_rope_table, dim3(B * K), dim3(64), 0, s, kv_len, K, pos_offset, half,
-                     log((double)theta), depth, cs);
+hipError_t launch_rope_table(const uno_config& c, const uno_kv& kv, int B, int K, int pos_offset,
+                             const int32_t* depth, float2* cs, int2* row_page, int32_t* status,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_rope_table, dim3(B * K), dim3(64), 0, s, kv.kv_len, K, pos_offset,
+                     c.head_dim / 2, log((double)c.rope_theta), depth, cs, kv.page_table,
+                     kv.max_pages_per_seq, kv.n_pages, c.page_size, row_page, status);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ RoPE + KV write
 // qkv row layout: [q heads | k heads | v heads], each head hd wide, fp32.
 // q (rotated, times log2(e)/sqrt(hd)) -> hi + lo bf16 [R, Hq*hd];
-// k (rotated) -> K page [slot][hd]; v -> V page transposed [hd][slot].
+// k (rotated) -> K page [slot][hd]; v -> V page transposed [hd][slot]
+// (rope_store.h).  A row's work is spread over gridDim.y workgroups (short
+// passes have few rows).
 __global__ void __launch_bounds__(256)
-k_rope_kv_write(const float* __restrict__ qkv, const float2* __restrict__ cs, int K,
-                int Hq, int Hkv, int hd, int pos_offset, const int32_t* __restrict__ kv_len,
-                const int32_t* __restrict__ page_table, int max_pages, int64_t n_pages,
-                int ps, uint16_t* __restrict__ k_layer, uint16_t* __restrict__ v_layer,
-                uint16_t* __restrict__ q_out, uint16_t* __restrict__ q_lo,
-                int32_t* __restrict__ status) {
+k_rope_kv_write(const float* __restrict__ qkv, RopeArgs ra) {
   const int r = blockIdx.x;
-  const int b = r / K, j = r % K;
-  const int half = hd / 2;
-  const int width = (Hq + 2 * Hkv) * hd;
-  const float q_scale = 1.4426950408889634f / sqrtf((float)hd);
+  const int half = ra.hd / 2;
+  const int width = (ra.Hq + 2 * ra.Hkv) * ra.hd;
   const float* row = qkv + (size_t)r * width;
-  const float2* c = cs + (size_t)r * half;
-  const int pos = kv_len[b] + pos_offset + j;
-  const int pidx = pos / ps, slot = pos % ps;
-  int page = -1;
-  if (pos >= 0 && pidx < max_pages) {
-    page = page_table[(size_t)b * max_pages + pidx];
-    if (page < 0 || page >= n_pages) {
-      if (threadIdx.x == 0 && status) atomicOr(status + b, UNO_DEV_BAD_PAGE);
-      page = -1;
-    }
-  } else if (threadIdx.x == 0 && status) {
-    atomicOr(status + b, UNO_DEV_CAPACITY);
-  }
-  // rotation pairs of q and k heads
-  const int n_pairs = (Hq + Hkv) * half;
-  // a row's work is spread over gridDim.y workgroups (short passes have few rows)
+  int slot;
+  const int page = rope_page(ra, r, &slot);
   const int t0 = blockIdx.y * blockDim.x + threadIdx.x, tstep = blockDim.x * gridDim.y;
+  const int n_pairs = (ra.Hq + ra.Hkv) * half;
   for (int t = t0; t < n_pairs; t += tstep) {
     const int head = t / half, i = t % half;
-    const float x1 = row[head * hd + i], x2 = row[head * hd + i + half];
-    const float2 a = c[i];
-    const float y1 = x1 * a.x - x2 * a.y;
-    const float y2 = x2 * a.x + x1 * a.y;
-    if (head < Hq) {
-      // q * log2(e)/sqrt(hd) (the attention works in base 2) as hi + lo bf16
-      // parts: the scores use both
-      const size_t o = (size_t)r * Hq * hd + head * hd;
-      const float z1 = y1 * q_scale, z2 = y2 * q_scale;
-      const uint16_t h1 = f32_to_bf16(z1), h2 = f32_to_bf16(z2);
-      q_out[o + i] = h1;
-      q_out[o + i + half] = h2;
-      q_lo[o + i] = f32_to_bf16(z1 - bf16_to_f32(h1));
-      q_lo[o + i + half] = f32_to_bf16(z2 - bf16_to_f32(h2));
-    } else if (page >= 0) {
-      const int g = head - Hq;
-      uint16_t* kp = k_layer + (((size_t)page * Hkv + g) * ps + slot) * hd;
-      kp[i] = f32_to_bf16(y1);
-      kp[i + half] = f32_to_bf16(y2);
-    }
+    rope_store_pair(ra, r, head, i, row[head * ra.hd + i], row[head * ra.hd + i + half], page,
+                    slot);
   }
-  if (page >= 0) {
-    for (int t = t0; t < Hkv * hd; t += tstep) {
-      const int g = t / hd, d = t % hd;
-      const float v = row[(Hq + Hkv) * hd + t];
-      v_layer[(((size_t)page * Hkv + g) * hd + d) * ps + slot] = f32_to_bf16(v);
-    }
-  }
+  if (page >= 0)
+    for (int t = t0; t < ra.Hkv * ra.hd; t += tstep)
+      rope_store_v(ra, t / ra.hd, t % ra.hd, row[(ra.Hq + ra.Hkv) * ra.hd + t], page, slot);
 }
 
-hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
-                                const uno_kv& kv, int layer, int B, int K, int pos_offset,
-                                bf16_raw_t* q_out, bf16_raw_t* q_lo, int32_t* status,
-                                hipStream_t s) {
-  const size_t layer_elems =
-      (size_t)kv.n_pages * c.n_kv_heads * c.page_size * c.head_dim;
-  uint16_t* kl = static_cast<uint16_t*>(kv.k_pages) + (size_t)layer * layer_elems;
-  uint16_t* vl = static_cast<uint16_t*>(kv.v_pages) + (size_t)layer * layer_elems;
-  const int R = B * K, split = R >= 256 ? 1 : R >= 64 ? 2 : 4;
-  hipLaunchKernelGGL(k_rope_kv_write, dim3(R, split), dim3(256), 0, s, qkv, cs, K, c.n_q_heads,
-                     c.n_kv_heads, c.head_dim, pos_offset, kv.kv_len, kv.page_table,
-                     kv.max_pages_per_seq, kv.n_pages, c.page_size, kl, vl, q_out, q_lo, status);
+RopeArgs make_rope_args(const uno_config& c, const float2* cs, const int2* row_page,
+                        const uno_kv& kv, int layer, int K, bf16_raw_t* q_out, bf16_raw_t* q_lo) {
+  const size_t layer_elems = (size_t)kv.n_pages * c.n_kv_heads * c.page_size * c.head_dim;
+  RopeArgs ra;
+  ra.cs = cs;
+  ra.row_page = row_page;
+  ra.K = K; ra.Hq = c.n_q_heads; ra.Hkv = c.n_kv_heads; ra.hd = c.head_dim; ra.ps = c.page_size;
+  ra.k_layer = static_cast<uint16_t*>(kv.k_pages) + (size_t)layer * layer_elems;
+  ra.v_layer = static_cast<uint16_t*>(kv.v_pages) + (size_t)layer * layer_elems;
+  ra.q_out = q_out; ra.q_lo = q_lo;
+  return ra;
+}
+
+hipError_t launch_rope_kv_write(const float* qkv, const RopeArgs& ra, int R, hipStream_t s) {
+  const int split = R >= 256 ? 1 : R >= 64 ? 2 : 4;
+  hipLaunchKernelGGL(k_rope_kv_write, dim3(R, split), dim3(256), 0, s, qkv, ra);
   return hipGetLastError();
 }
 

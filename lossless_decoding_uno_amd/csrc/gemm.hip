@@ -18,6 +18,7 @@
 // workgroups; a second kernel sums the splits in order (run-to-run identical).
 #include "uno_device.h"
 #include "uno_internal.h"
+#include "rope_store.h"
 
 namespace uno {
 
@@ -222,6 +223,46 @@ k_gemm_skinny_reduce(GemmArgs a, int gx, int gy, int splits) {
   if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
 }
 
+// Split-K reduction of a q|k|v product fused with RoPE and the K/V write:
+// one thread per output of a workgroup tile; for q and k the thread holding
+// channel i < hd/2 of a head also sums its partner i + hd/2 (hd/32 column
+// tiles on) and stores the rotated pair; v channels are stored as they are.
+template <int MT, int NT>
+__global__ void __launch_bounds__(256)
+k_gemm_skinny_reduce_rope(GemmArgs a, int gx, int gy, int splits) {
+  constexpr int kTile = MT * NT * 256;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= gx * gy * kTile) return;
+  const int wg = g / kTile, e = g % kTile;
+  const int bx = wg % gx, by = wg / gx;
+  const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
+  const SegView sv = pick_segment(a, bx * NT);
+  const int nl = sv.n0 + t * 16 + (ln & 15);
+  const int m = by * MT * 16 + mt * 16 + 4 * (ln >> 4) + i;
+  if (m >= a.M || nl >= sv.n) return;
+  const RopeArgs& ra = a.rope;
+  const int col = sv.col_base + nl, hd = ra.hd, half = hd / 2;
+  const int head = col / hd, ch = col % hd;
+  const bool rot = head < ra.Hq + ra.Hkv;
+  if (rot && ch >= half) return;                 // stored by its partner
+  auto sum_at = [&](int wgi, int ei) {
+    float v = a.part[(size_t)wgi * kTile + ei];
+    for (int z = 1; z < splits; ++z) v += a.part[((size_t)z * gx * gy + wgi) * kTile + ei];
+    return v;
+  };
+  const float x = sum_at(wg, e);
+  int slot;
+  const int page = rope_page(ra, m, &slot);
+  if (!rot) {
+    rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, x, page, slot);
+    return;
+  }
+  const int tp = bx * NT + t + half / 16;        // partner's global 16-column tile
+  const int ep = mt * NT * 256 + (tp % NT) * 256 + (e & 255);
+  const float xp = sum_at(by * gx + tp / NT, ep);
+  rope_store_pair(ra, m, head, ch, x, xp, page, slot);
+}
+
 // Split-K reduction of a residual-add projection over whole rows, fused with
 // the RMSNorm that follows it: one workgroup (16 waves) per row m sums each
 // column's splits in split order, adds the sum into the residual row (a.out),
@@ -325,6 +366,12 @@ static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
 template <int MT, int NT>
 static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
+  if (p.splits > 1 && a.rope_fuse) {
+    const int n = p.gx * p.gy * MT * NT * 256;
+    hipLaunchKernelGGL((k_gemm_skinny_reduce_rope<MT, NT>), dim3((n + 255) / 256), dim3(256), 0,
+                       s, a, p.gx, p.gy, p.splits);
+    return;
+  }
   if (p.splits > 1) {
     if (fuse_norm(a, p)) {
       hipLaunchKernelGGL((k_gemm_skinny_reduce_norm<MT, NT>), dim3(a.M), dim3(kRedNormThreads), 0,
@@ -337,9 +384,10 @@ static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   }
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped) {
   const SkinnyPlan p = plan_skinny(a);
   if (normed) *normed = fuse_norm(a, p);
+  if (roped) *roped = a.rope_fuse && p.splits > 1;
   switch (p.mt * 8 + p.nt) {
     case 8 + 4: launch_sk<1, 4>(a, p, s); break;
     case 8 + 2: launch_sk<1, 2>(a, p, s); break;
@@ -834,11 +882,78 @@ k_gemm_splitk_reduce_swiglu(GemmArgs a, int m_tiles, int n_tiles, int splits, in
       out[(size_t)(mb + k) * a.ldo + c] = f32_to_bf16(gv[k] / (1.0f + __expf(-gv[k])) * uv[k]);
 }
 
+// Split-K reduction of a q|k|v product (every tile split) fused with RoPE and
+// the K/V write: one thread per float4 (four rows of one column) of a partial
+// tile; for q and k the thread holding channel i < hd/2 of a head also sums the
+// float4 of channel i + hd/2 (same tile: segments and tiles hold whole heads).
 template <class C>
-static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
+__global__ void __launch_bounds__(256)
+k_gemm_splitk_reduce_rope(GemmArgs a, int m_tiles, int n_tiles, int splits) {
+  constexpr int Q = C::kTileFloats / 4;
+  const int rem = m_tiles * n_tiles;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= rem * Q) return;
+  const int tr = g / Q, q = g % Q;
+  const int mt = tr % m_tiles, nt = tr / m_tiles;
+  const int l = q & 63;
+  int r = q >> 6;
+  const int e4 = r & 3;
+  r >>= 2;
+  const int j = r % C::TJ;
+  r /= C::TJ;
+  const int i = r % C::TI, w = r / C::TI;
+  const int wm = w / C::WN, wn = w % C::WN;
+  const SegView sv = pick_segment(a, nt * (C::BN / 16));
+  const int nn = wn * C::TN + j * 32 + (l & 31);        // column in the tile
+  const int nl = sv.n0 + nn;
+  if (nl >= sv.n) return;
+  const RopeArgs& ra = a.rope;
+  const int col = sv.col_base + nl, hd = ra.hd, half = hd / 2;
+  const int head = col / hd, ch = col % hd;
+  const bool rot = head < ra.Hq + ra.Hkv;
+  if (rot && ch >= half) return;                       // stored by its partner
+  const float4* src = reinterpret_cast<const float4*>(a.part);
+  auto sum_at = [&](int qi) {
+    float4 t = src[(size_t)tr * Q + qi];
+    for (int z = 1; z < splits; ++z) {
+      const float4 u = src[((size_t)z * rem + tr) * Q + qi];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    return t;
+  };
+  const float4 x = sum_at(q);
+  float4 xp = x;
+  if (rot) {
+    const int np = nn + half;
+    const int wp = wm * C::WN + np / C::TN, jp = (np % C::TN) / 32;
+    xp = sum_at((((wp * C::TI + i) * C::TJ + jp) * 4 + e4) * 64 + l);
+  }
+  const int mb = mt * C::BM + wm * C::TM + i * 32 + e4 * 8 + (l >> 5) * 4;
+  const float xv[4] = {x.x, x.y, x.z, x.w}, pv[4] = {xp.x, xp.y, xp.z, xp.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int m = mb + c;
+    if (m >= a.M) break;
+    int slot;
+    const int page = rope_page(ra, m, &slot);
+    if (rot) rope_store_pair(ra, m, head, ch, xv[c], pv[c], page, slot);
+    else rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, xv[c], page, slot);
+  }
+}
+
+template <class C>
+static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_t s,
+                                 bool* roped) {
   const int rem = p.m_tiles * p.n_tiles - p.n_full;
   hipLaunchKernelGGL(k_gemm_big<C>, dim3(p.n_full + rem * p.splits), dim3(C::kThreads), C::kLds,
                      s, a, p.m_tiles, p.n_tiles, p.splits, p.n_full);
+  if (a.rope_fuse && p.splits > 1 && p.n_full == 0) {
+    if (roped) *roped = true;
+    const int n = rem * (C::kTileFloats / 4);
+    hipLaunchKernelGGL(k_gemm_splitk_reduce_rope<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
+                       p.m_tiles, p.n_tiles, p.splits);
+    return hipGetLastError();
+  }
   if (p.splits > 1 && a.epi == EPI_SWIGLU) {
     const int n = rem * (C::kTileFloats / 8);
     hipLaunchKernelGGL(k_gemm_splitk_reduce_swiglu<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
@@ -851,11 +966,11 @@ static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_
   return hipGetLastError();
 }
 
-static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s) {
+static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s, bool* roped) {
   switch (p.cfg) {
-    case CFG_L: return launch_big_cfg<big::CfgL>(a, p, s);
-    case CFG_M: return launch_big_cfg<big::CfgM>(a, p, s);
-    default: return launch_big_cfg<big::CfgS>(a, p, s);
+    case CFG_L: return launch_big_cfg<big::CfgL>(a, p, s, roped);
+    case CFG_M: return launch_big_cfg<big::CfgM>(a, p, s, roped);
+    default: return launch_big_cfg<big::CfgS>(a, p, s, roped);
   }
 }
 
@@ -866,14 +981,15 @@ bool gemm_swiglu_ok(const GemmArgs& a) {
   return a.epi == EPI_SWIGLU && a.M > 64 && plan_big(a).cfg >= 0;
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped) {
   if (normed) *normed = false;
+  if (roped) *roped = false;
   if (a.epi == EPI_SWIGLU && !gemm_swiglu_ok(a)) return hipErrorInvalidValue;
   if (a.M > 64) {
     const BigPlan p = plan_big(a);
-    if (p.cfg >= 0) return launch_big(a, p, s);
+    if (p.cfg >= 0) return launch_big(a, p, s, roped);
   }
-  return launch_gemm_skinny(a, s, normed);
+  return launch_gemm_skinny(a, s, normed, roped);
 }
 
 }  // namespace uno

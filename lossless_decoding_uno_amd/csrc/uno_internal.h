@@ -44,16 +44,17 @@ hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float
                           bf16_raw_t* out, hipStream_t s);
 // cos/sin table [R, head_dim/2] (fp32, angles evaluated in fp64) for the rows'
 // absolute positions kv_len[b] + pos_offset + j, or kv_len[b] + pos_offset +
-// depth[r] for the rows of a token tree (depth != null).
-hipError_t launch_rope_table(const int32_t* kv_len, int B, int K, int pos_offset, int half,
-                             float theta, const int32_t* depth, float2* cs, hipStream_t s);
+// depth[r] for the rows of a token tree (depth != null); and each row's K/V
+// slot kv_len[b] + pos_offset + j as (page, slot in page) in row_page [R]
+// (page -1, flagged in status, outside the table or the pool).
+hipError_t launch_rope_table(const uno_config& c, const uno_kv& kv, int B, int K, int pos_offset,
+                             const int32_t* depth, float2* cs, int2* row_page, int32_t* status,
+                             hipStream_t s);
 // RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]); q, scaled
 // by log2(e)/sqrt(hd), -> two bf16 planes [R, Hq*hd] (hi and the rounding
-// remainder lo), k/v (bf16) -> paged cache at the rows' positions.
-hipError_t launch_rope_kv_write(const uno_config& c, const float* qkv, const float2* cs,
-                                const uno_kv& kv, int layer, int B, int K, int pos_offset,
-                                bf16_raw_t* q_out, bf16_raw_t* q_lo, int32_t* status,
-                                hipStream_t s);
+// remainder lo), k/v (bf16) -> paged cache at the rows' slots.
+struct RopeArgs;
+hipError_t launch_rope_kv_write(const float* qkv, const RopeArgs& ra, int R, hipStream_t s);
 // act = silu(g) * u, gu fp32 [R, 2F] (gate then up) -> bf16 [R, F]
 hipError_t launch_silu_mul(const float* gu, int R, int F, bf16_raw_t* act, hipStream_t s);
 hipError_t launch_kv_commit(int32_t* kv_len, const int32_t* accept_len, int B, int K,
@@ -80,6 +81,20 @@ hipError_t launch_tree_walk(const int32_t* node_tokens, const int32_t* node_pare
 hipError_t launch_tree_commit(const uno_config& c, const uno_kv& kv, const int32_t* path,
                               const int32_t* accept_len, int B, int K, int32_t* status,
                               hipStream_t s);
+
+// RoPE + paged K/V write of q|k|v rows (row r's slot and page in row_page,
+// (cos, sin) of its position in cs, both from launch_rope_table).
+struct RopeArgs {
+  const float2* cs;      // [R, hd/2]
+  const int2* row_page;  // [R] (page or -1, slot in page), from launch_rope_table
+  int K, Hq, Hkv, hd, ps;
+  uint16_t* k_layer;     // this layer's K pages
+  uint16_t* v_layer;     // this layer's V pages
+  uint16_t* q_out;       // [R, Hq*hd] bf16 high part of q * log2(e)/sqrt(hd)
+  uint16_t* q_lo;        // [R, Hq*hd] bf16 remainder
+};
+RopeArgs make_rope_args(const uno_config& c, const float2* cs, const int2* row_page,
+                        const uno_kv& kv, int layer, int K, bf16_raw_t* q_out, bf16_raw_t* q_lo);
 
 // ---------------------------------------------------------------- GEMM
 // Y[m, n] = sum_k X[m, k] W[n, k]  (+ LoRA)  for up to 3 column segments.
@@ -117,12 +132,19 @@ struct GemmArgs {
   const float* norm_gain;
   uint16_t* norm_out;
   float norm_eps;
+  // optional RoPE + K/V write of a q|k|v product (EPI_STORE_F32, whole heads
+  // per segment): when every tile is split along K, the split-K reduction
+  // stores through `rope` instead of writing `out`; launch_gemm reports through
+  // *roped whether it did
+  int rope_fuse;
+  RopeArgs rope;
 };
 // split-K scratch carved per pass: 128 MB for passes of more than 64 rows
 // (tiled kernel), 4 MB for up to 64 (skinny kernel)
 constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr,
+                       bool* roped = nullptr);
 // whether launch_gemm can run this EPI_SWIGLU product (the tiled kernel takes it)
 bool gemm_swiglu_ok(const GemmArgs& a);
 
