@@ -21,8 +21,12 @@ traffic per launch that rocprofv3 counters measured for the same kernel source
 (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same counters give for a
 plain copy of known size, `--calibrate-copy`), or null when the kernel source
 has changed since.  `roofline_gemm` is the MFMA fraction of the projection
-GEMMs of both passes (flops / their probe-step time).  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.
+GEMMs of both passes (flops / their probe-step time).  `verify_step` is the
+verify pass as a whole (36 layers + LM head, timed with torch events around it
+in every timed step): its algorithmic HBM bytes (every AR weight once, every
+cached K/V entry the rows may see once per layer, the block's own K/V written,
+the fp32 logits written) / its summed duration.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 """
 import hashlib
 import argparse
@@ -119,11 +123,15 @@ class Workload:
         self.kv_len_host = np.full(B, ctx, dtype=np.int64)
         self.model = model
 
-    def step(self, i):
+    def step(self, i, verify_events=None):
         U = self.U
         U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, self.inv_t, 0, self.step_ctr,
                       self.zq, self.d, self.ws)
+        if verify_events is not None:
+            verify_events[0].record()
         U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws)
+        if verify_events is not None:
+            verify_events[1].record()
         U.spec_accept(self.zq, self.zp, self.d, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e,
                       self.aws, forced_accept=self.forced[i])
         U.kv_commit(self.kv, self.a, self.K, self.step_ctr)
@@ -141,6 +149,22 @@ class Workload:
 
     def advance_host(self, i):
         self.kv_len_host += self.forced_host[i].astype(np.int64) + 1
+
+    def verify_bytes(self):
+        """Algorithmic HBM bytes of the verify pass at the current kv_len: every
+        AR weight once (layers + LM head), every cached K/V entry the rows may
+        see once per layer, the block's own K/V written, the logits written."""
+        cfg = self.cfg
+        D, F, V = cfg["d_model"], cfg["d_ffn"], cfg["vocab"]
+        qd = cfg["n_q_heads"] * cfg["head_dim"]
+        kd = cfg["n_kv_heads"] * cfg["head_dim"]
+        per_layer_w = 2 * (D * (qd + 2 * kd) + qd * D + 2 * F * D + F * D)
+        weights = cfg["n_layers"] * per_layer_w + 2 * V * D
+        per_tok = cfg["n_kv_heads"] * cfg["head_dim"] * 2 * 2          # K and V, one layer
+        kv_read = cfg["n_layers"] * int(np.sum(self.kv_len_host + 1 + self.K)) * per_tok
+        kv_write = cfg["n_layers"] * self.B * self.K * per_tok
+        logits = self.B * self.K * V * 4
+        return weights + kv_read + kv_write + logits
 
 
 def gemm_flops_per_pass(cfg, R, draft):
@@ -214,16 +238,22 @@ def run_timed(W, steps, warmup, torch, timer=None):
     wall0 = time.perf_counter()
     t0.record()
     attn_bytes = []
+    vev, vbytes = [], 0
     for i in range(warmup, warmup + steps):
         db, vb = W.attn_bytes(i)
         attn_bytes += [db] * W.cfg["n_layers"] + [vb] * W.cfg["n_layers"]
-        W.step(i)
+        vbytes += W.verify_bytes()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        vev.append(ev)
+        W.step(i, ev)
         W.advance_host(i)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     used = timer.disarm() if timer is not None else 0
     ms = t0.elapsed_time(t1)
+    W.verify_ms = sum(a.elapsed_time(b) for a, b in vev)
+    W.verify_bytes_total = vbytes
     tokens = int(np.sum(W.forced_host[warmup:warmup + steps].astype(np.int64) + 1))
     got = W.kv.kv_len.cpu().numpy()
     assert np.array_equal(got, W.kv_len_host), "device kv_len diverged from the forced schedule"
@@ -569,6 +599,11 @@ def main():
            "roofline": roof,
            "roofline_gemm": roof_gemm,
            "measured_ceilings": ceil,
+           "verify_step": {"ms_per_step": round(W.verify_ms / args.steps, 3),
+                           "hbm_GBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9, 1),
+                           "frac_of_8TBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9
+                                                  / HBM_PEAK_GBS, 4),
+                           "algorithmic_GB_per_step": round(W.verify_bytes_total / args.steps / 1e9, 3)},
            "kernel_class_ms_per_step": {k: round(v, 3) for k, v in classes.items()},
            "forward_passes_per_s": round(2 * args.steps / (ms / 1e3), 2),
            "wall_s_timed": round(wall, 3)}
@@ -580,7 +615,10 @@ def main():
         ms1, _, tok1, _, _, _ = run_timed(W1, 40, 5, torch)
         out["secondary"] = {"workload": "qwen3-8b-shape b1 ctx1024 K%d forced" % K,
                             "value": round(tok1 / (ms1 / 1e3), 1), "unit": "accepted tokens/s",
-                            "ms_per_step": round(ms1 / 40, 3)}
+                            "ms_per_step": round(ms1 / 40, 3),
+                            "verify_step_hbm_GBps": round(W1.verify_bytes_total /
+                                                          (W1.verify_ms / 1e3) / 1e9, 1),
+                            "verify_ms_per_step": round(W1.verify_ms / 40, 3)}
         del W1
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
