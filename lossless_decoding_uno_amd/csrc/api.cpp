@@ -141,9 +141,6 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
 
 int check_layers(const uno_config& c, const uno_weights* w, bool lora) {
   if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->layers) return UNO_ERR_INVALID_ARG;
-  // set when a residual projection's split-K reduction also wrote the RMSNorm
-  // of the updated rows into W.xn (the stand-alone norm is then skipped)
-  bool normed = false;
   for (int li = 0; li < c.n_layers; ++li) {
     const uno_layer_weights& L = w->layers[li];
     if (!L.attn_norm || !L.mlp_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.wgate || !L.wup ||

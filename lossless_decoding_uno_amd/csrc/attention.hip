@@ -418,16 +418,46 @@ k_attn_merge(AttnArgs a) {
   const int qg = qr / QPW, ql = qr % QPW;
   const int NS = a.plan.n_wave_splits;
   const size_t base = ((size_t)bg * a.plan.n_qgroups + qg) * NS;
-  float M = -INFINITY;
-  for (int s = 0; s < NS; ++s) M = fmaxf(M, a.part_ml[((base + s) * 128 + ql) * 2]);
-  float L = 0.f, acc = 0.f;
   const int d = threadIdx.x;
-  for (int s = 0; s < NS; ++s) {
-    const float* ml = a.part_ml + ((base + s) * 128 + ql) * 2;
-    if (ml[0] == -INFINITY) continue;
-    const float f = exp2f(ml[0] - M);
-    L += ml[1] * f;
-    acc += a.part_o[((base + s) * 128 + ql) * HD + d] * f;
+  // the partials are combined in split order; their loads go out eight
+  // splits at a time so that the latencies overlap
+  constexpr int CH = 8;
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  float pm[CH], pl[CH], po[CH];
+  auto load = [&](int s0, bool with_o) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const bool ok = s0 + u < NS;
+      const size_t pr = (base + s0 + u) * 128 + ql;
+      pm[u] = ok ? a.part_ml[pr * 2] : -INFINITY;
+      pl[u] = ok ? a.part_ml[pr * 2 + 1] : 0.f;
+      po[u] = ok && with_o ? a.part_o[pr * HD + d] : 0.f;
+    }
+  };
+  auto accumulate = [&]() {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (pm[u] == -INFINITY) continue;
+      const float f = exp2f(pm[u] - M);
+      L += pl[u] * f;
+      acc += po[u] * f;
+    }
+  };
+  if (NS <= CH) {
+    load(0, true);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) M = fmaxf(M, pm[u]);
+    accumulate();
+  } else {
+    for (int s0 = 0; s0 < NS; s0 += CH) {
+      load(s0, false);
+#pragma unroll
+      for (int u = 0; u < CH; ++u) M = fmaxf(M, pm[u]);
+    }
+    for (int s0 = 0; s0 < NS; s0 += CH) {
+      load(s0, true);
+      accumulate();
+    }
   }
   const int j = qr / G, hh = qr % G;
   a.out[((size_t)(b * a.K + j) * a.Hq + g * G + hh) * HD + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);

@@ -74,6 +74,43 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int m, int n, float
   }
 }
 
+// Split-K sums p[0] + p[zs] + ... + p[(splits - 1) zs], added in split order
+// (run-to-run identical); the loads go out a chunk at a time so that their
+// latencies overlap instead of adding up.
+__device__ __forceinline__ float sum_splits(const float* p, size_t zs, int splits) {
+  float v = p[0];
+  for (int z0 = 1; z0 < splits; z0 += 8) {
+    float q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = z0 + u < splits ? p[(size_t)(z0 + u) * zs] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) v += q[u];
+  }
+  return v;
+}
+__device__ __forceinline__ float4 sum_splits4(const float4* p, size_t zs, int splits) {
+  float4 v = p[0];
+  for (int z0 = 1; z0 < splits; z0 += 4) {
+    float4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      q[u] = z0 + u < splits ? p[(size_t)(z0 + u) * zs] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (z0 + u < splits) {
+        v.x += q[u].x; v.y += q[u].y; v.z += q[u].z; v.w += q[u].w;
+      }
+  }
+  return v;
+}
+// output columns of all segments together
+__host__ __device__ __forceinline__ int skinny_cols(const GemmArgs& a) {
+  int n = 0;
+  for (int i = 0; i < a.n_seg; ++i) n += a.seg[i].n;
+  return n;
+}
+
 constexpr int kSkWaves = 8;
 
 // MT: 16-row tiles of X per workgroup; NT: 16-column tiles of W per
@@ -186,18 +223,28 @@ k_gemm_skinny(GemmArgs a) {
   __syncthreads();
   const float* redf = reinterpret_cast<const float*>(red);
   constexpr int kTile = MT * NT * 256;   // outputs of this workgroup
-  float* part = splits > 1
-      ? a.part + ((size_t)zs * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x) * kTile
-      : nullptr;
+  // split K: fp32 partial Y, row-major [split][M][ncols] (ncols = all segments'
+  // columns), so that the reductions read whole rows
+  if (splits > 1) {
+    const int ncols = skinny_cols(a);
+    float* part = a.part + (size_t)zs * a.M * ncols;
+    for (int e = threadIdx.x; e < kTile; e += kSkWaves * 64) {
+      const int r = e / (NT * 16), cl = e % (NT * 16);      // row / column in the tile
+      const int mt = r >> 4, rr = r & 15, t = cl >> 4, ln = (rr >> 2) * 16 + (cl & 15);
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kSkWaves; ++ww)
+        v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + (rr & 3)];
+      const int m = m0 + r, nl = sv.n0 + cl;
+      if (m < a.M && nl < sv.n) part[(size_t)m * ncols + sv.col_base + nl] = v;
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < kTile; e += kSkWaves * 64) {
     const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
     float v = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kSkWaves; ++ww) v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + i];
-    if (part) {
-      part[e] = v;
-      continue;
-    }
     const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
     const int nl = sv.n0 + t * 16 + (ln & 15);
     if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
@@ -205,61 +252,40 @@ k_gemm_skinny(GemmArgs a) {
 }
 
 // Sum the skinny kernel's split-K partials in split order and apply the
-// epilogue; one thread per output of a workgroup tile.
-template <int MT, int NT>
+// epilogue; one thread per output (m, column).
 __global__ void __launch_bounds__(256)
-k_gemm_skinny_reduce(GemmArgs a, int gx, int gy, int splits) {
-  constexpr int kTile = MT * NT * 256;
+k_gemm_skinny_reduce(GemmArgs a, int splits) {
+  const int ncols = skinny_cols(a);
   const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= gx * gy * kTile) return;
-  const int wg = g / kTile, e = g % kTile;
-  const int bx = wg % gx, by = wg / gx;
-  float v = a.part[(size_t)wg * kTile + e];
-  for (int z = 1; z < splits; ++z) v += a.part[((size_t)z * gx * gy + wg) * kTile + e];
-  const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
-  const SegView sv = pick_segment(a, bx * NT);
-  const int m = by * MT * 16 + mt * 16 + 4 * (ln >> 4) + i;
-  const int nl = sv.n0 + t * 16 + (ln & 15);
-  if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
+  if (g >= a.M * ncols) return;
+  const float v = sum_splits(a.part + g, (size_t)a.M * ncols, splits);
+  store_out(a, g / ncols, g % ncols, v);
 }
 
 // Split-K reduction of a q|k|v product fused with RoPE and the K/V write:
-// one thread per output of a workgroup tile; for q and k the thread holding
-// channel i < hd/2 of a head also sums its partner i + hd/2 (hd/32 column
-// tiles on) and stores the rotated pair; v channels are stored as they are.
-template <int MT, int NT>
+// one thread per output (m, column); for q and k the thread holding channel
+// i < hd/2 of a head also sums its partner i + hd/2 and stores the rotated
+// pair; v channels are stored as they are.
 __global__ void __launch_bounds__(256)
-k_gemm_skinny_reduce_rope(GemmArgs a, int gx, int gy, int splits) {
-  constexpr int kTile = MT * NT * 256;
+k_gemm_skinny_reduce_rope(GemmArgs a, int splits) {
+  const int ncols = skinny_cols(a);
   const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= gx * gy * kTile) return;
-  const int wg = g / kTile, e = g % kTile;
-  const int bx = wg % gx, by = wg / gx;
-  const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
-  const SegView sv = pick_segment(a, bx * NT);
-  const int nl = sv.n0 + t * 16 + (ln & 15);
-  const int m = by * MT * 16 + mt * 16 + 4 * (ln >> 4) + i;
-  if (m >= a.M || nl >= sv.n) return;
+  if (g >= a.M * ncols) return;
+  const int m = g / ncols, col = g % ncols;
   const RopeArgs& ra = a.rope;
-  const int col = sv.col_base + nl, hd = ra.hd, half = hd / 2;
+  const int hd = ra.hd, half = hd / 2;
   const int head = col / hd, ch = col % hd;
   const bool rot = head < ra.Hq + ra.Hkv;
   if (rot && ch >= half) return;                 // stored by its partner
-  auto sum_at = [&](int wgi, int ei) {
-    float v = a.part[(size_t)wgi * kTile + ei];
-    for (int z = 1; z < splits; ++z) v += a.part[((size_t)z * gx * gy + wgi) * kTile + ei];
-    return v;
-  };
-  const float x = sum_at(wg, e);
+  const size_t zs = (size_t)a.M * ncols;
+  const float x = sum_splits(a.part + g, zs, splits);
   int slot;
   const int page = rope_page(ra, m, &slot);
   if (!rot) {
     rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, x, page, slot);
     return;
   }
-  const int tp = bx * NT + t + half / 16;        // partner's global 16-column tile
-  const int ep = mt * NT * 256 + (tp % NT) * 256 + (e & 255);
-  const float xp = sum_at(by * gx + tp / NT, ep);
+  const float xp = sum_splits(a.part + g + half, zs, splits);
   rope_store_pair(ra, m, head, ch, x, xp, page, slot);
 }
 
@@ -270,10 +296,8 @@ k_gemm_skinny_reduce_rope(GemmArgs a, int gx, int gy, int splits) {
 // owns the columns 4t..4t+3 (+ 4096); the sum of squares is reduced in a fixed
 // order.
 constexpr int kRedNormThreads = 1024;
-template <int MT, int NT>
 __global__ void __launch_bounds__(kRedNormThreads)
-k_gemm_skinny_reduce_norm(GemmArgs a, int gx, int gy, int splits) {
-  constexpr int kTile = MT * NT * 256;
+k_gemm_skinny_reduce_norm(GemmArgs a, int splits) {
   constexpr int kStep = kRedNormThreads * 4;
   constexpr int kMaxIt = 2;                    // D <= 8192
   constexpr int kW = kRedNormThreads / UNO_WAVE;
@@ -281,27 +305,17 @@ k_gemm_skinny_reduce_norm(GemmArgs a, int gx, int gy, int splits) {
   const int m = blockIdx.x;
   const int D = a.seg[0].n;
   float* h = static_cast<float*>(a.out) + (size_t)m * a.ldo;
-  const int by = m / (MT * 16), mt = (m % (MT * 16)) / 16, mr = m % 16;
-  const int ebase = mt * NT * 256 + (mr >> 2) * 64 + (mr & 3);
+  const float4* pr = reinterpret_cast<const float4*>(a.part + (size_t)m * D);
+  const size_t zs4 = (size_t)a.M * D / 4;
   float4 hv[kMaxIt];
   float ss = 0.f;
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
     const int i = threadIdx.x * 4 + it * kStep;
     if (i >= D) break;
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int n = i + c;
-      const int bx = n / (16 * NT), t = (n >> 4) % NT;
-      const size_t e = ebase + t * 256 + (n & 15) * 4;
-      const size_t wg = (size_t)by * gx + bx;
-      float sum = a.part[wg * kTile + e];
-      for (int z = 1; z < splits; ++z) sum += a.part[((size_t)z * gx * gy + wg) * kTile + e];
-      v[c] = sum;
-    }
+    const float4 v = sum_splits4(pr + i / 4, zs4, splits);
     float4 x = *reinterpret_cast<const float4*>(h + i);
-    x.x += v[0]; x.y += v[1]; x.z += v[2]; x.w += v[3];
+    x.x += v.x; x.y += v.y; x.z += v.z; x.w += v.w;
     *reinterpret_cast<float4*>(h + i) = x;
     hv[it] = x;
     ss += (x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
@@ -350,9 +364,10 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   const int steps = a.Kd >> 5;
   const size_t tile = (size_t)p.mt * p.nt * 256;
   p.splits = 1;
+  const size_t per_split = (size_t)a.M * skinny_cols(a);
   if (a.part)
     while (p.gx * p.gy * p.splits < 512 && steps / (p.splits * 2) >= kSkWaves &&
-           (size_t)p.gx * p.gy * p.splits * 2 * tile <= a.part_floats)
+           (size_t)p.splits * 2 * per_split <= a.part_floats)
       p.splits *= 2;
   return p;
 }
@@ -366,22 +381,16 @@ static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
 template <int MT, int NT>
 static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
-  if (p.splits > 1 && a.rope_fuse) {
-    const int n = p.gx * p.gy * MT * NT * 256;
-    hipLaunchKernelGGL((k_gemm_skinny_reduce_rope<MT, NT>), dim3((n + 255) / 256), dim3(256), 0,
-                       s, a, p.gx, p.gy, p.splits);
-    return;
-  }
-  if (p.splits > 1) {
-    if (fuse_norm(a, p)) {
-      hipLaunchKernelGGL((k_gemm_skinny_reduce_norm<MT, NT>), dim3(a.M), dim3(kRedNormThreads), 0,
-                         s, a, p.gx, p.gy, p.splits);
-      return;
-    }
-    const int n = p.gx * p.gy * MT * NT * 256;
-    hipLaunchKernelGGL((k_gemm_skinny_reduce<MT, NT>), dim3((n + 255) / 256), dim3(256), 0, s, a,
-                       p.gx, p.gy, p.splits);
-  }
+  if (p.splits == 1) return;
+  const int n = a.M * skinny_cols(a);
+  if (a.rope_fuse)
+    hipLaunchKernelGGL(k_gemm_skinny_reduce_rope, dim3((n + 255) / 256), dim3(256), 0, s, a,
+                       p.splits);
+  else if (fuse_norm(a, p))
+    hipLaunchKernelGGL(k_gemm_skinny_reduce_norm, dim3(a.M), dim3(kRedNormThreads), 0, s, a,
+                       p.splits);
+  else
+    hipLaunchKernelGGL(k_gemm_skinny_reduce, dim3((n + 255) / 256), dim3(256), 0, s, a, p.splits);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped) {
@@ -732,11 +741,7 @@ k_gemm_splitk_reduce(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_ful
   const int tile = n_full + tr;
   const int mt = tile % m_tiles, nt = tile / m_tiles;
   const float4* src = reinterpret_cast<const float4*>(a.part);
-  float4 t = src[(size_t)tr * Q + q];
-  for (int z = 1; z < splits; ++z) {
-    const float4 u = src[((size_t)z * rem + tr) * Q + q];
-    t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-  }
+  const float4 t = sum_splits4(src + (size_t)tr * Q + q, (size_t)rem * Q, splits);
   // q = (((w * TI + i) * TJ + j) * 4 + e4) * 64 + l
   const int l = q & 63;
   int r = q >> 6;
@@ -863,13 +868,8 @@ k_gemm_splitk_reduce_swiglu(GemmArgs a, int m_tiles, int n_tiles, int splits, in
   const int q = (((w * C::TI + i) * C::TJ + j) * 4 + e4) * 64 + l;
   const int qu = ((((w + HW) * C::TI + i) * C::TJ + j) * 4 + e4) * 64 + l;
   const float4* src = reinterpret_cast<const float4*>(a.part);
-  float4 gs = src[(size_t)tr * Q + q], us = src[(size_t)tr * Q + qu];
-  for (int z = 1; z < splits; ++z) {
-    const float4 gz = src[((size_t)z * rem + tr) * Q + q];
-    const float4 uz = src[((size_t)z * rem + tr) * Q + qu];
-    gs.x += gz.x; gs.y += gz.y; gs.z += gz.z; gs.w += gz.w;
-    us.x += uz.x; us.y += uz.y; us.z += uz.z; us.w += uz.w;
-  }
+  const float4 gs = sum_splits4(src + (size_t)tr * Q + q, (size_t)rem * Q, splits);
+  const float4 us = sum_splits4(src + (size_t)tr * Q + qu, (size_t)rem * Q, splits);
   const int tile = n_full + tr;
   const int mt = tile % m_tiles, nt = tile / m_tiles;
   const int c = nt * (C::BN / 2) + wg * C::TN + j * 32 + (l & 31);
@@ -913,14 +913,7 @@ k_gemm_splitk_reduce_rope(GemmArgs a, int m_tiles, int n_tiles, int splits) {
   const bool rot = head < ra.Hq + ra.Hkv;
   if (rot && ch >= half) return;                       // stored by its partner
   const float4* src = reinterpret_cast<const float4*>(a.part);
-  auto sum_at = [&](int qi) {
-    float4 t = src[(size_t)tr * Q + qi];
-    for (int z = 1; z < splits; ++z) {
-      const float4 u = src[((size_t)z * rem + tr) * Q + qi];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-    }
-    return t;
-  };
+  auto sum_at = [&](int qi) { return sum_splits4(src + (size_t)tr * Q + qi, (size_t)rem * Q, splits); };
   const float4 x = sum_at(q);
   float4 xp = x;
   if (rot) {
