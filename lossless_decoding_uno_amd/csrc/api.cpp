@@ -279,12 +279,16 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.epi = EPI_SWIGLU; g.out = W.act; g.ldo = F;
       const bool fused = adjacent && gemm_swiglu_ok(g);
       if (!fused) {
+        // two segments; a split product applies SwiGLU in its reduction
         g.seg[1] = GemmSeg{bp(L.wup), F, lg ? bp(L.lora_b[P_UP]) : nullptr, r};
         g.n_seg = 2;
         g.epi = EPI_STORE_F32; g.out = W.gu; g.ldo = 2 * F;
+        g.act_out = W.act;
       }
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s); }, UNO_TIME_GEMM_GATE_UP));
-      if (!fused) UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
+      bool swiglued = false;
+      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, nullptr, nullptr, &swiglued); },
+                    UNO_TIME_GEMM_GATE_UP));
+      if (!fused && !swiglued) UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
     }
     if (ld) {
       const void* a1[1] = {L.lora_a[P_DOWN]};

@@ -289,6 +289,24 @@ k_gemm_skinny_reduce_rope(GemmArgs a, int splits) {
   rope_store_pair(ra, m, head, ch, x, xp, page, slot);
 }
 
+// Split-K reduction of a [gate | up] product fused with SwiGLU: one thread per
+// four adjacent act columns of one row.
+__global__ void __launch_bounds__(256)
+k_gemm_skinny_reduce_swiglu(GemmArgs a, int splits) {
+  const int F = a.seg[0].n, ncols = 2 * F;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= a.M * (F / 4)) return;
+  const int m = g / (F / 4), c = (g % (F / 4)) * 4;
+  const float4* pr = reinterpret_cast<const float4*>(a.part + (size_t)m * ncols + c);
+  const size_t zs4 = (size_t)a.M * ncols / 4;
+  const float4 gv = sum_splits4(pr, zs4, splits);
+  const float4 uv = sum_splits4(pr + F / 4, zs4, splits);
+  uint2 pk;
+  pk.x = pack_bf16x2(gv.x / (1.0f + __expf(-gv.x)) * uv.x, gv.y / (1.0f + __expf(-gv.y)) * uv.y);
+  pk.y = pack_bf16x2(gv.z / (1.0f + __expf(-gv.z)) * uv.z, gv.w / (1.0f + __expf(-gv.w)) * uv.w);
+  *reinterpret_cast<uint2*>(a.act_out + (size_t)m * F + c) = pk;
+}
+
 // Split-K reduction of a residual-add projection over whole rows, fused with
 // the RMSNorm that follows it: one workgroup (16 waves) per row m sums each
 // column's splits in split order, adds the sum into the residual row (a.out),
@@ -372,6 +390,12 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   return p;
 }
 
+// the fused reduce + SwiGLU applies to split [gate | up] products
+static bool fuse_swiglu(const GemmArgs& a, const SkinnyPlan& p) {
+  return p.splits > 1 && a.act_out && a.epi == EPI_STORE_F32 && a.n_seg == 2 &&
+         a.seg[0].n == a.seg[1].n && a.seg[0].n % 4 == 0;
+}
+
 // the fused reduce + RMSNorm applies to split residual adds over whole rows
 static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
   return p.splits > 1 && a.norm_gain && a.norm_out && a.epi == EPI_ADD_F32 && a.n_seg == 1 &&
@@ -389,14 +413,19 @@ static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   else if (fuse_norm(a, p))
     hipLaunchKernelGGL(k_gemm_skinny_reduce_norm, dim3(a.M), dim3(kRedNormThreads), 0, s, a,
                        p.splits);
+  else if (fuse_swiglu(a, p))
+    hipLaunchKernelGGL(k_gemm_skinny_reduce_swiglu, dim3((a.M * (a.seg[0].n / 4) + 255) / 256),
+                       dim3(256), 0, s, a, p.splits);
   else
     hipLaunchKernelGGL(k_gemm_skinny_reduce, dim3((n + 255) / 256), dim3(256), 0, s, a, p.splits);
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped,
+                              bool* swiglued) {
   const SkinnyPlan p = plan_skinny(a);
   if (normed) *normed = fuse_norm(a, p);
   if (roped) *roped = a.rope_fuse && p.splits > 1;
+  if (swiglued) *swiglued = !a.rope_fuse && !fuse_norm(a, p) && fuse_swiglu(a, p);
   switch (p.mt * 8 + p.nt) {
     case 8 + 4: launch_sk<1, 4>(a, p, s); break;
     case 8 + 2: launch_sk<1, 2>(a, p, s); break;
@@ -974,15 +1003,17 @@ bool gemm_swiglu_ok(const GemmArgs& a) {
   return a.epi == EPI_SWIGLU && a.M > 64 && plan_big(a).cfg >= 0;
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped,
+                       bool* swiglued) {
   if (normed) *normed = false;
   if (roped) *roped = false;
+  if (swiglued) *swiglued = false;
   if (a.epi == EPI_SWIGLU && !gemm_swiglu_ok(a)) return hipErrorInvalidValue;
   if (a.M > 64) {
     const BigPlan p = plan_big(a);
     if (p.cfg >= 0) return launch_big(a, p, s, roped);
   }
-  return launch_gemm_skinny(a, s, normed, roped);
+  return launch_gemm_skinny(a, s, normed, roped, swiglued);
 }
 
 }  // namespace uno

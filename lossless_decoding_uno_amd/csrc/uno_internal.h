@@ -138,13 +138,18 @@ struct GemmArgs {
   // *roped whether it did
   int rope_fuse;
   RopeArgs rope;
+  // optional SwiGLU of a [gate | up] product (EPI_STORE_F32, two segments of
+  // equal width F): when the product is split along K, the split-K reduction
+  // writes act_out[m, c] = bf16(silu(y[m, c]) * y[m, F + c]) [M, F] instead of
+  // `out`; launch_gemm reports through *swiglued whether it did
+  uint16_t* act_out;
 };
 // split-K scratch carved per pass: 128 MB for passes of more than 64 rows
 // (tiled kernel), 4 MB for up to 64 (skinny kernel)
 constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr,
-                       bool* roped = nullptr);
+                       bool* roped = nullptr, bool* swiglued = nullptr);
 // whether launch_gemm can run this EPI_SWIGLU product (the tiled kernel takes it)
 bool gemm_swiglu_ok(const GemmArgs& a);
 
