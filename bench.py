@@ -302,6 +302,18 @@ def proj_shape(cfg, name):
             "gemm_down": (D, F, 8), "lm_head": (cfg["vocab"], D, 4)}[name]
 
 
+def sampler_roofline(cfg, B, K, ms):
+    """The sampler launches of one step (draft sampling, acceptance statistics,
+    accept / resample) against HBM: algorithmic bytes = the fp32 draft logits
+    read once to sample the drafts, then the draft and verify logits read once
+    each to accept / resample (3 * B * K * V * 4), over their probe-step time."""
+    byts = 3.0 * B * K * cfg["vocab"] * 4
+    gbs = byts / (ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 3),
+            "algorithmic_bytes_per_step": int(byts)}
+
+
 def gemm_launch_work(cfg, name, R, draft):
     """Algorithmic (flops, bytes) of one launch: every weight (and, drafting, LoRA B
     and the LoRA input T) read once, X read once, the output written (and read,
@@ -604,6 +616,7 @@ def main():
                            "frac_of_8TBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9
                                                   / HBM_PEAK_GBS, 4),
                            "algorithmic_GB_per_step": round(W.verify_bytes_total / args.steps / 1e9, 3)},
+           "sampler": sampler_roofline(cfg, args.batch, K, classes["sampler"]),
            "kernel_class_ms_per_step": {k: round(v, 3) for k, v in classes.items()},
            "forward_passes_per_s": round(2 * args.steps / (ms / 1e3), 2),
            "wall_s_timed": round(wall, 3)}

@@ -101,20 +101,27 @@ struct RowShared {
 };
 
 // Block-wide max of a row; sets *nonfinite if any entry is NaN/Inf.
+// Rows are streamed kUnroll groups of four entries per thread at a time, their
+// loads issued together, so that every wave keeps several requests in flight.
+constexpr int kUnroll = 4;
+
 template <int TH>
 __device__ float block_row_max(const Row& row, RowShared<TH>& sh, bool* nonfinite) {
   float m = -INFINITY;
   int bad = 0;
-  for (int e0 = threadIdx.x * 4; e0 < row.V; e0 += TH * 4) {
-    float v[4];
-    bool ok[4];
-    row.load4(e0, v, ok);
+  for (int e0 = threadIdx.x * 4; e0 < row.V; e0 += TH * 4 * kUnroll) {
+    float v[kUnroll][4];
+    bool ok[kUnroll][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (ok[c]) {
-        bad |= !__builtin_isfinite(v[c]);
-        m = fmaxf(m, v[c]);
-      }
+    for (int u = 0; u < kUnroll; ++u) row.load4(e0 + u * TH * 4, v[u], ok[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (ok[u][c]) {
+          bad |= !__builtin_isfinite(v[u][c]);
+          m = fmaxf(m, v[u][c]);
+        }
   }
   m = wave_max(m);
   bad = __any(bad);
@@ -130,15 +137,23 @@ __device__ float block_row_max(const Row& row, RowShared<TH>& sh, bool* nonfinit
 }
 
 // Weight functors: four consecutive entries' integer weights.
+// (load: the raw entries; weights: their integer weights; get4: both)
 struct PlainWeights {  // W of one row
   Row row;
   float m, inv_temp;
-  __device__ __forceinline__ void get4(int e0, u128 w[4]) const {
+  struct Raw {
     float v[4];
     bool ok[4];
-    row.load4(e0, v, ok);
+  };
+  __device__ __forceinline__ void load(int e0, Raw& r) const { row.load4(e0, r.v, r.ok); }
+  __device__ __forceinline__ void weights(const Raw& r, u128 w[4]) const {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w[c] = u128_make(ok[c] ? weight_of(v[c], m, inv_temp) : 0u, 0);
+    for (int c = 0; c < 4; ++c) w[c] = u128_make(r.ok[c] ? weight_of(r.v[c], m, inv_temp) : 0u, 0);
+  }
+  __device__ __forceinline__ void get4(int e0, u128 w[4]) const {
+    Raw r;
+    load(e0, r);
+    weights(r, w);
   }
 };
 
@@ -146,20 +161,29 @@ struct ResidualWeights {  // max(0, Wp Sq - Wq Sp) of a row pair
   Row p, q;
   float mp, mq, inv_temp;
   uint64_t sp, sq;
-  __device__ __forceinline__ void get4(int e0, u128 w[4]) const {
+  struct Raw {
     float vp[4], vq[4];
     bool okp[4], okq[4];
-    p.load4(e0, vp, okp);
-    q.load4(e0, vq, okq);
+  };
+  __device__ __forceinline__ void load(int e0, Raw& r) const {
+    p.load4(e0, r.vp, r.okp);
+    q.load4(e0, r.vq, r.okq);
+  }
+  __device__ __forceinline__ void weights(const Raw& r, u128 w[4]) const {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       w[c] = u128_make(0, 0);
-      if (okp[c]) {
-        const u128 a = mul_64x64(weight_of(vp[c], mp, inv_temp), sq);
-        const u128 b = mul_64x64(weight_of(vq[c], mq, inv_temp), sp);
+      if (r.okp[c]) {
+        const u128 a = mul_64x64(weight_of(r.vp[c], mp, inv_temp), sq);
+        const u128 b = mul_64x64(weight_of(r.vq[c], mq, inv_temp), sp);
         if (u128_lt(b, a)) w[c] = u128_sub(a, b);
       }
     }
+  }
+  __device__ __forceinline__ void get4(int e0, u128 w[4]) const {
+    Raw r;
+    load(e0, r);
+    weights(r, w);
   }
 };
 
@@ -168,14 +192,22 @@ template <int TH, class WF>
 __device__ u128 block_weight_sum(const WF& wf, int V, u128* tiles, RowShared<TH>& sh) {
   const int w = threadIdx.x / UNO_WAVE, l = lane_id();
   const int n_tiles = (V + kTile - 1) / kTile;
+  constexpr int NW = TH / UNO_WAVE;
   u128 acc = u128_make(0, 0);
-  for (int t = w; t < n_tiles; t += (TH / UNO_WAVE)) {
-    u128 v[4];
-    wf.get4(t * kTile + l * 4, v);
-    u128 s = u128_add(u128_add(v[0], v[1]), u128_add(v[2], v[3]));
-    s = wave_sum_u128(s);
-    if (l == 0) tiles[t] = s;
-    acc = u128_add(acc, s);
+  for (int t = w; t < n_tiles; t += kUnroll * NW) {
+    typename WF::Raw raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) wf.load((t + u * NW) * kTile + l * 4, raw[u]);   // past V: no load
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t + u * NW >= n_tiles) break;
+      u128 v[4];
+      wf.weights(raw[u], v);
+      u128 s = u128_add(u128_add(v[0], v[1]), u128_add(v[2], v[3]));
+      s = wave_sum_u128(s);
+      if (l == 0) tiles[t + u * NW] = s;
+      acc = u128_add(acc, s);
+    }
   }
   if (l == 0) sh.red_u[w] = acc;
   __syncthreads();
@@ -291,13 +323,16 @@ k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, i
   const float m = block_row_max(row, sh, &bad);
   uint64_t acc = 0;
   if (!bad) {
-    for (int e0 = threadIdx.x * 4; e0 < V; e0 += TH * 4) {
-      float v[4];
-      bool ok[4];
-      row.load4(e0, v, ok);
+    for (int e0 = threadIdx.x * 4; e0 < V; e0 += TH * 4 * kUnroll) {
+      float v[kUnroll][4];
+      bool ok[kUnroll][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (ok[c]) acc += weight_of(v[c], m, inv_temp);
+      for (int u = 0; u < kUnroll; ++u) row.load4(e0 + u * TH * 4, v[u], ok[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (ok[u][c]) acc += weight_of(v[u][c], m, inv_temp);
     }
   }
   acc = wave_sum_u64(acc);
@@ -463,7 +498,7 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
                        n_each, inv_temp, m_all, s_all, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (B <= 16)   // one workgroup per sequence: wide only for a handful of sequences
+  if (B <= 128)   // one workgroup per sequence: wide unless they alone fill the chip
     hipLaunchKernelGGL(k_spec_accept<1024>, dim3(B), dim3(1024), tile_lds_bytes(V), s, zq, zp,
                        drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
                        accept_len, committed, extra_token, status);
