@@ -75,11 +75,28 @@ hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int3
 __global__ void __launch_bounds__(256)
 k_rmsnorm(const float* __restrict__ h, const float* __restrict__ gain, int D, float eps,
           uint16_t* __restrict__ out) {
+  // the first kRegs float4 of each thread stay in registers between the two
+  // passes, their loads (and the gains') issued together
+  constexpr int kRegs = 8;
   __shared__ float red[4];
   const int r = blockIdx.x;
   const float* x = h + (size_t)r * D;
+  float4 xv[kRegs], gv[kRegs];
+#pragma unroll
+  for (int k = 0; k < kRegs; ++k) {
+    const int i = threadIdx.x * 4 + k * 256 * 4;
+    if (i < D) {
+      xv[k] = *reinterpret_cast<const float4*>(x + i);
+      gv[k] = *reinterpret_cast<const float4*>(gain + i);
+    }
+  }
   float ss = 0.f;
-  for (int i = threadIdx.x * 4; i < D; i += 256 * 4) {
+#pragma unroll
+  for (int k = 0; k < kRegs; ++k) {
+    const int i = threadIdx.x * 4 + k * 256 * 4;
+    if (i < D) ss += xv[k].x * xv[k].x + xv[k].y * xv[k].y + xv[k].z * xv[k].z + xv[k].w * xv[k].w;
+  }
+  for (int i = threadIdx.x * 4 + kRegs * 256 * 4; i < D; i += 256 * 4) {
     const float4 v = *reinterpret_cast<const float4*>(x + i);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
@@ -89,14 +106,19 @@ k_rmsnorm(const float* __restrict__ h, const float* __restrict__ gain, int D, fl
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.0f / sqrtf(tot / (float)D + eps);
   uint16_t* o = out + (size_t)r * D;
-  for (int i = threadIdx.x * 4; i < D; i += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(x + i);
-    const float4 g = *reinterpret_cast<const float4*>(gain + i);
+  auto put = [&](int i, float4 v, float4 g) {
     uint2 pk;
     pk.x = pack_bf16x2(v.x * inv * g.x, v.y * inv * g.y);
     pk.y = pack_bf16x2(v.z * inv * g.z, v.w * inv * g.w);
     *reinterpret_cast<uint2*>(o + i) = pk;
+  };
+#pragma unroll
+  for (int k = 0; k < kRegs; ++k) {
+    const int i = threadIdx.x * 4 + k * 256 * 4;
+    if (i < D) put(i, xv[k], gv[k]);
   }
+  for (int i = threadIdx.x * 4 + kRegs * 256 * 4; i < D; i += 256 * 4)
+    put(i, *reinterpret_cast<const float4*>(x + i), *reinterpret_cast<const float4*>(gain + i));
 }
 
 hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
