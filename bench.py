@@ -47,7 +47,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # attention profile summary under profiles/): mean FETCH_SIZE and WRITE_SIZE per
 # dispatch, scaled by the copy calibration factor, for the kernel source with
 # this digest.
-ATTN_TRAFFIC = {"source": "ab7e00248e964c18", "bytes_per_launch": 2459161969,
+ATTN_TRAFFIC = {"source": "1adee9fde3195b47", "bytes_per_launch": 2459161969,
                 "fetch_kib": 1196707.5, "write_kib": 8192, "fetch_factor": 1.99993, "write_factor": 1.0}
 ATTN_SOURCES = ["lossless_decoding_uno_amd/csrc/attention.hip",
                 "lossless_decoding_uno_amd/csrc/uno_device.h"]

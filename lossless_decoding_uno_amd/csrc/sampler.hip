@@ -88,8 +88,7 @@ struct Row {
 
 constexpr int kTile = UNO_WAVE * 4;  // entries per wave tile
 
-// TH: threads per workgroup (one workgroup per row): 256, or 1024 when there
-// are too few rows to fill the chip with 256-thread workgroups.
+// TH: threads per workgroup (one workgroup per row).
 template <int TH>
 struct RowShared {
   float red_f[TH / UNO_WAVE];
@@ -445,20 +444,16 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
 // ------------------------------------------------------------ launchers
 static size_t tile_lds_bytes(int V) { return (size_t)((V + kTile - 1) / kTile) * sizeof(u128); }
 
-// 1024-thread workgroups when the rows would not fill the chip with 256
-static bool wide_rows(int rows) { return rows < 512; }
+// Every row pass runs in 1024-thread workgroups: at most a few rows per CU are
+// in flight, so a row's second pass finds it still in the last-level cache.
+constexpr int kRowThreads = 1024;
 
 hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
                                uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
                                int32_t* status, hipStream_t s) {
-  if (wide_rows(B * K))
-    hipLaunchKernelGGL(k_draft_sample<1024>, dim3(B * K), dim3(1024), tile_lds_bytes(V), s,
-                       logits, K, V, inv_temp, seed, slot, step, tokens, status, nullptr, 0,
-                       nullptr);
-  else
-    hipLaunchKernelGGL(k_draft_sample<256>, dim3(B * K), dim3(256), tile_lds_bytes(V), s,
-                       logits, K, V, inv_temp, seed, slot, step, tokens, status, nullptr, 0,
-                       nullptr);
+  hipLaunchKernelGGL(k_draft_sample<kRowThreads>, dim3(B * K), dim3(kRowThreads),
+                     tile_lds_bytes(V), s, logits, K, V, inv_temp, seed, slot, step, tokens,
+                     status, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
@@ -466,14 +461,9 @@ hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float in
                               uint64_t seed, const uint64_t* step, const int32_t* node_depth,
                               const int32_t* n_nodes, int32_t* samples, int32_t* status,
                               hipStream_t s) {
-  if (wide_rows(B * N))
-    hipLaunchKernelGGL(k_draft_sample<1024>, dim3(B * N), dim3(1024), tile_lds_bytes(V), s,
-                       logits, N, V, inv_temp, seed, 2, step, samples, status, node_depth, 1,
-                       n_nodes);
-  else
-    hipLaunchKernelGGL(k_draft_sample<256>, dim3(B * N), dim3(256), tile_lds_bytes(V), s,
-                       logits, N, V, inv_temp, seed, 2, step, samples, status, node_depth, 1,
-                       n_nodes);
+  hipLaunchKernelGGL(k_draft_sample<kRowThreads>, dim3(B * N), dim3(kRowThreads),
+                     tile_lds_bytes(V), s, logits, N, V, inv_temp, seed, 2, step, samples, status,
+                     node_depth, 1, n_nodes);
   return hipGetLastError();
 }
 
@@ -490,22 +480,13 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
   float* m_all = static_cast<float*>(ws);
   uint64_t* s_all = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                                 align_up(2 * (size_t)n_each * sizeof(float), 256));
-  if (wide_rows(2 * n_each))
-    hipLaunchKernelGGL(k_row_stats<1024>, dim3(2 * n_each), dim3(1024), 0, s, zq, zp, K, V,
-                       n_each, inv_temp, m_all, s_all, status);
-  else
-    hipLaunchKernelGGL(k_row_stats<256>, dim3(2 * n_each), dim3(256), 0, s, zq, zp, K, V,
-                       n_each, inv_temp, m_all, s_all, status);
+  hipLaunchKernelGGL(k_row_stats<kRowThreads>, dim3(2 * n_each), dim3(kRowThreads), 0, s, zq, zp,
+                     K, V, n_each, inv_temp, m_all, s_all, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (B <= 128)   // one workgroup per sequence: wide unless they alone fill the chip
-    hipLaunchKernelGGL(k_spec_accept<1024>, dim3(B), dim3(1024), tile_lds_bytes(V), s, zq, zp,
-                       drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
-                       accept_len, committed, extra_token, status);
-  else
-    hipLaunchKernelGGL(k_spec_accept<256>, dim3(B), dim3(256), tile_lds_bytes(V), s, zq, zp,
-                       drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
-                       accept_len, committed, extra_token, status);
+  hipLaunchKernelGGL(k_spec_accept<kRowThreads>, dim3(B), dim3(kRowThreads), tile_lds_bytes(V), s,
+                     zq, zp, drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
+                     accept_len, committed, extra_token, status);
   return hipGetLastError();
 }
 
