@@ -101,6 +101,7 @@ struct PassWs {
   float* part_ml;
   float* gemm_part;      // split-K partial tiles (passes of more than 64 rows)
   size_t gemm_part_floats;
+  float* lora_part;      // LoRA-A split-K partials read by the next projection (<= 64 rows)
   size_t total;
 };
 
@@ -135,6 +136,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.part_ml = reinterpret_cast<float*>(take(parts * 2 * 4));
   w.gemm_part_floats = R > 64 ? kGemmPartFloats : kGemmPartFloatsSkinny;
   w.gemm_part = reinterpret_cast<float*>(take(w.gemm_part_floats * 4));
+  w.lora_part = R <= 64 ? reinterpret_cast<float*>(take(kLoraPartFloats * 4)) : nullptr;
   w.total = off;
   return w;
 }
@@ -186,13 +188,28 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
     g.part_floats = W.gemm_part_floats;
     return g;
   };
-  auto lora_t = [&](const bf16_raw_t* x, int ldx, int Kd, const void* const* a_ptrs, int n_a) {
+  // the LoRA-A product T = scale * gate(row) * (X A^T) of a projection
+  auto lora_args = [&](const bf16_raw_t* x, int ldx, int Kd, const void* const* a_ptrs, int n_a) {
     GemmArgs g = scratch_args();
     g.x = x; g.M = R; g.Kd = Kd; g.ldx = ldx;
     for (int i = 0; i < n_a; ++i) g.seg[i] = GemmSeg{bp(a_ptrs[i]), r, nullptr, 0};
     g.n_seg = n_a;
     g.epi = EPI_LORA_T; g.out = W.t; g.ldo = n_a * r; g.scale = c.lora_scale; g.rows_per_seq = K;
-    return timed(UNO_TIME_LORA_A, s, [&] { return launch_gemm(g, s); });
+    return g;
+  };
+  // a projection after its LoRA-A product (when `ta` is given); at most 64 rows
+  // the projection sums the product's split-K partials itself
+  auto project = [&](const GemmArgs& g0, const GemmArgs* ta0, int cls, bool* normed_out,
+                     bool* roped_out, bool* swiglued_out) -> hipError_t {
+    GemmArgs g = g0;
+    if (ta0) {
+      GemmArgs ta;
+      gemm_lora_pair(g0, *ta0, W.lora_part, kLoraPartFloats, &g, &ta);
+      const hipError_t e = timed(UNO_TIME_LORA_A, s, [&] { return launch_gemm(ta, s); });
+      if (e != hipSuccess) return e;
+    }
+    return timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, normed_out, roped_out,
+                                                             swiglued_out); }, cls);
   };
 
   // set when a residual projection's split-K reduction also wrote the RMSNorm
@@ -205,11 +222,9 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
     // ---- attention block
     if (!normed)
       UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.attn_norm), R, D, c.rms_eps, W.xn, s));
-    if (lq) {
-      const void* a3[3] = {L.lora_a[P_Q], L.lora_a[P_K], L.lora_a[P_V]};
-      UNO_TRY(lora_t(W.xn, D, D, a3, 3));
-    }
     {
+      const void* a3[3] = {L.lora_a[P_Q], L.lora_a[P_K], L.lora_a[P_V]};
+      const GemmArgs ta = lq ? lora_args(W.xn, D, D, a3, 3) : GemmArgs{};
       GemmArgs g = scratch_args();
       g.x = W.xn; g.M = R; g.Kd = D; g.ldx = D;
       g.seg[0] = GemmSeg{bp(L.wq), QD, lq ? bp(L.lora_b[P_Q]) : nullptr, 0};
@@ -222,8 +237,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.rope_fuse = 1;
       g.rope = make_rope_args(c, W.cs, W.row_page, *kv, li, K, W.qb, W.qlo);
       bool roped = false;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, nullptr, &roped); },
-                    UNO_TIME_GEMM_QKV));
+      UNO_TRY(project(g, lq ? &ta : nullptr, UNO_TIME_GEMM_QKV, nullptr, &roped, nullptr));
       if (!roped) UNO_TRY(launch_rope_kv_write(W.qkv, g.rope, R, s));
     }
     {
@@ -242,11 +256,9 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       UNO_TRY(timed(UNO_TIME_ATTENTION, s, [&] { return launch_attention(a, s); }));
       UNO_TRY(launch_attn_merge(a, s));
     }
-    if (lo) {
-      const void* a1[1] = {L.lora_a[P_O]};
-      UNO_TRY(lora_t(W.ao, QD, QD, a1, 1));
-    }
     {
+      const void* a1[1] = {L.lora_a[P_O]};
+      const GemmArgs ta = lo ? lora_args(W.ao, QD, QD, a1, 1) : GemmArgs{};
       GemmArgs g = scratch_args();
       g.x = W.ao; g.M = R; g.Kd = QD; g.ldx = QD;
       g.seg[0] = GemmSeg{bp(L.wo), D, lo ? bp(L.lora_b[P_O]) : nullptr, 0};
@@ -254,16 +266,14 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
       g.t = lo ? W.t : nullptr; g.ldt = r; g.rank = r;
       g.epi = EPI_ADD_F32; g.out = W.h; g.ldo = D;
       g.norm_gain = static_cast<const float*>(L.mlp_norm); g.norm_out = W.xn; g.norm_eps = c.rms_eps;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, &normed); }, UNO_TIME_GEMM_O));
+      UNO_TRY(project(g, lo ? &ta : nullptr, UNO_TIME_GEMM_O, &normed, nullptr, nullptr));
     }
     // ---- MLP block
     if (!normed)
       UNO_TRY(launch_rmsnorm(W.h, static_cast<const float*>(L.mlp_norm), R, D, c.rms_eps, W.xn, s));
-    if (lg) {
-      const void* a2[2] = {L.lora_a[P_GATE], L.lora_a[P_UP]};
-      UNO_TRY(lora_t(W.xn, D, D, a2, 2));
-    }
     {
+      const void* a2[2] = {L.lora_a[P_GATE], L.lora_a[P_UP]};
+      const GemmArgs ta = lg ? lora_args(W.xn, D, D, a2, 2) : GemmArgs{};
       // gate and up rows stored back to back (and their LoRA B factors too):
       // the tiled kernel pairs them and writes silu(gate) * up directly
       const char* wg = static_cast<const char*>(L.wgate);
@@ -286,15 +296,12 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
         g.act_out = W.act;
       }
       bool swiglued = false;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, nullptr, nullptr, &swiglued); },
-                    UNO_TIME_GEMM_GATE_UP));
+      UNO_TRY(project(g, lg ? &ta : nullptr, UNO_TIME_GEMM_GATE_UP, nullptr, nullptr, &swiglued));
       if (!fused && !swiglued) UNO_TRY(launch_silu_mul(W.gu, R, F, W.act, s));
     }
-    if (ld) {
-      const void* a1[1] = {L.lora_a[P_DOWN]};
-      UNO_TRY(lora_t(W.act, F, F, a1, 1));
-    }
     {
+      const void* a1[1] = {L.lora_a[P_DOWN]};
+      const GemmArgs ta = ld ? lora_args(W.act, F, F, a1, 1) : GemmArgs{};
       GemmArgs g = scratch_args();
       g.x = W.act; g.M = R; g.Kd = F; g.ldx = F;
       g.seg[0] = GemmSeg{bp(L.wdown), D, ld ? bp(L.lora_b[P_DOWN]) : nullptr, 0};
@@ -305,7 +312,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
                               : logits             ? w->final_norm
                                                    : nullptr;
       g.norm_gain = static_cast<const float*>(next_norm); g.norm_out = W.xn; g.norm_eps = c.rms_eps;
-      UNO_TRY(timed(UNO_TIME_GEMM, s, [&] { return launch_gemm(g, s, &normed); }, UNO_TIME_GEMM_DOWN));
+      UNO_TRY(project(g, ld ? &ta : nullptr, UNO_TIME_GEMM_DOWN, &normed, nullptr, nullptr));
     }
   }
   if (logits) {

@@ -205,8 +205,22 @@ k_gemm_skinny(GemmArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = m0 + mt * 16 + rr;
-        ax[mt].u = (kin && m < a.M) ? ldg16(a.t + (size_t)m * a.ldt + sv.t_col + rs * 32 + kg * 8)
-                                    : make_uint4(0, 0, 0, 0);
+        const size_t to = (size_t)m * a.ldt + sv.t_col + rs * 32 + kg * 8;
+        if (!(kin && m < a.M)) {
+          ax[mt].u = make_uint4(0, 0, 0, 0);
+        } else if (a.t_part) {
+          // T from its LoRA-A product's split-K partials, summed in split order
+          // and rounded as that product's epilogue rounds it
+          const float4* tp = reinterpret_cast<const float4*>(a.t_part + to);
+          const size_t zs4 = (size_t)a.M * a.ldt / 4;
+          const float4 lo = sum_splits4(tp, zs4, a.t_splits);
+          const float4 hi = sum_splits4(tp + 1, zs4, a.t_splits);
+          const float g = (m % a.t_rows) != 0 ? a.t_scale : 0.f;
+          ax[mt].u = make_uint4(pack_bf16x2(g * lo.x, g * lo.y), pack_bf16x2(g * lo.z, g * lo.w),
+                                pack_bf16x2(g * hi.x, g * hi.y), pack_bf16x2(g * hi.z, g * hi.w));
+        } else {
+          ax[mt].u = ldg16(a.t + to);
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -385,7 +399,8 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   const size_t per_split = (size_t)a.M * skinny_cols(a);
   if (a.part)
     while (p.gx * p.gy * p.splits < 512 && steps / (p.splits * 2) >= kSkWaves &&
-           (size_t)p.splits * 2 * per_split <= a.part_floats)
+           (size_t)p.splits * 2 * per_split <= a.part_floats &&
+           (a.max_splits <= 0 || p.splits * 2 <= a.max_splits))
       p.splits *= 2;
   return p;
 }
@@ -405,7 +420,7 @@ static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
 template <int MT, int NT>
 static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
-  if (p.splits == 1) return;
+  if (p.splits == 1 || a.partials_only) return;
   const int n = a.M * skinny_cols(a);
   if (a.rope_fuse)
     hipLaunchKernelGGL(k_gemm_skinny_reduce_rope, dim3((n + 255) / 256), dim3(256), 0, s, a,
@@ -435,6 +450,27 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bo
     default: launch_sk<4, 1>(a, p, s); break;
   }
   return hipGetLastError();
+}
+
+void gemm_lora_pair(const GemmArgs& a, const GemmArgs& ta, float* t_part, size_t t_part_floats,
+                    GemmArgs* a_out, GemmArgs* ta_out) {
+  *a_out = a;
+  *ta_out = ta;
+  if (!t_part || a.M > 64 || ta.M != a.M || ta.epi != EPI_LORA_T || !a.t ||
+      a.ldt != skinny_cols(ta) || a.ldt % 4)
+    return;
+  GemmArgs t2 = ta;
+  t2.part = t_part;
+  t2.part_floats = t_part_floats;
+  t2.max_splits = 4;
+  const SkinnyPlan p = plan_skinny(t2);
+  if (p.splits < 2) return;
+  t2.partials_only = 1;
+  *ta_out = t2;
+  a_out->t_part = t_part;
+  a_out->t_splits = p.splits;
+  a_out->t_scale = ta.scale;
+  a_out->t_rows = ta.rows_per_seq;
 }
 
 // ============================================================================

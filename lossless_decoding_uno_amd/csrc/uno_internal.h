@@ -138,6 +138,18 @@ struct GemmArgs {
   // *roped whether it did
   int rope_fuse;
   RopeArgs rope;
+  // skinny kernel (at most 64 rows): at most this many K splits (0: no cap);
+  // partials_only: a split product leaves its fp32 partial sums in `part`
+  // [splits][M][all columns] for a later launch and runs no reduction
+  int max_splits;
+  int partials_only;
+  // LoRA input as the split-K partials of its LoRA-A product (set by
+  // gemm_lora_pair): T = bf16(t_scale * gate(m) * sum over t_splits partials
+  // [t_splits][M][ldt]), gate(m) = m % t_rows != 0; null: T is read from `t`
+  const float* t_part;
+  int t_splits;
+  float t_scale;
+  int t_rows;
   // optional SwiGLU of a [gate | up] product (EPI_STORE_F32, two segments of
   // equal width F): when the product is split along K, the split-K reduction
   // writes act_out[m, c] = bf16(silu(y[m, c]) * y[m, F + c]) [M, F] instead of
@@ -150,6 +162,15 @@ constexpr size_t kGemmPartFloats = size_t(32) << 20;
 constexpr size_t kGemmPartFloatsSkinny = size_t(1) << 20;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed = nullptr,
                        bool* roped = nullptr, bool* swiglued = nullptr);
+// A projection `a` and the LoRA-A product `ta` (EPI_LORA_T, same rows) that
+// feeds its LoRA step, as two launches.  At most 64 rows: `ta` is split along
+// K (at most 4 splits) with its partials left in t_part (t_part_floats of
+// scratch) and no reduction launch, and `a`'s last K split sums them itself;
+// otherwise both are returned unchanged (`ta` writes T, `a` reads it).
+void gemm_lora_pair(const GemmArgs& a, const GemmArgs& ta, float* t_part, size_t t_part_floats,
+                    GemmArgs* a_out, GemmArgs* ta_out);
+// T partial scratch a pass of at most 64 rows carves for gemm_lora_pair
+constexpr size_t kLoraPartFloats = size_t(1) << 18;
 // whether launch_gemm can run this EPI_SWIGLU product (the tiled kernel takes it)
 bool gemm_swiglu_ok(const GemmArgs& a);
 
