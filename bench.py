@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--temp", type=float, default=1.0, help="sampling temperature")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context lines (batch 16, context 32768, K 32)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
     ap.add_argument("--generate", type=int, default=0, metavar="N",
@@ -623,16 +625,36 @@ def main():
     del W
     torch.cuda.empty_cache()
     if not args.no_secondary:
-        log("secondary: batch 1, context 1024")
-        W1 = Workload(U, torch, synth, model, cfg, 1, 1024, K, 40 + 6, seed=7)
-        ms1, _, tok1, _, _, _ = run_timed(W1, 40, 5, torch)
-        out["secondary"] = {"workload": "qwen3-8b-shape b1 ctx1024 K%d forced" % K,
-                            "value": round(tok1 / (ms1 / 1e3), 1), "unit": "accepted tokens/s",
-                            "ms_per_step": round(ms1 / 40, 3),
-                            "verify_step_hbm_GBps": round(W1.verify_bytes_total /
-                                                          (W1.verify_ms / 1e3) / 1e9, 1),
-                            "verify_ms_per_step": round(W1.verify_ms / 40, 3)}
-        del W1
+        # batch 1 at the two contexts the single-sequence workload is quoted at
+        for key, ctx1 in (("secondary", 1024), ("secondary_ctx9216", 9216)):
+            log("%s: batch 1, context %d" % (key, ctx1))
+            W1 = Workload(U, torch, synth, model, cfg, 1, ctx1, K, 40 + 6, seed=7)
+            ms1, _, tok1, _, _, _ = run_timed(W1, 40, 5, torch)
+            out[key] = {"workload": "qwen3-8b-shape b1 ctx%d K%d forced" % (ctx1, K),
+                        "value": round(tok1 / (ms1 / 1e3), 1), "unit": "accepted tokens/s",
+                        "ms_per_step": round(ms1 / 40, 3),
+                        "verify_step_hbm_GBps": round(W1.verify_bytes_total /
+                                                      (W1.verify_ms / 1e3) / 1e9, 1),
+                        "verify_ms_per_step": round(W1.verify_ms / 40, 3)}
+            del W1
+    if not args.no_long:
+        # the long-context rollout shape, at temperature 0.7 and 1.0
+        Kl, ctxl, Bl = 32, 32768, 16
+        lines = []
+        for temp in (0.7, 1.0):
+            log("long context: batch %d, context %d, K %d, temperature %g" % (Bl, ctxl, Kl, temp))
+            WL = Workload(U, torch, synth, model, cfg, Bl, ctxl, Kl, 8 + 3, seed=9, temp=temp)
+            msl, _, tokl, _, abl, _ = run_timed(WL, 8, 2, torch)
+            lines.append({"workload": "qwen3-8b-shape b%d ctx%d K%d T%g forced a~U{0..%d}"
+                                      % (Bl, ctxl, Kl, temp, Kl),
+                          "value": round(tokl / (msl / 1e3), 1), "unit": "accepted tokens/s",
+                          "ms_per_step": round(msl / 8, 3),
+                          "verify_step_hbm_GBps": round(WL.verify_bytes_total /
+                                                        (WL.verify_ms / 1e3) / 1e9, 1),
+                          "verify_ms_per_step": round(WL.verify_ms / 8, 3)})
+            del WL
+            torch.cuda.empty_cache()
+        out["long_context"] = lines
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(K, args.ctx, (K + 2) / 2.0)
