@@ -20,6 +20,8 @@
 #include "uno_internal.h"
 #include "rope_store.h"
 
+#include <algorithm>
+
 namespace uno {
 
 union Frag {
@@ -870,6 +872,19 @@ static BigPlan plan_big(const GemmArgs& a) {
   BigPlan best = {-1, 0, 0, 0, 0, 1e30};
   const int pair = a.epi == EPI_SWIGLU ? 2 : 1;
   const int nk = a.Kd / big::BK + (a.t ? pair * a.rank / big::BK : 0);
+  // At most 128 rows the product is bound by streaming W (about 2*rows flop
+  // per weight byte, below the chip's ridge): one row of 128x128 tiles, split
+  // along K until about 256 workgroups stream W (measured best on the
+  // 121-row token-tree verify shapes).
+  if (a.M <= 128 && big_ok(a, 128)) {
+    int n_tiles = 0;
+    for (int i = 0; i < a.n_seg; ++i) n_tiles += (pair * a.seg[i].n + 127) / 128;
+    int sp = std::max(1, std::min(16, 256 / n_tiles));
+    while (sp > 1 && (a.Kd / big::BK / sp < 4 || !a.part ||
+                      (size_t)n_tiles * sp * 128 * 128 > a.part_floats))
+      --sp;
+    return BigPlan{CFG_S, 1, n_tiles, sp, sp == 1 ? n_tiles : 0, 0.0};
+  }
   for (int c = 0; c < 3; ++c) {
     const CfgInfo& ci = kCfgInfo[c];
     if (!big_ok(a, ci.bn)) continue;
