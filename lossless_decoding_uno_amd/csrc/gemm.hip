@@ -9,13 +9,15 @@
 //
 // Skinny kernel (decode rows, M <= 64 per workgroup): one workgroup owns
 // 16..64 columns of W and 16..64 rows of X; its 8 waves split the K dimension
-// (wave w takes the 32-wide K steps w, w+8, ...), so every weight byte is read
-// from HBM once and the 8 waves' loads cover 512 contiguous bytes of each
-// weight row at a time.  Each wave issues v_mfma_f32_16x16x32_bf16 (A = 16
-// rows of X, B = 16 columns of W^T); the eight partial tiles are summed in LDS
-// in a fixed order and the epilogue stores, accumulates into the fp32 residual
-// stream, or forms the gated, scaled LoRA input T.  Narrow outputs split K over
-// workgroups; a second kernel sums the splits in order (run-to-run identical).
+// (with one row tile, wave w takes blocks of four consecutive 32-wide K steps,
+// so each weight row is read in 256-byte runs), and every weight byte is read
+// from HBM once.  Each wave issues v_mfma_f32_16x16x32_bf16 (A = 16 rows of X,
+// B = 16 columns of W^T); the eight partial tiles are summed in LDS in a fixed
+// order and the epilogue stores, accumulates into the fp32 residual stream, or
+// forms the gated, scaled LoRA input T.  Most products also split K over
+// workgroups: the splits store fp32 partial rows and a second kernel sums them
+// in split order (run-to-run identical), applying the epilogue, RoPE, SwiGLU or
+// the residual add and RMSNorm.
 #include "uno_device.h"
 #include "uno_internal.h"
 #include "rope_store.h"
