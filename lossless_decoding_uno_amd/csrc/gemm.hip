@@ -93,47 +93,6 @@ __device__ __forceinline__ float sum_splits(const float* p, size_t zs, int split
   }
   return v;
 }
-// two such sums at once (their loads interleaved)
-__device__ __forceinline__ void sum_splits_2(const float* p, const float* q, size_t zs, int splits,
-                                             float& x, float& y) {
-  x = p[0];
-  y = q[0];
-  for (int z0 = 1; z0 < splits; z0 += 4) {
-    float a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = z0 + u < splits;
-      a[u] = ok ? p[(size_t)(z0 + u) * zs] : 0.f;
-      b[u] = ok ? q[(size_t)(z0 + u) * zs] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (z0 + u < splits) {
-        x += a[u];
-        y += b[u];
-      }
-  }
-}
-__device__ __forceinline__ void sum_splits4_2(const float4* p, const float4* q, size_t zs,
-                                              int splits, float4& x, float4& y) {
-  x = p[0];
-  y = q[0];
-  for (int z0 = 1; z0 < splits; z0 += 4) {
-    float4 a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = z0 + u < splits;
-      a[u] = ok ? p[(size_t)(z0 + u) * zs] : make_float4(0.f, 0.f, 0.f, 0.f);
-      b[u] = ok ? q[(size_t)(z0 + u) * zs] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (z0 + u < splits) {
-        x.x += a[u].x; x.y += a[u].y; x.z += a[u].z; x.w += a[u].w;
-        y.x += b[u].x; y.y += b[u].y; y.z += b[u].z; y.w += b[u].w;
-      }
-  }
-}
 __device__ __forceinline__ float4 sum_splits4(const float4* p, size_t zs, int splits) {
   float4 v = p[0];
   for (int z0 = 1; z0 < splits; z0 += 4) {
@@ -337,16 +296,15 @@ k_gemm_skinny_reduce_rope(GemmArgs a, int splits) {
   const bool rot = head < ra.Hq + ra.Hkv;
   if (rot && ch >= half) return;                 // stored by its partner
   const size_t zs = (size_t)a.M * ncols;
+  const float x = sum_splits(a.part + g, zs, splits);
   int slot;
   const int page = rope_page(ra, m, &slot);
   if (!rot) {
-    rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, sum_splits(a.part + g, zs, splits), page, slot);
+    rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, x, page, slot);
     return;
   }
-  const float2 cs = rope_cs(ra, m, ch);
-  float x, xp;
-  sum_splits_2(a.part + g, a.part + g + half, zs, splits, x, xp);
-  rope_store_pair_cs(ra, m, head, ch, x, xp, cs, page, slot);
+  const float xp = sum_splits(a.part + g + half, zs, splits);
+  rope_store_pair(ra, m, head, ch, x, xp, page, slot);
 }
 
 // Split-K reduction of a [gate | up] product fused with SwiGLU: one thread per
@@ -1037,31 +995,24 @@ k_gemm_splitk_reduce_rope(GemmArgs a, int m_tiles, int n_tiles, int splits) {
   const bool rot = head < ra.Hq + ra.Hkv;
   if (rot && ch >= half) return;                       // stored by its partner
   const float4* src = reinterpret_cast<const float4*>(a.part);
-  int qp = q;
+  auto sum_at = [&](int qi) { return sum_splits4(src + (size_t)tr * Q + qi, (size_t)rem * Q, splits); };
+  const float4 x = sum_at(q);
+  float4 xp = x;
   if (rot) {
     const int np = nn + half;
     const int wp = wm * C::WN + np / C::TN, jp = (np % C::TN) / 32;
-    qp = (((wp * C::TI + i) * C::TJ + jp) * 4 + e4) * 64 + l;
+    xp = sum_at((((wp * C::TI + i) * C::TJ + jp) * 4 + e4) * 64 + l);
   }
-  // the four rows' pages and rotation pairs load together with the partials
   const int mb = mt * C::BM + wm * C::TM + i * 32 + e4 * 8 + (l >> 5) * 4;
-  int page[4], slot[4];
-  float2 cs[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int m = mb + c < a.M ? mb + c : a.M - 1;
-    page[c] = rope_page(ra, m, &slot[c]);
-    cs[c] = rot ? rope_cs(ra, m, ch) : make_float2(1.f, 0.f);
-  }
-  float4 x, xp;
-  sum_splits4_2(src + (size_t)tr * Q + q, src + (size_t)tr * Q + qp, (size_t)rem * Q, splits, x, xp);
   const float xv[4] = {x.x, x.y, x.z, x.w}, pv[4] = {xp.x, xp.y, xp.z, xp.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int m = mb + c;
     if (m >= a.M) break;
-    if (rot) rope_store_pair_cs(ra, m, head, ch, xv[c], pv[c], cs[c], page[c], slot[c]);
-    else rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, xv[c], page[c], slot[c]);
+    int slot;
+    const int page = rope_page(ra, m, &slot);
+    if (rot) rope_store_pair(ra, m, head, ch, xv[c], pv[c], page, slot);
+    else rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, xv[c], page, slot);
   }
 }
 

@@ -20,17 +20,11 @@ __device__ __forceinline__ int rope_page(const RopeArgs& ra, int r, int* slot) {
   return p.x;
 }
 
-// (cos, sin) of channel pair i of row r
-__device__ __forceinline__ float2 rope_cs(const RopeArgs& ra, int r, int i) {
-  return ra.cs[(size_t)r * (ra.hd / 2) + i];
-}
-
-// channels (i, i + hd/2) of q or k head `head` (q heads first) of row r, with
-// the pair's (cos, sin) already loaded
-__device__ __forceinline__ void rope_store_pair_cs(const RopeArgs& ra, int r, int head, int i,
-                                                   float x1, float x2, float2 a, int page,
-                                                   int slot) {
+// channels (i, i + hd/2) of q or k head `head` (q heads first) of row r
+__device__ __forceinline__ void rope_store_pair(const RopeArgs& ra, int r, int head, int i,
+                                                float x1, float x2, int page, int slot) {
   const int hd = ra.hd, half = hd / 2;
+  const float2 a = ra.cs[(size_t)r * half + i];
   const float y1 = x1 * a.x - x2 * a.y;
   const float y2 = x2 * a.x + x1 * a.y;
   if (head < ra.Hq) {
@@ -47,11 +41,6 @@ __device__ __forceinline__ void rope_store_pair_cs(const RopeArgs& ra, int r, in
     kp[i] = f32_to_bf16(y1);
     kp[i + half] = f32_to_bf16(y2);
   }
-}
-
-__device__ __forceinline__ void rope_store_pair(const RopeArgs& ra, int r, int head, int i,
-                                                float x1, float x2, int page, int slot) {
-  rope_store_pair_cs(ra, r, head, i, x1, x2, rope_cs(ra, r, i), page, slot);
 }
 
 // channel d of v head g of a row whose slot is (page, slot)
