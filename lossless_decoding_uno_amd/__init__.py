@@ -151,13 +151,15 @@ def _need(t, dtype, shape, name):
 
 
 def make_config(cfg, page_size=16, lora=True):
-    """uno_config from a shape dict (keys as in the synthetic model shapes)."""
+    """uno_config from a shape dict (keys as in the synthetic model shapes).
+    ``lora``: True (LoRA on all seven projections), False, or a lora_mask."""
     r = int(cfg["lora_rank"])
+    mask = 0x7F if lora is True else (int(lora) if lora else 0)
     return UnoConfig(int(cfg["n_layers"]), int(cfg["d_model"]), int(cfg["n_q_heads"]),
                      int(cfg["n_kv_heads"]), int(cfg["head_dim"]), int(cfg["d_ffn"]),
                      int(cfg["vocab"]), int(cfg["mask_id"]), float(cfg["rms_eps"]),
                      float(cfg["rope_theta"]), r, float(cfg["lora_alpha"]) / r,
-                     0x7F if lora else 0, int(page_size), int(cfg.get("noise_prior", 0)))
+                     mask, int(page_size), int(cfg.get("noise_prior", 0)))
 
 
 class Model:
@@ -169,6 +171,7 @@ class Model:
     are."""
 
     def __init__(self, cfg, weights, page_size=16, lora=True, device="cuda"):
+        """``lora``: True, False, or a lora_mask (bit p: projection PROJ[p])."""
         self.cfg = dict(cfg)
         self.config = make_config(cfg, page_size, lora)
         dev = torch.device(device)
