@@ -1,0 +1,65 @@
+"""GPU parity of the draft and verify passes for head layouts the model tests
+do not use: q heads per kv head G = 1, 2, 8 and 16 with head_dim 128, G = 2
+and 8 with head_dim 64 (the attention kernel takes G*K query rows per kv
+head, so these change its row-group count and key split), K = 16 and 8,
+ragged contexts, shuffled pages.  Logits against the oracle."""
+import pytest
+import torch
+
+import synth
+from oracle import spec as ospec
+
+from gpu_util import assert_logits_close, gpu_or_fail, load_kv_logical, progress
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("hq,hkv,hd,K", [(2, 2, 128, 16), (4, 2, 128, 16), (8, 1, 128, 16),
+                                         (16, 1, 128, 8), (4, 2, 64, 16), (8, 1, 64, 16)])
+def test_head_layout_draft_verify(hq, hkv, hd, K):
+    U = gpu_or_fail()
+    cfg = dict(synth.SMALL_GQA, n_q_heads=hq, n_kv_heads=hkv, head_dim=hd,
+               d_model=max(256, hq * hd))
+    wts = synth.make_weights(cfg, 31)
+    w64 = synth.to_f64(wts)
+    model = U.Model(cfg, wts)
+    ctxs = [150, 33, 517]
+    B = len(ctxs)
+    cap = max(ctxs) + 2 * K + 8
+    n_pages = B * ((cap + 15) // 16)
+    kv = U.PagedKV(cfg, B, cap, page_order=torch.randperm(
+        n_pages, generator=torch.Generator().manual_seed(hq * 10 + hkv)))
+    seqs = []
+    for b, n in enumerate(ctxs):
+        k, v = synth.kv_values(cfg, n, seed=23, seq=b)
+        load_kv_logical(kv, b, k, v)
+        toks = synth.random_tokens(n + 1, cfg["vocab"], 500 + b, (n + 1,))
+        s = ospec.Sequence(cfg, toks, capacity=cap)
+        for li in range(cfg["n_layers"]):
+            s.cache.k[li][:n] = k[li].double().numpy()
+            s.cache.v[li][:n] = v[li].double().numpy()
+        s.kv_len = n
+        seqs.append(s)
+    kv.kv_len.copy_(torch.tensor(ctxs, dtype=torch.int32))
+    ws = U.alloc_workspace(U.workspace_bytes(model, B, K, cap))
+    V = cfg["vocab"]
+    dev = "cuda"
+    zq = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    zp = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    d = torch.empty((B, K), dtype=torch.int32, device=dev)
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    anchor = torch.tensor([s.tokens[-1] for s in seqs], dtype=torch.int32, device=dev)
+    U.draft_block(model, kv, anchor, K, cap, 1.0, 0, torch.zeros(B, dtype=torch.uint64).to(dev),
+                  zq, d, ws, status)
+    rows = synth.random_tokens(K, V, 88, (B, K))
+    U.verify_block(model, kv, torch.from_numpy(rows).to(dev), cap, 1, zp, ws, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    zq_c, zp_c = zq.cpu().numpy(), zp.cpu().numpy()
+    worst = 0.0
+    for b, s in enumerate(seqs):
+        worst = max(worst, assert_logits_close(zq_c[b], ospec.draft_logits(cfg, w64, s, K),
+                                               "G %d hd %d draft %d" % (hq // hkv, hd, b)))
+        worst = max(worst, assert_logits_close(zp_c[b], ospec.verify_logits(cfg, w64, s, list(rows[b])),
+                                               "G %d hd %d verify %d" % (hq // hkv, hd, b)))
+    progress("heads %d/%d x %d, K %d: worst logit error %.2e" % (hq, hkv, hd, K, worst))
