@@ -384,16 +384,18 @@ def generate_mode(args, U, synth, torch, cfg):
     t_prefill = time.perf_counter() - t0
     log("prefill done in %.2f s; generating %d tokens" % (t_prefill, args.generate))
     t0 = time.perf_counter()
-    last = t0
-    while min(len(o) for o in g.out) < args.generate:
-        g.step()
-        if time.perf_counter() - last > 30:
-            last = time.perf_counter()
+    last = [t0]
+
+    def progress():
+        if time.perf_counter() - last[0] > 30:
+            last[0] = time.perf_counter()
             log("%d steps, %d tokens" % (g.steps, min(len(o) for o in g.out)))
+
+    outs = g.generate(args.generate, on_step=progress)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t0
     st = g.stats()
-    toks = sum(len(o) for o in g.out)
+    toks = sum(len(o) for o in outs)
     out = {"metric": "generated tokens/s (natural acceptance, end to end)",
            "value": round(toks / t_gen, 1), "unit": "tokens/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "bf16",

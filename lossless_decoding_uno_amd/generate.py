@@ -158,17 +158,36 @@ class Generator:
         self.committed_per_step.append(a + 1)
         return a
 
-    def generate(self, n_new, forced=None):
+    def generate(self, n_new, forced=None, on_step=None):
+        """Step until every sequence has n_new tokens.  A sequence that is done
+        while others are not keeps stepping with the batch, but its cache is
+        put back to the length it finished at after every step (its later
+        tokens are dropped and its steps leave the statistics), so the page
+        table never needs more than prompt + n_new + two blocks per sequence.
+        ``on_step()`` is called after every step."""
+        held = np.full(self.B, -1, dtype=np.int64)
         while min(len(o) for o in self.out) < n_new:
             self.step(None if forced is None else forced[self.steps])
+            back = [b for b in range(self.B) if held[b] >= 0]
+            for b in back:
+                self.kv_len[b] = held[b]
+                self.committed_per_step[-1][b] = 0
+            for b in range(self.B):
+                if held[b] < 0 and len(self.out[b]) >= n_new:
+                    held[b] = self.kv_len[b]
+            if back:
+                self.kv.kv_len.copy_(torch.from_numpy(self.kv_len.astype(np.int32)))
+            if on_step is not None:
+                on_step()
         self._check_status()
         return [o[:n_new] for o in self.out]
 
     def stats(self):
         per = np.array(self.committed_per_step, dtype=np.float64)   # [steps, B]
+        live = per[per > 0]            # steps of sequences not yet done
         return {"steps": self.steps,
-                "AL": float(per.mean()) if per.size else 0.0,
-                "TPF": float(per.mean() / (self.n_passes + 1)) if per.size else 0.0,
+                "AL": float(live.mean()) if live.size else 0.0,
+                "TPF": float(live.mean() / (self.n_passes + 1)) if live.size else 0.0,
                 "pages_in_use": self.pool.pages_in_use()}
 
     def _check_status(self):
