@@ -138,3 +138,31 @@ def test_tree_generation_matches_oracle_step_by_step():
     progress("tree generation: %d steps, TPF %.2f, AL %.2f, %d K/V moves, worst logit err %.2e"
              % (st["steps"], st["TPF"], st["AL"], moves, worst))
     assert 2.0 <= st["AL"] <= K + 1
+
+
+def test_generate_holds_finished_sequences():
+    """Batched generation to a fixed length with a page table sized for
+    prompt + n_new + two blocks: sequences that are done hold their cache
+    length while the rest finish (no sequence outgrows its table), every
+    sequence returns exactly n_new tokens, and the statistics count only the
+    steps of unfinished sequences."""
+    U = gpu_or_fail()
+    from lossless_decoding_uno_amd.generate import Generator
+    cfg = synth.TINY
+    model = U.Model(cfg, synth.make_weights(cfg, 0))
+    B, K, P, n_new = 6, 4, 20, 60
+    prompts = np.stack([synth.prompt_ids(cfg, P, 70 + b) for b in range(B)])
+    max_ctx = P + n_new + 2 * K + 1
+    g = Generator(model, B, K, max_ctx, seed=SEED, prefill_chunk=16)
+    g.prefill(prompts)
+    outs = g.generate(n_new)
+    assert [len(o) for o in outs] == [n_new] * B
+    assert (g.kv_len <= P - 1 + n_new + K).all()
+    assert np.array_equal(g.kv.kv_len.cpu().numpy(), g.kv_len.astype(np.int32))
+    per = np.array(g.committed_per_step)
+    assert (per >= 0).all() and (per <= K + 1).all()
+    assert int(g.status.abs().sum().item()) == 0
+    st = g.stats()
+    assert 1.0 <= st["AL"] <= K + 1
+    progress("generation held: %d steps, AL %.2f, kv_len %s" % (st["steps"], st["AL"],
+                                                                 g.kv_len.tolist()))
