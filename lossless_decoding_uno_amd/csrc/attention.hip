@@ -54,23 +54,30 @@ __device__ __forceinline__ int row_limit(int j, int kvl, int K, int pos_offset, 
 __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
-constexpr int kStages = 4;         // KV chunks of 64 keys resident in LDS
 constexpr int kMaxPagesLds = 2048; // page ids of one key range cached in LDS
+constexpr int kCUs = 256;
 
 // A workgroup of RW x KH waves owns 16*RW query rows of one (sequence, kv
 // head) -- row group rg = w % RW the rows 16rg..16rg+15 -- and one range of
 // keys, walked in chunks of 64 keys; with KH = 2 the two waves of a row group
 // take one half (32 keys) of every chunk each, with their own online softmax,
-// and are merged through LDS at the end (twice the waves for the same LDS).  Chunks stream HBM -> LDS with global_load_lds_dwordx4 (no registers),
-// kStages deep, and every wave reads each chunk from LDS.  LDS layouts
+// and are merged through LDS at the end (twice the waves for the same LDS).
+// Chunks stream HBM -> LDS with global_load_lds_dwordx4 (no registers; with
+// the non-temporal hint, since each KV byte is read once per pass), ST deep,
+// and every wave reads each chunk from LDS.  ST = 4 stages (136 KB of LDS at
+// head_dim 128) keep one workgroup per CU three chunks ahead; where the grid
+// fills two workgroups per CU, ST = 2 (72 KB) lets two reside and cover each
+// other's waits (the 8-wave kernel is then held to 128 VGPRs, 4 waves per
+// SIMD).  LDS layouts
 // (16-byte chunks XOR-swizzled; the swizzle is applied by choosing which
 // source address each lane loads, since lane i of a DMA writes 16*i):
 //   K: [64 keys][HD]  row = one key,      chunk index ^ kswz(key) % (HD/8)
 //   V: [HD][64 keys]  row = one channel,  key-group index ^ vswz(channel)
 // TREE: the rows are a token tree's nodes (ancestor-bit mask past the context).
-template <int HD, int RW, int KH, bool TREE>
-__global__ void __launch_bounds__(RW * KH * 64)
+template <int HD, int RW, int KH, bool TREE, int ST>
+__global__ void __launch_bounds__(RW * KH * 64, ST == 2 ? RW * KH / 2 : 1)
 k_attention(AttnArgs a) {
+  constexpr int kStages = ST;
   constexpr int NW = RW * KH;             // waves per workgroup
   constexpr int NH = 2 / KH;              // 32-key halves of a chunk per wave
   constexpr int DS = HD / 32;             // 32-channel MFMA steps of S
@@ -152,29 +159,27 @@ k_attention(AttnArgs a) {
   const size_t head_stride = (size_t)HD << psh;   // elements of one (page, head) block
   const size_t page_stride = head_stride * a.Hkv;  // elements of one page (all heads)
   // Per lane and DMA instruction, the key it copies (offset in the chunk) and
-  // its element offset inside the page are fixed; per chunk only the page id
-  // changes.  Instructions 0..NINSTR/2-1 of a chunk copy K, the rest V (a wave
-  // may own instructions of both kinds when the workgroup has one wave).
+  // its byte offset from the K or V base inside the page are fixed; per chunk
+  // only the page id changes.  Instructions 0..NINSTR/2-1 of a chunk copy K,
+  // the rest V (a wave may own instructions of both kinds when the workgroup
+  // has one wave).  Both are packed in one register per instruction: the byte
+  // offset (< 2^17: at most 256 keys x 128 channels x 2 bytes) in the low 24
+  // bits, the key (0..63) above.
   const uint16_t* kbase = a.k_layer + (size_t)g * head_stride;
   const uint16_t* vbase = a.v_layer + (size_t)g * head_stride;
-  int koff[IW];                 // key offset in the chunk, 0..63
-  int pic[IW];                  // which of the chunk's pages holds that key
-  uint64_t gsrc[IW];            // source byte address with the page term left out
+  uint32_t slot[IW];
 #pragma unroll
   for (int ii = 0; ii < IW; ++ii) {
     const int ins = w * IW + ii;
     if (ins < NINSTR / 2) {                      // K: 1024/KROW keys per instruction
       const int key = ins * (1024 / KROW) + l / KCH;
       const int ch = (l % KCH) ^ (kswz(key) & (KCH - 1));
-      koff[ii] = key;
-      gsrc[ii] = (uint64_t)(uintptr_t)(kbase + (key & pmask) * HD + ch * 8);
+      slot[ii] = (uint32_t)(((key & pmask) * HD + ch * 8) * 2) | ((uint32_t)key << 24);
     } else {                                     // V: 8 channels per instruction
       const int d = (ins - NINSTR / 2) * 8 + l / 8;
       const int kg8 = (l % 8) ^ vswz(d);
-      koff[ii] = kg8 * 8;
-      gsrc[ii] = (uint64_t)(uintptr_t)(vbase + (d << psh) + ((kg8 * 8) & pmask));
+      slot[ii] = (uint32_t)(((d << psh) + ((kg8 * 8) & pmask)) * 2) | ((uint32_t)(kg8 * 8) << 24);
     }
-    pic[ii] = koff[ii] >> psh;                   // 0 when pages hold >= 64 keys
   }
   const uint32_t page_bytes = (uint32_t)(page_stride * sizeof(uint16_t));
   const uint64_t safe_src = (uint64_t)(uintptr_t)a.k_layer;   // any readable address
@@ -185,24 +190,35 @@ k_attention(AttnArgs a) {
     const int pb = (k0 >> psh) - p_lo;           // first page of the chunk in the list
     // bytes from a page's start to key k0 (nonzero only for pages > 64 keys)
     const uint32_t in_page = (uint32_t)((k0 & pmask) & ~63);
+    // the packed words enter each chunk's address arithmetic through an empty
+    // asm statement, so that the compiler cannot hoist IW 64-bit addresses
+    // out of the chunk loop (they would not fit the register budget)
+    uint32_t sl[IW];
+#pragma unroll
+    for (int ii = 0; ii < IW; ++ii) {
+      sl[ii] = slot[ii];
+      asm volatile("" : "+v"(sl[ii]));
+    }
     int pgv[IW];
 #pragma unroll
-    for (int ii = 0; ii < IW; ++ii) pgv[ii] = pages[pb + pic[ii]];
+    // key (0..63) first, then its page: psh reaches 8, and one 32-bit shift
+    // by 24 + psh = 32 would be undefined
+    for (int ii = 0; ii < IW; ++ii) pgv[ii] = pages[pb + (int)((sl[ii] >> 24) >> psh)];
     if (any_missing) {
 #pragma unroll
       for (int ii = 0; ii < IW; ++ii)
-        if (k0 + koff[ii] >= hi) pgv[ii] = -1;
+        if (k0 + (int)(sl[ii] >> 24) >= hi) pgv[ii] = -1;
     }
     const uint32_t stage = __builtin_amdgcn_readfirstlane(lds_base + (c % kStages) * STAGE);
 #pragma unroll
     for (int ii = 0; ii < IW; ++ii) {
-      const bool is_k = w * IW + ii < NINSTR / 2;
+      const bool is_k = w * IW + ii < NINSTR / 2;   // wave-uniform
       const int page = pgv[ii];
       const uint32_t pu = page < 0 ? 0u : (uint32_t)page;
-      uint64_t src = gsrc[ii] + (uint64_t)pu * page_bytes +
-                     (uint64_t)(in_page * (is_k ? HD * 2u : 2u));
+      uint64_t src = (uint64_t)(uintptr_t)(is_k ? kbase : vbase) + (sl[ii] & 0xFFFFFFu) +
+                     (uint64_t)pu * page_bytes + (uint64_t)(in_page * (is_k ? HD * 2u : 2u));
       src = page < 0 ? safe_src : src;           // zeroed below when used
-      lds_dma16((const void*)(uintptr_t)src, stage + ii * 1024);
+      lds_dma16_nt((const void*)(uintptr_t)src, stage + ii * 1024);
     }
   };
 
@@ -474,12 +490,21 @@ AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx) {
   const long groups = (long)B * c.n_kv_heads * p.n_qgroups;
   const long ctx = max_ctx > 1 ? max_ctx : 1;
   const long by_len = (ctx + 255) / 256;       // at least 4 chunks of 64 keys per range
-  long ns = (256 + groups - 1) / groups;       // one workgroup per CU
-  if (ns > by_len) ns = by_len;
   const long max_len = (long)(kMaxPagesLds - 2) * c.page_size - 64;
   const long by_lds = (ctx + max_len - 1) / max_len;
-  if (ns < by_lds) ns = by_lds;
-  if (ns < 1) ns = 1;
+  // key ranges for `per_cu` workgroups per CU, within the limits above
+  auto splits_for = [&](long per_cu) {
+    long ns = (per_cu * kCUs + groups - 1) / groups;
+    if (ns > by_len) ns = by_len;
+    if (ns < by_lds) ns = by_lds;
+    return ns < 1 ? 1L : ns;
+  };
+  long ns = splits_for(1);                     // one workgroup per CU, 4 stages
+  p.stages = 4;
+  if (c.head_dim == 128 && groups * splits_for(2) >= 2 * kCUs) {
+    ns = splits_for(2);                        // two per CU, 2 stages each
+    p.stages = 2;
+  }
   p.n_wave_splits = (int)ns;
   const long sl = (ctx + ns - 1) / ns;
   p.split_len = (int)((sl + 63) / 64 * 64);
@@ -492,25 +517,29 @@ size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx) {
   return align_up(parts * c.head_dim * sizeof(float), 256) + align_up(parts * 2 * sizeof(float), 256);
 }
 
-template <int HD, bool TREE>
+template <int HD, bool TREE, int ST>
 static hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.plan.n_wave_splits, a.plan.n_qgroups, a.B * a.Hkv);
-  const size_t lds = (size_t)kStages * 2 * 64 * HD * 2 + kMaxPagesLds * sizeof(int);
+  const size_t lds = (size_t)ST * 2 * 64 * HD * 2 + kMaxPagesLds * sizeof(int);
   const int kh = a.plan.key_halves;
   const dim3 block(64 * a.plan.waves * kh);
   switch (a.plan.waves * 10 + kh) {
-    case 12: hipLaunchKernelGGL((k_attention<HD, 1, 2, TREE>), grid, block, lds, s, a); break;
-    case 22: hipLaunchKernelGGL((k_attention<HD, 2, 2, TREE>), grid, block, lds, s, a); break;
-    case 42: hipLaunchKernelGGL((k_attention<HD, 4, 2, TREE>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_attention<HD, 8, 1, TREE>), grid, block, lds, s, a); break;
+    case 12: hipLaunchKernelGGL((k_attention<HD, 1, 2, TREE, ST>), grid, block, lds, s, a); break;
+    case 22: hipLaunchKernelGGL((k_attention<HD, 2, 2, TREE, ST>), grid, block, lds, s, a); break;
+    case 42: hipLaunchKernelGGL((k_attention<HD, 4, 2, TREE, ST>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_attention<HD, 8, 1, TREE, ST>), grid, block, lds, s, a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.tree_anc)
-    return a.hd == 128 ? launch_attention_hd<128, true>(a, s) : launch_attention_hd<64, true>(a, s);
-  return a.hd == 128 ? launch_attention_hd<128, false>(a, s) : launch_attention_hd<64, false>(a, s);
+  const bool two = a.plan.stages == 2;   // head_dim 128 only
+  if (a.tree_anc) {
+    if (a.hd != 128) return launch_attention_hd<64, true, 4>(a, s);
+    return two ? launch_attention_hd<128, true, 2>(a, s) : launch_attention_hd<128, true, 4>(a, s);
+  }
+  if (a.hd != 128) return launch_attention_hd<64, false, 4>(a, s);
+  return two ? launch_attention_hd<128, false, 2>(a, s) : launch_attention_hd<128, false, 4>(a, s);
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {

@@ -187,6 +187,7 @@ struct AttnPlan {
   int n_qgroups;        // groups of 16*waves query rows
   int n_wave_splits;    // key ranges per query group
   int split_len;        // keys per range (multiple of 64; the last runs to the end)
+  int stages;           // KV chunks resident in LDS per workgroup (2 or 4)
 };
 AttnPlan attn_plan(const uno_config& c, int B, int K, int max_ctx);
 size_t attn_ws_bytes(const uno_config& c, int B, int K, int max_ctx);
