@@ -47,8 +47,8 @@ BF16_PEAK_TFLOPS = 2500.0
 # attention profile summary under profiles/): mean FETCH_SIZE and WRITE_SIZE per
 # dispatch, scaled by the copy calibration factor, for the kernel source with
 # this digest.
-ATTN_TRAFFIC = {"source": "1adee9fde3195b47", "bytes_per_launch": 2459161969,
-                "fetch_kib": 1196707.5, "write_kib": 8192, "fetch_factor": 1.99993, "write_factor": 1.0}
+ATTN_TRAFFIC = {"source": "ee3f05b880047b37", "bytes_per_launch": 2460727231,
+                "fetch_kib": 1196956.97, "write_kib": 9216.0, "fetch_factor": 1.99994, "write_factor": 1.0}
 ATTN_SOURCES = ["lossless_decoding_uno_amd/csrc/attention.hip",
                 "lossless_decoding_uno_amd/csrc/uno_device.h"]
 
@@ -181,8 +181,10 @@ def gemm_flops_per_pass(cfg, R, draft):
 
 
 def measured_ceilings(torch):
-    """Streaming ceilings measured on this GPU with library kernels: a 2 GiB read
-    (torch sum) and a 1 GiB copy (read + write bytes)."""
+    """Streaming rates of torch's own kernels on this GPU, for context: a 2 GiB
+    read (torch sum) and a 1 GiB copy (read + write bytes).  They are not the
+    HBM's ceiling: a plain streaming read with 16-byte loads reaches ~6.3 TB/s,
+    and ~7.1 TB/s with the non-temporal hint."""
     x = torch.ones((1 << 31) // 4, dtype=torch.float32, device="cuda")
     y = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -199,8 +201,8 @@ def measured_ceilings(torch):
         best_c = min(best_c, ev[2].elapsed_time(ev[3]))
     del x, y
     torch.cuda.empty_cache()
-    return {"read_GBps": round((1 << 31) / (best_r / 1e3) / 1e9, 1),
-            "copy_GBps": round(2 * (1 << 30) / (best_c / 1e3) / 1e9, 1)}
+    return {"torch_sum_read_GBps": round((1 << 31) / (best_r / 1e3) / 1e9, 1),
+            "torch_copy_GBps": round(2 * (1 << 30) / (best_c / 1e3) / 1e9, 1)}
 
 
 def library_gemm_reference(torch, cfg, R):
@@ -590,8 +592,6 @@ def main():
                 "frac": None, "traffic": None, "kernel": dominant, "launches": int(used),
                 "avg_launch_us": avg_us}
     ceil = measured_ceilings(torch)
-    if roof["unit"] == "GB/s" and roof["achieved"] is not None:
-        roof["frac_of_measured_read"] = round(roof["achieved"] / ceil["read_GBps"], 4)
     # MFMA fraction of the projection GEMMs (both passes) from the probe step
     gemm_ms = sum(classes[k] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"))
     gfl = gemm_flops_per_pass(cfg, R, True) + gemm_flops_per_pass(cfg, R, False)
@@ -614,7 +614,7 @@ def main():
                "parallelism": "none (1 GPU)"},
            "roofline": roof,
            "roofline_gemm": roof_gemm,
-           "measured_ceilings": ceil,
+           "torch_streaming": ceil,
            "verify_step": {"ms_per_step": round(W.verify_ms / args.steps, 3),
                            "hbm_GBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9, 1),
                            "frac_of_8TBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9
