@@ -115,9 +115,9 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_off) {
                : "s"(m0v), "v"(src)
                : "memory", "m0");
 }
-// The same with the non-temporal hint, for data read once per launch (KV
-// pages, streamed weights): on gfx950 a stream of such loads moves ~7.1 TB/s
-// from HBM against ~6.3 TB/s without the hint.
+// The same with the non-temporal hint, for data read once per launch (the KV
+// pages of a pass): on gfx950 a stream of such loads moves ~7.1 TB/s from HBM
+// against ~6.3 TB/s without the hint.
 __device__ __forceinline__ void lds_dma16_nt(const void* src, uint32_t lds_off) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_off);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
@@ -165,12 +165,6 @@ __device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, uint32_t voff, uint32_
                                               uint32_t lds_off) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_off);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma16_buf_nt(i32x4 rsrc, uint32_t voff, uint32_t soff,
-                                                 uint32_t lds_off) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_off);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
