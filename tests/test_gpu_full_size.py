@@ -148,17 +148,20 @@ def test_8b_batch64_context_9216(big):
     _run(big, 64, 9216, 37)
 
 
-def test_8b_width_one_layer_tree_sampler(big1):
-    """Tree sampler at 8B width (one layer), batch 2, context 1023, K = 16,
-    top-2 per drafted position, 8 kept candidates (121 node rows per
+@pytest.mark.parametrize("ctx", [1023, 2100])
+def test_8b_width_one_layer_tree_sampler(big1, ctx):
+    """Tree sampler at 8B width (one layer), batch 2, context 1023 and 2100,
+    K = 16, top-2 per drafted position, 8 kept candidates (121 node rows per
     sequence): the tree built from the GPU's draft logits equals the oracle's
     tree on the same fp32 logits; every node's verify logits (121 x 151936)
     agree elementwise with the oracle's bf16-activation forward over the
-    tree; the draws and the walk equal the oracle's on the GPU's logits."""
+    tree; the draws and the walk equal the oracle's on the GPU's logits.
+    At context 2100 the tree-masked attention has 8 key ranges per (sequence,
+    kv head, row group), 512 workgroups, and takes its two-stage form."""
     from oracle import canonical as cn
     from oracle import tree as ot
     U, cfg, wts, w64, model = big1
-    B, ctx, b_check, topk, n_keep = 2, 1023, 1, 2, 8
+    B, b_check, topk, n_keep = 2, 1, 2, 8
     N = U.tree_rows(K, topk, n_keep)
     cap = ctx + N + K + 8
     kv = U.PagedKV(cfg, B, cap, page_order=torch.randperm(
