@@ -180,7 +180,7 @@ def gemm_flops_per_pass(cfg, R, draft):
     return 2.0 * R * per_layer * cfg["n_layers"]
 
 
-def measured_ceilings(torch):
+def torch_streaming_rates(torch):
     """Streaming rates of torch's own kernels on this GPU, for context: a 2 GiB
     read (torch sum) and a 1 GiB copy (read + write bytes).  They are not the
     HBM's ceiling: a plain streaming read with 16-byte loads reaches ~6.3 TB/s,
@@ -591,7 +591,7 @@ def main():
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": dominant, "launches": int(used),
                 "avg_launch_us": avg_us}
-    ceil = measured_ceilings(torch)
+    ceil = torch_streaming_rates(torch)
     # MFMA fraction of the projection GEMMs (both passes) from the probe step
     gemm_ms = sum(classes[k] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"))
     gfl = gemm_flops_per_pass(cfg, R, True) + gemm_flops_per_pass(cfg, R, False)
