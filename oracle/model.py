@@ -25,17 +25,18 @@ Everything here is fp64 numpy on logical (unpacked) weight layouts:
   v [Hkv*hd, D], o [D, Hq*hd], gate [F, D], up [F, D], down [D, F];
   LoRA: lora_a[p] [r, in_p], lora_b[p] [out_p, r] for p in PROJ.
 
-Precision.  By default every step is fp64 (the exact reference).  With
-``act_round=bf16_round`` the forward additionally rounds, to bfloat16
-(round-to-nearest-even), the activations a bf16 matrix-core implementation
-must hand to its bf16 products and its bf16 KV cache: the normalised inputs of
-every linear, the LoRA intermediate s*g*(x A^T), k and v (the cache entries),
-the attention output and the SwiGLU product.  Queries and softmax weights stay
-exact: an implementation can keep them at about twice bf16 precision by
-splitting them into two bf16 parts.  The pages fix no
-precision; this mode is the plainest model of "the same computation with bf16
-activations" and serves the deep full-size checks, where exact-arithmetic
-deviations of bf16 activations compound with depth.
+Precision.  By default every step is fp64 (the exact reference, and the one
+the parity tests gate on).  With ``act_round=bf16_round`` the forward models a
+plain bfloat16 implementation of the same computation: every operand of every
+matrix product that is not a (bf16) weight is rounded to bfloat16
+(round-to-nearest-even), and the products themselves are exact.  Those operands
+are the normalised inputs of the seven projections and of the LM head, the LoRA
+intermediate s*g*(x A^T), the queries and keys (after RoPE) and the values of
+the attention products, the softmax weights that multiply the values, the
+attention output and the SwiGLU product.  The pages fix no precision; the
+configurations name a bf16 model.  This mode is a yardstick, not a target: it
+says how far from the exact logits a bf16 implementation of this shape lands,
+so a GPU path can be held to "no less accurate than plain bf16".
 
 Parity: logit VALUES are "parity unpinned" against the pages (none are printed).
 Structural pins in tests/test_oracle_model.py: LoRA linear == dense
@@ -112,10 +113,11 @@ class KVCache:
         return c
 
 
-def attention(q, cache_k, cache_v, key_limit, n_kv_heads, key_sets=None):
+def attention(q, cache_k, cache_v, key_limit, n_kv_heads, key_sets=None, p_round=None):
     """Per row r and q head h: softmax over keys 0..key_limit[r] of the cache,
     or over the cache slots listed in key_sets[r] when ``key_sets`` is given
     (a token tree's rows see the context and their own ancestors only).
+    ``p_round`` rounds the softmax weights before they multiply the values.
 
     q [R, Hq, hd]; cache_k/v [cap, Hkv, hd]; returns [R, Hq, hd].
     """
@@ -138,12 +140,14 @@ def attention(q, cache_k, cache_v, key_limit, n_kv_heads, key_sets=None):
                 s = s - s.max()
                 p = np.exp(s)
                 p = p / p.sum()
+                if p_round is not None:
+                    p = p_round(p)
                 out[r, h] = p @ vg[idx]
     return out
 
 
 def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=None,
-            slots=None, key_sets=None):
+            slots=None, key_sets=None, taps=None):
     """One pass over a block of rows of ONE sequence.
 
     Writes the block's K/V (after RoPE) into ``cache`` at ``pos`` before the
@@ -154,6 +158,9 @@ def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=Non
     A token tree's rows sit at positions (RoPE) that differ from the cache
     slots holding their K/V: ``slots`` then gives the slots, and ``key_sets``
     the slots each row attends to (``key_limit`` is then unused).
+
+    ``taps`` (a list) receives a copy of the residual rows h entering each
+    layer, in layer order (the inputs a per-layer comparison starts from).
     """
     rd = act_round if act_round is not None else (lambda v: v)
     ids = np.asarray(ids)
@@ -166,6 +173,9 @@ def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=Non
     slots = pos if slots is None else np.asarray(slots)
     h = wts["embed"][ids].astype(np.float64)
     for li, lw in enumerate(wts["layers"]):
+        if taps is not None:
+            taps.append(h.copy())
+
         def lin(x, p):
             a = lw["lora_a"].get(p) if lora else None
             b = lw["lora_b"].get(p) if lora else None
@@ -175,11 +185,11 @@ def forward(cfg, wts, cache, ids, pos, gate, key_limit, lora=True, act_round=Non
         q = lin(x, "q").reshape(R, Hq, hd)
         k = lin(x, "k").reshape(R, Hkv, hd)
         v = rd(lin(x, "v").reshape(R, Hkv, hd))
-        q = rope(q, pos, cfg["rope_theta"])
+        q = rd(rope(q, pos, cfg["rope_theta"]))
         k = rd(rope(k, pos, cfg["rope_theta"]))
         cache.k[li][slots] = k
         cache.v[li][slots] = v
-        o = rd(attention(q, cache.k[li], cache.v[li], key_limit, Hkv, key_sets)
+        o = rd(attention(q, cache.k[li], cache.v[li], key_limit, Hkv, key_sets, act_round)
                .reshape(R, Hq * hd))
         h = h + lin(o, "o")
         x = rd(rms_norm(h, lw["mlp_norm"], eps))

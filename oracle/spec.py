@@ -91,7 +91,7 @@ def prefill(cfg, wts, seq):
     seq.kv_len = n - 1
 
 
-def draft_logits(cfg, wts, seq, K, act_round=None, draws=None, block=None):
+def draft_logits(cfg, wts, seq, K, act_round=None, draws=None, block=None, taps=None):
     """Draft pass: rows [anchor, noise x (K-1)], gate (0, 1, ..., 1). fp64 [K, V].
 
     The noisy block is the anchor followed by K-1 tokens from the diffusion
@@ -111,7 +111,7 @@ def draft_logits(cfg, wts, seq, K, act_round=None, draws=None, block=None):
     pos = n0 + np.arange(K)
     gate = np.array([0.0] + [1.0] * (K - 1))
     lim = np.array([n0] + [n0 + K - 1] * (K - 1))
-    return forward(cfg, wts, seq.cache, rows, pos, gate, lim, act_round=act_round)
+    return forward(cfg, wts, seq.cache, rows, pos, gate, lim, act_round=act_round, taps=taps)
 
 
 def draft_sample(zq32, inv_temp, draws, slot=SLOT_DRAFT):
@@ -137,11 +137,12 @@ def draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws):
     return zq, zq32, block
 
 
-def verify_logits(cfg, wts, seq, rows, pos_offset=1, act_round=None):
+def verify_logits(cfg, wts, seq, rows, pos_offset=1, act_round=None, taps=None):
     """Verify pass with AR weights, causal: row j at position kv_len+pos_offset+j."""
     K = len(rows)
     pos = seq.kv_len + pos_offset + np.arange(K)
-    return forward(cfg, wts, seq.cache, rows, pos, np.zeros(K), pos, act_round=act_round)
+    return forward(cfg, wts, seq.cache, rows, pos, np.zeros(K), pos, act_round=act_round,
+                   taps=taps)
 
 
 def spec_accept(zq32, zp32, drafts, inv_temp, draws, forced=None):

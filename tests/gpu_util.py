@@ -45,6 +45,74 @@ def assert_logits_close(got, ref, what):
     return float(err.max())
 
 
+# Parity of a bf16 path against the EXACT oracle where plain bf16 arithmetic
+# itself cannot meet the stated bar everywhere (8B width; sharpened LM heads).
+# The oracle's bf16 mode -- every operand of every matrix product rounded to
+# bfloat16, the products exact -- is the yardstick: a bf16 implementation of
+# this shape puts a small fraction of logits outside 2e-2 + 1e-2 |z| of the
+# exact values by rounding alone (about 0.3% at one layer of 8B width).  The
+# GPU path must be no less accurate than that yardstick, counted in the stated
+# bar, and no logit may be farther from the exact one than CAP_RATIO times the
+# bar (the yardstick's own worst logit is about twice the bar at one layer).
+CAP_RATIO = 3.0
+
+
+def yardstick_counts(got, exact, bf16_model):
+    """(logits of got outside the bar, of bf16_model outside it, got's worst
+    error / bar, got's largest error), all against the exact logits."""
+    got = np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    bar = LOGIT_ATOL + LOGIT_RTOL * np.abs(exact)
+    e_got = np.abs(got - exact)
+    e_bf = np.abs(np.asarray(bf16_model, dtype=np.float64) - exact)
+    return int((e_got > bar).sum()), int((e_bf > bar).sum()), float((e_got / bar).max()), \
+        float(e_got.max())
+
+
+def assert_within_cap(got, exact, what, cap=CAP_RATIO):
+    """Every logit within cap times the stated bar of the exact one."""
+    got = np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    bar = LOGIT_ATOL + LOGIT_RTOL * np.abs(exact)
+    ratio = np.abs(got - exact) / bar
+    assert ratio.max() <= cap, "%s: logit error %.3g times the bar at %s (cap %.1f)" % (
+        what, float(ratio.max()), np.unravel_index(np.argmax(ratio), ratio.shape), cap)
+    return float(ratio.max())
+
+
+def assert_no_less_accurate(got, exact, bf16_model, what, cap=CAP_RATIO):
+    """The yardstick criterion on one set of logits: every logit within cap
+    times the bar, and no more logits outside the bar than the bf16 model has.
+    Returns (n_got, n_bf16, worst ratio, largest error)."""
+    n_got, n_bf, worst, emax = yardstick_counts(got, exact, bf16_model)
+    assert_within_cap(got, exact, what, cap)
+    assert n_got <= n_bf, "%s: %d logits outside the bar, the bf16 yardstick %d" % (
+        what, n_got, n_bf)
+    return n_got, n_bf, worst, emax
+
+
+class YardstickTally:
+    """The yardstick criterion over many comparisons: each comparison checks
+    the cap on every logit at once, the counts outside the bar are summed and
+    compared at the end (``finish``), where they are large enough to compare."""
+
+    def __init__(self, what):
+        self.what, self.n_got, self.n_bf, self.worst = what, 0, 0, 0.0
+
+    def add(self, got, exact, bf16_model, where):
+        n_g, n_b, ratio, _ = yardstick_counts(got, exact, bf16_model)
+        assert_within_cap(got, exact, "%s %s" % (self.what, where))
+        self.n_got += n_g
+        self.n_bf += n_b
+        self.worst = max(self.worst, ratio)
+
+    def finish(self):
+        assert self.n_got <= self.n_bf, "%s: %d logits outside the bar, the bf16 yardstick %d" % (
+            self.what, self.n_got, self.n_bf)
+        return "%d logits outside the bar (bf16 yardstick %d), worst %.3g x bar" % (
+            self.n_got, self.n_bf, self.worst)
+
+
 def u24(seed, slot, j, b, step):
     return uniform24(seed, slot, j, b, step)
 

@@ -9,10 +9,13 @@ uno_tree_accept, uno_tree_commit) against oracle.tree.
   independent best-first enumeration and the tree against its invariants.
 * Tree steps on small models (LM head scaled up so that walks go deep): the
   tree built on the GPU from its draft logits equals the oracle's tree built
-  from the same fp32 logits; draft and verify logits of every node, divided
-  by the LM head's scale factor (the rounding error of the bf16 activations
-  grows with it), agree with the oracle's forward (bf16-activation mode)
-  within 2e-2 abs + 1e-2 rel;
+  from the same fp32 logits; draft and verify logits of every node are
+  compared with the exact oracle's forward: within 2e-2 abs + 1e-2 rel where
+  the head is not scaled; where it is scaled by s the logits, and the rounding
+  error of any bf16 implementation with them, grow s-fold, and the bf16
+  yardstick applies instead (tests/gpu_util.py: every logit within 3x the bar,
+  and over the whole test no more logits outside the bar than the oracle's
+  bf16 mode puts there);
   the per-node draws and the walk (a, committed, extra token, path) equal the
   oracle's on the GPU's verify logits; both sides commit the same path, so the
   next step's logits (and a direct read of the cache) check the moved K/V.
@@ -29,7 +32,8 @@ from oracle import model as om
 from oracle import spec as ospec
 from oracle import tree as ot
 
-from gpu_util import assert_logits_close, gpu_or_fail, kv_to_logical, progress, u24
+from gpu_util import (YardstickTally, assert_logits_close, gpu_or_fail, kv_to_logical,
+                      progress, u24)
 
 pytestmark = pytest.mark.gpu
 
@@ -213,6 +217,14 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
     status = torch.zeros(B, dtype=torch.int32, device=dev)
     step_g = torch.zeros(B, dtype=torch.uint64).to(dev)
     worst, depths, moves = 0.0, [], 0
+    tally = YardstickTally("%s logits" % name)
+
+    def compare(got, exact, bf, where):
+        if head_scale == 1.0:
+            return assert_logits_close(got, exact, "%s %s" % (name, where))
+        tally.add(got, exact, bf, where)
+        return float(np.abs(got - exact).max())
+
     for st in range(n_steps):
         anchor = torch.tensor([s.tokens[-1] for s in seqs], dtype=torch.int32, device=dev)
         U.draft_block(model, kv, anchor, K, max_ctx, inv_t, SEED, step_g, zq_g, d_g, ws, status)
@@ -223,18 +235,21 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
         d_all, a_all, c_all = d_g.cpu().numpy(), a_g.cpu().numpy(), c_g.cpu().numpy()
         e_all, path_all, smp = e_g.cpu().numpy(), tb.path.cpu().numpy(), tb.sample.cpu().numpy()
         for b, s in enumerate(seqs):
-            zq = ospec.draft_logits(cfg, w64, s, K, act_round=om.bf16_round)
-            worst = max(worst, assert_logits_close(zq_all[b] / head_scale, zq / head_scale,
-                                                   "%s draft b%d step %d" % (name, b, st)))
+            s_bf = s.copy() if head_scale != 1.0 else None
+            zq = ospec.draft_logits(cfg, w64, s, K)
+            zq_bf = (ospec.draft_logits(cfg, w64, s_bf, K, act_round=om.bf16_round)
+                     if s_bf is not None else None)
+            worst = max(worst, compare(zq_all[b], zq, zq_bf, "draft b%d step %d" % (b, st)))
             w0, _ = cn.row_weights(zq_all[b, 0], inv_t)
             d1 = cn.categorical(w0, u24(SEED, 0, 0, b, st))
             assert d_all[b, 0] == d1
             tree = ot.build_tree(zq_all[b], d1, topk, n_keep)
             _check_tree_equal(tb, b, tree)
-            zp = ot.tree_verify_logits(cfg, w64, s, tree, act_round=om.bf16_round)
-            worst = max(worst, assert_logits_close(zp_all[b, : tree.n_nodes] / head_scale,
-                                                   zp / head_scale,
-                                                   "%s tree verify b%d step %d" % (name, b, st)))
+            zp = ot.tree_verify_logits(cfg, w64, s, tree)
+            zp_bf = (ot.tree_verify_logits(cfg, w64, s_bf, tree, act_round=om.bf16_round)
+                     if s_bf is not None else None)
+            worst = max(worst, compare(zp_all[b, : tree.n_nodes], zp, zp_bf,
+                                       "tree verify b%d step %d" % (b, st)))
             for n in range(tree.n_nodes):
                 wn, _ = cn.row_weights(zp_all[b, n], inv_t)
                 assert smp[b, n] == cn.categorical(wn, u24(SEED, 2, tree.depth[n] + 1, b, st))
@@ -247,6 +262,9 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
             depths.append(a)
             moves += sum(1 for d in range(1, a) if path[d] != d)
             ot.tree_commit(s, path, a, committed)
+            for li in range(cfg["n_layers"]):      # the GPU stores the committed K/V in bf16
+                s.cache.k[li][:] = om.bf16_round(s.cache.k[li])
+                s.cache.v[li][:] = om.bf16_round(s.cache.v[li])
         U.tree_commit(model, kv, tb, a_g, step_g, status)
         kvl = kv.kv_len.cpu().numpy()
         assert [int(x) for x in kvl] == [s.kv_len for s in seqs]
@@ -257,6 +275,7 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
             kg, vg = kv_to_logical(kv, li, b, s.kv_len)
             assert_logits_close(kg, s.cache.k[li][: s.kv_len], "%s K layer %d b%d" % (name, li, b))
             assert_logits_close(vg, s.cache.v[li][: s.kv_len], "%s V layer %d b%d" % (name, li, b))
-    progress("tree steps %s: worst logit error %.2e, accept lengths %s, %d K/V moves"
-             % (name, worst, np.bincount(depths).tolist(), moves))
+    summary = tally.finish() if head_scale != 1.0 else "elementwise within the bar"
+    progress("tree steps %s: worst logit error %.2e (%s), accept lengths %s, %d K/V moves"
+             % (name, worst, summary, np.bincount(depths).tolist(), moves))
     assert moves >= min_moves, "no walked node left its slot: the K/V moves were not exercised"

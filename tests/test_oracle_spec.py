@@ -370,3 +370,96 @@ def test_chi_square_first_token_law_1e6_samples():
         keep = exp > 5
         stat, pval = scipy.stats.chisquare(obs[keep], exp[keep] * obs[keep].sum() / exp[keep].sum())
         assert pval > 0.01, (j, pval)
+
+
+# ---------------- the tiny model: the second committed token over 10^6 steps ----------------
+
+def _tiny_second_token_replay(cfg, w, prompt, n, seed, inv_t=1.0):
+    """One K = 2 step of the tiny model from ``prompt``, replayed for sequences
+    b = 0..n-1 at step 0 with the oracle's sampler arithmetic, vectorised.
+    The draft rows q_1, q_2 do not depend on the drafted tokens; the verify row
+    p_2 depends on d_1 only (causal), so it is computed once per value of d_1.
+    Returns (second committed token [n], q_1 weights, {d_1: p_2 weights})."""
+    seq = spec.Sequence(cfg, prompt, capacity=len(prompt) + 8)
+    spec.prefill(cfg, w, seq)
+    zq = spec.draft_logits(cfg, w, seq, 2).astype(np.float32)
+    (wq1, sq1), (wq2, sq2) = cn.row_weights(zq[0], inv_t), cn.row_weights(zq[1], inv_t)
+    b = np.arange(n, dtype=np.uint64)
+
+    def draw(w_, s_, u):
+        t = (u.astype(np.uint64) * np.uint64(s_)) >> np.uint64(24)     # U*S < 2^64
+        return np.searchsorted(np.cumsum(w_, dtype=np.uint64), t, side="right")
+
+    d1 = draw(wq1, sq1, uniform24_np(seed, SLOT_DRAFT, 0, b, 0))
+    d2 = draw(wq2, sq2, uniform24_np(seed, SLOT_DRAFT, 1, b, 0))
+    u_acc = uniform24_np(seed, SLOT_ACCEPT, 1, b, 0)
+    u_ext = uniform24_np(seed, SLOT_EXTRA, 1, b, 0)
+    p2 = {}
+    second = np.empty(n, dtype=np.int64)
+    for x1 in np.unique(d1):
+        s2 = seq.copy()
+        p2[int(x1)] = cn.row_weights(spec.verify_logits(cfg, w, s2, [int(x1), 0])[0]
+                                     .astype(np.float32), inv_t)
+        wp, sp = p2[int(x1)]
+        sel = np.nonzero(d1 == x1)[0]
+        dd = d2[sel]
+        lhs = u_acc[sel].astype(object) * wq2[dd].astype(object) * sp
+        rhs = wp[dd].astype(object) * sq2 * TWO24
+        keep = (lhs < rhs).astype(bool)
+        second[sel[keep]] = dd[keep]
+        rej = sel[~keep]
+        if rej.size:
+            r = cn.residual_weights(wp, sp, wq2, sq2)
+            r = [int(x) for x in wp] if sum(r) == 0 else r
+            cum = np.cumsum(np.array(r, dtype=object))
+            tot = int(cum[-1])
+            for k, uu in zip(rej, u_ext[rej]):
+                second[k] = int(np.searchsorted(cum, (int(uu) * tot) >> 24, side="right"))
+    return second, d1, (wq1, sq1), p2
+
+
+@pytest.fixture(scope="module")
+def tiny_second():
+    cfg = synth.TINY
+    w = synth.to_f64(synth.make_weights(cfg, 0))
+    prompt = list(synth.prompt_ids(cfg, 32, 1))
+    return cfg, w, prompt
+
+
+def test_tiny_second_token_replay_matches_oracle_steps(tiny_second):
+    """The vectorised replay takes the oracle step's own decisions, draw by draw."""
+    cfg, w, prompt = tiny_second
+    n = 300
+    second, d1, _, _ = _tiny_second_token_replay(cfg, w, prompt, n, seed=5)
+    seq0 = spec.Sequence(cfg, prompt, capacity=len(prompt) + 8)
+    spec.prefill(cfg, w, seq0)
+    for b in range(n):
+        r = spec.step(cfg, w, seq0.copy(), 2, 1.0, spec.PhiloxDraws(5, b, 0))
+        assert r["committed"][0] == d1[b]
+        assert r["committed"][1] == second[b], b
+
+
+def test_tiny_model_second_token_chi_square_1e6(tiny_second):
+    """The second token a step commits (the kept draft d_2, else the residual
+    draw) follows the AR marginal sum_x1 p(x1) p(x2 | x1) of the tiny model
+    (K = 2, 10^6 seeded steps, chi-square at p > 0.01)."""
+    cfg, w, prompt = tiny_second
+    n = 1_000_000
+    second, d1, (wq1, sq1), p2 = _tiny_second_token_replay(cfg, w, prompt, n, seed=0)
+    V = cfg["vocab"]
+    # the expected law uses every x1 with q_1(x1) > 0, not only the ones drawn
+    seq = spec.Sequence(cfg, prompt, capacity=len(prompt) + 8)
+    spec.prefill(cfg, w, seq)
+    spec.draft_logits(cfg, w, seq, 2)
+    exp = np.zeros(V)
+    for x1 in np.nonzero(wq1)[0]:
+        if int(x1) not in p2:
+            p2[int(x1)] = cn.row_weights(spec.verify_logits(cfg, w, seq.copy(), [int(x1), 0])[0]
+                                         .astype(np.float32), 1.0)
+        wp, sp = p2[int(x1)]
+        exp += (int(wq1[x1]) / sq1) * (wp.astype(np.float64) / sp)
+    assert abs(exp.sum() - 1) < 1e-9
+    obs = np.bincount(second, minlength=V).astype(np.float64)
+    keep = exp * n > 5
+    stat, pval = scipy.stats.chisquare(obs[keep], exp[keep] * n * obs[keep].sum() / (exp[keep] * n).sum())
+    assert pval > 0.01, pval
