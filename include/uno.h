@@ -218,6 +218,23 @@ int uno_spec_accept(const float *draft_logits, const float *verify_logits,
                     int32_t *committed, int32_t *extra_token, int32_t *status,
                     void *ws, size_t ws_bytes, void *stream);
 
+/* uno_spec_accept without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and device status flags as
+ * uno_spec_accept, minus ws/ws_bytes: the per-row statistics live in a static
+ * scratch array of the library (768 KiB per GPU, held until the process ends)
+ * that serves at most 2 * batch * K <= 65536 rows; larger shapes return
+ * UNO_ERR_WORKSPACE before anything is enqueued.  The first call on a device
+ * looks up that device's copy of the array (a host-side lookup, no
+ * allocation).  Every call on one GPU shares its array: calls that overlap on
+ * one GPU (two streams, two threads) race and must be ordered by the caller. */
+int uno_spec_accept_noalloc(const float *draft_logits, const float *verify_logits,
+                            const int32_t *draft_tokens, int batch, int K, int vocab,
+                            float inv_temp, uint64_t seed, const uint64_t *step,
+                            const int32_t *forced_accept, int32_t *accept_len,
+                            int32_t *committed, int32_t *extra_token, int32_t *status,
+                            void *stream);
+
 /* KV commit / rollback (picx.dev summary, "Practical Implications": one KV
  * cache serves drafting and verification).  kv_len[b] += 1 + accept_len[b]:
  * the anchor and the kept drafts stay, every later position becomes scratch

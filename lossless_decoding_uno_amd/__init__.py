@@ -25,7 +25,8 @@ DEV_CAPACITY, DEV_BAD_TOKEN, DEV_BAD_PAGE, DEV_NONFINITE, DEV_BAD_ACCEPT = 1, 2,
 
 EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_draft_block_from", "uno_verify_block",
            "uno_draft_sample",
-           "uno_spec_accept_workspace_bytes", "uno_spec_accept", "uno_kv_commit",
+           "uno_spec_accept_workspace_bytes", "uno_spec_accept", "uno_spec_accept_noalloc",
+           "uno_kv_commit",
            "uno_tree_rows", "uno_tree_workspace_bytes", "uno_tree_build", "uno_verify_tree",
            "uno_tree_accept", "uno_tree_commit",
            "uno_set_timing_events", "uno_timing_events_used", "uno_status_string",
@@ -91,6 +92,8 @@ def load_library():
     lib.uno_spec_accept_workspace_bytes.argtypes = [I, I]
     lib.uno_spec_accept.restype = I
     lib.uno_spec_accept.argtypes = [P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P, SZ, P]
+    lib.uno_spec_accept_noalloc.restype = I
+    lib.uno_spec_accept_noalloc.argtypes = [P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P]
     lib.uno_kv_commit.restype = I
     lib.uno_kv_commit.argtypes = [P, P, I, I, P, P, P]
     lib.uno_tree_rows.restype = I
@@ -353,6 +356,28 @@ def spec_accept(draft_logits, verify_logits, draft_tokens, inv_temp, seed, step,
                                V, float(inv_temp), int(seed), _ptr(step), _ptr(forced_accept),
                                _ptr(accept_len), _ptr(committed), _ptr(extra_token),
                                _ptr(status), _ptr(ws), ws.numel(), _stream()))
+
+
+def spec_accept_noalloc(draft_logits, verify_logits, draft_tokens, inv_temp, seed, step,
+                        accept_len, committed, extra_token, forced_accept=None, status=None):
+    """uno_spec_accept_noalloc: as spec_accept, on the library's static scratch
+    (no workspace argument)."""
+    lib = load_library()
+    B, K, V = draft_logits.shape
+    _need(draft_logits, torch.float32, (B, K, V), "draft_logits")
+    _need(verify_logits, torch.float32, (B, K, V), "verify_logits")
+    _need(draft_tokens, torch.int32, (B, K), "draft_tokens")
+    _need(step, torch.uint64, (B,), "step")
+    _need(accept_len, torch.int32, (B,), "accept_len")
+    _need(committed, torch.int32, (B, K + 1), "committed")
+    _need(extra_token, torch.int32, (B,), "extra_token")
+    if forced_accept is not None:
+        _need(forced_accept, torch.int32, (B,), "forced_accept")
+    _check(lib.uno_spec_accept_noalloc(_ptr(draft_logits), _ptr(verify_logits),
+                                       _ptr(draft_tokens), B, K, V, float(inv_temp), int(seed),
+                                       _ptr(step), _ptr(forced_accept), _ptr(accept_len),
+                                       _ptr(committed), _ptr(extra_token), _ptr(status),
+                                       _stream()))
 
 
 def kv_commit(kv, accept_len, K, step=None, status=None):

@@ -425,6 +425,28 @@ int uno_spec_accept(const float* draft_logits, const float* verify_logits,
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 
+int uno_spec_accept_noalloc(const float* draft_logits, const float* verify_logits,
+                            const int32_t* draft_tokens, int batch, int K, int vocab,
+                            float inv_temp, uint64_t seed, const uint64_t* step,
+                            const int32_t* forced_accept, int32_t* accept_len,
+                            int32_t* committed, int32_t* extra_token, int32_t* status,
+                            void* stream) {
+  if (!draft_logits || !verify_logits || !draft_tokens || !step || !accept_len || !committed ||
+      !extra_token)
+    return UNO_ERR_INVALID_ARG;
+  if (batch < 1 || K < 1 || K > 4096 || vocab < 1 || vocab > (1 << 20))
+    return UNO_ERR_INVALID_ARG;
+  if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
+  if (2 * (int64_t)batch * K > static_accept_max_rows()) return UNO_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
+    return launch_spec_accept_static(draft_logits, verify_logits, draft_tokens, batch, K, vocab,
+                                     inv_temp, seed, step, forced_accept, accept_len, committed,
+                                     extra_token, status, s);
+  });
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
 int uno_kv_commit(const uno_kv* kv, const int32_t* accept_len, int batch, int K, uint64_t* step,
                   int32_t* status, void* stream) {
   if (!kv || !kv->kv_len || !accept_len) return UNO_ERR_INVALID_ARG;

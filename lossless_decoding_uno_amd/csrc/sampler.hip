@@ -21,6 +21,8 @@
 #include "uno_device.h"
 #include "uno_internal.h"
 
+#include <mutex>
+
 #pragma clang fp contract(off)
 
 namespace uno {
@@ -488,6 +490,53 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
                      zq, zp, drafts, K, V, inv_temp, seed, step, forced, m_all, s_all, n_each,
                      accept_len, committed, extra_token, status);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ no-allocation variant
+// The per-row statistics of uno_spec_accept_noalloc live in a file-scope
+// device array instead of a caller-supplied workspace: 2*B*K row maxima
+// (fp32) and weight sums (uint64) for at most kStaticAcceptRows rows.  Every
+// GPU the library runs on holds its own copy until the process ends; the host
+// learns each copy's address once per device (hipGetSymbolAddress, with that
+// device current) and passes that address to the kernels.  Nothing in it has to
+// start at zero: k_row_stats writes every entry k_spec_accept reads.
+constexpr int kStaticAcceptRows = 65536;
+static __device__ __align__(256) unsigned char scratch[(size_t)kStaticAcceptRows * 12];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int static_accept_max_rows() { return kStaticAcceptRows; }
+
+hipError_t static_accept_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_spec_accept_static(const float* zq, const float* zp, const int32_t* drafts,
+                                     int B, int K, int V, float inv_temp, uint64_t seed,
+                                     const uint64_t* step, const int32_t* forced,
+                                     int32_t* accept_len, int32_t* committed,
+                                     int32_t* extra_token, int32_t* status, hipStream_t s) {
+  void* ws = nullptr;
+  const hipError_t e = static_accept_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_spec_accept(zq, zp, drafts, B, K, V, inv_temp, seed, step, forced, accept_len,
+                            committed, extra_token, status, ws, s);
 }
 
 }  // namespace uno

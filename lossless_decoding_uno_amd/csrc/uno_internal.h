@@ -30,6 +30,15 @@ hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* d
                               const int32_t* forced, int32_t* accept_len, int32_t* committed,
                               int32_t* extra_token, int32_t* status, void* ws, hipStream_t s);
 
+// The same on the library's per-device static scratch (no workspace; rows
+// 2*B*K at most static_accept_max_rows(); the caller checks).
+int static_accept_max_rows();
+hipError_t launch_spec_accept_static(const float* zq, const float* zp, const int32_t* drafts,
+                                     int B, int K, int V, float inv_temp, uint64_t seed,
+                                     const uint64_t* step, const int32_t* forced,
+                                     int32_t* accept_len, int32_t* committed,
+                                     int32_t* extra_token, int32_t* status, hipStream_t s);
+
 // ---------------------------------------------------------------- elementwise / small ops
 // Block rows: draft (anchor + mask ids) or given rows; gathers embeddings into
 // the fp32 residual stream h [R, D]; also writes ids [R].

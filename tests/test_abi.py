@@ -62,6 +62,11 @@ def test_entry_points_reject_bad_arguments_on_the_host():
     # workspace too small
     assert lib.uno_spec_accept(fake, fake, fake, 2, 4, 512, 1.0, 0, fake, None, fake, fake, fake,
                                None, fake, 8, None) == 4
+    # the no-allocation accept step: shapes past its static scratch
+    assert lib.uno_spec_accept_noalloc(fake, fake, fake, 2049, 16, 512, 1.0, 0, fake, None, fake,
+                                       fake, fake, None, None) == 4
+    assert lib.uno_spec_accept_noalloc(None, fake, fake, 2, 4, 512, 1.0, 0, fake, None, fake,
+                                       fake, fake, None, None) == 1
     # unsupported head_dim
     bad = U.make_config(dict(synth.TINY, head_dim=48))
     assert lib.uno_verify_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
