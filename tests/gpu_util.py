@@ -151,6 +151,17 @@ def kv_to_logical(kv, layer, b, n):
     return k.double().numpy(), v.double().numpy()
 
 
+def teacher_force_cache(seq, kv, b):
+    """Set the oracle sequence's cached K/V (positions 0..kv_len-1) to the
+    library's stored bf16 K/V of sequence b: a step then starts from the same
+    committed state on both sides."""
+    n = seq.kv_len
+    for li in range(len(seq.cache.k)):
+        k, v = kv_to_logical(kv, li, b, n)
+        seq.cache.k[li][:n] = k
+        seq.cache.v[li][:n] = v
+
+
 def load_kv_logical(kv, b, k_log, v_log):
     """Write logical K/V [L, n, Hkv, hd] (positions 0..n-1) into sequence b's pages."""
     ps = kv.page_size

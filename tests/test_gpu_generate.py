@@ -74,6 +74,7 @@ def test_tree_generation_matches_oracle_step_by_step():
     """The generator with the tree sampler (top-4 per drafted position, 6
     kept candidates, K = 5) on a vocab-32 tiny model whose LM head is scaled
     by 4 (sharper laws, so walks go deep): chunked prefill, pages on demand;
+    every step starts the oracle from the library's committed bf16 K/V;
     every step's tree equals the oracle's tree on the GPU's draft logits,
     every node's verify logits meet the bf16 yardstick against the exact
     oracle's forward (the head's scale makes the logits, and the rounding of
@@ -85,7 +86,7 @@ def test_tree_generation_matches_oracle_step_by_step():
     from oracle import canonical as cn
     from oracle import model as om
     from oracle import tree as ot
-    from gpu_util import YardstickTally, u24
+    from gpu_util import YardstickTally, teacher_force_cache, u24
     cfg = dict(synth.TINY, vocab=32, mask_id=31)
     wts = synth.make_weights(cfg, 2)
     hs = 4.0
@@ -103,9 +104,6 @@ def test_tree_generation_matches_oracle_step_by_step():
     for b in range(B):
         s = ospec.Sequence(cfg, list(prompts[b]), capacity=max_ctx)
         ospec.prefill(cfg, w64, s)
-        for li in range(cfg["n_layers"]):
-            s.cache.k[li][:] = om.bf16_round(s.cache.k[li])
-            s.cache.v[li][:] = om.bf16_round(s.cache.v[li])
         seqs.append(s)
     moves = 0
     tally = YardstickTally("tree generation logits")
@@ -115,6 +113,8 @@ def test_tree_generation_matches_oracle_step_by_step():
         c, path_g = g.c.cpu().numpy(), g.tb.path.cpu().numpy()
         for b in range(B):
             s = seqs[b]
+            # the step starts from the library's committed bf16 K/V
+            teacher_force_cache(s, g.kv, b)
             s_bf = s.copy()
             zq_o = ospec.draft_logits(cfg, w64, s, K)
             tally.add(zq[b], zq_o, ospec.draft_logits(cfg, w64, s_bf, K, act_round=om.bf16_round),
@@ -134,9 +134,6 @@ def test_tree_generation_matches_oracle_step_by_step():
             np.testing.assert_array_equal(path_g[b, :a], path)
             moves += sum(1 for dd in range(1, a) if path[dd] != dd)
             ot.tree_commit(s, path, a, committed)
-            for li in range(cfg["n_layers"]):      # the GPU stores the committed K/V in bf16
-                s.cache.k[li][:] = om.bf16_round(s.cache.k[li])
-                s.cache.v[li][:] = om.bf16_round(s.cache.v[li])
             assert s.kv_len == int(g.kv_len[b])
     st = g.stats()
     assert int(g.status.abs().sum().item()) == 0

@@ -9,16 +9,18 @@ uno_tree_accept, uno_tree_commit) against oracle.tree.
   independent best-first enumeration and the tree against its invariants.
 * Tree steps on small models (LM head scaled up so that walks go deep): the
   tree built on the GPU from its draft logits equals the oracle's tree built
-  from the same fp32 logits; draft and verify logits of every node are
-  compared with the exact oracle's forward: within 2e-2 abs + 1e-2 rel where
+  from the same fp32 logits; each step starts the oracle from the library's
+  committed bf16 K/V (teacher forcing); draft and verify logits of every node
+  are compared with the exact oracle's forward: within 2e-2 abs + 1e-2 rel where
   the head is not scaled; where it is scaled by s the logits, and the rounding
   error of any bf16 implementation with them, grow s-fold, and the bf16
   yardstick applies instead (tests/gpu_util.py: every logit within 3x the bar,
   and over the whole test no more logits outside the bar than the oracle's
   bf16 mode puts there);
   the per-node draws and the walk (a, committed, extra token, path) equal the
-  oracle's on the GPU's verify logits; both sides commit the same path, so the
-  next step's logits (and a direct read of the cache) check the moved K/V.
+  oracle's on the GPU's verify logits; both sides commit the same path, and
+  after every step the library's cache over the newly committed positions
+  (the moved K/V) must hold the oracle's K/V.
 """
 import heapq
 
@@ -33,7 +35,7 @@ from oracle import spec as ospec
 from oracle import tree as ot
 
 from gpu_util import (YardstickTally, assert_logits_close, gpu_or_fail, kv_to_logical,
-                      progress, u24)
+                      progress, teacher_force_cache, u24)
 
 pytestmark = pytest.mark.gpu
 
@@ -203,9 +205,6 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
     for b in range(B):
         s = ospec.Sequence(cfg, prompts[b], capacity=cap)
         ospec.prefill(cfg, w64, s)
-        for li in range(cfg["n_layers"]):          # the GPU cache holds bf16 K/V
-            s.cache.k[li][:] = om.bf16_round(s.cache.k[li])
-            s.cache.v[li][:] = om.bf16_round(s.cache.v[li])
         seqs.append(s)
     tb = U.TreeBuffers(B, K, topk, n_keep, V)
     zq_g = torch.empty((B, K, V), dtype=torch.float32, device=dev)
@@ -234,7 +233,9 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
         zq_all, zp_all = zq_g.cpu().numpy(), zp_g.cpu().numpy()
         d_all, a_all, c_all = d_g.cpu().numpy(), a_g.cpu().numpy(), c_g.cpu().numpy()
         e_all, path_all, smp = e_g.cpu().numpy(), tb.path.cpu().numpy(), tb.sample.cpu().numpy()
+        kv_before = [s.kv_len for s in seqs]
         for b, s in enumerate(seqs):
+            teacher_force_cache(s, kv, b)
             s_bf = s.copy() if head_scale != 1.0 else None
             zq = ospec.draft_logits(cfg, w64, s, K)
             zq_bf = (ospec.draft_logits(cfg, w64, s_bf, K, act_round=om.bf16_round)
@@ -262,19 +263,19 @@ def test_tree_steps_match_oracle(name, cfg, B, K, topk, n_keep, n_steps, prompt_
             depths.append(a)
             moves += sum(1 for d in range(1, a) if path[d] != d)
             ot.tree_commit(s, path, a, committed)
-            for li in range(cfg["n_layers"]):      # the GPU stores the committed K/V in bf16
-                s.cache.k[li][:] = om.bf16_round(s.cache.k[li])
-                s.cache.v[li][:] = om.bf16_round(s.cache.v[li])
         U.tree_commit(model, kv, tb, a_g, step_g, status)
         kvl = kv.kv_len.cpu().numpy()
         assert [int(x) for x in kvl] == [s.kv_len for s in seqs]
         assert int(status.abs().sum()) == 0
-    # the committed cache (moved K/V included) holds the oracle's K/V
-    for b, s in enumerate(seqs):
-        for li in range(cfg["n_layers"]):
-            kg, vg = kv_to_logical(kv, li, b, s.kv_len)
-            assert_logits_close(kg, s.cache.k[li][: s.kv_len], "%s K layer %d b%d" % (name, li, b))
-            assert_logits_close(vg, s.cache.v[li][: s.kv_len], "%s V layer %d b%d" % (name, li, b))
+        # the newly committed positions (moved K/V included) hold the oracle's K/V
+        for b, s in enumerate(seqs):
+            n0, n1 = kv_before[b], s.kv_len
+            for li in range(cfg["n_layers"]):
+                kg, vg = kv_to_logical(kv, li, b, n1)
+                assert_logits_close(kg[n0:], s.cache.k[li][n0:n1],
+                                    "%s K layer %d b%d step %d" % (name, li, b, st))
+                assert_logits_close(vg[n0:], s.cache.v[li][n0:n1],
+                                    "%s V layer %d b%d step %d" % (name, li, b, st))
     summary = tally.finish() if head_scale != 1.0 else "elementwise within the bar"
     progress("tree steps %s: worst logit error %.2e (%s), accept lengths %s, %d K/V moves"
              % (name, worst, summary, np.bincount(depths).tolist(), moves))
