@@ -120,6 +120,8 @@ class Workload:
         self.c = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
         self.e = torch.from_numpy(synth.prompt_ids(cfg, B, seed)).to(dev)   # first anchors
         self.step_ctr = torch.zeros(B, dtype=torch.uint64).to(dev)
+        # device-side fault flags of every call; checked after the timed region
+        self.status = torch.zeros(B, dtype=torch.int32, device=dev)
         self.forced_host = synth.forced_accepts(B, K, n_steps, seed=2)
         self.forced = torch.from_numpy(self.forced_host).to(dev)
         self.kv_len_host = np.full(B, ctx, dtype=np.int64)
@@ -128,15 +130,20 @@ class Workload:
     def step(self, i, verify_events=None):
         U = self.U
         U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, self.inv_t, 0, self.step_ctr,
-                      self.zq, self.d, self.ws)
+                      self.zq, self.d, self.ws, self.status)
         if verify_events is not None:
             verify_events[0].record()
-        U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws)
+        U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws, self.status)
         if verify_events is not None:
             verify_events[1].record()
         U.spec_accept(self.zq, self.zp, self.d, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e,
-                      self.aws, forced_accept=self.forced[i])
-        U.kv_commit(self.kv, self.a, self.K, self.step_ctr)
+                      self.aws, forced_accept=self.forced[i], status=self.status)
+        U.kv_commit(self.kv, self.a, self.K, self.step_ctr, self.status)
+
+    def check_status(self):
+        """No call raised a device fault flag (outside any timed region)."""
+        st = self.status.cpu().numpy()
+        assert (st == 0).all(), "device status flags raised: %s" % np.unique(st).tolist()
 
     def attn_bytes(self, i):
         """Algorithmic bytes of the two attention launches of one layer at step i:
@@ -180,29 +187,63 @@ def gemm_flops_per_pass(cfg, R, draft):
     return 2.0 * R * per_layer * cfg["n_layers"]
 
 
-def torch_streaming_rates(torch):
-    """Streaming rates of torch's own kernels on this GPU, for context: a 2 GiB
-    read (torch sum) and a 1 GiB copy (read + write bytes).  They are not the
-    HBM's ceiling: a plain streaming read with 16-byte loads reaches ~6.3 TB/s,
-    and ~7.1 TB/s with the non-temporal hint."""
-    x = torch.ones((1 << 31) // 4, dtype=torch.float32, device="cuda")
-    y = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for _ in range(2):
-        x.sum()
-        y.copy_(x[: y.numel()])
-    torch.cuda.synchronize()
-    best_r, best_c = 1e9, 1e9
-    for _ in range(5):
-        ev[0].record(); x.sum(); ev[1].record()
-        ev[2].record(); y.copy_(x[: y.numel()]); ev[3].record()
+def measured_ceilings(torch):
+    """Ceilings measured on this GPU with the probe kernels of libuno_probe.so
+    (include/uno_probe.h), beside the vendor peaks: a streaming read of a cold
+    4 GiB buffer (16x the last-level cache) with 16-byte loads, plain and
+    non-temporal, four or eight in flight per lane; a 1 GiB -> 1 GiB copy
+    (bytes read + written); a register-only loop of v_mfma_f32_32x32x16_bf16.
+    Each is the best of three runs at its best grid size of a small sweep."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "lossless_decoding_uno_amd", "libuno_probe.so"))
+    P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.uno_probe_read.argtypes = [P, SZ, I, I, P, P]
+    lib.uno_probe_copy.argtypes = [P, P, SZ, I, P]
+    lib.uno_probe_mfma.argtypes = [I, I, P, P]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    big = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1 << 16, dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best_ms(launch, reps=3):
+        launch()
         torch.cuda.synchronize()
-        best_r = min(best_r, ev[0].elapsed_time(ev[1]))
-        best_c = min(best_c, ev[2].elapsed_time(ev[3]))
-    del x, y
+        best = 1e30
+        for _ in range(reps):
+            ev[0].record()
+            launch()
+            ev[1].record()
+            torch.cuda.synchronize()
+            best = min(best, ev[0].elapsed_time(ev[1]))
+        return best
+
+    out = {}
+    for nt, key in ((1, "read_nontemporal_GBps"), (0, "read_GBps")):
+        rate = 0.0
+        for depth in (0, 2):                 # four or eight loads in flight per lane
+            for n_wg in (2048, 4096, 8192, 16384):
+                ms = best_ms(lambda: lib.uno_probe_read(
+                    ctypes.c_void_p(big.data_ptr()), big.numel(), nt | depth, n_wg,
+                    ctypes.c_void_p(sink.data_ptr()), stream))
+                rate = max(rate, big.numel() / (ms / 1e3) / 1e9)
+        out[key] = round(rate, 1)
+    half = big.numel() // 2
+    rate = 0.0
+    for n_wg in (4096, 16384):
+        ms = best_ms(lambda: lib.uno_probe_copy(ctypes.c_void_p(big.data_ptr()),
+                                                ctypes.c_void_p(big.data_ptr() + half), half // 2,
+                                                n_wg, stream))
+        rate = max(rate, 2 * (half // 2) / (ms / 1e3) / 1e9)
+    out["copy_GBps"] = round(rate, 1)
+    del big
+    rate, iters = 0.0, 400
+    for n_wg in (256, 512, 1024, 2048):
+        ms = best_ms(lambda: lib.uno_probe_mfma(iters, n_wg, ctypes.c_void_p(sink.data_ptr()),
+                                                stream))
+        rate = max(rate, n_wg * 4 * iters * 4 * 32768 / (ms / 1e3) / 1e12)
+    out["mfma_bf16_TFLOPs"] = round(rate, 1)
     torch.cuda.empty_cache()
-    return {"torch_sum_read_GBps": round((1 << 31) / (best_r / 1e3) / 1e9, 1),
-            "torch_copy_GBps": round(2 * (1 << 30) / (best_c / 1e3) / 1e9, 1)}
+    return out
 
 
 def library_gemm_reference(torch, cfg, R):
@@ -261,6 +302,7 @@ def run_timed(W, steps, warmup, torch, timer=None):
     tokens = int(np.sum(W.forced_host[warmup:warmup + steps].astype(np.int64) + 1))
     got = W.kv.kv_len.cpu().numpy()
     assert np.array_equal(got, W.kv_len_host), "device kv_len diverged from the forced schedule"
+    W.check_status()
     return ms, wall, tokens, used, attn_bytes, kv0
 
 
@@ -306,7 +348,7 @@ def proj_shape(cfg, name):
             "gemm_down": (D, F, 8), "lm_head": (cfg["vocab"], D, 4)}[name]
 
 
-def sampler_roofline(cfg, B, K, ms):
+def sampler_roofline(cfg, B, K, ms, read_ceiling):
     """The sampler launches of one step (draft sampling, acceptance statistics,
     accept / resample) against HBM: algorithmic bytes = the fp32 draft logits
     read once to sample the drafts, then the draft and verify logits read once
@@ -314,7 +356,8 @@ def sampler_roofline(cfg, B, K, ms):
     byts = 3.0 * B * K * cfg["vocab"] * 4
     gbs = byts / (ms / 1e3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 3),
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "frac_of_measured": round(gbs / read_ceiling, 4), "ms_per_step": round(ms, 3),
             "algorithmic_bytes_per_step": int(byts)}
 
 
@@ -327,6 +370,32 @@ def gemm_launch_work(cfg, name, R, draft):
     flops = 2.0 * R * N * (Kd + r)
     byts = 2.0 * N * (Kd + r) + 2.0 * R * (Kd + r) + ob * R * N
     return flops, byts
+def host_description():
+    """The host the CPU baseline ran on: CPU model, logical CPUs, and the
+    thread counts of the BLAS numpy calls and of torch."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        import threadpoolctl
+        blas = [{"api": p.get("internal_api"), "threads": p.get("num_threads")}
+                for p in threadpoolctl.threadpool_info()]
+    except Exception:
+        pass
+    import torch
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+            "numpy_blas": blas, "torch_threads": int(torch.get_num_threads())}
+
+
 def cpu_baseline(K, ctx, forced_mean_tokens):
     """The oracle (fp64 model, exact-integer sampler) on one sequence of the
     workload: a whole step (best of two) with 1 and with 5 layers of the 8B
@@ -358,7 +427,7 @@ def cpu_baseline(K, ctx, forced_mean_tokens):
     per_layer = max((times[5] - times[1]) / 4.0, 1e-9)
     t36 = times[1] + (cfg["n_layers"] - 1) * per_layer
     return {"value": forced_mean_tokens / t36, "unit": "accepted tokens/s",
-            "cores": int(torch.get_num_threads()), "kind": "oracle",
+            "cores": int(torch.get_num_threads()), "kind": "oracle", "host": host_description(),
             "sample": ("one sequence of the workload, one full step (draft+sample+verify+accept+"
                        "commit) at context %d, K=%d, timed with 1 and 5 of the 36 layers "
                        "(%.2f s, %.2f s; best of 2), extrapolated linearly to 36 layers "
@@ -396,6 +465,8 @@ def generate_mode(args, U, synth, torch, cfg):
     outs = g.generate(args.generate, on_step=progress)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t0
+    st_flags = g.status.cpu().numpy()
+    assert (st_flags == 0).all(), "device status flags raised: %s" % np.unique(st_flags).tolist()
     st = g.stats()
     toks = sum(len(o) for o in outs)
     out = {"metric": "generated tokens/s (natural acceptance, end to end)",
@@ -439,15 +510,17 @@ class TreeWorkload:
         self.c = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
         self.e = torch.from_numpy(synth.prompt_ids(cfg, B, seed)).to(dev)
         self.step_ctr = torch.zeros(B, dtype=torch.uint64).to(dev)
+        self.status = torch.zeros(B, dtype=torch.int32, device=dev)
 
     def step(self, i):
         U = self.U
         U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, self.inv_t, 0,
-                      self.step_ctr, self.zq, self.d, self.ws)
-        U.tree_build(self.zq, self.d, self.tb)
-        U.verify_tree(self.model, self.kv, self.tb, self.max_ctx, self.zp, self.ws)
-        U.tree_accept(self.zp, self.tb, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e)
-        U.tree_commit(self.model, self.kv, self.tb, self.a, self.step_ctr)
+                      self.step_ctr, self.zq, self.d, self.ws, self.status)
+        U.tree_build(self.zq, self.d, self.tb, self.status)
+        U.verify_tree(self.model, self.kv, self.tb, self.max_ctx, self.zp, self.ws, self.status)
+        U.tree_accept(self.zp, self.tb, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e,
+                      self.status)
+        U.tree_commit(self.model, self.kv, self.tb, self.a, self.step_ctr, self.status)
 
 
 def tree_mode(args, U, synth, torch, cfg):
@@ -478,6 +551,8 @@ def tree_mode(args, U, synth, torch, cfg):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
     tokens = int(np.sum(W.kv.kv_len.cpu().numpy().astype(np.int64) - kv0))
+    st = W.status.cpu().numpy()
+    assert (st == 0).all(), "device status flags raised: %s" % np.unique(st).tolist()
     # projection GEMMs of both passes against HBM: every weight read once per pass
     L = cfg["n_layers"]
     gemm_ms = sum(classes[k] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"))
@@ -591,7 +666,11 @@ def main():
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": dominant, "launches": int(used),
                 "avg_launch_us": avg_us}
-    ceil = torch_streaming_rates(torch)
+    log("measured ceilings (probe kernels)")
+    ceil = measured_ceilings(torch)
+    if roof.get("achieved") is not None:
+        c = ceil["read_nontemporal_GBps"] if roof["bound"] == "hbm" else ceil["mfma_bf16_TFLOPs"]
+        roof["frac_of_measured"] = round(roof["achieved"] / c, 4)
     # MFMA fraction of the projection GEMMs (both passes) from the probe step
     gemm_ms = sum(classes[k] for k in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down"))
     gfl = gemm_flops_per_pass(cfg, R, True) + gemm_flops_per_pass(cfg, R, False)
@@ -603,6 +682,7 @@ def main():
                  "verify_flop_per_step": vfl,
                  "kernel": "k_gemm: q|k|v, o, gate|up, down projections of both passes",
                  "torch_matmul_ms_per_step": library_gemm_reference(torch, cfg, R)}
+    roof_gemm["frac_of_measured"] = round(roof_gemm["achieved"] / ceil["mfma_bf16_TFLOPs"], 4)
     out = {"metric": "accepted tokens/s/GPU (Qwen3-8B shape, Psi-Spec draft+verify step)",
            "value": round(value, 1), "unit": "accepted tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
@@ -614,13 +694,16 @@ def main():
                "parallelism": "none (1 GPU)"},
            "roofline": roof,
            "roofline_gemm": roof_gemm,
-           "torch_streaming": ceil,
+           "measured_ceilings": ceil,
            "verify_step": {"ms_per_step": round(W.verify_ms / args.steps, 3),
                            "hbm_GBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9, 1),
                            "frac_of_8TBps": round(W.verify_bytes_total / (W.verify_ms / 1e3) / 1e9
                                                   / HBM_PEAK_GBS, 4),
+                           "frac_of_measured": round(W.verify_bytes_total / (W.verify_ms / 1e3)
+                                                     / 1e9 / ceil["read_nontemporal_GBps"], 4),
                            "algorithmic_GB_per_step": round(W.verify_bytes_total / args.steps / 1e9, 3)},
-           "sampler": sampler_roofline(cfg, args.batch, K, classes["sampler"]),
+           "sampler": sampler_roofline(cfg, args.batch, K, classes["sampler"],
+                                       ceil["read_nontemporal_GBps"]),
            "kernel_class_ms_per_step": {k: round(v, 3) for k, v in classes.items()},
            "forward_passes_per_s": round(2 * args.steps / (ms / 1e3), 2),
            "wall_s_timed": round(wall, 3)}

@@ -14,14 +14,21 @@
  * ---------------------------------------
  * - Pointers marked [dev] are device (HBM) pointers; [host] are host pointers.
  *   The caller owns every buffer (weights, KV pages, page table, lengths,
- *   logits, tokens, workspace).  The library allocates and frees nothing and
- *   keeps no mutable global state, so calls are re-entrant.
+ *   logits, tokens, workspace).  The library allocates and frees nothing.
+ *   Mutable global state: the measurement hook of uno_set_timing_events
+ *   (process-wide, not thread-safe: set it from one thread with no other call
+ *   in flight), the per-thread text of uno_last_hip_error, and the per-GPU
+ *   static scratch of uno_spec_accept_noalloc (calls of it that overlap on one
+ *   GPU race).  Apart from these, calls on distinct buffers are re-entrant.
  * - Every call validates its host-visible arguments, then enqueues kernels on
  *   `stream` (a hipStream_t; NULL = the default stream) and returns without a
  *   host synchronisation.  No call issues hipMemset/hipMemcpy or allocates, so a
  *   whole step can be captured into a HIP graph.  Outputs are valid once the
  *   stream has reached them.
- * - Return value: UNO_OK, or an error code; on error nothing was enqueued.
+ * - Return value: UNO_OK, or an error code.  Argument, shape, capacity and
+ *   workspace errors are found on the host before anything is enqueued;
+ *   UNO_ERR_HIP (a launch failure) can leave the kernels launched before it
+ *   enqueued, i.e. a partly run pass whose outputs are undefined.
  *   Conditions only the device can see (a kv_len that would overflow the page
  *   table, a token id outside the vocabulary, a page id outside the pool, a
  *   non-finite logit in a sampled row) are reported per sequence through the

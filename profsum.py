@@ -1,11 +1,11 @@
 """Summaries of rocprofv3 CSV output (kernel statistics and counter means).
 
-    python -m lossless_decoding_uno_amd.profsum stats DIR [N]
+    python profsum.py stats DIR [N]
         top N kernels of DIR/**/*_kernel_stats.csv by total time
-    python -m lossless_decoding_uno_amd.profsum pmc DIR REGEX
+    python profsum.py pmc DIR REGEX
         per-dispatch mean of every counter in DIR/**/*_counter_collection.csv
         over the kernels whose name matches REGEX
-    python -m lossless_decoding_uno_amd.profsum trace DIR REGEX
+    python profsum.py trace DIR REGEX
         dispatch count and mean / median duration from DIR/**/*_kernel_trace.csv
 """
 import collections
