@@ -31,6 +31,9 @@ SLOT_ACCEPT = 1    # accept test of draft i uses j = i - 1
 SLOT_EXTRA = 2     # residual / bonus token uses j = a
 SLOT_NOISE = 3     # uniform-prior noise token of draft row j >= 1
 SLOT_PASS = 4      # sample j of intermediate draft pass i uses slot SLOT_PASS + i
+SLOT_KEEP = 64     # corrector after draft pass i: keep-or-remask decision of row j
+SLOT_RENOISE = 128  # corrector after draft pass i: fresh uniform token of a remasked row j
+MAX_PASSES = 60    # draft passes per step (slots SLOT_PASS + i stay below SLOT_KEEP)
 
 
 def philox4x64_10(counter, key):
@@ -53,10 +56,15 @@ def uniform24(seed, slot, j, b, step):
     return philox4x64_10((slot, j, b, step), (seed, 0))[0] >> 40
 
 
+def token_id(seed, slot, j, b, step, vocab):
+    """Uniform token floor(w * vocab / 2^64), w = word 0 at counter (slot, j, b, step)."""
+    return (philox4x64_10((slot, j, b, step), (seed, 0))[0] * int(vocab)) >> 64
+
+
 def noise_id(seed, j, b, step, vocab):
     """Uniform noise token of draft row j for a uniform-state prior:
     floor(w * vocab / 2^64), w = word 0 at counter (SLOT_NOISE, j, b, step)."""
-    return (philox4x64_10((SLOT_NOISE, j, b, step), (seed, 0))[0] * int(vocab)) >> 64
+    return token_id(seed, SLOT_NOISE, j, b, step, vocab)
 
 
 # ---- vectorised form (numpy uint64), used for large batches of draws ----

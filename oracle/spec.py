@@ -40,7 +40,10 @@ import numpy as np
 
 from . import canonical as cn
 from .model import KVCache, forward
-from .philox import SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, SLOT_PASS, noise_id, uniform24
+from .philox import (MAX_PASSES, SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, SLOT_KEEP, SLOT_PASS,
+                     SLOT_RENOISE, noise_id, token_id, uniform24)
+
+TWO24 = 1 << 24
 
 
 class PhiloxDraws:
@@ -54,6 +57,14 @@ class PhiloxDraws:
 
     def noise(self, j, vocab):
         return noise_id(self.seed, j, self.b, self.step, vocab)
+
+    def keep(self, i, j, keep_q24):
+        """Corrector after draft pass i: row j keeps its token iff U < keep_q24."""
+        return uniform24(self.seed, SLOT_KEEP + i, j, self.b, self.step) < int(keep_q24)
+
+    def renoise(self, i, j, vocab):
+        """Corrector after draft pass i: a fresh uniform token for row j."""
+        return token_id(self.seed, SLOT_RENOISE + i, j, self.b, self.step, vocab)
 
     def categorical(self, slot, j, weights):
         return cn.categorical(weights, self.u(slot, j))
@@ -120,20 +131,58 @@ def draft_sample(zq32, inv_temp, draws, slot=SLOT_DRAFT):
             for j in range(zq32.shape[0])]
 
 
-def draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws):
+def keep_threshold(kappa):
+    """Correction strength kappa in [0, 1] as the 24-bit threshold of the keep
+    test U < round(kappa * 2^24) (kappa = 1 always keeps, 0 always remasks)."""
+    k = float(kappa)
+    if not 0.0 <= k <= 1.0:
+        raise ValueError("kappa must lie in [0, 1]")
+    return int(round(k * TWO24))
+
+
+def corrected_block(cfg, drafts, pass_i, keep_q24, draws):
+    """The block the draft pass after pass ``pass_i`` reads, from that pass's
+    samples d_1..d_K (paperglide reader, "Supplementary Details": a
+    Psi-sampler is a predictor-corrector sampler whose correction strength
+    kappa_t in [0, 1] interpolates between the reverse posterior, kappa_t = 1
+    being ancestral sampling, and the forward noising process, which remasks a
+    masked model's tokens and re-draws a uniform-state model's).  Row j >= 1
+    keeps d_j with probability kappa = keep_q24 / 2^24 (U < keep_q24, Philox
+    slot SLOT_KEEP + pass_i); otherwise it returns to the prior: the mask token,
+    or a fresh uniform token (slot SLOT_RENOISE + pass_i)."""
+    K = len(drafts)
+    out = []
+    for j in range(1, K):
+        if int(keep_q24) >= TWO24 or draws.keep(pass_i, j, keep_q24):
+            out.append(int(drafts[j - 1]))
+        elif cfg.get("noise_prior", 0) == 1:
+            out.append(draws.renoise(pass_i, j, cfg["vocab"]))
+        else:
+            out.append(cfg["mask_id"])
+    return out
+
+
+def draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws, kappa=1.0):
     """Multi-pass draft (paperglide reader, "Supplementary Details": a
-    Psi-sampler refines the block over several denoising steps).  Pass i
-    re-runs the draft block with rows 1..K-1 holding the tokens pass i-1
-    sampled (intermediate samples use Philox slot SLOT_PASS + i); the last pass
-    samples the drafts with SLOT_DRAFT.  Returns (zq fp64, zq fp32, drafts) of
-    the last pass: only those enter the accept test, so any number of passes
-    keeps the decode lossless."""
+    Psi-sampler refines the block over several denoising steps, and sample
+    quality grows with the number of steps).  Pass 0 reads the prior's noisy
+    block; pass i > 0 reads the block the corrector makes from pass i-1's
+    samples (``corrected_block``, correction strength ``kappa``: one value, or
+    one per transition).  Intermediate samples use Philox slot SLOT_PASS + i;
+    the last pass samples the drafts with SLOT_DRAFT.  Returns (zq fp64, zq
+    fp32, drafts) of the last pass: only those enter the accept test, and
+    conditional on everything drawn before it the last pass is an ordinary
+    draft, so any number of passes and any kappa keep the decode lossless."""
+    if not 1 <= n_passes <= MAX_PASSES:
+        raise ValueError("1 <= n_passes <= %d" % MAX_PASSES)
+    kap = list(kappa) if isinstance(kappa, (list, tuple)) else [kappa] * max(0, n_passes - 1)
     block = None
     for i in range(n_passes):
         zq = draft_logits(cfg, wts, seq, K, draws=draws, block=block)
         zq32 = zq.astype(np.float32)
         last = i == n_passes - 1
-        block = draft_sample(zq32, inv_temp, draws, SLOT_DRAFT if last else SLOT_PASS + i)
+        d = draft_sample(zq32, inv_temp, draws, SLOT_DRAFT if last else SLOT_PASS + i)
+        block = d if last else corrected_block(cfg, d, i, keep_threshold(kap[i]), draws)
     return zq, zq32, block
 
 
@@ -193,14 +242,14 @@ def commit(seq, a, committed):
     seq.step += 1
 
 
-def step(cfg, wts, seq, K, inv_temp, draws, forced=None, n_passes=1):
-    """One full draft (n_passes passes) -> sample -> verify -> accept -> commit
-    step.
+def step(cfg, wts, seq, K, inv_temp, draws, forced=None, n_passes=1, kappa=1.0):
+    """One full draft (n_passes passes, correction strength kappa between
+    them) -> sample -> verify -> accept -> commit step.
 
     Returns a dict with the logits (fp64 and the fp32 copies the sampler saw),
     drafts, a, committed tokens and the extra token.
     """
-    zq, zq32, drafts = draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws)
+    zq, zq32, drafts = draft_passes(cfg, wts, seq, K, n_passes, inv_temp, draws, kappa)
     zp = verify_logits(cfg, wts, seq, drafts)
     zp32 = zp.astype(np.float32)
     a, committed, extra = spec_accept(zq32, zp32, drafts, inv_temp, draws, forced)

@@ -24,8 +24,8 @@ import synth
 from oracle import canonical as cn
 from oracle import model as om
 from oracle import spec
-from oracle.philox import (SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, SLOT_PASS, noise_id,
-                           uniform24_np)
+from oracle.philox import (SLOT_ACCEPT, SLOT_DRAFT, SLOT_EXTRA, SLOT_KEEP, SLOT_PASS, noise_id,
+                           token_id, uniform24, uniform24_np)
 
 TWO24 = 1 << 24
 
@@ -66,6 +66,20 @@ class _EnumDraws:
         # must hold for any draft distribution, hence for any noise)
         return noise_id(7, j, 0, 0, vocab)
 
+    def keep(self, i, j, keep_q24):
+        # corrector decisions are enumerated with their exact probabilities
+        def dist():
+            out = {}
+            if keep_q24 > 0:
+                out[True] = Fraction(int(keep_q24), TWO24)
+            if keep_q24 < TWO24:
+                out[False] = Fraction(TWO24 - int(keep_q24), TWO24)
+            return out
+        return self._take(dist)
+
+    def renoise(self, i, j, vocab):
+        return token_id(7, SLOT_KEEP + 64 + i, j, 0, 0, vocab)
+
     def categorical(self, slot, j, weights):
         def dist():
             w = list(weights)
@@ -100,9 +114,10 @@ class _FixedPassDraws(_EnumDraws):
         return super().categorical(slot, j, weights)
 
 
-def _enumerate_step(cfg, w, seq, K, inv_t, n_passes=1, fixed=None):
+def _enumerate_step(cfg, w, seq, K, inv_t, n_passes=1, fixed=None, kappa=1.0):
     """{committed tuple: probability} of one step from ``seq`` (exact; with
-    ``fixed`` the intermediate draft passes' samples are held fixed)."""
+    ``fixed`` the intermediate draft passes' samples are held fixed, and the
+    corrector's keep decisions between passes are enumerated)."""
     out = {}
     stack = [([], Fraction(1))]
     while stack:
@@ -110,7 +125,7 @@ def _enumerate_step(cfg, w, seq, K, inv_t, n_passes=1, fixed=None):
         s = seq.copy()
         draws = _EnumDraws(path) if fixed is None else _FixedPassDraws(path, fixed)
         try:
-            r = spec.step(cfg, w, s, K, inv_t, draws, n_passes=n_passes)
+            r = spec.step(cfg, w, s, K, inv_t, draws, n_passes=n_passes, kappa=kappa)
         except _Branch as br:
             for dec, p in br.dist.items():
                 stack.append((path + [dec], prob * p))
@@ -137,10 +152,10 @@ def toy():
     return cfg, synth.to_f64(wts)
 
 
-def _check_one_step(cfg, w, prompt, K, inv_t, n_passes=1, fixed=None):
+def _check_one_step(cfg, w, prompt, K, inv_t, n_passes=1, fixed=None, kappa=1.0):
     seq = spec.Sequence(cfg, prompt, capacity=len(prompt) + 2 * K + 4)
     spec.prefill(cfg, w, seq)
-    dist = _enumerate_step(cfg, w, seq, K, inv_t, n_passes, fixed)
+    dist = _enumerate_step(cfg, w, seq, K, inv_t, n_passes, fixed, kappa)
     assert abs(sum(dist.values()) - 1) == 0
     for c in dist:
         assert 2 <= len(c) <= K + 1          # tokens per step within [2, K+1]
@@ -208,6 +223,48 @@ def test_exact_enumeration_multi_pass_draft(toy, fixed):
     cfg, w = toy
     n_passes = 1 + max(slot for slot, _ in fixed) - 3
     _check_one_step(cfg, w, [3, 1, 4], 2, 1.0, n_passes, fixed)
+
+
+@pytest.mark.parametrize("kappa", [0.0, 0.5, 1.0])
+@pytest.mark.parametrize("prior", [0, 1])
+def test_exact_enumeration_corrector_strength(toy, kappa, prior):
+    """Multi-pass drafting with a correction strength kappa between passes
+    (each drafted row keeps its sample with probability kappa, else returns
+    to the prior; paperglide reader, "Supplementary Details", Psi-samplers):
+    the keep decisions are enumerated with their exact probabilities, the
+    intermediate samples held fixed; the committed prefix is exactly p_AR for
+    kappa 0, 1/2 and 1 and both priors."""
+    cfg, w = toy
+    cfg = dict(cfg, noise_prior=prior)
+    fixed = {(4, 0): 2, (4, 1): 5, (5, 0): 1, (5, 1): 3}
+    _check_one_step(cfg, w, [3, 1, 4], 2, 1.0, 3, fixed, kappa)
+
+
+def test_corrector_limits_and_keep_rate(toy):
+    """kappa = 1 is the plain multi-pass draft (every sample kept); kappa = 0
+    with the mask prior hands the last pass the all-mask block, so its logits
+    equal a one-pass draft's bit for bit; the keep rate is kappa."""
+    cfg, w = toy
+    seq = spec.Sequence(cfg, [3, 1, 4, 1, 5], capacity=20)
+    spec.prefill(cfg, w, seq)
+    z1 = spec.draft_logits(cfg, w, seq.copy(), 3, draws=spec.PhiloxDraws(0, 0, 0))
+    z_k1, _, _ = spec.draft_passes(cfg, w, seq.copy(), 3, 3, 1.0, spec.PhiloxDraws(0, 0, 0), 1.0)
+    block = None
+    for i in range(3):        # the corrector-free chain, written out
+        z = spec.draft_logits(cfg, w, seq.copy(), 3, block=block)
+        d = spec.draft_sample(z.astype(np.float32), 1.0, spec.PhiloxDraws(0, 0, 0),
+                              SLOT_DRAFT if i == 2 else SLOT_PASS + i)
+        block = d[:2]
+    assert np.array_equal(z_k1, z)
+    z_k0, _, _ = spec.draft_passes(cfg, w, seq.copy(), 3, 3, 1.0, spec.PhiloxDraws(0, 0, 0), 0.0)
+    assert np.array_equal(z_k0, z1)
+    thr = spec.keep_threshold(0.3)
+    assert thr == round(0.3 * TWO24) and spec.keep_threshold(1.0) == TWO24
+    draws = [spec.PhiloxDraws(9, b, 0).keep(i, j, thr) for b in range(400) for i in range(3)
+             for j in range(1, 17)]
+    n, k = len(draws), sum(draws)
+    assert abs(k / n - 0.3) < 4 * (0.3 * 0.7 / n) ** 0.5
+    assert draws[0] == (uniform24(9, SLOT_KEEP, 1, 0, 0) < thr)
 
 
 def test_multi_pass_changes_the_draft(toy):
