@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--prior", type=int, default=0, help="draft noise prior: 0 mask, 1 uniform")
     ap.add_argument("--passes", type=int, default=1, help="draft passes per step (generate mode)")
+    ap.add_argument("--kappa", type=float, default=1.0,
+                    help="corrector strength between draft passes (generate mode)")
     ap.add_argument("--tree", type=str, default="", metavar="TOPK,NKEEP",
                     help="tree-sampler mode: steps of draft -> tree build (top-TOPK per drafted "
                          "position, best NKEEP candidates) -> tree verify -> walk -> commit, "
@@ -446,6 +448,7 @@ def generate_mode(args, U, synth, torch, cfg):
     extra = U.tree_rows(K, *tree) if tree else K
     max_ctx = args.prompt + args.generate + 2 * K + extra + 8
     g = Generator(model, args.batch, K, max_ctx, seed=0, prefill_chunk=512, n_passes=args.passes,
+                  kappa=args.kappa,
                   tree=tree)
     prompts = synth.prompt_ids(cfg, args.prompt, 1, batch=args.batch)
     torch.cuda.synchronize()
@@ -473,8 +476,9 @@ def generate_mode(args, U, synth, torch, cfg):
            "value": round(toks / t_gen, 1), "unit": "tokens/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "bf16",
            "data": "synthetic (random-init weights, uniform random prompts)",
-           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d passes%d%s" % (
-               args.batch, args.prompt, args.generate, K, args.prior, args.passes,
+           "config": {"workload": "qwen3-8b-shape b%d prompt%d gen%d K%d natural prior%d passes%d "
+                                  "kappa%g%s" % (
+               args.batch, args.prompt, args.generate, K, args.prior, args.passes, args.kappa,
                " tree topk%d keep%d" % tree if tree else "")},
            "steps": st["steps"], "TPF": round(st["TPF"], 3), "AL": round(st["AL"], 3),
            "ms_per_step": round(1e3 * t_gen / st["steps"], 3),

@@ -39,7 +39,9 @@
  *   counter (slot, j, b, step[b]); the uniform is the top 24 bits of word 0.
  *   Slots: 0 draft token j+1; 1 accept test of draft j+1; 2 extra token (j = a;
  *   a tree node at depth d draws with j = d + 1); 3 uniform-prior noise of
- *   draft row j; 4 + i samples of intermediate draft pass i.
+ *   draft row j; 4 + i samples of intermediate draft pass i; 64 + i the
+ *   corrector's keep test of draft row j after pass i, 128 + i its fresh
+ *   uniform token for a remasked row.
  */
 #ifndef UNO_H
 #define UNO_H
@@ -158,24 +160,34 @@ int uno_draft_block(const uno_config *cfg, const uno_weights *w, const uno_kv *k
                     void *ws, size_t ws_bytes, void *stream);
 
 /* One draft pass of a multi-pass draft (paperglide reader, "Supplementary
- * Details": Psi-samplers refine a block over several denoising steps, and
- * sample quality grows with the number of steps).  Same as uno_draft_block,
- * except that
- *   block        [dev] int32 [batch, K] or NULL: when given, draft rows
- *                1..K-1 of sequence b hold block[b*K + 0 .. K-2] (the tokens
- *                d_1..d_{K-1} the previous pass sampled) instead of the
- *                prior's noise; it may alias draft_tokens (it is read before
- *                draft_tokens is written);
+ * Details": Psi-samplers are predictor-corrector samplers that refine a block
+ * over several denoising steps; a correction strength kappa_t in [0, 1]
+ * interpolates between ancestral sampling (kappa_t = 1) and the forward
+ * noising process, which remasks a masked model's tokens and re-draws a
+ * uniform-state model's).  Same as uno_draft_block, except that
+ *   block        [dev] int32 [batch, K] or NULL: when given, draft row j in
+ *                1..K-1 of sequence b is the corrector's output for the token
+ *                block[b*K + j-1] (the token d_j the previous pass sampled): it
+ *                is kept iff keep_q24 == 2^24 or U < keep_q24, U the 24-bit
+ *                uniform of Philox counter (64 + corr_pass, j, b, step[b]);
+ *                otherwise the row returns to the prior: mask_id, or (noise
+ *                prior 1) the uniform token floor(w * vocab / 2^64), w word 0
+ *                of counter (128 + corr_pass, j, b, step[b]).  block may
+ *                alias draft_tokens (it is read before draft_tokens is written);
  *   sample_slot  Philox slot of this pass's draft sampling: 0 for the pass
  *                whose drafts go to verification (as uno_draft_block), 4 + i
- *                for intermediate pass i (4 <= sample_slot <= 63).
- * Only the final pass's logits and tokens enter uno_spec_accept, so the
- * decode stays lossless for any number of passes. */
+ *                for intermediate pass i (4 <= sample_slot <= 63);
+ *   keep_q24     round(kappa * 2^24) in [0, 2^24] (ignored without block);
+ *   corr_pass    index of the pass whose samples the block holds (0..59).
+ * Only the final pass's logits and tokens enter uno_spec_accept; conditional
+ * on everything drawn before it that pass is an ordinary draft, so the decode
+ * stays lossless for any number of passes and any kappa. */
 int uno_draft_block_from(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
                          const int32_t *anchor, const int32_t *block, int batch, int K,
                          int max_ctx, float inv_temp, uint64_t seed, const uint64_t *step,
-                         int sample_slot, float *draft_logits, int32_t *draft_tokens,
-                         int32_t *status, void *ws, size_t ws_bytes, void *stream);
+                         int sample_slot, uint32_t keep_q24, int corr_pass,
+                         float *draft_logits, int32_t *draft_tokens, int32_t *status, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* Verify block (picx.dev summary, "Architecture": verification uses the AR
  * weights only).  Rows of sequence b: rows[b, 0..K-1] at positions

@@ -83,7 +83,8 @@ def load_library():
     lib.uno_draft_block.restype = I
     lib.uno_draft_block.argtypes = [P, P, P, P, I, I, I, F, U64, P, P, P, P, P, SZ, P]
     lib.uno_draft_block_from.restype = I
-    lib.uno_draft_block_from.argtypes = [P, P, P, P, P, I, I, I, F, U64, P, I, P, P, P, P, SZ, P]
+    lib.uno_draft_block_from.argtypes = [P, P, P, P, P, I, I, I, F, U64, P, I, ctypes.c_uint32,
+                                         I, P, P, P, P, SZ, P]
     lib.uno_verify_block.restype = I
     lib.uno_verify_block.argtypes = [P, P, P, P, I, I, I, I, P, P, P, SZ, P]
     lib.uno_draft_sample.restype = I
@@ -285,10 +286,21 @@ def draft_block(model, kv, anchor, K, max_ctx, inv_temp, seed, step, draft_logit
                                _ptr(draft_tokens), _ptr(status), _ptr(ws), ws.numel(), _stream()))
 
 
+def keep_threshold(kappa):
+    """Correction strength kappa in [0, 1] as the 24-bit keep threshold
+    round(kappa * 2^24) of uno_draft_block_from."""
+    k = float(kappa)
+    if not 0.0 <= k <= 1.0:
+        raise ValueError("kappa must lie in [0, 1]")
+    return int(round(k * (1 << 24)))
+
+
 def draft_block_from(model, kv, anchor, block, K, max_ctx, inv_temp, seed, step, sample_slot,
-                     draft_logits, draft_tokens, ws, status=None):
+                     draft_logits, draft_tokens, ws, status=None, kappa=1.0, corr_pass=0):
     """uno_draft_block_from: one pass of a multi-pass draft; block [B, K] int32
-    (rows 1..K-1 take block[:, :K-1]) or None; sample_slot 0 or 4 + pass."""
+    (rows 1..K-1 are the corrector's output for block[:, :K-1], each kept with
+    probability kappa) or None; sample_slot 0 or 4 + pass; corr_pass the index
+    of the pass that sampled block."""
     lib = load_library()
     B = anchor.shape[0]
     V = model.cfg["vocab"]
@@ -301,19 +313,23 @@ def draft_block_from(model, kv, anchor, block, K, max_ctx, inv_temp, seed, step,
     _check(lib.uno_draft_block_from(ctypes.byref(model.config), ctypes.byref(model.weights),
                                     ctypes.byref(kv.struct), _ptr(anchor), _ptr(block), B, K,
                                     max_ctx, float(inv_temp), int(seed), _ptr(step),
-                                    int(sample_slot), _ptr(draft_logits), _ptr(draft_tokens),
-                                    _ptr(status), _ptr(ws), ws.numel(), _stream()))
+                                    int(sample_slot), keep_threshold(kappa), int(corr_pass),
+                                    _ptr(draft_logits), _ptr(draft_tokens), _ptr(status),
+                                    _ptr(ws), ws.numel(), _stream()))
 
 
 def draft_passes(model, kv, anchor, K, max_ctx, inv_temp, seed, step, n_passes, draft_logits,
-                 draft_tokens, ws, status=None):
-    """n_passes draft passes: pass i > 0 reads the tokens pass i-1 sampled (slot
-    4 + (i-1)); the last pass samples with slot 0 and leaves the logits and
-    tokens that verification uses."""
+                 draft_tokens, ws, status=None, kappa=1.0):
+    """n_passes draft passes: pass i > 0 reads the corrector's output for the
+    tokens pass i-1 sampled (slot 4 + (i-1)), each kept with probability kappa
+    (one value, or one per transition); the last pass samples with slot 0 and
+    leaves the logits and tokens that verification uses."""
+    kap = list(kappa) if isinstance(kappa, (list, tuple)) else [kappa] * max(0, n_passes - 1)
     for i in range(n_passes):
         draft_block_from(model, kv, anchor, draft_tokens if i else None, K, max_ctx, inv_temp,
                          seed, step, 0 if i == n_passes - 1 else 4 + i, draft_logits,
-                         draft_tokens, ws, status)
+                         draft_tokens, ws, status, kappa=kap[i - 1] if i else 1.0,
+                         corr_pass=i - 1 if i else 0)
 
 
 def verify_block(model, kv, rows, max_ctx, pos_offset, verify_logits, ws, status=None):

@@ -165,7 +165,8 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
              bool lora,
              uint64_t seed, const uint64_t* step, float* logits, int32_t* status, void* ws,
              hipStream_t s, const int32_t* tree_depth = nullptr,
-             const uint32_t* tree_anc = nullptr) {
+             const uint32_t* tree_anc = nullptr, uint32_t keep_q24 = 1u << 24,
+             int corr_pass = 0) {
   const PassWs W = carve(c, B, K, max_ctx, ws);
   const int R = B * K;
   const int D = c.d_model, F = c.d_ffn, hd = c.head_dim;
@@ -176,7 +177,8 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   hipError_t e;
 #define UNO_TRY(x) do { e = (x); if (e != hipSuccess) return hip_fail(e); } while (0)
 
-  UNO_TRY(launch_embed(c, bp(w->embed), anchor, block, rows, B, K, seed, step, W.h, status, s));
+  UNO_TRY(launch_embed(c, bp(w->embed), anchor, block, rows, B, K, seed, step, keep_q24, corr_pass,
+                       W.h, status, s));
   UNO_TRY(launch_rope_table(c, *kv, B, K, draft ? 0 : pos_offset, tree_depth, W.cs, W.row_page,
                             status, s));
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
@@ -341,20 +343,22 @@ size_t uno_workspace_bytes(const uno_config* cfg, int batch, int K, int max_ctx)
 int uno_draft_block_from(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
                          const int32_t* anchor, const int32_t* block, int batch, int K,
                          int max_ctx, float inv_temp, uint64_t seed, const uint64_t* step,
-                         int sample_slot, float* draft_logits, int32_t* draft_tokens,
-                         int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                         int sample_slot, uint32_t keep_q24, int corr_pass, float* draft_logits,
+                         int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
+                         void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || K < 1 || K > 64 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
   if (!anchor || !step || !draft_logits || !draft_tokens || !ws) return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
   if (sample_slot != 0 && (sample_slot < 4 || sample_slot > 63)) return UNO_ERR_INVALID_ARG;
+  if (keep_q24 > (1u << 24) || corr_pass < 0 || corr_pass > 59) return UNO_ERR_INVALID_ARG;
   if ((rc = check_kv(*cfg, kv, K, 0))) return rc;
   if ((rc = check_layers(*cfg, w, true))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = run_pass(*cfg, w, kv, anchor, block, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
-                seed, step, draft_logits, status, ws, s);
+                seed, step, draft_logits, status, ws, s, nullptr, nullptr, keep_q24, corr_pass);
   if (rc) return rc;
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
     return launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed, sample_slot,
@@ -369,7 +373,8 @@ int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* k
                     int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
                     void* stream) {
   return uno_draft_block_from(cfg, w, kv, anchor, nullptr, batch, K, max_ctx, inv_temp, seed,
-                              step, 0, draft_logits, draft_tokens, status, ws, ws_bytes, stream);
+                              step, 0, 1u << 24, 0, draft_logits, draft_tokens, status, ws,
+                              ws_bytes, stream);
 }
 
 int uno_verify_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,

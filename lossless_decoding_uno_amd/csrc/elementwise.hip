@@ -16,30 +16,39 @@ namespace uno {
 
 // ------------------------------------------------------------ embedding
 // One workgroup per row r = b*K + j.  Draft mode (anchor != null): id =
-// anchor[b] for j == 0; the rows j >= 1 hold block[b*K + j-1] in a later draft
-// pass, else the prior's noise: mask_id (noise_prior 0) or a uniform token
-// floor(w * V / 2^64), w = Philox word 0 at counter (3, j, b, step[b]) under
-// key (seed, 0) (noise_prior 1).  Verify mode: id = rows[r].
+// anchor[b] for j == 0; the rows j >= 1 are the prior's noise -- mask_id
+// (noise_prior 0) or a uniform token floor(w * V / 2^64), w = Philox word 0 at
+// counter (3, j, b, step[b]) under key (seed, 0) (noise_prior 1) -- or, in a
+// later draft pass (block != null), the corrector's output: block[b*K + j-1]
+// kept iff keep_q24 >= 2^24 or the uniform of counter (64 + corr_pass, j, b,
+// step[b]) is below keep_q24, else returned to the prior (mask_id, or a fresh
+// uniform token from counter (128 + corr_pass, j, b, step[b])).  Verify mode:
+// id = rows[r].
 __global__ void __launch_bounds__(256)
 k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
         const int32_t* __restrict__ block, const int32_t* __restrict__ rows, int K, int D, int V,
         int mask_id, int noise_prior,
-        uint64_t seed, const uint64_t* __restrict__ step, float* __restrict__ h,
-        int32_t* __restrict__ status) {
+        uint64_t seed, const uint64_t* __restrict__ step, uint32_t keep_q24, int corr_pass,
+        float* __restrict__ h, int32_t* __restrict__ status) {
   const int r = blockIdx.x;
   const int b = r / K, j = r % K;
+  const uint64_t st = step ? step[b] : 0;
   int id;
   if (!anchor) {
     id = rows[r];
   } else if (j == 0) {
     id = anchor[b];
-  } else if (block) {
-    id = block[b * K + j - 1];
-  } else if (noise_prior == 0) {
-    id = mask_id;
   } else {
-    const uint64_t w = philox_word0(3, j, b, step ? step[b] : 0, seed, 0);
-    id = (int)__umul64hi(w, (uint64_t)V);
+    bool noise = true;
+    uint64_t noise_slot = 3;
+    if (block) {
+      noise = keep_q24 < (1u << 24) &&
+              (uint32_t)(philox_word0(64 + corr_pass, j, b, st, seed, 0) >> 40) >= keep_q24;
+      noise_slot = 128 + corr_pass;
+    }
+    if (!noise) id = block[b * K + j - 1];
+    else if (noise_prior == 0) id = mask_id;
+    else id = (int)__umul64hi(philox_word0(noise_slot, j, b, st, seed, 0), (uint64_t)V);
   }
   const bool bad = id < 0 || id >= V;
   if (bad) {
@@ -63,9 +72,11 @@ k_embed(const uint16_t* __restrict__ embed, const int32_t* __restrict__ anchor,
 
 hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
                         const int32_t* block, const int32_t* rows, int B, int K, uint64_t seed,
-                        const uint64_t* step, float* h, int32_t* status, hipStream_t s) {
+                        const uint64_t* step, uint32_t keep_q24, int corr_pass, float* h,
+                        int32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(k_embed, dim3(B * K), dim3(256), 0, s, embed, anchor, block, rows, K,
-                     c.d_model, c.vocab, c.mask_id, c.noise_prior, seed, step, h, status);
+                     c.d_model, c.vocab, c.mask_id, c.noise_prior, seed, step, keep_q24, corr_pass,
+                     h, status);
   return hipGetLastError();
 }
 

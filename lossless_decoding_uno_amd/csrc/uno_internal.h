@@ -42,12 +42,15 @@ hipError_t launch_spec_accept_static(const float* zq, const float* zp, const int
 // ---------------------------------------------------------------- elementwise / small ops
 // Block rows: draft (anchor + mask ids) or given rows; gathers embeddings into
 // the fp32 residual stream h [R, D]; also writes ids [R].
-// Draft rows (anchor != null): rows j >= 1 take block[b*K + j-1] when block is
-// given (a later draft pass), else the prior's noise: mask_id, or uniform
-// tokens from (seed, step) when c.noise_prior == 1.
+// Draft rows (anchor != null): rows j >= 1 take the prior's noise (mask_id, or
+// uniform tokens from (seed, step) when c.noise_prior == 1); in a later draft
+// pass (block given) row j keeps block[b*K + j-1] with probability
+// keep_q24 / 2^24 (Philox slot 64 + corr_pass) and otherwise returns to the
+// prior (a fresh uniform token: slot 128 + corr_pass).
 hipError_t launch_embed(const uno_config& c, const bf16_raw_t* embed, const int32_t* anchor,
                         const int32_t* block, const int32_t* rows, int B, int K, uint64_t seed,
-                        const uint64_t* step, float* h, int32_t* status, hipStream_t s);
+                        const uint64_t* step, uint32_t keep_q24, int corr_pass, float* h,
+                        int32_t* status, hipStream_t s);
 // RMSNorm of fp32 rows into bf16 rows.
 hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float eps,
                           bf16_raw_t* out, hipStream_t s);

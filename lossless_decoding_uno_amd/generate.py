@@ -75,9 +75,11 @@ class Generator:
     """
 
     def __init__(self, model, batch, K, max_ctx, n_pages=None, inv_temp=1.0, seed=0,
-                 prefill_chunk=512, page_size=16, device="cuda", n_passes=1, tree=None):
+                 prefill_chunk=512, page_size=16, device="cuda", n_passes=1, tree=None,
+                 kappa=1.0):
         self.model, self.B, self.K = model, batch, K
         self.n_passes = int(n_passes)      # draft passes per step (multi-pass drafting)
+        self.kappa = kappa                  # corrector strength between draft passes
         self.cfg = model.cfg
         self.inv_temp, self.seed = float(inv_temp), int(seed)
         self.chunk = int(prefill_chunk)
@@ -133,7 +135,8 @@ class Generator:
             self.pool.ensure(b, int(self.kv_len[b]) + self.n_rows + 1)
         self.pool.sync()
         draft_passes(self.model, self.kv, self.e, K, self.max_ctx, self.inv_temp, self.seed,
-                     self.step_ctr, self.n_passes, self.zq, self.d, self.ws, self.status)
+                     self.step_ctr, self.n_passes, self.zq, self.d, self.ws, self.status,
+                     kappa=self.kappa)
         if self.tb is not None:
             if forced is not None:
                 raise ValueError("forced accept lengths apply to the linear sampler only")

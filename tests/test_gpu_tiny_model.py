@@ -241,13 +241,20 @@ def test_many_rows_tiled_gemm_matches_oracle(B, K_blk, prompt_len):
                             "verify seq %d" % b)
 
 
-def test_multi_pass_draft_matches_oracle(setup):
-    """Multi-pass draft, pass by pass: pass 1 samples its block with Philox
-    slot 4, pass 2 re-runs the draft with rows 1..K-1 holding those tokens and
-    samples the drafts with slot 0.  Each pass's logits must match the oracle's
-    on the same block, and its tokens must be exactly the oracle sampler's on
-    the GPU's own logits; then verification and the accept step as usual."""
+@pytest.mark.parametrize("prior,kappa", [(0, 1.0), (0, 0.5), (1, 0.5), (0, 0.0)])
+def test_multi_pass_draft_matches_oracle(setup, prior, kappa):
+    """Multi-pass draft with the corrector, pass by pass: three passes, the
+    first two sampling with Philox slots 4 and 5, the last with slot 0; between
+    passes each drafted row keeps its sample with probability kappa and else
+    returns to the prior (mask or a fresh uniform token).  Each pass's logits
+    must match the oracle's on the block the oracle's corrector makes from the
+    GPU's samples (a differing keep decision changes a row's token and its
+    logits), and its tokens must be exactly the oracle sampler's on the GPU's
+    own logits; then verification and the accept step as usual."""
     U, cfg, wts, w64, model = setup
+    if prior:
+        cfg = dict(cfg, noise_prior=1)
+        model = U.Model(cfg, wts)
     prompt = synth.prompt_ids(cfg, 24, 9)
     cap = len(prompt) + 4 * (K + 1) + 8
     kv = U.PagedKV(cfg, 1, cap)
@@ -267,19 +274,25 @@ def test_multi_pass_draft_matches_oracle(setup):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     step_g = torch.zeros(1, dtype=torch.uint64).to(dev)
     aws = U.alloc_workspace(U.spec_accept_workspace_bytes(1, K))
+    kept = total = 0
     for _ in range(4):
         draws = ospec.PhiloxDraws(SEED, 0, seq.step)
         anchor = torch.tensor([seq.tokens[-1]], dtype=torch.int32, device=dev)
         block = None
-        for p, slot in enumerate((4, 0)):
+        for p, slot in enumerate((4, 5, 0)):
             U.draft_block_from(model, kv, anchor, d_g if p else None, K, cap, 1.0, SEED, step_g,
-                               slot, zq_g, d_g, ws, status)
+                               slot, zq_g, d_g, ws, status, kappa=kappa, corr_pass=p - 1 if p else 0)
             zq = ospec.draft_logits(cfg, w64, seq, K, draws=draws, block=block)
             zq_gpu = zq_g.cpu().numpy()[0]
             assert_logits_close(zq_gpu, zq, "pass %d step %d" % (p, seq.step))
             toks = ospec.draft_sample(zq_gpu, 1.0, draws, slot)
             np.testing.assert_array_equal(d_g.cpu().numpy()[0], toks)
-            block = toks
+            if slot:
+                block = ospec.corrected_block(cfg, toks, p, ospec.keep_threshold(kappa), draws)
+                kept += sum(int(x == y) for x, y in zip(block, toks[:K - 1]))
+                total += K - 1
+            else:
+                block = toks
         drafts = block
         rows = torch.tensor([drafts], dtype=torch.int32, device=dev)
         U.verify_block(model, kv, rows, cap, 1, zp_g, ws, status)
@@ -293,3 +306,9 @@ def test_multi_pass_draft_matches_oracle(setup):
         U.kv_commit(kv, a_g, K, step_g, status)
         ospec.commit(seq, a, committed)
     assert int(status.item()) == 0
+    if kappa == 1.0:
+        assert kept == total
+    elif kappa == 0.0 and prior == 0:
+        assert kept == 0
+    progress("multi-pass draft prior %d kappa %g: %d of %d rows kept" % (prior, kappa, kept,
+                                                                       total))
