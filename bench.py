@@ -118,6 +118,9 @@ class Workload:
         self.zq = torch.empty((B, K, V), dtype=torch.float32, device=dev)
         self.zp = torch.empty((B, K, V), dtype=torch.float32, device=dev)
         self.d = torch.empty((B, K), dtype=torch.int32, device=dev)
+        # exact row maxima of the draft / verify logits, written by the LM head
+        self.qmax = torch.empty((B, K), dtype=torch.float32, device=dev)
+        self.pmax = torch.empty((B, K), dtype=torch.float32, device=dev)
         self.a = torch.empty(B, dtype=torch.int32, device=dev)
         self.c = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
         self.e = torch.from_numpy(synth.prompt_ids(cfg, B, seed)).to(dev)   # first anchors
@@ -132,14 +135,16 @@ class Workload:
     def step(self, i, verify_events=None):
         U = self.U
         U.draft_block(self.model, self.kv, self.e, self.K, self.max_ctx, self.inv_t, 0, self.step_ctr,
-                      self.zq, self.d, self.ws, self.status)
+                      self.zq, self.d, self.ws, self.status, row_max=self.qmax)
         if verify_events is not None:
             verify_events[0].record()
-        U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws, self.status)
+        U.verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws, self.status,
+                       row_max=self.pmax)
         if verify_events is not None:
             verify_events[1].record()
         U.spec_accept(self.zq, self.zp, self.d, self.inv_t, 0, self.step_ctr, self.a, self.c, self.e,
-                      self.aws, forced_accept=self.forced[i], status=self.status)
+                      self.aws, forced_accept=self.forced[i], status=self.status,
+                      draft_row_max=self.qmax, verify_row_max=self.pmax)
         U.kv_commit(self.kv, self.a, self.K, self.step_ctr, self.status)
 
     def check_status(self):
@@ -354,7 +359,9 @@ def sampler_roofline(cfg, B, K, ms, read_ceiling):
     """The sampler launches of one step (draft sampling, acceptance statistics,
     accept / resample) against HBM: algorithmic bytes = the fp32 draft logits
     read once to sample the drafts, then the draft and verify logits read once
-    each to accept / resample (3 * B * K * V * 4), over their probe-step time."""
+    each to accept / resample (3 * B * K * V * 4), over their probe-step time.
+    The row maxima come from the LM head (its class holds the reduction of
+    their per-tile partials), so each row is streamed once per kernel."""
     byts = 3.0 * B * K * cfg["vocab"] * 4
     gbs = byts / (ms / 1e3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

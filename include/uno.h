@@ -148,6 +148,10 @@ size_t uno_workspace_bytes(const uno_config *cfg, int batch, int K, int max_ctx)
  *   anchor        [dev] int32 [batch]
  *   draft_logits  [dev] fp32 [batch, K, V]   q_1..q_K (untempered logits)
  *   draft_tokens  [dev] int32 [batch, K]     d_j+1 ~ q_j+1 at temperature 1/inv_temp
+ *   row_max       [dev] fp32 [batch, K] or NULL: receives the exact maximum of
+ *                 every draft logits row (the LM head's epilogue finds it, so
+ *                 the sampler streams each row once); pass it to
+ *                 uno_spec_accept as draft_row_max
  *   step          [dev] uint64 [batch]       Philox step counter per sequence
  *                                            (draft sampling; uniform noise)
  *   status        [dev] int32 [batch] or NULL
@@ -156,8 +160,8 @@ size_t uno_workspace_bytes(const uno_config *cfg, int batch, int K, int max_ctx)
 int uno_draft_block(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
                     const int32_t *anchor, int batch, int K, int max_ctx,
                     float inv_temp, uint64_t seed, const uint64_t *step,
-                    float *draft_logits, int32_t *draft_tokens, int32_t *status,
-                    void *ws, size_t ws_bytes, void *stream);
+                    float *draft_logits, int32_t *draft_tokens, float *row_max,
+                    int32_t *status, void *ws, size_t ws_bytes, void *stream);
 
 /* One draft pass of a multi-pass draft (paperglide reader, "Supplementary
  * Details": Psi-samplers are predictor-corrector samplers that refine a block
@@ -186,8 +190,8 @@ int uno_draft_block_from(const uno_config *cfg, const uno_weights *w, const uno_
                          const int32_t *anchor, const int32_t *block, int batch, int K,
                          int max_ctx, float inv_temp, uint64_t seed, const uint64_t *step,
                          int sample_slot, uint32_t keep_q24, int corr_pass,
-                         float *draft_logits, int32_t *draft_tokens, int32_t *status, void *ws,
-                         size_t ws_bytes, void *stream);
+                         float *draft_logits, int32_t *draft_tokens, float *row_max,
+                         int32_t *status, void *ws, size_t ws_bytes, void *stream);
 
 /* Verify block (picx.dev summary, "Architecture": verification uses the AR
  * weights only).  Rows of sequence b: rows[b, 0..K-1] at positions
@@ -196,18 +200,23 @@ int uno_draft_block_from(const uno_config *cfg, const uno_weights *w, const uno_
  * pos_offset = 1 after a draft block (the anchor sits at kv_len[b]);
  * pos_offset = 0 for a prompt chunk (prefill, followed by a commit with
  * accept_len = K-1).  verify_logits [dev] fp32 [batch, K, V] may be NULL to
- * skip the LM head.  1 <= K <= 4096. */
+ * skip the LM head.  row_max [dev] fp32 [batch, K] or NULL (and NULL when
+ * verify_logits is) receives the exact maximum of every logits row, for
+ * uno_spec_accept's verify_row_max.  1 <= K <= 4096. */
 int uno_verify_block(const uno_config *cfg, const uno_weights *w, const uno_kv *kv,
                      const int32_t *rows, int batch, int K, int max_ctx, int pos_offset,
-                     float *verify_logits, int32_t *status,
+                     float *verify_logits, float *row_max, int32_t *status,
                      void *ws, size_t ws_bytes, void *stream);
 
 /* Draft sampling alone (the categorical draw that uno_draft_block ends with):
  * tokens[b, j] = integer-weight categorical draw from logits[b, j, :] at
  * temperature 1/inv_temp with the slot-0 uniform of (j, b, step[b]).
- * logits [dev] fp32 [batch, K, V]; tokens [dev] int32 [batch, K]. */
-int uno_draft_sample(const float *logits, int batch, int K, int vocab, float inv_temp,
-                     uint64_t seed, const uint64_t *step, int32_t *tokens,
+ * logits [dev] fp32 [batch, K, V]; tokens [dev] int32 [batch, K]; row_max
+ * [dev] fp32 [batch, K] or NULL: the exact maximum of each row (then each row
+ * is streamed once; an entry that is not finite or exceeds its row's given
+ * maximum flags UNO_DEV_NONFINITE and the row's token is -1). */
+int uno_draft_sample(const float *logits, const float *row_max, int batch, int K, int vocab,
+                     float inv_temp, uint64_t seed, const uint64_t *step, int32_t *tokens,
                      int32_t *status, void *stream);
 
 /* Workspace for uno_spec_accept: per-row statistics of both logit sets. */
@@ -224,6 +233,11 @@ size_t uno_spec_accept_workspace_bytes(int batch, int K);
  * a < K: extra token ~ R_v = max(0, Wp_{a+1,v} Sq_{a+1} - Wq_{a+1,v} Sp_{a+1})
  * (p_{a+1} itself if R is all zero); a = K: bonus token ~ p_{K+1}.
  *   draft_logits, verify_logits [dev] fp32 [batch, K, V]
+ *   draft_row_max, verify_row_max [dev] fp32 [batch, K], both or neither: the
+ *                exact row maxima the passes wrote (row_max of
+ *                uno_draft_block / uno_verify_block); with them every logits
+ *                row is streamed once, and an entry that is not finite or
+ *                exceeds its given maximum flags UNO_DEV_NONFINITE
  *   draft_tokens [dev] int32 [batch, K]
  *   forced_accept [dev] int32 [batch] or NULL
  *   accept_len   [dev] int32 [batch]           a
@@ -231,6 +245,7 @@ size_t uno_spec_accept_workspace_bytes(int batch, int K);
  *   extra_token  [dev] int32 [batch]           the new anchor
  *   ws/ws_bytes  [dev] uno_spec_accept_workspace_bytes(batch, K) bytes */
 int uno_spec_accept(const float *draft_logits, const float *verify_logits,
+                    const float *draft_row_max, const float *verify_row_max,
                     const int32_t *draft_tokens, int batch, int K, int vocab,
                     float inv_temp, uint64_t seed, const uint64_t *step,
                     const int32_t *forced_accept, int32_t *accept_len,
@@ -248,6 +263,7 @@ int uno_spec_accept(const float *draft_logits, const float *verify_logits,
  * allocation).  Every call on one GPU shares its array: calls that overlap on
  * one GPU (two streams, two threads) race and must be ordered by the caller. */
 int uno_spec_accept_noalloc(const float *draft_logits, const float *verify_logits,
+                            const float *draft_row_max, const float *verify_row_max,
                             const int32_t *draft_tokens, int batch, int K, int vocab,
                             float inv_temp, uint64_t seed, const uint64_t *step,
                             const int32_t *forced_accept, int32_t *accept_len,

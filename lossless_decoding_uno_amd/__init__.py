@@ -81,20 +81,20 @@ def load_library():
     lib.uno_workspace_bytes.restype = SZ
     lib.uno_workspace_bytes.argtypes = [P, I, I, I]
     lib.uno_draft_block.restype = I
-    lib.uno_draft_block.argtypes = [P, P, P, P, I, I, I, F, U64, P, P, P, P, P, SZ, P]
+    lib.uno_draft_block.argtypes = [P, P, P, P, I, I, I, F, U64, P, P, P, P, P, P, SZ, P]
     lib.uno_draft_block_from.restype = I
     lib.uno_draft_block_from.argtypes = [P, P, P, P, P, I, I, I, F, U64, P, I, ctypes.c_uint32,
-                                         I, P, P, P, P, SZ, P]
+                                         I, P, P, P, P, P, SZ, P]
     lib.uno_verify_block.restype = I
-    lib.uno_verify_block.argtypes = [P, P, P, P, I, I, I, I, P, P, P, SZ, P]
+    lib.uno_verify_block.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, SZ, P]
     lib.uno_draft_sample.restype = I
-    lib.uno_draft_sample.argtypes = [P, I, I, I, F, U64, P, P, P, P]
+    lib.uno_draft_sample.argtypes = [P, P, I, I, I, F, U64, P, P, P, P]
     lib.uno_spec_accept_workspace_bytes.restype = SZ
     lib.uno_spec_accept_workspace_bytes.argtypes = [I, I]
     lib.uno_spec_accept.restype = I
-    lib.uno_spec_accept.argtypes = [P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P, SZ, P]
+    lib.uno_spec_accept.argtypes = [P, P, P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P, SZ, P]
     lib.uno_spec_accept_noalloc.restype = I
-    lib.uno_spec_accept_noalloc.argtypes = [P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P]
+    lib.uno_spec_accept_noalloc.argtypes = [P, P, P, P, P, I, I, I, F, U64, P, P, P, P, P, P, P]
     lib.uno_kv_commit.restype = I
     lib.uno_kv_commit.argtypes = [P, P, I, I, P, P, P]
     lib.uno_tree_rows.restype = I
@@ -269,10 +269,17 @@ def alloc_workspace(nbytes, device="cuda"):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _row_max_arg(row_max, B, K):
+    if row_max is not None:
+        _need(row_max, torch.float32, (B, K), "row_max")
+    return _ptr(row_max)
+
+
 def draft_block(model, kv, anchor, K, max_ctx, inv_temp, seed, step, draft_logits,
-                draft_tokens, ws, status=None):
+                draft_tokens, ws, status=None, row_max=None):
     """uno_draft_block: anchor [B] int32, step [B] uint64 -> draft_logits
-    [B, K, V] fp32 and draft_tokens [B, K] int32 (written in place)."""
+    [B, K, V] fp32 and draft_tokens [B, K] int32 (written in place); row_max
+    [B, K] fp32 (optional) receives every logits row's maximum."""
     lib = load_library()
     B = anchor.shape[0]
     V = model.cfg["vocab"]
@@ -283,7 +290,8 @@ def draft_block(model, kv, anchor, K, max_ctx, inv_temp, seed, step, draft_logit
     _check(lib.uno_draft_block(ctypes.byref(model.config), ctypes.byref(model.weights),
                                ctypes.byref(kv.struct), _ptr(anchor), B, K, max_ctx,
                                float(inv_temp), int(seed), _ptr(step), _ptr(draft_logits),
-                               _ptr(draft_tokens), _ptr(status), _ptr(ws), ws.numel(), _stream()))
+                               _ptr(draft_tokens), _row_max_arg(row_max, B, K), _ptr(status),
+                               _ptr(ws), ws.numel(), _stream()))
 
 
 def keep_threshold(kappa):
@@ -296,7 +304,8 @@ def keep_threshold(kappa):
 
 
 def draft_block_from(model, kv, anchor, block, K, max_ctx, inv_temp, seed, step, sample_slot,
-                     draft_logits, draft_tokens, ws, status=None, kappa=1.0, corr_pass=0):
+                     draft_logits, draft_tokens, ws, status=None, kappa=1.0, corr_pass=0,
+                     row_max=None):
     """uno_draft_block_from: one pass of a multi-pass draft; block [B, K] int32
     (rows 1..K-1 are the corrector's output for block[:, :K-1], each kept with
     probability kappa) or None; sample_slot 0 or 4 + pass; corr_pass the index
@@ -314,12 +323,13 @@ def draft_block_from(model, kv, anchor, block, K, max_ctx, inv_temp, seed, step,
                                     ctypes.byref(kv.struct), _ptr(anchor), _ptr(block), B, K,
                                     max_ctx, float(inv_temp), int(seed), _ptr(step),
                                     int(sample_slot), keep_threshold(kappa), int(corr_pass),
-                                    _ptr(draft_logits), _ptr(draft_tokens), _ptr(status),
+                                    _ptr(draft_logits), _ptr(draft_tokens),
+                                    _row_max_arg(row_max, B, K), _ptr(status),
                                     _ptr(ws), ws.numel(), _stream()))
 
 
 def draft_passes(model, kv, anchor, K, max_ctx, inv_temp, seed, step, n_passes, draft_logits,
-                 draft_tokens, ws, status=None, kappa=1.0):
+                 draft_tokens, ws, status=None, kappa=1.0, row_max=None):
     """n_passes draft passes: pass i > 0 reads the corrector's output for the
     tokens pass i-1 sampled (slot 4 + (i-1)), each kept with probability kappa
     (one value, or one per transition); the last pass samples with slot 0 and
@@ -329,11 +339,13 @@ def draft_passes(model, kv, anchor, K, max_ctx, inv_temp, seed, step, n_passes, 
         draft_block_from(model, kv, anchor, draft_tokens if i else None, K, max_ctx, inv_temp,
                          seed, step, 0 if i == n_passes - 1 else 4 + i, draft_logits,
                          draft_tokens, ws, status, kappa=kap[i - 1] if i else 1.0,
-                         corr_pass=i - 1 if i else 0)
+                         corr_pass=i - 1 if i else 0, row_max=row_max)
 
 
-def verify_block(model, kv, rows, max_ctx, pos_offset, verify_logits, ws, status=None):
-    """uno_verify_block: rows [B, K] int32 -> verify_logits [B, K, V] fp32 (or None)."""
+def verify_block(model, kv, rows, max_ctx, pos_offset, verify_logits, ws, status=None,
+                 row_max=None):
+    """uno_verify_block: rows [B, K] int32 -> verify_logits [B, K, V] fp32 (or None);
+    row_max [B, K] fp32 (optional) receives every logits row's maximum."""
     lib = load_library()
     B, K = rows.shape
     _need(rows, torch.int32, (B, K), "rows")
@@ -341,22 +353,24 @@ def verify_block(model, kv, rows, max_ctx, pos_offset, verify_logits, ws, status
         _need(verify_logits, torch.float32, (B, K, model.cfg["vocab"]), "verify_logits")
     _check(lib.uno_verify_block(ctypes.byref(model.config), ctypes.byref(model.weights),
                                 ctypes.byref(kv.struct), _ptr(rows), B, K, max_ctx, pos_offset,
-                                _ptr(verify_logits), _ptr(status), _ptr(ws), ws.numel(),
-                                _stream()))
+                                _ptr(verify_logits), _row_max_arg(row_max, B, K), _ptr(status),
+                                _ptr(ws), ws.numel(), _stream()))
 
 
-def draft_sample(logits, inv_temp, seed, step, tokens, status=None):
+def draft_sample(logits, inv_temp, seed, step, tokens, status=None, row_max=None):
     lib = load_library()
     B, K, V = logits.shape
     _need(logits, torch.float32, (B, K, V), "logits")
     _need(step, torch.uint64, (B,), "step")
     _need(tokens, torch.int32, (B, K), "tokens")
-    _check(lib.uno_draft_sample(_ptr(logits), B, K, V, float(inv_temp), int(seed), _ptr(step),
-                                _ptr(tokens), _ptr(status), _stream()))
+    _check(lib.uno_draft_sample(_ptr(logits), _row_max_arg(row_max, B, K), B, K, V,
+                                float(inv_temp), int(seed), _ptr(step), _ptr(tokens),
+                                _ptr(status), _stream()))
 
 
 def spec_accept(draft_logits, verify_logits, draft_tokens, inv_temp, seed, step, accept_len,
-                committed, extra_token, ws, forced_accept=None, status=None):
+                committed, extra_token, ws, forced_accept=None, status=None,
+                draft_row_max=None, verify_row_max=None):
     lib = load_library()
     B, K, V = draft_logits.shape
     _need(draft_logits, torch.float32, (B, K, V), "draft_logits")
@@ -368,14 +382,17 @@ def spec_accept(draft_logits, verify_logits, draft_tokens, inv_temp, seed, step,
     _need(extra_token, torch.int32, (B,), "extra_token")
     if forced_accept is not None:
         _need(forced_accept, torch.int32, (B,), "forced_accept")
-    _check(lib.uno_spec_accept(_ptr(draft_logits), _ptr(verify_logits), _ptr(draft_tokens), B, K,
+    _check(lib.uno_spec_accept(_ptr(draft_logits), _ptr(verify_logits),
+                               _row_max_arg(draft_row_max, B, K),
+                               _row_max_arg(verify_row_max, B, K), _ptr(draft_tokens), B, K,
                                V, float(inv_temp), int(seed), _ptr(step), _ptr(forced_accept),
                                _ptr(accept_len), _ptr(committed), _ptr(extra_token),
                                _ptr(status), _ptr(ws), ws.numel(), _stream()))
 
 
 def spec_accept_noalloc(draft_logits, verify_logits, draft_tokens, inv_temp, seed, step,
-                        accept_len, committed, extra_token, forced_accept=None, status=None):
+                        accept_len, committed, extra_token, forced_accept=None, status=None,
+                        draft_row_max=None, verify_row_max=None):
     """uno_spec_accept_noalloc: as spec_accept, on the library's static scratch
     (no workspace argument)."""
     lib = load_library()
@@ -390,6 +407,8 @@ def spec_accept_noalloc(draft_logits, verify_logits, draft_tokens, inv_temp, see
     if forced_accept is not None:
         _need(forced_accept, torch.int32, (B,), "forced_accept")
     _check(lib.uno_spec_accept_noalloc(_ptr(draft_logits), _ptr(verify_logits),
+                                       _row_max_arg(draft_row_max, B, K),
+                                       _row_max_arg(verify_row_max, B, K),
                                        _ptr(draft_tokens), B, K, V, float(inv_temp), int(seed),
                                        _ptr(step), _ptr(forced_accept), _ptr(accept_len),
                                        _ptr(committed), _ptr(extra_token), _ptr(status),

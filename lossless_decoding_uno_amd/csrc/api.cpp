@@ -102,6 +102,8 @@ struct PassWs {
   float* gemm_part;      // split-K partial tiles (passes of more than 64 rows)
   size_t gemm_part_floats;
   float* lora_part;      // LoRA-A split-K partials read by the next projection (<= 64 rows)
+  float* max_part;       // [R, V/16] LM-head row-maxima partials (per column group)
+  float* row_max;        // [R] row maxima of the logits (when the caller passes none)
   size_t total;
 };
 
@@ -137,6 +139,9 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.gemm_part_floats = R > 64 ? kGemmPartFloats : kGemmPartFloatsSkinny;
   w.gemm_part = reinterpret_cast<float*>(take(w.gemm_part_floats * 4));
   w.lora_part = R <= 64 ? reinterpret_cast<float*>(take(kLoraPartFloats * 4)) : nullptr;
+  w.max_part = reinterpret_cast<float*>(
+      take(R * gemm_row_max_parts_bound(c.vocab, (int)R) * 4));
+  w.row_max = reinterpret_cast<float*>(take(R * 4));
   w.total = off;
   return w;
 }
@@ -163,7 +168,8 @@ const bf16_raw_t* bp(const void* p) { return static_cast<const bf16_raw_t*>(p); 
 int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const int32_t* anchor,
              const int32_t* block, const int32_t* rows, int B, int K, int max_ctx, int pos_offset,
              bool lora,
-             uint64_t seed, const uint64_t* step, float* logits, int32_t* status, void* ws,
+             uint64_t seed, const uint64_t* step, float* logits, float* row_max,
+             int32_t* status, void* ws,
              hipStream_t s, const int32_t* tree_depth = nullptr,
              const uint32_t* tree_anc = nullptr, uint32_t keep_q24 = 1u << 24,
              int corr_pass = 0) {
@@ -325,7 +331,22 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
     g.seg[0] = GemmSeg{bp(w->lm_head), c.vocab, nullptr, 0};
     g.n_seg = 1;
     g.epi = EPI_STORE_F32; g.out = logits; g.ldo = c.vocab;
-    UNO_TRY(timed(UNO_TIME_LM_HEAD, s, [&] { return launch_gemm(g, s); }));
+    if (row_max) {
+      // the LM head also yields every logits row's exact maximum, so that the
+      // sampler streams each row once
+      g.max_part = W.max_part;
+      g.max_part_ld = gemm_row_max_parts(g);
+    }
+    // a plan with more column groups than carved for: the maxima are taken
+    // from the stored rows instead (one row per workgroup)
+    const bool from_rows = row_max && g.max_part_ld > gemm_row_max_parts_bound(c.vocab, R);
+    if (from_rows) g.max_part = nullptr;
+    UNO_TRY(timed(UNO_TIME_LM_HEAD, s, [&] {
+      const hipError_t e1 = launch_gemm(g, s);
+      if (e1 != hipSuccess || !row_max) return e1;
+      if (from_rows) return launch_row_max(logits, c.vocab, c.vocab, R, row_max, s);
+      return launch_row_max(W.max_part, g.max_part_ld, g.max_part_ld, R, row_max, s);
+    }));
   }
 #undef UNO_TRY
   return UNO_OK;
@@ -344,8 +365,8 @@ int uno_draft_block_from(const uno_config* cfg, const uno_weights* w, const uno_
                          const int32_t* anchor, const int32_t* block, int batch, int K,
                          int max_ctx, float inv_temp, uint64_t seed, const uint64_t* step,
                          int sample_slot, uint32_t keep_q24, int corr_pass, float* draft_logits,
-                         int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         int32_t* draft_tokens, float* row_max, int32_t* status, void* ws,
+                         size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || K < 1 || K > 64 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
@@ -357,12 +378,14 @@ int uno_draft_block_from(const uno_config* cfg, const uno_weights* w, const uno_
   if ((rc = check_layers(*cfg, w, true))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  float* rmax = row_max ? row_max : carve(*cfg, batch, K, max_ctx, ws).row_max;
   rc = run_pass(*cfg, w, kv, anchor, block, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
-                seed, step, draft_logits, status, ws, s, nullptr, nullptr, keep_q24, corr_pass);
+                seed, step, draft_logits, rmax, status, ws, s, nullptr, nullptr, keep_q24,
+                corr_pass);
   if (rc) return rc;
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
-    return launch_draft_sample(draft_logits, batch, K, cfg->vocab, inv_temp, seed, sample_slot,
-                               step, draft_tokens, status, s);
+    return launch_draft_sample(draft_logits, rmax, batch, K, cfg->vocab, inv_temp, seed,
+                               sample_slot, step, draft_tokens, status, s);
   });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
@@ -370,37 +393,39 @@ int uno_draft_block_from(const uno_config* cfg, const uno_weights* w, const uno_
 int uno_draft_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
                     const int32_t* anchor, int batch, int K, int max_ctx, float inv_temp,
                     uint64_t seed, const uint64_t* step, float* draft_logits,
-                    int32_t* draft_tokens, int32_t* status, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    int32_t* draft_tokens, float* row_max, int32_t* status, void* ws,
+                    size_t ws_bytes, void* stream) {
   return uno_draft_block_from(cfg, w, kv, anchor, nullptr, batch, K, max_ctx, inv_temp, seed,
-                              step, 0, 1u << 24, 0, draft_logits, draft_tokens, status, ws,
-                              ws_bytes, stream);
+                              step, 0, 1u << 24, 0, draft_logits, draft_tokens, row_max, status,
+                              ws, ws_bytes, stream);
 }
 
 int uno_verify_block(const uno_config* cfg, const uno_weights* w, const uno_kv* kv,
                      const int32_t* rows, int batch, int K, int max_ctx, int pos_offset,
-                     float* verify_logits, int32_t* status, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     float* verify_logits, float* row_max, int32_t* status, void* ws,
+                     size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (batch < 1 || K < 1 || K > 4096 || max_ctx < 1) return UNO_ERR_INVALID_ARG;
   if (pos_offset < 0 || pos_offset > 1) return UNO_ERR_INVALID_ARG;
   if (!rows || !ws) return UNO_ERR_INVALID_ARG;
+  if (row_max && !verify_logits) return UNO_ERR_INVALID_ARG;
   if ((rc = check_kv(*cfg, kv, K, pos_offset))) return rc;
   if ((rc = check_layers(*cfg, w, false))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   return run_pass(*cfg, w, kv, nullptr, nullptr, rows, batch, K, max_ctx, pos_offset, false, 0,
-                  nullptr, verify_logits, status, ws, static_cast<hipStream_t>(stream));
+                  nullptr, verify_logits, row_max, status, ws, static_cast<hipStream_t>(stream));
 }
 
-int uno_draft_sample(const float* logits, int batch, int K, int vocab, float inv_temp,
-                     uint64_t seed, const uint64_t* step, int32_t* tokens, int32_t* status,
-                     void* stream) {
+int uno_draft_sample(const float* logits, const float* row_max, int batch, int K, int vocab,
+                     float inv_temp, uint64_t seed, const uint64_t* step, int32_t* tokens,
+                     int32_t* status, void* stream) {
   if (!logits || !step || !tokens) return UNO_ERR_INVALID_ARG;
   if (batch < 1 || K < 1 || vocab < 1 || vocab > (1 << 20)) return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
-  const hipError_t e = launch_draft_sample(logits, batch, K, vocab, inv_temp, seed, 0, step, tokens,
-                                           status, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_draft_sample(logits, row_max, batch, K, vocab, inv_temp, seed, 0,
+                                           step, tokens, status,
+                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 
@@ -410,6 +435,7 @@ size_t uno_spec_accept_workspace_bytes(int batch, int K) {
 }
 
 int uno_spec_accept(const float* draft_logits, const float* verify_logits,
+                    const float* draft_row_max, const float* verify_row_max,
                     const int32_t* draft_tokens, int batch, int K, int vocab, float inv_temp,
                     uint64_t seed, const uint64_t* step, const int32_t* forced_accept,
                     int32_t* accept_len, int32_t* committed, int32_t* extra_token,
@@ -417,20 +443,22 @@ int uno_spec_accept(const float* draft_logits, const float* verify_logits,
   if (!draft_logits || !verify_logits || !draft_tokens || !step || !accept_len || !committed ||
       !extra_token || !ws)
     return UNO_ERR_INVALID_ARG;
+  if (!draft_row_max != !verify_row_max) return UNO_ERR_INVALID_ARG;
   if (batch < 1 || K < 1 || K > 4096 || vocab < 1 || vocab > (1 << 20))
     return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
   if (ws_bytes < spec_accept_ws_bytes(batch, K)) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
-    return launch_spec_accept(draft_logits, verify_logits, draft_tokens, batch, K, vocab,
-                              inv_temp, seed, step, forced_accept, accept_len, committed,
-                              extra_token, status, ws, s);
+    return launch_spec_accept(draft_logits, verify_logits, draft_row_max, verify_row_max,
+                              draft_tokens, batch, K, vocab, inv_temp, seed, step, forced_accept,
+                              accept_len, committed, extra_token, status, ws, s);
   });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 
 int uno_spec_accept_noalloc(const float* draft_logits, const float* verify_logits,
+                            const float* draft_row_max, const float* verify_row_max,
                             const int32_t* draft_tokens, int batch, int K, int vocab,
                             float inv_temp, uint64_t seed, const uint64_t* step,
                             const int32_t* forced_accept, int32_t* accept_len,
@@ -439,15 +467,16 @@ int uno_spec_accept_noalloc(const float* draft_logits, const float* verify_logit
   if (!draft_logits || !verify_logits || !draft_tokens || !step || !accept_len || !committed ||
       !extra_token)
     return UNO_ERR_INVALID_ARG;
+  if (!draft_row_max != !verify_row_max) return UNO_ERR_INVALID_ARG;
   if (batch < 1 || K < 1 || K > 4096 || vocab < 1 || vocab > (1 << 20))
     return UNO_ERR_INVALID_ARG;
   if (!(inv_temp > 0.f) || !isfinite(inv_temp)) return UNO_ERR_INVALID_ARG;
   if (2 * (int64_t)batch * K > static_accept_max_rows()) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
-    return launch_spec_accept_static(draft_logits, verify_logits, draft_tokens, batch, K, vocab,
-                                     inv_temp, seed, step, forced_accept, accept_len, committed,
-                                     extra_token, status, s);
+    return launch_spec_accept_static(draft_logits, verify_logits, draft_row_max, verify_row_max,
+                                     draft_tokens, batch, K, vocab, inv_temp, seed, step,
+                                     forced_accept, accept_len, committed, extra_token, status, s);
   });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
@@ -508,7 +537,7 @@ int uno_verify_tree(const uno_config* cfg, const uno_weights* w, const uno_kv* k
   if ((rc = check_layers(*cfg, w, false))) return rc;
   if (ws_bytes < carve(*cfg, batch, n_rows, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   return run_pass(*cfg, w, kv, nullptr, nullptr, node_tokens, batch, n_rows, max_ctx, 1, false, 0,
-                  nullptr, verify_logits, status, ws, static_cast<hipStream_t>(stream),
+                  nullptr, verify_logits, nullptr, status, ws, static_cast<hipStream_t>(stream),
                   node_depth, node_anc);
 }
 

@@ -123,6 +123,8 @@ template <int MT, int NT>
 __global__ void __launch_bounds__(kSkWaves * 64)
 k_gemm_skinny(GemmArgs a) {
   __shared__ f32x4 red[kSkWaves * MT * NT * 64];
+  __shared__ float rmax[MT * 16];             // row maxima of this workgroup (max_part)
+  if (threadIdx.x < MT * 16) reinterpret_cast<int*>(rmax)[threadIdx.x] = kNegInfBits;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int rr = l & 15, kg = l >> 4;
   const SegView sv = pick_segment(a, blockIdx.x * NT);
@@ -265,7 +267,16 @@ k_gemm_skinny(GemmArgs a) {
     for (int ww = 0; ww < kSkWaves; ++ww) v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + i];
     const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
     const int nl = sv.n0 + t * 16 + (ln & 15);
-    if (m < a.M && nl < sv.n) store_out(a, m, sv.col_base + nl, v);
+    if (m < a.M && nl < sv.n) {
+      store_out(a, m, sv.col_base + nl, v);
+      if (a.max_part) atomic_max_f32(&rmax[m - m0], v);
+    }
+  }
+  if (a.max_part) {
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < MT * 16 && m0 + t < a.M)
+      a.max_part[(size_t)(m0 + t) * a.max_part_ld + blockIdx.x] = rmax[t];
   }
 }
 
@@ -401,7 +412,7 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   const size_t tile = (size_t)p.mt * p.nt * 256;
   p.splits = 1;
   const size_t per_split = (size_t)a.M * skinny_cols(a);
-  if (a.part)
+  if (a.part && !a.max_part)
     while (p.gx * p.gy * p.splits < 512 && steps / (p.splits * 2) >= kSkWaves &&
            (size_t)p.splits * 2 * per_split <= a.part_floats &&
            (a.max_splits <= 0 || p.splits * 2 <= a.max_splits))
@@ -795,6 +806,30 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
         if (m < a.M) store_out(a, m, sv.col_base + nl, acc[i][j][e]);
       }
   }
+  if (a.max_part) {
+    // row maxima over the tile's columns: a lane's columns, then the 32 lanes
+    // that share its rows, then the WN waves (LDS), one partial per row
+    __syncthreads();                                   // stages no longer read
+    float* rmax = reinterpret_cast<float*>(lds);
+    for (int t = tid; t < C::BM; t += C::kThreads) reinterpret_cast<int*>(rmax)[t] = kNegInfBits;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          if (n0 + wn * C::TN + j * 32 + (l & 31) < sv.n) mx = fmaxf(mx, acc[i][j][e]);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, UNO_WAVE));
+        if ((l & 31) == 0)
+          atomic_max_f32(&rmax[wm * C::TM + i * 32 + (e >> 2) * 8 + (l >> 5) * 4 + (e & 3)], mx);
+      }
+    __syncthreads();
+    for (int t = tid; t < C::BM; t += C::kThreads)
+      if (m0 + t < a.M) a.max_part[(size_t)(m0 + t) * a.max_part_ld + nt] = rmax[t];
+  }
 }
 
 // Sum the split-K partial tiles in split order and apply the epilogue; one
@@ -1016,6 +1051,27 @@ k_gemm_splitk_reduce_rope(GemmArgs a, int m_tiles, int n_tiles, int splits) {
   }
 }
 
+// Row maxima (max_part) of the split tiles n_full, n_full + 1, ... from their
+// stored rows, after the split-K reduction: one wave per row of a tile.
+template <class C>
+__global__ void __launch_bounds__(256)
+k_tile_row_max(GemmArgs a, int m_tiles, int n_full) {
+  constexpr int WGS = C::BM / 4;                 // workgroups per tile
+  const int tr = blockIdx.x / WGS;
+  const int row = (blockIdx.x % WGS) * 4 + (threadIdx.x >> 6);
+  const int tile = n_full + tr;
+  const int mt = tile % m_tiles, nt = tile / m_tiles;
+  const int m = mt * C::BM + row;
+  if (m >= a.M) return;
+  const SegView sv = pick_segment(a, nt * (C::BN / 16));
+  const int n1 = sv.n0 + C::BN < sv.n ? sv.n0 + C::BN : sv.n;
+  const float* y = static_cast<const float*>(a.out) + (size_t)m * a.ldo + sv.col_base;
+  float mx = -INFINITY;
+  for (int c = sv.n0 + (threadIdx.x & 63); c < n1; c += 64) mx = fmaxf(mx, y[c]);
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) a.max_part[(size_t)m * a.max_part_ld + nt] = mx;
+}
+
 template <class C>
 static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_t s,
                                  bool* roped) {
@@ -1037,6 +1093,9 @@ static hipError_t launch_big_cfg(const GemmArgs& a, const BigPlan& p, hipStream_
     const int n = rem * (C::kTileFloats / 4);
     hipLaunchKernelGGL(k_gemm_splitk_reduce<C>, dim3((n + 255) / 256), dim3(256), 0, s, a,
                        p.m_tiles, p.n_tiles, p.splits, p.n_full);
+    if (a.max_part && a.epi == EPI_STORE_F32)
+      hipLaunchKernelGGL(k_tile_row_max<C>, dim3(rem * (C::BM / 4)), dim3(256), 0, s, a,
+                         p.m_tiles, p.n_full);
   }
   return hipGetLastError();
 }
@@ -1054,6 +1113,33 @@ static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s,
 // the rows held in registers (past 64 rows it would stream W once per 64).
 bool gemm_swiglu_ok(const GemmArgs& a) {
   return a.epi == EPI_SWIGLU && a.M > 64 && plan_big(a).cfg >= 0;
+}
+
+int gemm_row_max_parts(const GemmArgs& a) {
+  if (a.M > 64) {
+    const BigPlan p = plan_big(a);
+    if (p.cfg >= 0) return p.n_tiles;
+  }
+  return plan_skinny(a).gx;
+}
+
+// One workgroup per row: the maximum of its column-group partials.
+__global__ void __launch_bounds__(256)
+k_row_max(const float* __restrict__ part, int ld, int n_parts, float* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  float mx = -INFINITY;
+  for (int i = threadIdx.x; i < n_parts; i += 256) mx = fmaxf(mx, part[(size_t)r * ld + i]);
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) out[r] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+hipError_t launch_row_max(const float* max_part, int ld, int n_parts, int R, float* row_max,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_row_max, dim3(R), dim3(256), 0, s, max_part, ld, n_parts, row_max);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped,

@@ -15,9 +15,12 @@
 // rounded fp32 op: contraction into FMA is switched off in this file.
 //
 // Layout: logits are fp32 rows of V entries; row (b, j) of a [B, K, V] tensor
-// starts at (b*K + j)*V.  Each row is handled by one workgroup of 4 waves (16
-// when there are fewer than 512 rows); rows are streamed with 16-byte loads
-// when V % 4 == 0.
+// starts at (b*K + j)*V.  Each row is handled by one 1024-thread workgroup;
+// rows are streamed with 16-byte loads when V % 4 == 0.  When the row maxima
+// are given (the LM head's epilogue produces them exactly), every row is
+// streamed once: the weights are formed in the same pass that checks each
+// entry (finite, not above the given maximum); otherwise a maximum pass
+// precedes it.
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -218,6 +221,46 @@ __device__ u128 block_weight_sum(const WF& wf, int V, u128* tiles, RowShared<TH>
   return tot;
 }
 
+// The same for a plain row whose maximum m is given (the LM head's epilogue
+// found it): one pass over the row, which also checks every entry -- a NaN or
+// Inf entry, or one above m, sets *bad (the draw is then skipped).
+template <int TH>
+__device__ u128 block_weight_sum_given_max(const PlainWeights& wf, int V, u128* tiles,
+                                           RowShared<TH>& sh, bool* bad_out) {
+  const int w = threadIdx.x / UNO_WAVE, l = lane_id();
+  const int n_tiles = (V + kTile - 1) / kTile;
+  constexpr int NW = TH / UNO_WAVE;
+  u128 acc = u128_make(0, 0);
+  int bad = 0;
+  for (int t = w; t < n_tiles; t += kUnroll * NW) {
+    PlainWeights::Raw raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) wf.load((t + u * NW) * kTile + l * 4, raw[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t + u * NW >= n_tiles) break;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (raw[u].ok[c]) bad |= !__builtin_isfinite(raw[u].v[c]) || raw[u].v[c] > wf.m;
+      u128 v[4];
+      wf.weights(raw[u], v);
+      u128 s = u128_add(u128_add(v[0], v[1]), u128_add(v[2], v[3]));
+      s = wave_sum_u128(s);
+      if (l == 0) tiles[t + u * NW] = s;
+      acc = u128_add(acc, s);
+    }
+  }
+  bad = __any(bad);
+  if (l == 0) { sh.red_u[w] = acc; sh.red_i[w] = bad; }
+  __syncthreads();
+  u128 tot = sh.red_u[0];
+  int rb = sh.red_i[0];
+  for (int i = 1; i < (TH / UNO_WAVE); ++i) { tot = u128_add(tot, sh.red_u[i]); rb |= sh.red_i[i]; }
+  __syncthreads();
+  *bad_out = rb != 0 || !__builtin_isfinite(wf.m);
+  return tot;
+}
+
 // Smallest entry whose running weight sum exceeds `t` (t < total).  Needs the
 // tile sums from block_weight_sum.  Every thread returns the index.
 template <int TH, class WF>
@@ -281,7 +324,8 @@ __device__ __forceinline__ void flag(int32_t* status, int b, int32_t f) {
 // j = row_j[row] + j_add, and rows at or past n_valid[b] are skipped (-1).
 template <int TH>
 __global__ void __launch_bounds__(TH)
-k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, uint64_t seed,
+k_draft_sample(const float* __restrict__ logits, const float* __restrict__ row_max, int K, int V,
+               float inv_temp, uint64_t seed,
                int slot, const uint64_t* __restrict__ step, int32_t* __restrict__ tokens,
                int32_t* __restrict__ status, const int32_t* __restrict__ row_j, int j_add,
                const int32_t* __restrict__ n_valid) {
@@ -296,13 +340,20 @@ k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, u
   const int j = row_j ? row_j[row_id] + j_add : row_id % K;
   Row row{logits + (size_t)row_id * V, V, (V & 3) == 0};
   bool bad = false;
-  const float m = block_row_max(row, sh, &bad);
+  u128 S;
+  PlainWeights wf{row, 0.f, inv_temp};
+  if (row_max) {
+    // one pass: the maximum is given
+    wf.m = row_max[row_id];
+    S = block_weight_sum_given_max(wf, V, tiles, sh, &bad);
+  } else {
+    wf.m = block_row_max(row, sh, &bad);
+    if (!bad) S = block_weight_sum(wf, V, tiles, sh);
+  }
   if (bad) {
     if (threadIdx.x == 0) { tokens[row_id] = -1; flag(status, b, UNO_DEV_NONFINITE); }
     return;
   }
-  PlainWeights wf{row, m, inv_temp};
-  const u128 S = block_weight_sum(wf, V, tiles, sh);
   const uint32_t U = uniform24(seed, slot, j, b, step[b]);
   const int v = block_find(wf, V, tiles, scaled_target(U, S), sh);
   if (threadIdx.x == 0) tokens[row_id] = v;
@@ -312,7 +363,8 @@ k_draft_sample(const float* __restrict__ logits, int K, int V, float inv_temp, u
 // row maximum and exact weight sum (fits 64 bits: V <= 2^20, W <= 2^31).
 template <int TH>
 __global__ void __launch_bounds__(TH)
-k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, int V,
+k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp,
+            const float* __restrict__ mq_given, const float* __restrict__ mp_given, int K, int V,
             int n_rows_each, float inv_temp, float* __restrict__ m_out,
             uint64_t* __restrict__ s_out, int32_t* __restrict__ status) {
   __shared__ RowShared<TH> sh;
@@ -320,8 +372,12 @@ k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, i
   const bool is_p = r >= n_rows_each;
   const int rr = is_p ? r - n_rows_each : r;
   Row row{(is_p ? zp : zq) + (size_t)rr * V, V, (V & 3) == 0};
+  const float* given = is_p ? mp_given : mq_given;
   bool bad = false;
-  const float m = block_row_max(row, sh, &bad);
+  // with the row maximum given, one pass that also checks every entry;
+  // otherwise a maximum pass first
+  const float m = given ? given[rr] : block_row_max(row, sh, &bad);
+  int chk = given ? !__builtin_isfinite(m) : 0;
   uint64_t acc = 0;
   if (!bad) {
     for (int e0 = threadIdx.x * 4; e0 < V; e0 += TH * 4 * kUnroll) {
@@ -333,16 +389,20 @@ k_row_stats(const float* __restrict__ zq, const float* __restrict__ zp, int K, i
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (ok[u][c]) acc += weight_of(v[u][c], m, inv_temp);
+          if (ok[u][c]) {
+            if (given) chk |= !__builtin_isfinite(v[u][c]) || v[u][c] > m;
+            acc += weight_of(v[u][c], m, inv_temp);
+          }
     }
   }
   acc = wave_sum_u64(acc);
+  chk = __any(chk);
   const int w = threadIdx.x / UNO_WAVE;
-  if (lane_id() == 0) sh.red_u[w] = u128_make(acc, 0);
+  if (lane_id() == 0) { sh.red_u[w] = u128_make(acc, 0); sh.red_i[w] = chk; }
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t tot = 0;
-    for (int i = 0; i < (TH / UNO_WAVE); ++i) tot += sh.red_u[i].lo;
+    for (int i = 0; i < (TH / UNO_WAVE); ++i) { tot += sh.red_u[i].lo; bad |= sh.red_i[i] != 0; }
     m_out[r] = m;
     s_out[r] = bad ? 0ull : tot;
     if (bad) flag(status, rr / K, UNO_DEV_NONFINITE);
@@ -450,12 +510,12 @@ static size_t tile_lds_bytes(int V) { return (size_t)((V + kTile - 1) / kTile) *
 // in flight, so a row's second pass finds it still in the last-level cache.
 constexpr int kRowThreads = 1024;
 
-hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
-                               uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
-                               int32_t* status, hipStream_t s) {
+hipError_t launch_draft_sample(const float* logits, const float* row_max, int B, int K, int V,
+                               float inv_temp, uint64_t seed, int slot, const uint64_t* step,
+                               int32_t* tokens, int32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(k_draft_sample<kRowThreads>, dim3(B * K), dim3(kRowThreads),
-                     tile_lds_bytes(V), s, logits, K, V, inv_temp, seed, slot, step, tokens,
-                     status, nullptr, 0, nullptr);
+                     tile_lds_bytes(V), s, logits, row_max, K, V, inv_temp, seed, slot, step,
+                     tokens, status, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
@@ -464,8 +524,8 @@ hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float in
                               const int32_t* n_nodes, int32_t* samples, int32_t* status,
                               hipStream_t s) {
   hipLaunchKernelGGL(k_draft_sample<kRowThreads>, dim3(B * N), dim3(kRowThreads),
-                     tile_lds_bytes(V), s, logits, N, V, inv_temp, seed, 2, step, samples, status,
-                     node_depth, 1, n_nodes);
+                     tile_lds_bytes(V), s, logits, nullptr, N, V, inv_temp, seed, 2, step, samples,
+                     status, node_depth, 1, n_nodes);
   return hipGetLastError();
 }
 
@@ -474,16 +534,17 @@ size_t spec_accept_ws_bytes(int B, int K) {
   return align_up(rows * sizeof(float), 256) + align_up(rows * sizeof(uint64_t), 256);
 }
 
-hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* drafts, int B,
-                              int K, int V, float inv_temp, uint64_t seed, const uint64_t* step,
-                              const int32_t* forced, int32_t* accept_len, int32_t* committed,
-                              int32_t* extra_token, int32_t* status, void* ws, hipStream_t s) {
+hipError_t launch_spec_accept(const float* zq, const float* zp, const float* mq, const float* mp,
+                              const int32_t* drafts, int B, int K, int V, float inv_temp,
+                              uint64_t seed, const uint64_t* step, const int32_t* forced,
+                              int32_t* accept_len, int32_t* committed, int32_t* extra_token,
+                              int32_t* status, void* ws, hipStream_t s) {
   const int n_each = B * K;
   float* m_all = static_cast<float*>(ws);
   uint64_t* s_all = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                                 align_up(2 * (size_t)n_each * sizeof(float), 256));
   hipLaunchKernelGGL(k_row_stats<kRowThreads>, dim3(2 * n_each), dim3(kRowThreads), 0, s, zq, zp,
-                     K, V, n_each, inv_temp, m_all, s_all, status);
+                     mq, mp, K, V, n_each, inv_temp, m_all, s_all, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_spec_accept<kRowThreads>, dim3(B), dim3(kRowThreads), tile_lds_bytes(V), s,
@@ -527,16 +588,17 @@ hipError_t static_accept_scratch(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_spec_accept_static(const float* zq, const float* zp, const int32_t* drafts,
-                                     int B, int K, int V, float inv_temp, uint64_t seed,
-                                     const uint64_t* step, const int32_t* forced,
-                                     int32_t* accept_len, int32_t* committed,
-                                     int32_t* extra_token, int32_t* status, hipStream_t s) {
+hipError_t launch_spec_accept_static(const float* zq, const float* zp, const float* mq,
+                                     const float* mp, const int32_t* drafts, int B, int K, int V,
+                                     float inv_temp, uint64_t seed, const uint64_t* step,
+                                     const int32_t* forced, int32_t* accept_len,
+                                     int32_t* committed, int32_t* extra_token, int32_t* status,
+                                     hipStream_t s) {
   void* ws = nullptr;
   const hipError_t e = static_accept_scratch(&ws);
   if (e != hipSuccess) return e;
-  return launch_spec_accept(zq, zp, drafts, B, K, V, inv_temp, seed, step, forced, accept_len,
-                            committed, extra_token, status, ws, s);
+  return launch_spec_accept(zq, zp, mq, mp, drafts, B, K, V, inv_temp, seed, step, forced,
+                            accept_len, committed, extra_token, status, ws, s);
 }
 
 }  // namespace uno

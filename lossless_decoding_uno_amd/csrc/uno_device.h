@@ -43,6 +43,15 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (UNO_WAVE - 1); }
 
+// fp32 maximum by integer atomics (LDS or global), exact and order free: a
+// non-negative float orders like its bits as int, a negative one inversely to
+// its bits as unsigned.  The slot starts at -inf (kNegInfBits).
+constexpr int kNegInfBits = (int)0xFF800000u;
+__device__ __forceinline__ void atomic_max_f32(float* p, float v) {
+  if (__float_as_int(v) >= 0) atomicMax(reinterpret_cast<int*>(p), __float_as_int(v));
+  else atomicMin(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
 // ---------------------------------------------------------------- 128-bit unsigned
 struct u128 {
   uint64_t lo, hi;

@@ -14,9 +14,11 @@ typedef uint16_t bf16_raw_t;  // bf16 bits in memory
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- sampler
-hipError_t launch_draft_sample(const float* logits, int B, int K, int V, float inv_temp,
-                               uint64_t seed, int slot, const uint64_t* step, int32_t* tokens,
-                               int32_t* status, hipStream_t s);
+// row_max [B*K] (the exact maximum of each logits row) or null: with it every
+// row is streamed once, without it a maximum pass comes first.
+hipError_t launch_draft_sample(const float* logits, const float* row_max, int B, int K, int V,
+                               float inv_temp, uint64_t seed, int slot, const uint64_t* step,
+                               int32_t* tokens, int32_t* status, hipStream_t s);
 // Per-node draws of a token tree's verify rows [B, N]: row (b, n) draws from
 // its own logits with Philox slot 2, j = node_depth + 1; rows n >= n_nodes[b]
 // get -1.
@@ -25,19 +27,22 @@ hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float in
                               const int32_t* n_nodes, int32_t* samples, int32_t* status,
                               hipStream_t s);
 size_t spec_accept_ws_bytes(int B, int K);
-hipError_t launch_spec_accept(const float* zq, const float* zp, const int32_t* drafts, int B,
-                              int K, int V, float inv_temp, uint64_t seed, const uint64_t* step,
-                              const int32_t* forced, int32_t* accept_len, int32_t* committed,
-                              int32_t* extra_token, int32_t* status, void* ws, hipStream_t s);
+// mq, mp [B*K]: the row maxima of zq and zp (both or neither; null: computed)
+hipError_t launch_spec_accept(const float* zq, const float* zp, const float* mq, const float* mp,
+                              const int32_t* drafts, int B, int K, int V, float inv_temp,
+                              uint64_t seed, const uint64_t* step, const int32_t* forced,
+                              int32_t* accept_len, int32_t* committed, int32_t* extra_token,
+                              int32_t* status, void* ws, hipStream_t s);
 
 // The same on the library's per-device static scratch (no workspace; rows
 // 2*B*K at most static_accept_max_rows(); the caller checks).
 int static_accept_max_rows();
-hipError_t launch_spec_accept_static(const float* zq, const float* zp, const int32_t* drafts,
-                                     int B, int K, int V, float inv_temp, uint64_t seed,
-                                     const uint64_t* step, const int32_t* forced,
-                                     int32_t* accept_len, int32_t* committed,
-                                     int32_t* extra_token, int32_t* status, hipStream_t s);
+hipError_t launch_spec_accept_static(const float* zq, const float* zp, const float* mq,
+                                     const float* mp, const int32_t* drafts, int B, int K, int V,
+                                     float inv_temp, uint64_t seed, const uint64_t* step,
+                                     const int32_t* forced, int32_t* accept_len,
+                                     int32_t* committed, int32_t* extra_token, int32_t* status,
+                                     hipStream_t s);
 
 // ---------------------------------------------------------------- elementwise / small ops
 // Block rows: draft (anchor + mask ids) or given rows; gathers embeddings into
@@ -167,6 +172,14 @@ struct GemmArgs {
   // writes act_out[m, c] = bf16(silu(y[m, c]) * y[m, F + c]) [M, F] instead of
   // `out`; launch_gemm reports through *swiglued whether it did
   uint16_t* act_out;
+  // optional per-row maxima of the stored outputs (EPI_STORE_F32): for each
+  // of its rows every column group (a workgroup's columns; a tile of the
+  // tiled kernel) gets the exact maximum over its columns in
+  // max_part[m * max_part_ld + group] (max_part_ld = gemm_row_max_parts(a)
+  // groups); the skinny kernel then runs without a K split, the tiled kernel
+  // takes the maxima of its split tiles from their reduced rows
+  float* max_part;
+  int max_part_ld;
 };
 // split-K scratch carved per pass: 128 MB for passes of more than 64 rows
 // (tiled kernel), 4 MB for up to 64 (skinny kernel)
@@ -185,6 +198,18 @@ void gemm_lora_pair(const GemmArgs& a, const GemmArgs& ta, float* t_part, size_t
 constexpr size_t kLoraPartFloats = size_t(1) << 18;
 // whether launch_gemm can run this EPI_SWIGLU product (the tiled kernel takes it)
 bool gemm_swiglu_ok(const GemmArgs& a);
+// column groups of a product with max_part set (the row-maxima partials per row)
+int gemm_row_max_parts(const GemmArgs& a);
+// the row-maxima partials a pass carves room for: M rows of n output columns
+// in groups of 16 (at most 64 rows, the skinny kernel) or 128 (the tiled
+// kernel's narrowest tile); a plan with more groups computes the maxima from
+// the stored rows instead
+static inline int gemm_row_max_parts_bound(int n, int M) {
+  return M <= 64 ? (n + 15) / 16 : (n + 127) / 128;
+}
+// row_max[r] = max over parts of max_part[r * ld + part] (rows r < R)
+hipError_t launch_row_max(const float* max_part, int ld, int n_parts, int R, float* row_max,
+                          hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // Block attention of a pass over the paged cache.  Query rows of sequence b

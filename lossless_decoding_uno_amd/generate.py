@@ -98,6 +98,10 @@ class Generator:
         self.zq = torch.empty((batch, K, V), dtype=torch.float32, device=device)
         self.zp = torch.empty((batch, self.n_rows, V), dtype=torch.float32, device=device)
         self.d = torch.empty((batch, K), dtype=torch.int32, device=device)
+        # row maxima of the draft and verify logits (the LM head writes them,
+        # the sampler then streams every row once)
+        self.qmax = torch.empty((batch, K), dtype=torch.float32, device=device)
+        self.pmax = torch.empty((batch, K), dtype=torch.float32, device=device)
         self.a = torch.empty(batch, dtype=torch.int32, device=device)
         self.c = torch.empty((batch, K + 1), dtype=torch.int32, device=device)
         self.e = torch.empty(batch, dtype=torch.int32, device=device)
@@ -136,7 +140,7 @@ class Generator:
         self.pool.sync()
         draft_passes(self.model, self.kv, self.e, K, self.max_ctx, self.inv_temp, self.seed,
                      self.step_ctr, self.n_passes, self.zq, self.d, self.ws, self.status,
-                     kappa=self.kappa)
+                     kappa=self.kappa, row_max=self.qmax)
         if self.tb is not None:
             if forced is not None:
                 raise ValueError("forced accept lengths apply to the linear sampler only")
@@ -147,10 +151,11 @@ class Generator:
             tree_commit(self.model, self.kv, self.tb, self.a, self.step_ctr, self.status)
         else:
             verify_block(self.model, self.kv, self.d, self.max_ctx, 1, self.zp, self.ws,
-                         self.status)
+                         self.status, row_max=self.pmax)
             spec_accept(self.zq, self.zp, self.d, self.inv_temp, self.seed, self.step_ctr,
                         self.a, self.c, self.e, self.aws, status=self.status,
-                        forced_accept=forced)
+                        forced_accept=forced, draft_row_max=self.qmax,
+                        verify_row_max=self.pmax)
             kv_commit(self.kv, self.a, K, self.step_ctr, self.status)
         a = self.a.cpu().numpy().astype(np.int64)
         c = self.c.cpu().numpy()

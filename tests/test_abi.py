@@ -53,31 +53,39 @@ def test_entry_points_reject_bad_arguments_on_the_host():
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
     # null anchor / logits
     assert lib.uno_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), None, 1, 4,
-                               64, 1.0, 0, fake, fake, fake, None, fake, 1 << 20, None) == 1
+                               64, 1.0, 0, fake, fake, fake, None, None, fake, 1 << 20,
+                               None) == 1
     # K out of range
     assert lib.uno_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 65,
-                               64, 1.0, 0, fake, fake, fake, None, fake, 1 << 20, None) == 1
+                               64, 1.0, 0, fake, fake, fake, None, None, fake, 1 << 20,
+                               None) == 1
     # bad temperature
-    assert lib.uno_draft_sample(fake, 1, 4, 512, 0.0, 0, fake, fake, None, None) == 1
+    assert lib.uno_draft_sample(fake, None, 1, 4, 512, 0.0, 0, fake, fake, None, None) == 1
     # workspace too small
-    assert lib.uno_spec_accept(fake, fake, fake, 2, 4, 512, 1.0, 0, fake, None, fake, fake, fake,
-                               None, fake, 8, None) == 4
+    assert lib.uno_spec_accept(fake, fake, None, None, fake, 2, 4, 512, 1.0, 0, fake, None, fake,
+                               fake, fake, None, fake, 8, None) == 4
+    # only one of the two row-maximum arrays
+    assert lib.uno_spec_accept(fake, fake, fake, None, fake, 2, 4, 512, 1.0, 0, fake, None, fake,
+                               fake, fake, None, fake, 1 << 20, None) == 1
     # the no-allocation accept step: shapes past its static scratch
-    assert lib.uno_spec_accept_noalloc(fake, fake, fake, 2049, 16, 512, 1.0, 0, fake, None, fake,
-                                       fake, fake, None, None) == 4
-    assert lib.uno_spec_accept_noalloc(None, fake, fake, 2, 4, 512, 1.0, 0, fake, None, fake,
-                                       fake, fake, None, None) == 1
+    assert lib.uno_spec_accept_noalloc(fake, fake, None, None, fake, 2049, 16, 512, 1.0, 0, fake,
+                                       None, fake, fake, fake, None, None) == 4
+    assert lib.uno_spec_accept_noalloc(None, fake, None, None, fake, 2, 4, 512, 1.0, 0, fake,
+                                       None, fake, fake, fake, None, None) == 1
     # unsupported head_dim
     bad = U.make_config(dict(synth.TINY, head_dim=48))
     assert lib.uno_verify_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
-                                64, 1, fake, None, fake, 1 << 20, None) == 2
+                                64, 1, fake, None, None, fake, 1 << 20, None) == 2
     # unknown noise prior
     bad = U.make_config(dict(synth.TINY, noise_prior=2))
     assert lib.uno_verify_block(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
-                                64, 1, fake, None, fake, 1 << 20, None) == 1
+                                64, 1, fake, None, None, fake, 1 << 20, None) == 1
     # verify: empty kv struct
     assert lib.uno_verify_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
-                                64, 1, fake, None, fake, 1 << 30, None) == 1
+                                64, 1, fake, None, None, fake, 1 << 30, None) == 1
+    # verify: row maxima without logits
+    assert lib.uno_verify_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
+                                64, 1, None, fake, None, fake, 1 << 30, None) == 1
     assert lib.uno_kv_commit(None, fake, 1, 4, None, None, None) == 1
 
 

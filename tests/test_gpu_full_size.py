@@ -101,15 +101,20 @@ def _end_to_end(big, B, ctx, b_check):
     status = torch.zeros(B, dtype=torch.int32, device="cuda")
     step = torch.zeros(B, dtype=torch.uint64, device="cuda")
     anchor = torch.from_numpy(toks[:, -1].copy()).cuda()
-    U.draft_block(model, kv, anchor, K, cap, 1.0, 0, step, zq, d, ws, status)
-    U.verify_block(model, kv, d, cap, 1, zp, ws, status)
+    qmax = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    pmax = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    U.draft_block(model, kv, anchor, K, cap, 1.0, 0, step, zq, d, ws, status, row_max=qmax)
+    U.verify_block(model, kv, d, cap, 1, zp, ws, status, row_max=pmax)
     a = torch.empty(B, dtype=torch.int32, device="cuda")
     c = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
     e = torch.empty(B, dtype=torch.int32, device="cuda")
     U.spec_accept(zq, zp, d, 1.0, 0, step, a, c, e,
-                  U.alloc_workspace(U.spec_accept_workspace_bytes(B, K)), status=status)
+                  U.alloc_workspace(U.spec_accept_workspace_bytes(B, K)), status=status,
+                  draft_row_max=qmax, verify_row_max=pmax)
     torch.cuda.synchronize()
     assert (status.cpu().numpy() == 0).all()
+    # the LM head's row maxima (every sequence) are the logits' exact maxima
+    assert torch.equal(qmax, zq.amax(dim=-1)) and torch.equal(pmax, zp.amax(dim=-1))
     zq_g = zq[b_check].cpu().numpy()
     zp_g = zp[b_check].cpu().numpy()
     drafts = [int(x) for x in d[b_check].cpu().numpy()]

@@ -20,12 +20,14 @@ def _steps(B):
     return np.array([3 + 7 * b for b in range(B)], dtype=np.uint64)
 
 
-def _gpu_draft_sample(U, zq, inv_t, steps):
+def _gpu_draft_sample(U, zq, inv_t, steps, given_max=False, row_max=None):
     z = torch.from_numpy(zq).cuda()
     st = torch.from_numpy(steps.astype(np.uint64)).cuda()
     tok = torch.full(zq.shape[:2], -7, dtype=torch.int32, device="cuda")
     status = torch.zeros(zq.shape[0], dtype=torch.int32, device="cuda")
-    U.draft_sample(z, inv_t, SEED, st, tok, status)
+    if given_max and row_max is None:
+        row_max = z.amax(dim=-1).contiguous()
+    U.draft_sample(z, inv_t, SEED, st, tok, status, row_max=row_max)
     torch.cuda.synchronize()
     return tok.cpu().numpy(), status.cpu().numpy()
 
@@ -38,16 +40,31 @@ def _oracle_drafts(zq, inv_t, steps, rows=None):
     return out
 
 
+@pytest.mark.parametrize("given_max", [False, True])
 @pytest.mark.parametrize("B,K,V", [(3, 5, 1000), (2, 3, 1003), (1, 1, 16), (4, 2, 4096),
                                    (2, 4, 257)])
-def test_draft_sample_bit_exact_small(B, K, V):
+def test_draft_sample_bit_exact_small(B, K, V, given_max):
+    """Two passes per row (maximum, then weights) or one (maximum given)."""
     U = gpu_or_fail()
     zq, _ = synth.sampler_logits(B, K, V, seed=V)
     for inv_t in (1.0, np.float32(1 / 0.7)):
         steps = _steps(B)
-        got, status = _gpu_draft_sample(U, zq, inv_t, steps)
+        got, status = _gpu_draft_sample(U, zq, inv_t, steps, given_max)
         assert (status == 0).all()
         np.testing.assert_array_equal(got, _oracle_drafts(zq, inv_t, steps))
+
+
+def test_given_row_max_below_an_entry_is_flagged():
+    """A given maximum below one of its row's entries (or a non-finite entry)
+    flags the row and skips its draw; the other rows are unaffected."""
+    U = gpu_or_fail()
+    zq, _ = synth.sampler_logits(2, 3, 512, seed=3)
+    rm = torch.from_numpy(zq.max(axis=-1)).cuda()
+    rm[1, 1] -= 0.5
+    got, status = _gpu_draft_sample(U, zq, 1.0, _steps(2), row_max=rm)
+    assert status[0] == 0 and status[1] & U.DEV_NONFINITE
+    assert got[1, 1] == -1
+    np.testing.assert_array_equal(got[0], _oracle_drafts(zq, 1.0, _steps(2), rows=[0])[0])
 
 
 def test_draft_sample_flags_nonfinite_rows():
@@ -60,7 +77,7 @@ def test_draft_sample_flags_nonfinite_rows():
     np.testing.assert_array_equal(got[0], _oracle_drafts(zq, 1.0, _steps(2), rows=[0])[0])
 
 
-def _gpu_accept(U, zq, zp, drafts, inv_t, steps, forced=None):
+def _gpu_accept(U, zq, zp, drafts, inv_t, steps, forced=None, given_max=False):
     B, K, V = zq.shape
     dev = "cuda"
     out = dict(a=torch.full((B,), -9, dtype=torch.int32, device=dev),
@@ -69,10 +86,12 @@ def _gpu_accept(U, zq, zp, drafts, inv_t, steps, forced=None):
                s=torch.zeros(B, dtype=torch.int32, device=dev))
     ws = U.alloc_workspace(U.spec_accept_workspace_bytes(B, K))
     f = None if forced is None else torch.from_numpy(forced.astype(np.int32)).to(dev)
-    U.spec_accept(torch.from_numpy(zq).to(dev), torch.from_numpy(zp).to(dev),
-                  torch.from_numpy(drafts.astype(np.int32)).to(dev), inv_t, SEED,
+    zq_d, zp_d = torch.from_numpy(zq).to(dev), torch.from_numpy(zp).to(dev)
+    mq = zq_d.amax(dim=-1).contiguous() if given_max else None
+    mp = zp_d.amax(dim=-1).contiguous() if given_max else None
+    U.spec_accept(zq_d, zp_d, torch.from_numpy(drafts.astype(np.int32)).to(dev), inv_t, SEED,
                   torch.from_numpy(steps).to(dev), out["a"], out["c"], out["e"], ws,
-                  forced_accept=f, status=out["s"])
+                  forced_accept=f, status=out["s"], draft_row_max=mq, verify_row_max=mp)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -89,18 +108,19 @@ def _check_accept(zq, zp, drafts, inv_t, steps, got, rows, forced=None):
         np.testing.assert_array_equal(got["c"][b], comm + [-1] * (K + 1 - len(comm)))
 
 
+@pytest.mark.parametrize("given_max", [False, True])
 @pytest.mark.parametrize("B,K,V,sig,noise", [(4, 6, 1000, 3.0, 0.5), (3, 8, 512, 1.0, 2.0),
                                              (2, 1, 64, 3.0, 0.5), (5, 4, 16, 0.5, 3.0)])
-def test_spec_accept_bit_exact_small(B, K, V, sig, noise):
+def test_spec_accept_bit_exact_small(B, K, V, sig, noise, given_max):
     U = gpu_or_fail()
     zq, zp = synth.sampler_logits(B, K, V, seed=K * V, sigma_p=sig, sigma_noise=noise)
     steps = _steps(B)
     for inv_t in (1.0, np.float32(1 / 0.7)):
         drafts = _oracle_drafts(zq, inv_t, steps)
-        got = _gpu_accept(U, zq, zp, drafts, inv_t, steps)
+        got = _gpu_accept(U, zq, zp, drafts, inv_t, steps, given_max=given_max)
         _check_accept(zq, zp, drafts, inv_t, steps, got, range(B))
         forced = synth.forced_accepts(B, K, 1, seed=V)[0]
-        got = _gpu_accept(U, zq, zp, drafts, inv_t, steps, forced)
+        got = _gpu_accept(U, zq, zp, drafts, inv_t, steps, forced, given_max=given_max)
         _check_accept(zq, zp, drafts, inv_t, steps, got, range(B), forced)
 
 
@@ -125,8 +145,13 @@ def test_sampler_only_workload_full_size():
     assert (st == 0).all()
     ref_d = _oracle_drafts(zq, 1.0, steps)
     np.testing.assert_array_equal(got_d, ref_d)
-    progress("full sampler workload: drafts bit-exact")
+    got_d1, st = _gpu_draft_sample(U, zq, 1.0, steps, given_max=True)
+    assert (st == 0).all()
+    np.testing.assert_array_equal(got_d1, ref_d)
+    progress("full sampler workload: drafts bit-exact (two-pass and one-pass rows)")
     got = _gpu_accept(U, zq, zp, ref_d, 1.0, steps)
+    _check_accept(zq, zp, ref_d, 1.0, steps, got, range(B))
+    got = _gpu_accept(U, zq, zp, ref_d, 1.0, steps, given_max=True)
     _check_accept(zq, zp, ref_d, 1.0, steps, got, range(B))
     progress("full sampler workload: accept bit-exact, mean a = %.2f" % got["a"].mean())
     forced = synth.forced_accepts(B, K, 1, seed=2)[0]

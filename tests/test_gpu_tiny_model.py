@@ -84,27 +84,34 @@ def _teacher_forced(U, cfg, w64, model, n_new):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     step_g = torch.zeros(1, dtype=torch.uint64).to(dev)
     aws = U.alloc_workspace(U.spec_accept_workspace_bytes(1, K))
+    qmax = torch.empty((1, K), dtype=torch.float32, device=dev)
+    pmax = torch.empty((1, K), dtype=torch.float32, device=dev)
     worst = 0.0
     n_steps_rejected = 0
     while len(seq.tokens) - len(prompt) < n_new:
         st = seq.step
         anchor = torch.tensor([seq.tokens[-1]], dtype=torch.int32, device=dev)
-        U.draft_block(model, kv, anchor, K, max_ctx, 1.0, SEED, step_g, zq_g, d_g, ws, status)
+        U.draft_block(model, kv, anchor, K, max_ctx, 1.0, SEED, step_g, zq_g, d_g, ws, status,
+                      row_max=qmax)
         draws = ospec.PhiloxDraws(SEED, 0, st)
         zq = ospec.draft_logits(cfg, w64, seq, K, draws=draws)
         zq_gpu = zq_g.cpu().numpy()[0]
+        # the LM head's row maxima are the logits' exact maxima
+        np.testing.assert_array_equal(qmax.cpu().numpy()[0], zq_gpu.max(axis=-1))
         worst = max(worst, assert_logits_close(zq_gpu, zq, "draft logits step %d" % st))
         # the oracle's sampler on the GPU's logits takes the GPU's draws
         drafts = ospec.draft_sample(zq_gpu, 1.0, draws)
         assert [int(x) for x in d_g.cpu().numpy()[0]] == drafts, st
 
-        U.verify_block(model, kv, d_g, max_ctx, 1, zp_g, ws, status)
+        U.verify_block(model, kv, d_g, max_ctx, 1, zp_g, ws, status, row_max=pmax)
         zp = ospec.verify_logits(cfg, w64, seq, drafts)
         zp_gpu = zp_g.cpu().numpy()[0]
         worst = max(worst, assert_logits_close(zp_gpu, zp, "verify logits step %d" % st))
+        np.testing.assert_array_equal(pmax.cpu().numpy()[0], zp_gpu.max(axis=-1))
 
         a, committed, extra = ospec.spec_accept(zq_gpu, zp_gpu, drafts, 1.0, draws)
-        U.spec_accept(zq_g, zp_g, d_g, 1.0, SEED, step_g, a_g, c_g, e_g, aws, status=status)
+        U.spec_accept(zq_g, zp_g, d_g, 1.0, SEED, step_g, a_g, c_g, e_g, aws, status=status,
+                      draft_row_max=qmax, verify_row_max=pmax)
         assert (int(a_g.item()), int(e_g.item())) == (a, extra), st
         np.testing.assert_array_equal(c_g.cpu().numpy()[0],
                                       committed + [-1] * (K + 1 - len(committed)))
