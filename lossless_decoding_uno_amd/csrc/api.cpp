@@ -104,6 +104,7 @@ struct PassWs {
   float* lora_part;      // LoRA-A split-K partials read by the next projection (<= 64 rows)
   float* max_part;       // [R, V/16] LM-head row-maxima partials (per column group)
   float* row_max;        // [R] row maxima of the logits (when the caller passes none)
+  uint64_t* chunk_sums;  // [R, 128] exact chunk sums of the draft sampler
   size_t total;
 };
 
@@ -142,6 +143,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
   w.max_part = reinterpret_cast<float*>(
       take(R * gemm_row_max_parts_bound(c.vocab, (int)R) * 4));
   w.row_max = reinterpret_cast<float*>(take(R * 4));
+  w.chunk_sums = reinterpret_cast<uint64_t*>(take(chunk_sums_bytes((int)R)));
   w.total = off;
   return w;
 }
@@ -378,14 +380,15 @@ int uno_draft_block_from(const uno_config* cfg, const uno_weights* w, const uno_
   if ((rc = check_layers(*cfg, w, true))) return rc;
   if (ws_bytes < carve(*cfg, batch, K, max_ctx, nullptr).total) return UNO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* rmax = row_max ? row_max : carve(*cfg, batch, K, max_ctx, ws).row_max;
+  const PassWs W = carve(*cfg, batch, K, max_ctx, ws);
+  float* rmax = row_max ? row_max : W.row_max;
   rc = run_pass(*cfg, w, kv, anchor, block, nullptr, batch, K, max_ctx, 0, cfg->lora_mask != 0,
                 seed, step, draft_logits, rmax, status, ws, s, nullptr, nullptr, keep_q24,
                 corr_pass);
   if (rc) return rc;
   const hipError_t e = timed(UNO_TIME_SAMPLER, s, [&] {
-    return launch_draft_sample(draft_logits, rmax, batch, K, cfg->vocab, inv_temp, seed,
-                               sample_slot, step, draft_tokens, status, s);
+    return launch_draft_sample_chunked(draft_logits, rmax, W.chunk_sums, batch, K, cfg->vocab,
+                                       inv_temp, seed, sample_slot, step, draft_tokens, status, s);
   });
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }

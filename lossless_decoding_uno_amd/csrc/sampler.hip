@@ -503,12 +503,369 @@ k_spec_accept(const float* __restrict__ zq, const float* __restrict__ zp,
   if (threadIdx.x == 0) { accept_len[b] = a; extra_token[b] = e; }
 }
 
+// ------------------------------------------------------------ chunked rows
+// With the row maxima given, every row is cut into chunks of kChunk entries
+// that separate workgroups weigh in parallel (so that even one sequence's few
+// rows fill the chip); a second kernel per row (or per sequence) adds the
+// exact chunk sums, picks the chunk that holds the draw, and weighs that chunk
+// once more to find the entry.  The sums are exact integers, so the draws are
+// the same as with one workgroup per row.
+constexpr int kChunk = 8192;
+constexpr int kChunkThreads = 256;
+constexpr int kMaxChunks = 128;               // V <= 2^20
+constexpr uint64_t kBadChunk = ~0ull;         // the chunk holds a non-finite entry or one above
+                                              // its row's given maximum
+__host__ __device__ inline int n_chunks_of(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Plain weights of chunk blockIdx.x of row blockIdx.y (rows 0..n_q-1 are zq's,
+// the rest zp's): sums[row * kMaxChunks + chunk] = their exact sum, or kBadChunk.
+__global__ void __launch_bounds__(kChunkThreads)
+k_chunk_sums(const float* __restrict__ zq, const float* __restrict__ zp, int n_q,
+             const float* __restrict__ mq, const float* __restrict__ mp, int V, float inv_temp,
+             uint64_t* __restrict__ sums) {
+  __shared__ uint64_t red_s[kChunkThreads / UNO_WAVE];
+  __shared__ int red_b[kChunkThreads / UNO_WAVE];
+  const int row = blockIdx.y, c = blockIdx.x;
+  const bool is_p = row >= n_q;
+  const int rr = is_p ? row - n_q : row;
+  const float m = (is_p ? mp : mq)[rr];
+  const int c0 = c * kChunk;
+  const int len = V - c0 < kChunk ? V - c0 : kChunk;
+  const Row r{(is_p ? zp : zq) + (size_t)rr * V + c0, len, (V & 3) == 0};
+  constexpr int U = kChunk / (kChunkThreads * 4);
+  float v[U][4];
+  bool ok[U][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u) r.load4((u * kChunkThreads + threadIdx.x) * 4, v[u], ok[u]);
+  uint64_t acc = 0;
+  int bad = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (ok[u][e]) {
+        bad |= !__builtin_isfinite(v[u][e]) || v[u][e] > m;
+        acc += weight_of(v[u][e], m, inv_temp);
+      }
+  acc = wave_sum_u64(acc);
+  bad = __any(bad);
+  const int w = threadIdx.x / UNO_WAVE;
+  if (lane_id() == 0) { red_s[w] = acc; red_b[w] = bad; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t tot = 0;
+    int b = !__builtin_isfinite(m);
+    for (int i = 0; i < kChunkThreads / UNO_WAVE; ++i) { tot += red_s[i]; b |= red_b[i]; }
+    sums[(size_t)row * kMaxChunks + c] = b ? kBadChunk : tot;
+  }
+}
+
+// Residual weights max(0, Wp Sq - Wq Sp) of chunk blockIdx.x of sequence
+// blockIdx.y's row pair (p_{a+1}, q_{a+1}) when its accept length a < K:
+// rsums[b * kMaxChunks + chunk] (exact, 128-bit).
+__global__ void __launch_bounds__(kChunkThreads)
+k_resid_chunk_sums(const float* __restrict__ zq, const float* __restrict__ zp,
+                   const float* __restrict__ m_all, const uint64_t* __restrict__ s_all,
+                   const int32_t* __restrict__ a_ws, const int32_t* __restrict__ err_ws, int K,
+                   int V, float inv_temp, int n_each, u128* __restrict__ rsums) {
+  __shared__ u128 red[kChunkThreads / UNO_WAVE];
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int a = a_ws[b];
+  if (err_ws[b] || a >= K) return;
+  const bool p_from_q = a == 0;      // p_1 is draft row 0
+  const size_t prow = p_from_q ? (size_t)b * K : (size_t)b * K + a - 1;
+  const size_t qrow = (size_t)b * K + a;
+  const int ip = p_from_q ? (int)prow : n_each + (int)prow;
+  const int c0 = c * kChunk;
+  const int len = V - c0 < kChunk ? V - c0 : kChunk;
+  const bool vec = (V & 3) == 0;
+  const ResidualWeights rw{Row{(p_from_q ? zq : zp) + prow * V + c0, len, vec},
+                           Row{zq + qrow * V + c0, len, vec}, m_all[ip], m_all[qrow], inv_temp,
+                           s_all[ip], s_all[qrow]};
+  constexpr int U = kChunk / (kChunkThreads * 4);
+  u128 acc = u128_make(0, 0);
+  ResidualWeights::Raw raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) rw.load((u * kChunkThreads + threadIdx.x) * 4, raw[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    u128 wv[4];
+    rw.weights(raw[u], wv);
+    acc = u128_add(acc, u128_add(u128_add(wv[0], wv[1]), u128_add(wv[2], wv[3])));
+  }
+  acc = wave_sum_u128(acc);
+  const int w = threadIdx.x / UNO_WAVE;
+  if (lane_id() == 0) red[w] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u128 tot = red[0];
+    for (int i = 1; i < kChunkThreads / UNO_WAVE; ++i) tot = u128_add(tot, red[i]);
+    rsums[(size_t)b * kMaxChunks + c] = tot;
+  }
+}
+
+// The entry a draw with target t picks inside a row whose chunk sums are cs
+// (nc chunks, total > t): the chunk whose running sum first exceeds t, then the
+// entry inside it (weighed again with wf_of(chunk start, chunk length)).
+template <class WF, class MakeWF>
+__device__ int chunked_find(const u128* cs, int nc, int V, u128 t, const MakeWF& wf_of,
+                            u128* tiles, RowShared<kChunkThreads>& sh) {
+  __shared__ int s_chunk;
+  __shared__ u128 s_before;
+  if (threadIdx.x < UNO_WAVE) {
+    // wave 0: running sums of the chunk sums, 64 chunks at a time; the first
+    // chunk whose running sum exceeds t (the last chunk if none does)
+    const int l = lane_id();
+    u128 base = u128_make(0, 0);
+    int chunk = -1;
+    u128 before = base;
+    for (int c0 = 0; c0 < nc && chunk < 0; c0 += UNO_WAVE) {
+      const u128 v = c0 + l < nc ? cs[c0 + l] : u128_make(0, 0);
+      const u128 incl = u128_add(wave_inclusive_scan_u128(v), base);
+      const uint64_t hit = __ballot(u128_lt(t, incl) && c0 + l < nc);
+      if (hit) {
+        const int f = __ffsll((long long)hit) - 1;
+        chunk = c0 + f;
+        before = u128_sub(u128_shfl(incl, f), u128_shfl(v, f));
+      } else {
+        base = u128_shfl(incl, UNO_WAVE - 1);
+      }
+    }
+    if (l == 0) {
+      s_chunk = chunk < 0 ? nc - 1 : chunk;
+      s_before = chunk < 0 ? u128_sub(base, cs[nc - 1]) : before;
+    }
+  }
+  __syncthreads();
+  const int c = s_chunk;
+  const u128 tt = u128_sub(t, s_before);
+  __syncthreads();
+  const int c0 = c * kChunk;
+  const int len = V - c0 < kChunk ? V - c0 : kChunk;
+  const WF wf = wf_of(c0, len);
+  block_weight_sum(wf, len, tiles, sh);
+  return c0 + block_find(wf, len, tiles, tt, sh);
+}
+
+// One workgroup per draft row: the draw from the chunk sums (maximum given).
+__global__ void __launch_bounds__(kChunkThreads)
+k_draft_find(const float* __restrict__ logits, const float* __restrict__ row_max,
+             const uint64_t* __restrict__ sums, int K, int V, float inv_temp, uint64_t seed,
+             int slot, const uint64_t* __restrict__ step, int32_t* __restrict__ tokens,
+             int32_t* __restrict__ status) {
+  __shared__ RowShared<kChunkThreads> sh;
+  __shared__ u128 tiles[kChunk / kTile];
+  __shared__ u128 cs[kMaxChunks];
+  __shared__ int s_bad;
+  __shared__ u128 s_tot;
+  const int row = blockIdx.x, b = row / K, j = row % K;
+  const int nc = n_chunks_of(V);
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  for (int c = threadIdx.x; c < nc; c += kChunkThreads) {
+    const uint64_t x = sums[(size_t)row * kMaxChunks + c];
+    cs[c] = u128_make(x == kBadChunk ? 0 : x, 0);
+    if (x == kBadChunk) s_bad = 1;
+  }
+  __syncthreads();
+  if (threadIdx.x < UNO_WAVE) {
+    u128 tot = u128_make(0, 0);
+    for (int c = lane_id(); c < nc; c += UNO_WAVE) tot = u128_add(tot, cs[c]);
+    tot = wave_sum_u128(tot);
+    if (threadIdx.x == 0) s_tot = tot;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (threadIdx.x == 0) { tokens[row] = -1; flag(status, b, UNO_DEV_NONFINITE); }
+    return;
+  }
+  const float m = row_max[row];
+  const float* z = logits + (size_t)row * V;
+  const bool vec = (V & 3) == 0;
+  const uint32_t U = uniform24(seed, slot, j, b, step[b]);
+  const int v = chunked_find<PlainWeights>(
+      cs, nc, V, scaled_target(U, s_tot),
+      [&](int c0, int len) { return PlainWeights{Row{z + c0, len, vec}, m, inv_temp}; }, tiles, sh);
+  if (threadIdx.x == 0) tokens[row] = v;
+}
+
+// One small workgroup per sequence: every row's exact weight sum from its
+// chunk sums, the accept tests and the first rejection (as k_spec_accept),
+// into m_all / s_all / a_ws / err_ws.
+__global__ void __launch_bounds__(UNO_WAVE)
+k_accept_decide(const float* __restrict__ zq, const float* __restrict__ zp,
+                const float* __restrict__ mq, const float* __restrict__ mp,
+                const uint64_t* __restrict__ sums, const int32_t* __restrict__ drafts, int K,
+                int V, float inv_temp, uint64_t seed, const uint64_t* __restrict__ step,
+                const int32_t* __restrict__ forced, int n_each, float* __restrict__ m_all,
+                uint64_t* __restrict__ s_all, int32_t* __restrict__ a_ws,
+                int32_t* __restrict__ err_ws, int32_t* __restrict__ status) {
+  const int b = blockIdx.x;
+  const int nc = n_chunks_of(V);
+  int bad_rows = 0;
+  // lane l sums rows l, l + 64, ... of the sequence's 2K rows
+  for (int i = lane_id(); i < 2 * K; i += UNO_WAVE) {
+    const bool is_p = i >= K;
+    const int row = (is_p ? n_each : 0) + b * K + (is_p ? i - K : i);
+    uint64_t S = 0;
+    bool bad = false;
+    for (int c = 0; c < nc; ++c) {
+      const uint64_t x = sums[(size_t)row * kMaxChunks + c];
+      bad |= x == kBadChunk;
+      S += x;
+    }
+    m_all[row] = (is_p ? mp : mq)[b * K + (is_p ? i - K : i)];
+    s_all[row] = bad ? 0ull : S;
+    bad_rows |= bad;
+  }
+  bad_rows = __any(bad_rows);
+  __syncthreads();             // m_all / s_all of the sequence are written
+  const uint64_t st = step[b];
+  const float* qrow0 = zq + (size_t)b * K * V;
+  const float* prow0 = zp + (size_t)b * K * V;
+  const float* mq_b = m_all + (size_t)b * K;
+  const uint64_t* sq = s_all + (size_t)b * K;
+  const float* mp_b = m_all + n_each + (size_t)b * K;
+  const uint64_t* sp = s_all + n_each + (size_t)b * K;
+  int bad_tok = 0;
+  for (int j = lane_id(); j < K; j += UNO_WAVE) {
+    const int d = drafts[b * K + j];
+    bad_tok |= d < 0 || d >= V;
+  }
+  bad_tok = __any(bad_tok);
+  const int err0 = (bad_rows ? UNO_DEV_NONFINITE : 0) | (bad_tok ? UNO_DEV_BAD_TOKEN : 0);
+  // every accept test i = 2..K is independent of the others: lanes take them
+  // in parallel, and a is the draft count before the first rejection
+  int a = K;
+  if (!err0) {
+    for (int i0 = 2; i0 <= K; i0 += UNO_WAVE) {
+      const int i = i0 + lane_id();
+      bool rej = false;
+      if (i <= K) {
+        const int d = drafts[b * K + i - 1];
+        const uint64_t wq = weight_of(qrow0[(size_t)(i - 1) * V + d], mq_b[i - 1], inv_temp);
+        const uint64_t wp = weight_of(prow0[(size_t)(i - 2) * V + d], mp_b[i - 2], inv_temp);
+        const uint32_t U = uniform24(seed, 1, i - 1, b, st);
+        const u128 lhs = mul_64x64((uint64_t)U * wq, sp[i - 2]);
+        const u128 r0 = mul_64x64(wp, sq[i - 1]);
+        const u128 rhs = u128_make(r0.lo << 24, (r0.hi << 24) | (r0.lo >> 40));
+        rej = !u128_lt(lhs, rhs);
+      }
+      const uint64_t hit = __ballot(rej);
+      if (hit) { a = i0 + __ffsll((long long)hit) - 2; break; }
+    }
+  }
+  if (threadIdx.x != 0) return;
+  int err = err0;
+  if (!err && forced) {
+    const int fa = forced[b];
+    if (fa < 0 || fa > K) err |= UNO_DEV_BAD_ACCEPT;
+    else a = fa;
+  }
+  a_ws[b] = a;
+  err_ws[b] = err;
+  if (err) flag(status, b, err);
+}
+
+// One workgroup per sequence: the residual (or bonus) draw from the chunk
+// sums, and the outputs.
+__global__ void __launch_bounds__(kChunkThreads)
+k_extra_find(const float* __restrict__ zq, const float* __restrict__ zp,
+             const int32_t* __restrict__ drafts, int K, int V, float inv_temp, uint64_t seed,
+             const uint64_t* __restrict__ step, const float* __restrict__ m_all,
+             const uint64_t* __restrict__ s_all, const uint64_t* __restrict__ sums,
+             const u128* __restrict__ rsums, const int32_t* __restrict__ a_ws,
+             const int32_t* __restrict__ err_ws, int n_each, int32_t* __restrict__ accept_len,
+             int32_t* __restrict__ committed, int32_t* __restrict__ extra_token) {
+  __shared__ RowShared<kChunkThreads> sh;
+  __shared__ u128 tiles[kChunk / kTile];
+  __shared__ u128 cs[kMaxChunks];
+  __shared__ u128 s_tot;
+  const int b = blockIdx.x;
+  const int a = a_ws[b];
+  if (err_ws[b]) {
+    for (int j = threadIdx.x; j <= K; j += kChunkThreads) committed[b * (K + 1) + j] = -1;
+    if (threadIdx.x == 0) { accept_len[b] = 0; extra_token[b] = -1; }
+    return;
+  }
+  const int nc = n_chunks_of(V);
+  const bool vec = (V & 3) == 0;
+  // p_{a+1}: draft row 0 when a == 0, else verify row a-1 (verify row K-1 for
+  // the bonus draw a == K); q_{a+1}: draft row a
+  const bool p_from_q = a == 0;
+  const size_t prow = p_from_q ? (size_t)b * K : (size_t)b * K + a - 1;
+  const int ip = p_from_q ? (int)prow : n_each + (int)prow;
+  const float* pz = (p_from_q ? zq : zp) + prow * V;
+  bool resid = false;
+  if (a < K) {
+    for (int c = threadIdx.x; c < nc; c += kChunkThreads) cs[c] = rsums[(size_t)b * kMaxChunks + c];
+    __syncthreads();
+    if (threadIdx.x < UNO_WAVE) {
+      u128 tot = u128_make(0, 0);
+      for (int c = lane_id(); c < nc; c += UNO_WAVE) tot = u128_add(tot, cs[c]);
+      tot = wave_sum_u128(tot);
+      if (threadIdx.x == 0) s_tot = tot;
+    }
+    __syncthreads();
+    resid = !u128_is_zero(s_tot);
+  }
+  const uint32_t U = uniform24(seed, 2, a, b, step[b]);
+  int e;
+  if (resid) {
+    const size_t qrow = (size_t)b * K + a;
+    const float* qz = zq + qrow * V;
+    const float mpp = m_all[ip], mqq = m_all[qrow];
+    const uint64_t spp = s_all[ip], sqq = s_all[qrow];
+    e = chunked_find<ResidualWeights>(
+        cs, nc, V, scaled_target(U, s_tot),
+        [&](int c0, int len) {
+          return ResidualWeights{Row{pz + c0, len, vec}, Row{qz + c0, len, vec}, mpp, mqq,
+                                 inv_temp, spp, sqq};
+        },
+        tiles, sh);
+  } else {
+    // the bonus draw, or a residual of zero mass: p_{a+1} itself
+    __syncthreads();
+    for (int c = threadIdx.x; c < nc; c += kChunkThreads)
+      cs[c] = u128_make(sums[(size_t)ip * kMaxChunks + c], 0);
+    __syncthreads();
+    const float mpp = m_all[ip];
+    e = chunked_find<PlainWeights>(
+        cs, nc, V, scaled_target(U, u128_make(s_all[ip], 0)),
+        [&](int c0, int len) { return PlainWeights{Row{pz + c0, len, vec}, mpp, inv_temp}; },
+        tiles, sh);
+  }
+  for (int j = threadIdx.x; j <= K; j += kChunkThreads) {
+    int v = -1;
+    if (j < a) v = drafts[b * K + j];
+    else if (j == a) v = e;
+    committed[b * (K + 1) + j] = v;
+  }
+  if (threadIdx.x == 0) { accept_len[b] = a; extra_token[b] = e; }
+}
+
 // ------------------------------------------------------------ launchers
 static size_t tile_lds_bytes(int V) { return (size_t)((V + kTile - 1) / kTile) * sizeof(u128); }
 
 // Every row pass runs in 1024-thread workgroups: at most a few rows per CU are
 // in flight, so a row's second pass finds it still in the last-level cache.
 constexpr int kRowThreads = 1024;
+
+size_t chunk_sums_bytes(int rows) { return (size_t)rows * kMaxChunks * sizeof(uint64_t); }
+
+hipError_t launch_draft_sample_chunked(const float* logits, const float* row_max,
+                                       uint64_t* sums, int B, int K, int V, float inv_temp,
+                                       uint64_t seed, int slot, const uint64_t* step,
+                                       int32_t* tokens, int32_t* status, hipStream_t s) {
+  const int R = B * K;
+  hipLaunchKernelGGL(k_chunk_sums, dim3(n_chunks_of(V), R), dim3(kChunkThreads), 0, s, logits,
+                     logits, R, row_max, row_max, V, inv_temp, sums);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_draft_find, dim3(R), dim3(kChunkThreads), 0, s, logits, row_max, sums, K,
+                     V, inv_temp, seed, slot, step, tokens, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_draft_sample(const float* logits, const float* row_max, int B, int K, int V,
                                float inv_temp, uint64_t seed, int slot, const uint64_t* step,
@@ -529,20 +886,73 @@ hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float in
   return hipGetLastError();
 }
 
-size_t spec_accept_ws_bytes(int B, int K) {
+// Workspace of the accept step: per-row maxima and weight sums (m_all,
+// s_all) for both paths, then, for the chunked path (row maxima given), the
+// per-sequence decisions, the plain chunk sums of every row and the residual
+// chunk sums of every sequence.
+struct AcceptWs {
+  float* m_all;
+  uint64_t* s_all;
+  int32_t* a_ws;
+  int32_t* err_ws;
+  uint64_t* sums;
+  u128* rsums;
+  size_t total;
+};
+static AcceptWs carve_accept(int B, int K, void* base) {
+  AcceptWs w;
   const size_t rows = 2 * (size_t)B * K;
-  return align_up(rows * sizeof(float), 256) + align_up(rows * sizeof(uint64_t), 256);
+  size_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return q;
+  };
+  w.m_all = reinterpret_cast<float*>(take(rows * sizeof(float)));
+  w.s_all = reinterpret_cast<uint64_t*>(take(rows * sizeof(uint64_t)));
+  w.a_ws = reinterpret_cast<int32_t*>(take((size_t)B * sizeof(int32_t)));
+  w.err_ws = reinterpret_cast<int32_t*>(take((size_t)B * sizeof(int32_t)));
+  w.sums = reinterpret_cast<uint64_t*>(take(rows * kMaxChunks * sizeof(uint64_t)));
+  w.rsums = reinterpret_cast<u128*>(take((size_t)B * kMaxChunks * sizeof(u128)));
+  w.total = off;
+  return w;
 }
+
+size_t spec_accept_ws_bytes(int B, int K) { return carve_accept(B, K, nullptr).total; }
 
 hipError_t launch_spec_accept(const float* zq, const float* zp, const float* mq, const float* mp,
                               const int32_t* drafts, int B, int K, int V, float inv_temp,
                               uint64_t seed, const uint64_t* step, const int32_t* forced,
                               int32_t* accept_len, int32_t* committed, int32_t* extra_token,
-                              int32_t* status, void* ws, hipStream_t s) {
+                              int32_t* status, void* ws, hipStream_t s, bool ws_is_full) {
   const int n_each = B * K;
-  float* m_all = static_cast<float*>(ws);
-  uint64_t* s_all = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
-                                                align_up(2 * (size_t)n_each * sizeof(float), 256));
+  float* m_all;
+  uint64_t* s_all;
+  if (mq && mp && ws_is_full) {
+    // chunked rows: plain chunk sums of every row, decisions, residual chunk
+    // sums, the extra token
+    const AcceptWs w = carve_accept(B, K, ws);
+    const int nc = n_chunks_of(V);
+    hipLaunchKernelGGL(k_chunk_sums, dim3(nc, 2 * n_each), dim3(kChunkThreads), 0, s, zq, zp,
+                       n_each, mq, mp, V, inv_temp, w.sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_accept_decide, dim3(B), dim3(UNO_WAVE), 0, s, zq, zp, mq, mp, w.sums,
+                       drafts, K, V, inv_temp, seed, step, forced, n_each, w.m_all, w.s_all,
+                       w.a_ws, w.err_ws, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_resid_chunk_sums, dim3(nc, B), dim3(kChunkThreads), 0, s, zq, zp,
+                       w.m_all, w.s_all, w.a_ws, w.err_ws, K, V, inv_temp, n_each, w.rsums);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_extra_find, dim3(B), dim3(kChunkThreads), 0, s, zq, zp, drafts, K, V,
+                       inv_temp, seed, step, w.m_all, w.s_all, w.sums, w.rsums, w.a_ws, w.err_ws,
+                       n_each, accept_len, committed, extra_token);
+    return hipGetLastError();
+  }
+  m_all = static_cast<float*>(ws);
+  s_all = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
+                                      align_up(2 * (size_t)n_each * sizeof(float), 256));
   hipLaunchKernelGGL(k_row_stats<kRowThreads>, dim3(2 * n_each), dim3(kRowThreads), 0, s, zq, zp,
                      mq, mp, K, V, n_each, inv_temp, m_all, s_all, status);
   hipError_t e = hipGetLastError();
@@ -597,8 +1007,9 @@ hipError_t launch_spec_accept_static(const float* zq, const float* zp, const flo
   void* ws = nullptr;
   const hipError_t e = static_accept_scratch(&ws);
   if (e != hipSuccess) return e;
+  // the static scratch holds the per-row statistics only: one workgroup per row
   return launch_spec_accept(zq, zp, mq, mp, drafts, B, K, V, inv_temp, seed, step, forced,
-                            accept_len, committed, extra_token, status, ws, s);
+                            accept_len, committed, extra_token, status, ws, s, false);
 }
 
 }  // namespace uno

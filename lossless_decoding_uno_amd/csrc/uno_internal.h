@@ -27,12 +27,22 @@ hipError_t launch_tree_sample(const float* logits, int B, int N, int V, float in
                               const int32_t* n_nodes, int32_t* samples, int32_t* status,
                               hipStream_t s);
 size_t spec_accept_ws_bytes(int B, int K);
-// mq, mp [B*K]: the row maxima of zq and zp (both or neither; null: computed)
+// mq, mp [B*K]: the row maxima of zq and zp (both or neither; null: computed).
+// With them and a full workspace (spec_accept_ws_bytes) every row is cut into
+// chunks that separate workgroups weigh; otherwise one workgroup per row, and
+// ws needs only the per-row statistics (2*B*K floats, then as many uint64).
 hipError_t launch_spec_accept(const float* zq, const float* zp, const float* mq, const float* mp,
                               const int32_t* drafts, int B, int K, int V, float inv_temp,
                               uint64_t seed, const uint64_t* step, const int32_t* forced,
                               int32_t* accept_len, int32_t* committed, int32_t* extra_token,
-                              int32_t* status, void* ws, hipStream_t s);
+                              int32_t* status, void* ws, hipStream_t s, bool ws_is_full = true);
+// Draft sampling with the row maxima given, rows cut into chunks weighed by
+// separate workgroups; sums: chunk_sums_bytes(B*K) of workspace.
+size_t chunk_sums_bytes(int rows);
+hipError_t launch_draft_sample_chunked(const float* logits, const float* row_max,
+                                       uint64_t* sums, int B, int K, int V, float inv_temp,
+                                       uint64_t seed, int slot, const uint64_t* step,
+                                       int32_t* tokens, int32_t* status, hipStream_t s);
 
 // The same on the library's per-device static scratch (no workspace; rows
 // 2*B*K at most static_accept_max_rows(); the caller checks).
