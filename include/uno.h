@@ -97,10 +97,12 @@ typedef struct uno_config {
                              step[b]), key (seed, 0), for draft row j >= 1.  */
 } uno_config;
 
-/* One layer's weights [dev].  Base weights are bf16 [out, in] (row-major,
- * `in` contiguous); LoRA factors are bf16 A [r, in] and B [out, r]; norm gains
- * are fp32 [d_model].  LoRA pointers of projections whose bit is clear in
- * lora_mask are ignored. */
+/* One layer's weights [dev].  Base weights W [out, in] and LoRA factors A
+ * [r, in] are bf16 in the tile-packed layout uno_pack_weight writes (the
+ * layout of the matrix cores' weight operand, so that every 16 x 32 fragment
+ * is 1 KB of contiguous memory); LoRA factors B [out, r] are bf16 row-major;
+ * norm gains are fp32 [d_model].  LoRA pointers of projections whose bit is
+ * clear in lora_mask are ignored. */
 typedef struct uno_layer_weights {
   const void *attn_norm, *mlp_norm;                    /* fp32 [D]             */
   const void *wq, *wk, *wv, *wo, *wgate, *wup, *wdown; /* bf16                  */
@@ -109,8 +111,8 @@ typedef struct uno_layer_weights {
 } uno_layer_weights;
 
 typedef struct uno_weights {
-  const void *embed;       /* bf16 [V, D] [dev]                                 */
-  const void *lm_head;     /* bf16 [V, D] [dev] (untied, no LoRA)               */
+  const void *embed;       /* bf16 [V, D] [dev], row-major                      */
+  const void *lm_head;     /* bf16 [V, D] [dev], tile-packed (untied, no LoRA)  */
   const void *final_norm;  /* fp32 [D]    [dev]                                 */
   const uno_layer_weights *layers; /* [host] array of n_layers                  */
 } uno_weights;
@@ -130,6 +132,13 @@ typedef struct uno_kv {
   int32_t max_pages_per_seq;
   int32_t *kv_len;               /* [dev] int32 [batch]                       */
 } uno_kv;
+
+/* Tile-packed copy of a row-major bf16 matrix (a weight's layout on the
+ * device): src [dev] bf16 [n_out, n_in] row-major, dst [dev] bf16 of the same
+ * size (distinct buffers); element (n, k) goes to
+ *   ((n / 16) * (n_in / 32) + k / 32) * 512 + ((k % 32) / 8) * 128 + (n % 16) * 8 + k % 8.
+ * n_out % 16 == 0, n_in % 32 == 0.  Enqueued on `stream`. */
+int uno_pack_weight(const void *src, void *dst, int n_out, int n_in, void *stream);
 
 /* Bytes of workspace the two forward passes need for `batch` sequences of up
  * to `K` rows and up to `max_ctx` cached positions (the split of the attention

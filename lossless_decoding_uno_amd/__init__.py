@@ -29,6 +29,7 @@ EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_draft_block_from", "un
            "uno_kv_commit",
            "uno_tree_rows", "uno_tree_workspace_bytes", "uno_tree_build", "uno_verify_tree",
            "uno_tree_accept", "uno_tree_commit",
+           "uno_pack_weight",
            "uno_set_timing_events", "uno_timing_events_used", "uno_status_string",
            "uno_last_hip_error")
 
@@ -109,6 +110,8 @@ def load_library():
     lib.uno_tree_accept.argtypes = [P, P, P, P, P, I, I, I, I, F, U64, P, P, P, P, P, P, P, P]
     lib.uno_tree_commit.restype = I
     lib.uno_tree_commit.argtypes = [P, P, P, P, I, I, P, P, P]
+    lib.uno_pack_weight.restype = I
+    lib.uno_pack_weight.argtypes = [P, P, I, I, P]
     lib.uno_status_string.restype = ctypes.c_char_p
     lib.uno_status_string.argtypes = [I]
     lib.uno_last_hip_error.restype = ctypes.c_char_p
@@ -166,15 +169,27 @@ def make_config(cfg, page_size=16, lora=True):
                      mask, int(page_size), int(cfg.get("noise_prior", 0)))
 
 
+def pack_weight(t):
+    """Tile-packed device copy of a row-major bf16 [out, in] GPU matrix
+    (uno_pack_weight): the layout the library reads weights in."""
+    lib = load_library()
+    n_out, n_in = t.shape
+    out = torch.empty_like(t)
+    _check(lib.uno_pack_weight(_ptr(t), _ptr(out), n_out, n_in, _stream()))
+    return out
+
+
 class Model:
     """Device-resident weights of one model and the uno_weights table over them.
 
-    ``weights`` holds torch tensors in the logical layout of include/uno.h
-    (bf16 [out, in] base weights, bf16 LoRA A [r, in] / B [out, r], fp32 norm
-    gains); CPU tensors are copied to the GPU once, GPU tensors are used as they
-    are."""
+    ``weights`` holds torch tensors in the logical layout (bf16 [out, in]
+    base weights, bf16 LoRA A [r, in] / B [out, r], fp32 norm gains); they are
+    copied to the GPU and the base weights, LoRA A factors and LM head are
+    stored tile-packed (uno_pack_weight), the layout include/uno.h prescribes.
+    ``packed`` names top-level entries ("lm_head") given already packed on the
+    GPU, used as they are."""
 
-    def __init__(self, cfg, weights, page_size=16, lora=True, device="cuda"):
+    def __init__(self, cfg, weights, page_size=16, lora=True, device="cuda", packed=()):
         """``lora``: True, False, or a lora_mask (bit p: projection PROJ[p])."""
         self.cfg = dict(cfg)
         self.config = make_config(cfg, page_size, lora)
@@ -183,18 +198,26 @@ class Model:
         def up(t, dtype):
             return t.to(device=dev, dtype=dtype).contiguous()
 
+        def upk(t):
+            return pack_weight(up(t, torch.bfloat16))
+
         self.embed = up(weights["embed"], torch.bfloat16)
-        self.lm_head = up(weights["lm_head"], torch.bfloat16)
+        self.lm_head = (up(weights["lm_head"], torch.bfloat16) if "lm_head" in packed
+                        else upk(weights["lm_head"]))
         self.final_norm = up(weights["final_norm"], torch.float32)
         self.layers = []
         n = len(weights["layers"])
         if n != cfg["n_layers"]:
             raise ValueError("weights hold %d layers, config %d" % (n, cfg["n_layers"]))
         self._table = (UnoLayerWeights * n)()
-        def up_pair(a, b, dtype):
+
+        def up_pair(a, b, pack):
             # gate and up stored back to back: the library then fuses SwiGLU
             # into the gate|up product (any placement works, this one is faster)
-            both = torch.cat([a.to(device=dev, dtype=dtype), b.to(device=dev, dtype=dtype)])
+            both = torch.cat([a.to(device=dev, dtype=torch.bfloat16),
+                              b.to(device=dev, dtype=torch.bfloat16)])
+            if pack:
+                both = pack_weight(both)
             return both[: a.shape[0]], both[a.shape[0]:]
 
         for li, lw in enumerate(weights["layers"]):
@@ -202,15 +225,14 @@ class Model:
                  "mlp_norm": up(lw["mlp_norm"], torch.float32)}
             for p in PROJ:
                 if p not in ("gate", "up"):
-                    d[p] = up(lw[p], torch.bfloat16)
-            d["gate"], d["up"] = up_pair(lw["gate"], lw["up"], torch.bfloat16)
-            d["lora_a"] = {p: up(t, torch.bfloat16) for p, t in lw.get("lora_a", {}).items()}
+                    d[p] = upk(lw[p])
+            d["gate"], d["up"] = up_pair(lw["gate"], lw["up"], True)
+            d["lora_a"] = {p: upk(t) for p, t in lw.get("lora_a", {}).items()}
             d["lora_b"] = {p: up(t, torch.bfloat16) for p, t in lw.get("lora_b", {}).items()
                            if p not in ("gate", "up")}
             lb = lw.get("lora_b", {})
             if "gate" in lb and "up" in lb:
-                d["lora_b"]["gate"], d["lora_b"]["up"] = up_pair(lb["gate"], lb["up"],
-                                                                 torch.bfloat16)
+                d["lora_b"]["gate"], d["lora_b"]["up"] = up_pair(lb["gate"], lb["up"], False)
             self.layers.append(d)
             e = self._table[li]
             e.attn_norm, e.mlp_norm = d["attn_norm"].data_ptr(), d["mlp_norm"].data_ptr()

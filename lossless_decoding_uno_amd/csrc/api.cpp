@@ -583,6 +583,15 @@ int uno_tree_commit(const uno_config* cfg, const uno_kv* kv, const int32_t* path
   return e == hipSuccess ? UNO_OK : hip_fail(e);
 }
 
+int uno_pack_weight(const void* src, void* dst, int n_out, int n_in, void* stream) {
+  if (!src || !dst || src == dst || n_out < 16 || n_in < 32 || n_out % 16 || n_in % 32)
+    return UNO_ERR_INVALID_ARG;
+  const hipError_t e = launch_pack_tiles(static_cast<const uint16_t*>(src),
+                                         static_cast<uint16_t*>(dst), n_out, n_in,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UNO_OK : hip_fail(e);
+}
+
 int uno_set_timing_events(int kernel_class, void* const* start, void* const* stop, int n) {
   if (kernel_class == 0) {
     g_hook = TimingHook();

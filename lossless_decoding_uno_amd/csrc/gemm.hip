@@ -7,6 +7,13 @@
 // verification; picx.dev summary, "Architecture"; paperglide reader, "Sampler
 // Extensions").
 //
+// Weights (W of every product: the projections, the LoRA A factors, the LM
+// head) are stored tile-packed: the 16-row x 32-column fragment of 16-row tile
+// nt and K step s is 1 KB at element ((nt * K/32) + s) * 512, laid out in the
+// lane order of the MFMA operand (lane l = 16 * chunk + row holds the 8 values
+// of that row and 8-column chunk), so a wave reads each fragment as one
+// contiguous 1 KB.  LoRA B factors stay row-major.
+//
 // Skinny kernel (decode rows, M <= 64 per workgroup): one workgroup owns
 // 16..64 columns of W and 16..64 rows of X; its 8 waves split the K dimension
 // (with one row tile, wave w takes blocks of four consecutive 32-wide K steps,
@@ -131,12 +138,15 @@ k_gemm_skinny(GemmArgs a) {
   const int m0 = blockIdx.y * MT * 16;
   const int splits = gridDim.z, zs = blockIdx.z;
 
-  // W rows of the NT column tiles (rows past the segment re-read its last row)
+  // W in the tile-packed layout: the 16 x 32 fragment of 16-row tile nt and
+  // K step s is 1 KB at ((nt * Kd/32) + s) * 512 elements, lane l's 8 values
+  // at l * 8, so a wave's fragment load is one contiguous 1 KB read (tiles past
+  // the segment re-read its last tile)
   const uint16_t* wrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int n = sv.n0 + t * 16 + rr;
-    wrow[t] = sv.w + (size_t)(n < sv.n ? n : sv.n - 1) * a.Kd + kg * 8;
+    const int nt = (sv.n0 + t * 16 < sv.n ? sv.n0 + t * 16 : sv.n - 16) >> 4;
+    wrow[t] = sv.w + (size_t)nt * (a.Kd >> 5) * 512 + l * 8;
   }
   const uint16_t* xrow[MT];
   bool xok[MT];
@@ -168,7 +178,7 @@ k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16(wrow[t] + (s + u * kUS) * 32);
+      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16(wrow[t] + (size_t)(s + u * kUS) * 512);
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
@@ -186,7 +196,7 @@ k_gemm_skinny(GemmArgs a) {
   for (; s < ks1; s += kBlk ? 1 : kSkWaves) {
     Frag bw[NT], ax[MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bw[t].u = ldg16(wrow[t] + s * 32);
+    for (int t = 0; t < NT; ++t) bw[t].u = ldg16(wrow[t] + (size_t)s * 512);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) ax[mt].u = xok[mt] ? ldg16(xrow[mt] + s * 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -622,7 +632,9 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
       int n;
       if (pair) n = row < HALF ? n0 + row : sv.n + n0 + row - HALF;
       else n = n0 + row < sv.n ? n0 + row : sv.n - 1;
-      vb[ii] = (uint32_t)(((size_t)n * a.Kd + ch * 8) * 2);
+      // tile-packed W: row n's logical chunk ch of a 32-wide K slice sits at
+      // byte ((n / 16) * Kd/32 * 1024) + (ch * 16 + n % 16) * 16 of its tile
+      vb[ii] = (uint32_t)((size_t)(n >> 4) * (a.Kd >> 5) * 1024 + (ch * 16 + (n & 15)) * 16);
       vl[ii] = (uint32_t)(((size_t)n * a.rank + ch * 8) * 2);
     }
   }
@@ -636,10 +648,11 @@ k_gemm_big(GemmArgs a, int m_tiles, int n_tiles, int splits, int n_full) {
     const uint32_t so = stage * C::kStage;
     if (kk < kb1) {
       const uint32_t soff = __builtin_amdgcn_readfirstlane(kk * BK * 2);
+      const uint32_t soff_w = __builtin_amdgcn_readfirstlane(kk * 1024);   // packed W
 #pragma unroll
       for (int ii = 0; ii < IW; ++ii) {
         if (ii < IA) lds_dma16_buf(rs_x, vb[ii], soff, dst_a + so + ii * 1024);
-        else lds_dma16_buf(rs_w, vb[ii], soff, dst_b + so + (ii - IA) * 1024);
+        else lds_dma16_buf(rs_w, vb[ii], soff_w, dst_b + so + (ii - IA) * 1024);
       }
     } else {
       const int q = kk - kb1;
@@ -1113,6 +1126,29 @@ static hipError_t launch_big(const GemmArgs& a, const BigPlan& p, hipStream_t s,
 // the rows held in registers (past 64 rows it would stream W once per 64).
 bool gemm_swiglu_ok(const GemmArgs& a) {
   return a.epi == EPI_SWIGLU && a.M > 64 && plan_big(a).cfg >= 0;
+}
+
+// Tile-packed copy of a row-major bf16 matrix [N, K] (N % 16 == 0, K % 32 ==
+// 0): one thread per 16 bytes of the output, 8 values of one row.
+__global__ void __launch_bounds__(256)
+k_pack_tiles(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K) {
+  const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;       // 16-byte unit
+  const size_t n_units = (size_t)N * K / 8;
+  if (o >= n_units) return;
+  const int lane = (int)(o & 63);
+  const size_t blk = o >> 6;
+  const int ks = (int)(blk % (size_t)(K >> 5));
+  const size_t nt = blk / (size_t)(K >> 5);
+  const size_t row = nt * 16 + (lane & 15);
+  const int k0 = ks * 32 + (lane >> 4) * 8;
+  *reinterpret_cast<uint4*>(dst + o * 8) = *reinterpret_cast<const uint4*>(src + row * K + k0);
+}
+
+hipError_t launch_pack_tiles(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t s) {
+  const size_t n_units = (size_t)N * K / 8;
+  hipLaunchKernelGGL(k_pack_tiles, dim3((unsigned)((n_units + 255) / 256)), dim3(256), 0, s, src,
+                     dst, N, K);
+  return hipGetLastError();
 }
 
 int gemm_row_max_parts(const GemmArgs& a) {

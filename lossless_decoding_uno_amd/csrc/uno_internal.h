@@ -124,6 +124,10 @@ RopeArgs make_rope_args(const uno_config& c, const float2* cs, const int2* row_p
                         const uno_kv& kv, int layer, int K, bf16_raw_t* q_out, bf16_raw_t* q_lo);
 
 // ---------------------------------------------------------------- GEMM
+// Tile-packed copy of a row-major bf16 [N, K] matrix (N % 16 == 0, K % 32 == 0):
+// element (n, k) goes to ((n/16) * K/32 + k/32) * 512 + ((k%32)/8) * 128 +
+// (n%16) * 8 + k%8, the layout every GEMM here reads its weight operand in.
+hipError_t launch_pack_tiles(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t s);
 // Y[m, n] = sum_k X[m, k] W[n, k]  (+ LoRA)  for up to 3 column segments.
 struct GemmSeg {
   const bf16_raw_t* w;      // [n, K] bf16

@@ -87,6 +87,10 @@ def test_entry_points_reject_bad_arguments_on_the_host():
     assert lib.uno_verify_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, 1, 4,
                                 64, 1, None, fake, None, fake, 1 << 30, None) == 1
     assert lib.uno_kv_commit(None, fake, 1, 4, None, None, None) == 1
+    # weight packing: shapes off the 16 x 32 tile grid, aliasing
+    assert lib.uno_pack_weight(fake, ctypes.c_void_p(0x2000), 24, 64, None) == 1
+    assert lib.uno_pack_weight(fake, ctypes.c_void_p(0x2000), 32, 48, None) == 1
+    assert lib.uno_pack_weight(fake, fake, 32, 64, None) == 1
 
 
 def test_tree_entry_points_shape_rules_and_host_validation():

@@ -156,7 +156,8 @@ def _check_per_layer(big, B, ctx, b_check):
     # embedding table whose rows 0..2K-1 receive the teacher-forced inputs, and
     # its layer entry pointed at layer l of the 8B model's device weights
     one = U.Model(cfg1, {"embed": model.embed.clone(), "lm_head": model.lm_head,
-                         "final_norm": model.final_norm, "layers": [wts["layers"][0]]})
+                         "final_norm": model.final_norm, "layers": [wts["layers"][0]]},
+                  packed=("lm_head",))
     kv = U.PagedKV(cfg1, B, cap, page_order=torch.randperm(
         B * ((cap + 15) // 16), generator=torch.Generator().manual_seed(ctx + 1)))
     synth.fill_kv_device(kv.k_pages, kv.v_pages, seed=ctx + 1)
