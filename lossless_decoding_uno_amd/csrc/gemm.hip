@@ -15,16 +15,19 @@
 // contiguous 1 KB.  LoRA B factors stay row-major.
 //
 // Skinny kernel (decode rows, M <= 64 per workgroup): one workgroup owns
-// 16..64 columns of W and 16..64 rows of X; its 8 waves split the K dimension
-// (with one row tile, wave w takes blocks of four consecutive 32-wide K steps,
-// so each weight row is read in 256-byte runs), and every weight byte is read
-// from HBM once.  Each wave issues v_mfma_f32_16x16x32_bf16 (A = 16 rows of X,
-// B = 16 columns of W^T); the eight partial tiles are summed in LDS in a fixed
-// order and the epilogue stores, accumulates into the fp32 residual stream, or
-// forms the gated, scaled LoRA input T.  Most products also split K over
-// workgroups: the splits store fp32 partial rows and a second kernel sums them
-// in split order (run-to-run identical), applying the epilogue, RoPE, SwiGLU or
-// the residual add and RMSNorm.
+// 16..64 columns of W and 16..64 rows of X; its 2 or 4 waves split the K
+// dimension (with one row tile, wave w takes blocks of four or eight
+// consecutive 32-wide K steps, so each wave reads its fragments in 4-8 KB
+// runs), and every weight byte is read from HBM once, with non-temporal loads.
+// Each wave issues v_mfma_f32_16x16x32_bf16 (A = 16 rows of X, B = 16 columns
+// of W^T); the waves' partial tiles are summed in LDS in a fixed order and the
+// epilogue stores, accumulates into the fp32 residual stream, or forms the
+// gated, scaled LoRA input T.  q|k|v and [gate | up] products pair the two
+// 16-column tiles that RoPE (channels i and i + hd/2) or SwiGLU (gate and up
+// column c) combine in one workgroup over the whole K and apply that in the
+// epilogue.  The residual products (o, down) split K over workgroups: the
+// splits store fp32 partial rows and a second kernel sums them in split order
+// (run-to-run identical) and applies the residual add and RMSNorm.
 #include "uno_device.h"
 #include "uno_internal.h"
 #include "rope_store.h"
@@ -40,6 +43,12 @@ union Frag {
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_w;
+// 16-byte load marked non-temporal (weights: each byte is read once per pass)
+__device__ __forceinline__ uint4 ldg16_nt(const uint16_t* p) {
+  const u32x4_w v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_w*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 struct SegView {
@@ -122,19 +131,41 @@ __host__ __device__ __forceinline__ int skinny_cols(const GemmArgs& a) {
   return n;
 }
 
-constexpr int kSkWaves = 8;
+// Waves per workgroup: a workgroup streams its columns' W over K, split among
+// its waves.  Fewer waves per workgroup, each with more K steps, stream faster
+// on this chip: at 16 rows the [gate | up] product (201 MB of W) took 56 us
+// with 8 waves per workgroup, 41 us with 4 and 39 us with 2.
+constexpr int kSkWaves = 4;         // paired and LoRA-A products
+constexpr int kSkWavesSplit = 2;    // split-K products and the LM head
+
+// 16-column tile t of workgroup g: consecutive tiles, or (PAIR) the tile pair
+// (p0, p0 + P), p0 = (g / P) * 2P + g % P, P = a.pair_tiles: the partner
+// columns of a rotate-half RoPE pair (P = head_dim / 32) or of SwiGLU's gate
+// and up (P = d_ffn / 16) land in one workgroup.
+template <int NT, bool PAIR>
+__device__ __forceinline__ int skinny_tile(const GemmArgs& a, int g, int t) {
+  if (!PAIR) return g * NT + t;
+  const int P = a.pair_tiles;
+  return (g / P) * 2 * P + g % P + t * P;
+}
 
 // MT: 16-row tiles of X per workgroup; NT: 16-column tiles of W per
-// workgroup (MT * NT <= 4).  grid = (column groups, row groups, K splits).
-template <int MT, int NT>
-__global__ void __launch_bounds__(kSkWaves * 64)
+// workgroup (MT * NT <= 4); WV waves split the workgroup's K range, each with
+// UN K steps of loads in flight; PAIR: the tile pairs of skinny_tile, with
+// the RoPE + K/V write or the SwiGLU product applied in the epilogue (no K
+// split across workgroups).  grid = (column groups, row groups, K splits).
+template <int MT, int NT, int WV, int UN, bool PAIR>
+__global__ void __launch_bounds__(WV * 64)
 k_gemm_skinny(GemmArgs a) {
-  __shared__ f32x4 red[kSkWaves * MT * NT * 64];
+  __shared__ f32x4 red[WV * MT * NT * 64];
   __shared__ float rmax[MT * 16];             // row maxima of this workgroup (max_part)
   if (threadIdx.x < MT * 16) reinterpret_cast<int*>(rmax)[threadIdx.x] = kNegInfBits;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int rr = l & 15, kg = l >> 4;
-  const SegView sv = pick_segment(a, blockIdx.x * NT);
+  SegView svt[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) svt[t] = pick_segment(a, skinny_tile<NT, PAIR>(a, blockIdx.x, t));
+  const SegView& sv = svt[0];
   const int m0 = blockIdx.y * MT * 16;
   const int splits = gridDim.z, zs = blockIdx.z;
 
@@ -145,8 +176,9 @@ k_gemm_skinny(GemmArgs a) {
   const uint16_t* wrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int nt = (sv.n0 + t * 16 < sv.n ? sv.n0 + t * 16 : sv.n - 16) >> 4;
-    wrow[t] = sv.w + (size_t)nt * (a.Kd >> 5) * 512 + l * 8;
+    const int c = PAIR ? svt[t].n0 : sv.n0 + t * 16;
+    const int nt = (c < svt[t].n ? c : svt[t].n - 16) >> 4;
+    wrow[t] = svt[t].w + (size_t)nt * (a.Kd >> 5) * 512 + l * 8;
   }
   const uint16_t* xrow[MT];
   bool xok[MT];
@@ -163,22 +195,21 @@ k_gemm_skinny(GemmArgs a) {
     for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // this split's 32-wide K steps.  One row tile (MT = 1): wave w takes blocks
-  // of UN consecutive steps (ks0 + UN*w, then every 8th block), so each of its
+  // of UN consecutive steps (ks0 + UN*w, then every WV-th block), so each of its
   // W rows is read in 256-byte runs; more row tiles: wave w takes the steps
-  // ks0 + w, ks0 + w + 8, ... (even split of short ranges over the waves).
+  // ks0 + w, ks0 + w + WV, ... (even split of short ranges over the waves).
   const int n_all = a.Kd >> 5;
   const int ks0 = n_all * zs / splits, ks1 = n_all * (zs + 1) / splits;
-  constexpr int UN = 4;   // K steps in flight per wave
   constexpr bool kBlk = MT == 1;
-  constexpr int kUS = kBlk ? 1 : kSkWaves;          // step distance inside a group
+  constexpr int kUS = kBlk ? 1 : WV;          // step distance inside a group
   int s = ks0 + (kBlk ? w * UN : w);
-  for (; s + (UN - 1) * kUS < ks1; s += UN * kSkWaves) {
+  for (; s + (UN - 1) * kUS < ks1; s += UN * WV) {
     Frag bw[UN][NT];
     Frag ax[UN][MT];
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16(wrow[t] + (size_t)(s + u * kUS) * 512);
+      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16_nt(wrow[t] + (size_t)(s + u * kUS) * 512);
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
@@ -193,10 +224,10 @@ k_gemm_skinny(GemmArgs a) {
           acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][mt].v, bw[u][t].v, acc[mt][t], 0, 0, 0);
   }
   // the rest: the wave's partial block (blocked), or its remaining steps
-  for (; s < ks1; s += kBlk ? 1 : kSkWaves) {
+  for (; s < ks1; s += kBlk ? 1 : WV) {
     Frag bw[NT], ax[MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bw[t].u = ldg16(wrow[t] + (size_t)s * 512);
+    for (int t = 0; t < NT; ++t) bw[t].u = ldg16_nt(wrow[t] + (size_t)s * 512);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) ax[mt].u = xok[mt] ? ldg16(xrow[mt] + s * 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -209,19 +240,23 @@ k_gemm_skinny(GemmArgs a) {
   if (a.t && sv.lb && zs == splits - 1) {
     // rank 16 fills half of a 32-wide step: lanes past the rank feed zeros
     const int r_steps = (a.rank + 31) >> 5;
-    for (int rs = w; rs < r_steps; rs += kSkWaves) {
+    for (int rs = w; rs < r_steps; rs += WV) {
       const bool kin = rs * 32 + kg * 8 < a.rank;
-      Frag bw[NT], ax[MT];
+      Frag bw[NT], axt[PAIR ? NT : 1][MT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int n = sv.n0 + t * 16 + rr;
-        const uint16_t* brow = sv.lb + (size_t)(n < sv.n ? n : sv.n - 1) * a.rank + kg * 8;
+        const int n = (PAIR ? svt[t].n0 : sv.n0 + t * 16) + rr;
+        const uint16_t* brow =
+            svt[t].lb + (size_t)(n < svt[t].n ? n : svt[t].n - 1) * a.rank + kg * 8;
         bw[t].u = kin ? ldg16(brow + rs * 32) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
+      for (int tt = 0; tt < (PAIR ? NT : 1); ++tt)
+#pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        Frag* ax = axt[tt];
         const int m = m0 + mt * 16 + rr;
-        const size_t to = (size_t)m * a.ldt + sv.t_col + rs * 32 + kg * 8;
+        const size_t to = (size_t)m * a.ldt + svt[tt].t_col + rs * 32 + kg * 8;
         if (!(kin && m < a.M)) {
           ax[mt].u = make_uint4(0, 0, 0, 0);
         } else if (a.t_part) {
@@ -242,10 +277,11 @@ k_gemm_skinny(GemmArgs a) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[mt].v, bw[t].v, acc[mt][t], 0, 0, 0);
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(axt[PAIR ? t : 0][mt].v, bw[t].v,
+                                                               acc[mt][t], 0, 0, 0);
     }
   }
-  // the eight waves' partial tiles are summed in a fixed order
+  // the waves' partial tiles are summed in a fixed order
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -258,27 +294,59 @@ k_gemm_skinny(GemmArgs a) {
   if (splits > 1) {
     const int ncols = skinny_cols(a);
     float* part = a.part + (size_t)zs * a.M * ncols;
-    for (int e = threadIdx.x; e < kTile; e += kSkWaves * 64) {
+    for (int e = threadIdx.x; e < kTile; e += WV * 64) {
       const int r = e / (NT * 16), cl = e % (NT * 16);      // row / column in the tile
       const int mt = r >> 4, rr = r & 15, t = cl >> 4, ln = (rr >> 2) * 16 + (cl & 15);
       float v = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kSkWaves; ++ww)
+      for (int ww = 0; ww < WV; ++ww)
         v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + (rr & 3)];
-      const int m = m0 + r, nl = sv.n0 + cl;
-      if (m < a.M && nl < sv.n) part[(size_t)m * ncols + sv.col_base + nl] = v;
+      const SegView& st = svt[t];
+      const int m = m0 + r, nl = (PAIR ? st.n0 : sv.n0 + t * 16) + (cl & 15);
+      if (m < a.M && nl < st.n) part[(size_t)m * ncols + st.col_base + nl] = v;
     }
     return;
   }
-  for (int e = threadIdx.x; e < kTile; e += kSkWaves * 64) {
+  if (PAIR) {
+    // tile 0 holds the first channel of each pair, tile 1 its partner
+    for (int e = threadIdx.x; e < MT * 256; e += WV * 64) {
+      const int mt = e / 256, ln = (e & 255) >> 2, i = e & 3;
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WV; ++ww) {
+        v0 += redf[((((ww * MT + mt) * NT + 0) * 64) + ln) * 4 + i];
+        v1 += redf[((((ww * MT + mt) * NT + 1) * 64) + ln) * 4 + i];
+      }
+      const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
+      if (m >= a.M) continue;
+      const int c0 = svt[0].col_base + svt[0].n0 + (ln & 15);
+      if (a.rope_fuse) {
+        const RopeArgs& ra = a.rope;
+        const int head = c0 / ra.hd, ch = c0 % ra.hd;
+        int slot;
+        const int page = rope_page(ra, m, &slot);
+        if (head < ra.Hq + ra.Hkv) {
+          rope_store_pair(ra, m, head, ch, v0, v1, page, slot);
+        } else {
+          rope_store_v(ra, head - ra.Hq - ra.Hkv, ch, v0, page, slot);
+          rope_store_v(ra, head - ra.Hq - ra.Hkv, ch + ra.hd / 2, v1, page, slot);
+        }
+      } else {
+        a.act_out[(size_t)m * svt[0].n + svt[0].n0 + (ln & 15)] =
+            f32_to_bf16(v0 / (1.0f + __expf(-v0)) * v1);
+      }
+    }
+    return;
+  }
+  for (int e = threadIdx.x; e < kTile; e += WV * 64) {
     const int mt = e / (NT * 256), t = (e / 256) % NT, ln = (e & 255) >> 2, i = e & 3;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kSkWaves; ++ww) v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + i];
+    for (int ww = 0; ww < WV; ++ww) v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + i];
     const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
     const int nl = sv.n0 + t * 16 + (ln & 15);
-    if (m < a.M && nl < sv.n) {
-      store_out(a, m, sv.col_base + nl, v);
+    if (m < a.M && nl < svt[t].n) {
+      store_out(a, m, svt[t].col_base + nl, v);
       if (a.max_part) atomic_max_f32(&rmax[m - m0], v);
     }
   }
@@ -399,13 +467,18 @@ k_gemm_skinny_reduce_norm(GemmArgs a, int splits) {
 }
 
 struct SkinnyPlan {
-  int mt, nt, gx, gy, splits;
+  int mt, nt, gx, gy, splits, waves, un;
 };
 
 // Column tiles per workgroup: as many as keep >= 128 workgroups (fewer
-// re-reads of X); K splits until about 512 workgroups are in flight.
+// re-reads of X); K splits until about 512 workgroups are in flight.  Waves
+// and loads in flight per wave as measured best at 16 rows: 2 waves for the
+// long streams (split products, the LM head with 8 K steps in flight), 4 for
+// the small LoRA-A products.
 static SkinnyPlan plan_skinny(const GemmArgs& a) {
   SkinnyPlan p;
+  p.waves = a.epi == EPI_LORA_T ? kSkWaves : kSkWavesSplit;
+  p.un = a.max_part ? 8 : 4;
   p.mt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
   p.gy = a.M <= 32 ? 1 : (a.M + 63) / 64;
   int tiles16 = 0;
@@ -423,7 +496,7 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   p.splits = 1;
   const size_t per_split = (size_t)a.M * skinny_cols(a);
   if (a.part && !a.max_part)
-    while (p.gx * p.gy * p.splits < 512 && steps / (p.splits * 2) >= kSkWaves &&
+    while (p.gx * p.gy * p.splits < 512 && steps / (p.splits * 2) >= p.waves &&
            (size_t)p.splits * 2 * per_split <= a.part_floats &&
            (a.max_splits <= 0 || p.splits * 2 <= a.max_splits))
       p.splits *= 2;
@@ -444,7 +517,15 @@ static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
 
 template <int MT, int NT>
 static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_skinny<MT, NT>), dim3(p.gx, p.gy, p.splits), dim3(kSkWaves * 64), 0, s, a);
+  const dim3 grid(p.gx, p.gy, p.splits);
+  if (p.waves == kSkWaves)
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, kSkWaves, 4, false>), grid, dim3(kSkWaves * 64), 0, s, a);
+  else if (p.un == 8)
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, kSkWavesSplit, 8, false>), grid,
+                       dim3(kSkWavesSplit * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, kSkWavesSplit, 4, false>), grid,
+                       dim3(kSkWavesSplit * 64), 0, s, a);
   if (p.splits == 1 || a.partials_only) return;
   const int n = a.M * skinny_cols(a);
   if (a.rope_fuse)
@@ -460,8 +541,45 @@ static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
     hipLaunchKernelGGL(k_gemm_skinny_reduce, dim3((n + 255) / 256), dim3(256), 0, s, a, p.splits);
 }
 
+// RoPE and SwiGLU need both columns of a pair (channel i and i + hd/2 of a
+// head; gate and up column c): instead of splitting K and pairing them in a
+// reduction launch, one workgroup computes both 16-column tiles over the whole
+// K and applies the epilogue itself.  Returns the tile distance P of the
+// pairs, or 0.
+static int skinny_pair_tiles(const GemmArgs& a) {
+  if (a.max_part || a.partials_only || a.epi != EPI_STORE_F32 || a.M > 64) return 0;
+  if (a.rope_fuse) {
+    const int hd = a.rope.hd;
+    if (hd % 32) return 0;
+    for (int i = 0; i < a.n_seg; ++i)
+      if (a.seg[i].n % hd) return 0;
+    return hd / 32;
+  }
+  if (a.act_out && a.n_seg == 2 && a.seg[0].n == a.seg[1].n && a.seg[0].n % 16 == 0)
+    return a.seg[0].n / 16;
+  return 0;
+}
+
+template <int MT>
+static void launch_sk_pair(const GemmArgs& a, hipStream_t s) {
+  const int gx = skinny_cols(a) / 32, gy = (a.M + MT * 16 - 1) / (MT * 16);
+  hipLaunchKernelGGL((k_gemm_skinny<MT, 2, kSkWaves, 4, true>), dim3(gx, gy, 1),
+                     dim3(kSkWaves * 64), 0, s, a);
+}
+
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bool* roped,
                               bool* swiglued) {
+  if (const int P = skinny_pair_tiles(a)) {
+    GemmArgs b = a;
+    b.pair_tiles = P;
+    if (normed) *normed = false;
+    if (roped) *roped = a.rope_fuse != 0;
+    if (swiglued) *swiglued = !a.rope_fuse;
+    if (a.M <= 16) launch_sk_pair<1>(b, s);
+    else if (a.M <= 32) launch_sk_pair<2>(b, s);
+    else launch_sk_pair<4>(b, s);
+    return hipGetLastError();
+  }
   const SkinnyPlan p = plan_skinny(a);
   if (normed) *normed = fuse_norm(a, p);
   if (roped) *roped = a.rope_fuse && p.splits > 1;

@@ -194,6 +194,9 @@ struct GemmArgs {
   // takes the maxima of its split tiles from their reduced rows
   float* max_part;
   int max_part_ld;
+  // set by the skinny launcher (callers leave it 0): tile pairing of a fused
+  // RoPE or SwiGLU epilogue without a K split
+  int pair_tiles;
 };
 // split-K scratch carved per pass: 128 MB for passes of more than 64 rows
 // (tiled kernel), 4 MB for up to 64 (skinny kernel)

@@ -2,14 +2,21 @@
 do not use: q heads per kv head G = 1, 2, 8 and 16 with head_dim 128, G = 2
 and 8 with head_dim 64 (the attention kernel takes G*K query rows per kv
 head, so these change its row-group count and key split), K = 16 and 8,
-ragged contexts, shuffled pages.  Logits against the oracle."""
+ragged contexts, shuffled pages.  Logits against the exact oracle, with the
+bf16 yardstick (the oracle's bf16 mode on the same inputs) as the criterion:
+at 16 q heads of 128 (model width 2048) plain bf16 arithmetic itself puts a
+few logits per pass past 2e-2 + 1e-2 |z| of the exact ones, so the GPU path
+must put no more there than the bf16 mode does, summed over the test's
+passes, and none past three times the bar.  Where the yardstick puts none
+there (the narrower layouts) that is the plain bar."""
 import pytest
 import torch
 
 import synth
 from oracle import spec as ospec
 
-from gpu_util import assert_logits_close, gpu_or_fail, load_kv_logical, progress
+from gpu_util import YardstickTally, gpu_or_fail, load_kv_logical, progress
+from oracle import model as om
 
 pytestmark = pytest.mark.gpu
 
@@ -34,12 +41,15 @@ def test_head_layout_draft_verify(hq, hkv, hd, K):
         k, v = synth.kv_values(cfg, n, seed=23, seq=b)
         load_kv_logical(kv, b, k, v)
         toks = synth.random_tokens(n + 1, cfg["vocab"], 500 + b, (n + 1,))
-        s = ospec.Sequence(cfg, toks, capacity=cap)
-        for li in range(cfg["n_layers"]):
-            s.cache.k[li][:n] = k[li].double().numpy()
-            s.cache.v[li][:n] = v[li].double().numpy()
-        s.kv_len = n
-        seqs.append(s)
+        pair = []
+        for _ in range(2):      # exact and bf16-mode oracle states
+            s = ospec.Sequence(cfg, toks, capacity=cap)
+            for li in range(cfg["n_layers"]):
+                s.cache.k[li][:n] = k[li].double().numpy()
+                s.cache.v[li][:n] = v[li].double().numpy()
+            s.kv_len = n
+            pair.append(s)
+        seqs.append(pair)
     kv.kv_len.copy_(torch.tensor(ctxs, dtype=torch.int32))
     ws = U.alloc_workspace(U.workspace_bytes(model, B, K, cap))
     V = cfg["vocab"]
@@ -48,7 +58,7 @@ def test_head_layout_draft_verify(hq, hkv, hd, K):
     zp = torch.empty((B, K, V), dtype=torch.float32, device=dev)
     d = torch.empty((B, K), dtype=torch.int32, device=dev)
     status = torch.zeros(B, dtype=torch.int32, device=dev)
-    anchor = torch.tensor([s.tokens[-1] for s in seqs], dtype=torch.int32, device=dev)
+    anchor = torch.tensor([s.tokens[-1] for s, _ in seqs], dtype=torch.int32, device=dev)
     U.draft_block(model, kv, anchor, K, cap, 1.0, 0, torch.zeros(B, dtype=torch.uint64).to(dev),
                   zq, d, ws, status)
     rows = synth.random_tokens(K, V, 88, (B, K))
@@ -56,10 +66,11 @@ def test_head_layout_draft_verify(hq, hkv, hd, K):
     torch.cuda.synchronize()
     assert (status.cpu().numpy() == 0).all()
     zq_c, zp_c = zq.cpu().numpy(), zp.cpu().numpy()
-    worst = 0.0
-    for b, s in enumerate(seqs):
-        worst = max(worst, assert_logits_close(zq_c[b], ospec.draft_logits(cfg, w64, s, K),
-                                               "G %d hd %d draft %d" % (hq // hkv, hd, b)))
-        worst = max(worst, assert_logits_close(zp_c[b], ospec.verify_logits(cfg, w64, s, list(rows[b])),
-                                               "G %d hd %d verify %d" % (hq // hkv, hd, b)))
-    progress("heads %d/%d x %d, K %d: worst logit error %.2e" % (hq, hkv, hd, K, worst))
+    tally = YardstickTally("G %d hd %d" % (hq // hkv, hd))
+    rnd = {"act_round": om.bf16_round}
+    for b, (s, s_bf) in enumerate(seqs):
+        tally.add(zq_c[b], ospec.draft_logits(cfg, w64, s, K),
+                  ospec.draft_logits(cfg, w64, s_bf, K, **rnd), "draft %d" % b)
+        tally.add(zp_c[b], ospec.verify_logits(cfg, w64, s, list(rows[b])),
+                  ospec.verify_logits(cfg, w64, s_bf, list(rows[b]), **rnd), "verify %d" % b)
+    progress("heads %d/%d x %d, K %d: %s" % (hq, hkv, hd, K, tally.finish()))
