@@ -47,8 +47,8 @@ BF16_PEAK_TFLOPS = 2500.0
 # attention profile summary under profiles/): mean FETCH_SIZE and WRITE_SIZE per
 # dispatch, scaled by the copy calibration factor, for the kernel source with
 # this digest.
-ATTN_TRAFFIC = {"source": "ee3f05b880047b37", "bytes_per_launch": 2460727231,
-                "fetch_kib": 1196956.97, "write_kib": 9216.0, "fetch_factor": 1.99994, "write_factor": 1.0}
+ATTN_TRAFFIC = {"source": "273908c7a7243788", "bytes_per_launch": 2460721323,
+                "fetch_kib": 1196956.93, "write_kib": 9216.01, "fetch_factor": 1.99993, "write_factor": 1.0}
 ATTN_SOURCES = ["lossless_decoding_uno_amd/csrc/attention.hip",
                 "lossless_decoding_uno_amd/csrc/uno_device.h"]
 
