@@ -68,7 +68,8 @@ enum {
   UNO_DEV_BAD_TOKEN = 2,    /* a token id outside [0, vocab)                    */
   UNO_DEV_BAD_PAGE = 4,     /* a page id outside [0, n_pages)                   */
   UNO_DEV_NONFINITE = 8,    /* a sampled logit row held NaN or Inf              */
-  UNO_DEV_BAD_ACCEPT = 16   /* a forced / given accept length outside [0, K]    */
+  UNO_DEV_BAD_ACCEPT = 16,  /* a forced / given accept length outside [0, K]    */
+  UNO_DEV_SYNC_TIMEOUT = 32 /* a projection waited too long for its LoRA-A part  */
 };
 
 /* Model shape.  Supported: head_dim 64 or 128; n_q_heads a multiple of
@@ -377,7 +378,10 @@ enum {
   UNO_TIME_ATTENTION = 1, /* block attention (the split-KV partial kernel)    */
   UNO_TIME_GEMM = 2,      /* the four projections of every layer (q|k|v, o,
                              gate|up, down), LoRA B fused when drafting       */
-  UNO_TIME_LORA_A = 3,    /* the LoRA A products (x A^T, gated and scaled)    */
+  UNO_TIME_LORA_A = 3,    /* the LoRA A products (x A^T, gated and scaled)
+                             launched on their own (passes of more than 64
+                             rows; at most 64 they share their projection's
+                             launch and count in its class)                   */
   UNO_TIME_LM_HEAD = 4,   /* the final vocabulary projection                  */
   UNO_TIME_SAMPLER = 5,   /* draft sampling and the accept / resample kernels */
   /* one projection of every layer (also counted in UNO_TIME_GEMM); a launch

@@ -146,8 +146,11 @@ __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_
                              double log_theta, const int32_t* __restrict__ depth,
                              float2* __restrict__ cs, const int32_t* __restrict__ page_table,
                              int max_pages, int64_t n_pages, int ps, int2* __restrict__ row_page,
-                             int32_t* __restrict__ status) {
+                             int32_t* __restrict__ status, unsigned* __restrict__ zero,
+                             int n_zero) {
   const int r = blockIdx.x;
+  if (r == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0u;
   const int b = r / K, j = r % K;
   const double pos = (double)(kv_len[b] + pos_offset + (depth ? depth[r] : j));
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
@@ -176,10 +179,11 @@ __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_
 
 hipError_t launch_rope_table(const uno_config& c, const uno_kv& kv, int B, int K, int pos_offset,
                              const int32_t* depth, float2* cs, int2* row_page, int32_t* status,
-                             hipStream_t s) {
+                             unsigned* zero, int n_zero, hipStream_t s) {
   hipLaunchKernelGGL(k_rope_table, dim3(B * K), dim3(64), 0, s, kv.kv_len, K, pos_offset,
                      c.head_dim / 2, log((double)c.rope_theta), depth, cs, kv.page_table,
-                     kv.max_pages_per_seq, kv.n_pages, c.page_size, row_page, status);
+                     kv.max_pages_per_seq, kv.n_pages, c.page_size, row_page, status, zero,
+                     n_zero);
   return hipGetLastError();
 }
 

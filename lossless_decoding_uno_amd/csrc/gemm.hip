@@ -138,6 +138,59 @@ __host__ __device__ __forceinline__ int skinny_cols(const GemmArgs& a) {
 constexpr int kSkWaves = 4;         // paired and LoRA-A products
 constexpr int kSkWavesSplit = 2;    // split-K products and the LM head
 
+// Producer / consumer handshake of a fused LoRA-A product (k_gemm_skinny_lora).
+// The producers store their partials with device-scope (write-through)
+// stores, wait until every store of the workgroup has completed, and one
+// thread bumps the counter; a consumer's first thread polls the counter with
+// device-scope loads (bounded: on timeout it flags UNO_DEV_SYNC_TIMEOUT in
+// status[0] and goes on), and the partials are then read with device-scope
+// loads.  No L2 write-back or invalidation is needed on either side.
+constexpr unsigned kLoraSpinLimit = 1u << 22;
+__device__ __forceinline__ void signal_done(unsigned* counter) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_lora_t(const GemmArgs& a) {
+  if (threadIdx.x == 0) {
+    unsigned it = 0;
+    while (__hip_atomic_load(a.t_wait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           a.t_wait_target) {
+      if (++it > kLoraSpinLimit) {
+        if (a.t_timeout) atomicOr(a.t_timeout, UNO_DEV_SYNC_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  __syncthreads();
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// eight consecutive floats, summed over `splits` partial planes zs apart in
+// split order (device-scope loads, all issued before the first add)
+__device__ __forceinline__ void sum_splits8_coherent(const float* p, size_t zs, int splits,
+                                                     float4* lo, float4* hi) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = ld_coherent(p + i);
+  for (int z0 = 1; z0 < splits; z0 += 2) {
+    float q[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[u][i] = z0 + u < splits ? ld_coherent(p + (size_t)(z0 + u) * zs + i) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (z0 + u < splits)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += q[u][i];
+  }
+  *lo = make_float4(v[0], v[1], v[2], v[3]);
+  *hi = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // 16-column tile t of workgroup g: consecutive tiles, or (PAIR) the tile pair
 // (p0, p0 + P), p0 = (g / P) * 2P + g % P, P = a.pair_tiles: the partner
 // columns of a rotate-half RoPE pair (P = head_dim / 32) or of SwiGLU's gate
@@ -155,8 +208,8 @@ __device__ __forceinline__ int skinny_tile(const GemmArgs& a, int g, int t) {
 // the RoPE + K/V write or the SwiGLU product applied in the epilogue (no K
 // split across workgroups).  grid = (column groups, row groups, K splits).
 template <int MT, int NT, int WV, int UN, bool PAIR>
-__global__ void __launch_bounds__(WV * 64)
-k_gemm_skinny(GemmArgs a) {
+__device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, const int by,
+                                            const int zs, const int splits) {
   __shared__ f32x4 red[WV * MT * NT * 64];
   __shared__ float rmax[MT * 16];             // row maxima of this workgroup (max_part)
   if (threadIdx.x < MT * 16) reinterpret_cast<int*>(rmax)[threadIdx.x] = kNegInfBits;
@@ -164,10 +217,9 @@ k_gemm_skinny(GemmArgs a) {
   const int rr = l & 15, kg = l >> 4;
   SegView svt[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) svt[t] = pick_segment(a, skinny_tile<NT, PAIR>(a, blockIdx.x, t));
+  for (int t = 0; t < NT; ++t) svt[t] = pick_segment(a, skinny_tile<NT, PAIR>(a, bx, t));
   const SegView& sv = svt[0];
-  const int m0 = blockIdx.y * MT * 16;
-  const int splits = gridDim.z, zs = blockIdx.z;
+  const int m0 = by * MT * 16;
 
   // W in the tile-packed layout: the 16 x 32 fragment of 16-row tile nt and
   // K step s is 1 KB at ((nt * Kd/32) + s) * 512 elements, lane l's 8 values
@@ -238,6 +290,7 @@ k_gemm_skinny(GemmArgs a) {
   }
   // fused LoRA (last split): T [M, r] (already gated and scaled) times B [n, r]^T
   if (a.t && sv.lb && zs == splits - 1) {
+    if (a.t_wait) wait_lora_t(a);
     // rank 16 fills half of a 32-wide step: lanes past the rank feed zeros
     const int r_steps = (a.rank + 31) >> 5;
     for (int rs = w; rs < r_steps; rs += WV) {
@@ -261,11 +314,17 @@ k_gemm_skinny(GemmArgs a) {
           ax[mt].u = make_uint4(0, 0, 0, 0);
         } else if (a.t_part) {
           // T from its LoRA-A product's split-K partials, summed in split order
-          // and rounded as that product's epilogue rounds it
-          const float4* tp = reinterpret_cast<const float4*>(a.t_part + to);
-          const size_t zs4 = (size_t)a.M * a.ldt / 4;
-          const float4 lo = sum_splits4(tp, zs4, a.t_splits);
-          const float4 hi = sum_splits4(tp + 1, zs4, a.t_splits);
+          // and rounded as that product's epilogue rounds it (read from the
+          // device coherence point when they come from the same launch)
+          float4 lo, hi;
+          if (a.t_wait && !a.t_lines_owned) {
+            sum_splits8_coherent(a.t_part + to, (size_t)a.M * a.ldt, a.t_splits, &lo, &hi);
+          } else {
+            const float4* tp = reinterpret_cast<const float4*>(a.t_part + to);
+            const size_t zs4 = (size_t)a.M * a.ldt / 4;
+            lo = sum_splits4(tp, zs4, a.t_splits);
+            hi = sum_splits4(tp + 1, zs4, a.t_splits);
+          }
           const float g = (m % a.t_rows) != 0 ? a.t_scale : 0.f;
           ax[mt].u = make_uint4(pack_bf16x2(g * lo.x, g * lo.y), pack_bf16x2(g * lo.z, g * lo.w),
                                 pack_bf16x2(g * hi.x, g * hi.y), pack_bf16x2(g * hi.z, g * hi.w));
@@ -301,10 +360,17 @@ k_gemm_skinny(GemmArgs a) {
 #pragma unroll
       for (int ww = 0; ww < WV; ++ww)
         v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + (rr & 3)];
-      const SegView& st = svt[t];
+      // (unpaired tiles of a workgroup share one segment: no dynamic index
+      // into svt, which would put it in scratch memory)
+      const SegView& st = PAIR ? svt[t] : sv;
       const int m = m0 + r, nl = (PAIR ? st.n0 : sv.n0 + t * 16) + (cl & 15);
-      if (m < a.M && nl < st.n) part[(size_t)m * ncols + st.col_base + nl] = v;
+      if (m < a.M && nl < st.n) {
+        float* dst = part + (size_t)m * ncols + st.col_base + nl;
+        if (a.t_signal) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = v;
+      }
     }
+    if (a.t_signal) signal_done(a.t_signal);
     return;
   }
   if (PAIR) {
@@ -345,8 +411,8 @@ k_gemm_skinny(GemmArgs a) {
     for (int ww = 0; ww < WV; ++ww) v += redf[((((ww * MT + mt) * NT + t) * 64) + ln) * 4 + i];
     const int m = m0 + mt * 16 + 4 * (ln >> 4) + i;
     const int nl = sv.n0 + t * 16 + (ln & 15);
-    if (m < a.M && nl < svt[t].n) {
-      store_out(a, m, svt[t].col_base + nl, v);
+    if (m < a.M && nl < sv.n) {
+      store_out(a, m, sv.col_base + nl, v);
       if (a.max_part) atomic_max_f32(&rmax[m - m0], v);
     }
   }
@@ -354,8 +420,47 @@ k_gemm_skinny(GemmArgs a) {
     __syncthreads();
     const int t = threadIdx.x;
     if (t < MT * 16 && m0 + t < a.M)
-      a.max_part[(size_t)(m0 + t) * a.max_part_ld + blockIdx.x] = rmax[t];
+      a.max_part[(size_t)(m0 + t) * a.max_part_ld + bx] = rmax[t];
   }
+}
+
+// The bodies read their GemmArgs in place in the kernel-argument segment: a
+// reference to the by-value parameter itself makes the compiler copy the whole
+// struct to scratch memory (and lose the global address space of every
+// pointer loaded from it).
+__device__ __forceinline__ const GemmArgs& kernarg_gemm(int i) {
+  return ((const GemmArgs*)__builtin_amdgcn_kernarg_segment_ptr())[i];
+}
+
+template <int MT, int NT, int WV, int UN, bool PAIR>
+__global__ void __launch_bounds__(WV * 64) k_gemm_skinny(GemmArgs) {
+  skinny_body<MT, NT, WV, UN, PAIR>(kernarg_gemm(0), blockIdx.x, blockIdx.y, blockIdx.z,
+                                    gridDim.z);
+}
+
+// A projection and the LoRA-A product T = X A^T that feeds its LoRA step in
+// one launch: workgroups [0, n_prod) compute T's split-K partials (`ta`,
+// stored at the device coherence point, each workgroup then bumps the
+// counter), the rest run the projection (`a`), which streams its W first and
+// waits for the counter only when it reaches its LoRA step.  Producers come
+// first in dispatch order, so they are running or done by the time any
+// projection workgroup waits.  grid = n_prod + gx * gy * splits, 1-D.
+template <int MT, int NT, int WV, int UN, bool PAIR>
+__global__ void __launch_bounds__(WV * 64)
+k_gemm_skinny_lora(GemmArgs /*ta*/, GemmArgs /*a*/, int n_prod, int tgx, int tgy, int tsplits,
+                   int gx, int gy, int splits) {
+  int b = blockIdx.x;
+  if (b < n_prod) {
+    const int bx = b % tgx, by = (b / tgx) % tgy, bz = b / (tgx * tgy);
+    if (kernarg_gemm(1).t_lines_owned)
+      skinny_body<MT, 2, WV, 4, false>(kernarg_gemm(0), bx, by, bz, tsplits);
+    else
+      skinny_body<MT, 1, WV, 4, false>(kernarg_gemm(0), bx, by, bz, tsplits);
+    return;
+  }
+  b -= n_prod;
+  const int bx = b % gx, by = (b / gx) % gy, bz = b / (gx * gy);
+  skinny_body<MT, NT, WV, UN, PAIR>(kernarg_gemm(1), bx, by, bz, splits);
 }
 
 // Sum the skinny kernel's split-K partials in split order and apply the
@@ -484,12 +589,13 @@ static SkinnyPlan plan_skinny(const GemmArgs& a) {
   int tiles16 = 0;
   for (int i = 0; i < a.n_seg; ++i) tiles16 += (a.seg[i].n + 15) / 16;
   p.nt = 1;
-  for (int nt = 4 / p.mt; nt > 1; nt /= 2) {
+  for (int nt = a.sk_nt ? 1 : 4 / p.mt; nt > 1; nt /= 2) {
     bool ok = true;
     if (a.n_seg > 1)
       for (int i = 0; i < a.n_seg; ++i) ok = ok && a.seg[i].n % (16 * nt) == 0;
     if (ok && (tiles16 + nt - 1) / nt * p.gy >= 128) { p.nt = nt; break; }
   }
+  if (a.sk_nt) p.nt = a.sk_nt;
   p.gx = (tiles16 + p.nt - 1) / p.nt;
   const int steps = a.Kd >> 5;
   const size_t tile = (size_t)p.mt * p.nt * 256;
@@ -515,6 +621,9 @@ static bool fuse_norm(const GemmArgs& a, const SkinnyPlan& p) {
          a.seg[0].n == a.ldo && a.ldo % 4 == 0 && a.ldo <= 8192;
 }
 
+// the reduction launch that follows a split skinny product
+static void launch_sk_reduce(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s);
+
 template <int MT, int NT>
 static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   const dim3 grid(p.gx, p.gy, p.splits);
@@ -526,6 +635,10 @@ static void launch_sk(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   else
     hipLaunchKernelGGL((k_gemm_skinny<MT, NT, kSkWavesSplit, 4, false>), grid,
                        dim3(kSkWavesSplit * 64), 0, s, a);
+  launch_sk_reduce(a, p, s);
+}
+
+static void launch_sk_reduce(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   if (p.splits == 1 || a.partials_only) return;
   const int n = a.M * skinny_cols(a);
   if (a.rope_fuse)
@@ -592,6 +705,87 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s, bool* normed, bo
     case 16 + 1: launch_sk<2, 1>(a, p, s); break;
     default: launch_sk<4, 1>(a, p, s); break;
   }
+  return hipGetLastError();
+}
+
+// One launch of a projection and its LoRA-A product (k_gemm_skinny_lora):
+// MT row tiles, the projection's NT column tiles, WV waves, UN loads in flight.
+template <int MT, int NT, int WV, int UN, bool PAIR>
+static void launch_sk_lora(const GemmArgs& ta, const SkinnyPlan& tp, const GemmArgs& a, int gx,
+                           int gy, int splits, hipStream_t s) {
+  const int n_prod = tp.gx * tp.gy * tp.splits;
+  hipLaunchKernelGGL((k_gemm_skinny_lora<MT, NT, WV, UN, PAIR>), dim3(n_prod + gx * gy * splits),
+                     dim3(WV * 64), 0, s, ta, a, n_prod, tp.gx, tp.gy, tp.splits, gx, gy, splits);
+}
+
+hipError_t launch_gemm_lora(const GemmArgs& a, const GemmArgs& ta, float* t_part,
+                            size_t t_part_floats, unsigned* counter, int* timeout_flag,
+                            hipStream_t s, bool* normed, bool* roped, bool* swiglued,
+                            bool* fused) {
+  GemmArgs g, t2;
+  gemm_lora_pair(a, ta, t_part, t_part_floats, &g, &t2);
+  *fused = false;
+  if (!counter || !t2.partials_only || a.M > 32) {
+    const hipError_t e = launch_gemm(t2, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm(g, s, normed, roped, swiglued);
+  }
+  // LoRA-A workgroups of two 16-column tiles: with 32-float aligned rows each
+  // 128-byte line of the partials has one writer
+  bool owned = g.ldt == skinny_cols(t2);
+  for (int i = 0; i < t2.n_seg; ++i) owned = owned && t2.seg[i].n % 32 == 0;
+  if (owned) t2.sk_nt = 2;
+  SkinnyPlan tp = plan_skinny(t2);
+  g.t_splits = tp.splits;
+  t2.t_signal = counter;
+  g.t_wait = counter;
+  g.t_wait_target = (unsigned)(tp.gx * tp.gy * tp.splits);
+  g.t_timeout = timeout_flag;
+  g.t_lines_owned = owned && tp.nt == 2;
+  const int P = skinny_pair_tiles(g);
+  SkinnyPlan p = plan_skinny(g);
+  if (tp.nt != (owned ? 2 : 1) || tp.splits < 2 || (!P && p.mt != tp.mt)) {
+    const hipError_t e = launch_gemm(t2, s);
+    if (e != hipSuccess) return e;
+    g.t_wait = nullptr;
+    return launch_gemm(g, s, normed, roped, swiglued);
+  }
+  *fused = true;
+  if (P) {
+    g.pair_tiles = P;
+    if (normed) *normed = false;
+    if (roped) *roped = g.rope_fuse != 0;
+    if (swiglued) *swiglued = !g.rope_fuse;
+    const int gx = skinny_cols(g) / 32;
+    if (g.M <= 16)
+      launch_sk_lora<1, 2, kSkWaves, 4, true>(t2, tp, g, gx, 1, 1, s);
+    else if (g.M <= 32)
+      launch_sk_lora<2, 2, kSkWaves, 4, true>(t2, tp, g, gx, 1, 1, s);
+    else
+      launch_sk_lora<4, 2, kSkWaves, 4, true>(t2, tp, g, gx, (g.M + 63) / 64, 1, s);
+    return hipGetLastError();
+  }
+  if (normed) *normed = fuse_norm(g, p);
+  if (roped) *roped = g.rope_fuse && p.splits > 1;
+  if (swiglued) *swiglued = !g.rope_fuse && !fuse_norm(g, p) && fuse_swiglu(g, p);
+  // the LoRA-A workgroups run with the projection's wave count
+#define UNO_SK_LORA(MT_, NT_)                                                              \
+  (p.waves == kSkWaves                                                                     \
+       ? launch_sk_lora<MT_, NT_, kSkWaves, 4, false>(t2, tp, g, p.gx, p.gy, p.splits, s)  \
+       : p.un == 8 ? launch_sk_lora<MT_, NT_, kSkWavesSplit, 8, false>(t2, tp, g, p.gx,    \
+                                                                       p.gy, p.splits, s)  \
+                   : launch_sk_lora<MT_, NT_, kSkWavesSplit, 4, false>(t2, tp, g, p.gx,    \
+                                                                       p.gy, p.splits, s))
+  switch (p.mt * 8 + p.nt) {
+    case 8 + 4: UNO_SK_LORA(1, 4); break;
+    case 8 + 2: UNO_SK_LORA(1, 2); break;
+    case 8 + 1: UNO_SK_LORA(1, 1); break;
+    case 16 + 2: UNO_SK_LORA(2, 2); break;
+    case 16 + 1: UNO_SK_LORA(2, 1); break;
+    default: UNO_SK_LORA(4, 1); break;
+  }
+#undef UNO_SK_LORA
+  launch_sk_reduce(g, p, s);
   return hipGetLastError();
 }
 

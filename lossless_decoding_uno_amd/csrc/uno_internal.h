@@ -73,10 +73,11 @@ hipError_t launch_rmsnorm(const float* h, const float* gain, int R, int D, float
 // absolute positions kv_len[b] + pos_offset + j, or kv_len[b] + pos_offset +
 // depth[r] for the rows of a token tree (depth != null); and each row's K/V
 // slot kv_len[b] + pos_offset + j as (page, slot in page) in row_page [R]
-// (page -1, flagged in status, outside the table or the pool).
+// (page -1, flagged in status, outside the table or the pool).  It also
+// zeroes the n_zero words at `zero` (the pass's synchronisation counters).
 hipError_t launch_rope_table(const uno_config& c, const uno_kv& kv, int B, int K, int pos_offset,
                              const int32_t* depth, float2* cs, int2* row_page, int32_t* status,
-                             hipStream_t s);
+                             unsigned* zero, int n_zero, hipStream_t s);
 // RoPE on q and k of the fused qkv rows (fp32 [R, (Hq+2Hkv)*hd]); q, scaled
 // by log2(e)/sqrt(hd), -> two bf16 planes [R, Hq*hd] (hi and the rounding
 // remainder lo), k/v (bf16) -> paged cache at the rows' slots.
@@ -197,6 +198,22 @@ struct GemmArgs {
   // set by the skinny launcher (callers leave it 0): tile pairing of a fused
   // RoPE or SwiGLU epilogue without a K split
   int pair_tiles;
+  // set by launch_gemm_lora (callers leave them 0): a LoRA-A product run in
+  // the same launch as its projection stores its partials at the device
+  // coherence point and bumps *t_signal per workgroup; the projection waits
+  // until *t_wait reaches t_wait_target before its LoRA step (bounded; on
+  // timeout UNO_DEV_SYNC_TIMEOUT is OR-ed into *t_timeout)
+  unsigned* t_signal;
+  const unsigned* t_wait;
+  unsigned t_wait_target;
+  int* t_timeout;
+  // with t_wait: every 128-byte line of the partials was written by one
+  // LoRA-A workgroup, so the projection may read them through its L2 (no
+  // line of them can be cached there before the wait ends); otherwise it
+  // reads them at the device coherence point
+  int t_lines_owned;
+  // skinny kernel: column tiles per workgroup (0: the planner's choice)
+  int sk_nt;
 };
 // split-K scratch carved per pass: 128 MB for passes of more than 64 rows
 // (tiled kernel), 4 MB for up to 64 (skinny kernel)
@@ -213,6 +230,16 @@ void gemm_lora_pair(const GemmArgs& a, const GemmArgs& ta, float* t_part, size_t
                     GemmArgs* a_out, GemmArgs* ta_out);
 // T partial scratch a pass of at most 64 rows carves for gemm_lora_pair
 constexpr size_t kLoraPartFloats = size_t(1) << 18;
+// A projection `a` with the LoRA-A product `ta` that feeds it.  At most 64
+// rows, when the LoRA-A product splits along K: one launch (the LoRA-A
+// workgroups first, then the projection's, which wait for them through
+// `counter`, a zeroed word of device memory used once), and *fused is set.
+// Otherwise the two launches of gemm_lora_pair.  `timeout_flag` (may be
+// null) receives UNO_DEV_SYNC_TIMEOUT if a wait ran out.
+hipError_t launch_gemm_lora(const GemmArgs& a, const GemmArgs& ta, float* t_part,
+                            size_t t_part_floats, unsigned* counter, int* timeout_flag,
+                            hipStream_t s, bool* normed, bool* roped, bool* swiglued,
+                            bool* fused);
 // whether launch_gemm can run this EPI_SWIGLU product (the tiled kernel takes it)
 bool gemm_swiglu_ok(const GemmArgs& a);
 // column groups of a product with max_part set (the row-maxima partials per row)
