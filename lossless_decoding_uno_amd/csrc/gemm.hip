@@ -288,21 +288,34 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
       for (int t = 0; t < NT; ++t)
         acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[mt].v, bw[t].v, acc[mt][t], 0, 0, 0);
   }
-  // fused LoRA (last split): T [M, r] (already gated and scaled) times B [n, r]^T
+  // fused LoRA (last split): T [M, r] (already gated and scaled) times B [n, r]^T.
+  // Wave w takes the rank steps w, w + WV, ... (rank <= 256: at most RS each);
+  // its B fragments are loaded first, so that their latency overlaps the wait
+  // for T when T comes from the same launch.
   if (a.t && sv.lb && zs == splits - 1) {
-    if (a.t_wait) wait_lora_t(a);
+    constexpr int RS = (8 + WV - 1) / WV;
     // rank 16 fills half of a 32-wide step: lanes past the rank feed zeros
     const int r_steps = (a.rank + 31) >> 5;
-    for (int rs = w; rs < r_steps; rs += WV) {
-      const bool kin = rs * 32 + kg * 8 < a.rank;
-      Frag bw[NT], axt[PAIR ? NT : 1][MT];
+    Frag bwp[RS][NT];
+#pragma unroll
+    for (int q = 0; q < RS; ++q) {
+      const int rs = w + q * WV;
+      const bool kin = rs < r_steps && rs * 32 + kg * 8 < a.rank;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int n = (PAIR ? svt[t].n0 : sv.n0 + t * 16) + rr;
         const uint16_t* brow =
             svt[t].lb + (size_t)(n < svt[t].n ? n : svt[t].n - 1) * a.rank + kg * 8;
-        bw[t].u = kin ? ldg16(brow + rs * 32) : make_uint4(0, 0, 0, 0);
+        bwp[q][t].u = kin ? ldg16(brow + rs * 32) : make_uint4(0, 0, 0, 0);
       }
+    }
+    if (a.t_wait) wait_lora_t(a);
+#pragma unroll
+    for (int q = 0; q < RS; ++q) {
+      const int rs = w + q * WV;
+      if (rs >= r_steps) break;
+      const bool kin = rs * 32 + kg * 8 < a.rank;
+      Frag axt[PAIR ? NT : 1][MT];
 #pragma unroll
       for (int tt = 0; tt < (PAIR ? NT : 1); ++tt)
 #pragma unroll
@@ -315,7 +328,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
         } else if (a.t_part) {
           // T from its LoRA-A product's split-K partials, summed in split order
           // and rounded as that product's epilogue rounds it (read from the
-          // device coherence point when they come from the same launch)
+          // device coherence point when they come from the same launch and
+          // their lines are shared)
           float4 lo, hi;
           if (a.t_wait && !a.t_lines_owned) {
             sum_splits8_coherent(a.t_part + to, (size_t)a.M * a.ldt, a.t_splits, &lo, &hi);
@@ -336,8 +350,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(axt[PAIR ? t : 0][mt].v, bw[t].v,
-                                                               acc[mt][t], 0, 0, 0);
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(axt[PAIR ? t : 0][mt].v,
+                                                               bwp[q][t].v, acc[mt][t], 0, 0, 0);
     }
   }
   // the waves' partial tiles are summed in a fixed order
