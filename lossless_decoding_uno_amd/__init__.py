@@ -22,6 +22,7 @@ UNO_OK = 0
 STATUS_NAMES = {1: "invalid argument", 2: "unsupported shape", 3: "page table too small",
                 4: "workspace too small", 5: "HIP launch failure"}
 DEV_CAPACITY, DEV_BAD_TOKEN, DEV_BAD_PAGE, DEV_NONFINITE, DEV_BAD_ACCEPT = 1, 2, 4, 8, 16
+DEV_SYNC_TIMEOUT = 32
 
 EXPORTS = ("uno_workspace_bytes", "uno_draft_block", "uno_draft_block_from", "uno_verify_block",
            "uno_draft_sample",

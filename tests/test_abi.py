@@ -128,3 +128,15 @@ def test_tree_entry_points_shape_rules_and_host_validation():
     assert lib.uno_tree_accept(fake, fake, fake, fake, fake, 1, 16, 9, 512, 1.0, 0, fake, fake,
                                fake, fake, fake, fake, None, None) == 1
     assert lib.uno_tree_commit(ctypes.byref(cfg), None, fake, fake, 1, 3, None, None, None) == 1
+
+
+def test_device_status_bits_match_the_header():
+    """The binding's device status bits are the header's UNO_DEV_* values."""
+    import lossless_decoding_uno_amd as U
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "uno.h")).read()
+    bits = {m.group(1): int(m.group(2)) for m in re.finditer(r"UNO_DEV_(\w+) = (\d+)", hdr)}
+    assert bits == {"CAPACITY": U.DEV_CAPACITY, "BAD_TOKEN": U.DEV_BAD_TOKEN,
+                    "BAD_PAGE": U.DEV_BAD_PAGE, "NONFINITE": U.DEV_NONFINITE,
+                    "BAD_ACCEPT": U.DEV_BAD_ACCEPT, "SYNC_TIMEOUT": U.DEV_SYNC_TIMEOUT}
+    assert sorted(bits.values()) == [1 << i for i in range(len(bits))]
