@@ -105,7 +105,7 @@ struct PassWs {
   float* max_part;       // [R, V/16] LM-head row-maxima partials (per column group)
   float* row_max;        // [R] row maxima of the logits (when the caller passes none)
   uint64_t* chunk_sums;  // [R, 128] exact chunk sums of the draft sampler
-  unsigned* sync;        // [4 * n_layers] LoRA-A -> projection counters (<= 64 rows),
+  unsigned* sync;        // [4 * n_layers, kLoraSyncWords] LoRA-A -> projection counters (<= 64 rows),
                          // zeroed by the pass's RoPE-table kernel
   size_t total;
 };
@@ -146,7 +146,7 @@ PassWs carve(const uno_config& c, int B, int K, int max_ctx, void* base) {
       take(R * gemm_row_max_parts_bound(c.vocab, (int)R) * 4));
   w.row_max = reinterpret_cast<float*>(take(R * 4));
   w.chunk_sums = reinterpret_cast<uint64_t*>(take(chunk_sums_bytes((int)R)));
-  w.sync = R <= 64 ? reinterpret_cast<unsigned*>(take((size_t)4 * c.n_layers * 4)) : nullptr;
+  w.sync = R <= 64 ? reinterpret_cast<unsigned*>(take((size_t)4 * c.n_layers * kLoraSyncWords * 4)) : nullptr;
   w.total = off;
   return w;
 }
@@ -191,7 +191,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   UNO_TRY(launch_embed(c, bp(w->embed), anchor, block, rows, B, K, seed, step, keep_q24, corr_pass,
                        W.h, status, s));
   UNO_TRY(launch_rope_table(c, *kv, B, K, draft ? 0 : pos_offset, tree_depth, W.cs, W.row_page,
-                            status, W.sync, W.sync ? 4 * c.n_layers : 0, s));
+                            status, W.sync, W.sync ? 4 * c.n_layers * kLoraSyncWords : 0, s));
   const AttnPlan plan = attn_plan(c, B, K, max_ctx);
   const size_t layer_elems = (size_t)kv->n_pages * Hkv * c.page_size * hd;
 
@@ -217,7 +217,7 @@ int run_pass(const uno_config& c, const uno_weights* w, const uno_kv* kv, const 
   auto project = [&](const GemmArgs& g0, const GemmArgs* ta0, int cls, bool* normed_out,
                      bool* roped_out, bool* swiglued_out) -> hipError_t {
     if (ta0 && W.sync && W.lora_part) {
-      unsigned* ctr = W.sync + 4 * li_cur + (cls - UNO_TIME_GEMM_QKV);
+      unsigned* ctr = W.sync + (size_t)(4 * li_cur + cls - UNO_TIME_GEMM_QKV) * kLoraSyncWords;
       bool fused = false;
       return timed(UNO_TIME_GEMM, s, [&] {
         return launch_gemm_lora(g0, *ta0, W.lora_part, kLoraPartFloats, ctr, status, s,

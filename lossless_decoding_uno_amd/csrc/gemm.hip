@@ -144,7 +144,11 @@ constexpr int kSkWavesSplit = 2;    // split-K products and the LM head
 // thread bumps the counter; a consumer's first thread polls the counter with
 // device-scope loads (bounded: on timeout it flags UNO_DEV_SYNC_TIMEOUT in
 // status[0] and goes on), and the partials are then read with device-scope
-// loads.  No L2 write-back or invalidation is needed on either side.
+// loads.  No L2 write-back or invalidation is needed on either side.  When
+// each column group's K splits count themselves in a counter of their own,
+// the last of them to arrive (it reads the others' partials with
+// device-scope loads) writes the group's final bf16 T the same way and alone
+// bumps the projection's counter, which then waits for one bump per group.
 constexpr unsigned kLoraSpinLimit = 1u << 22;
 __device__ __forceinline__ void signal_done(unsigned* counter) {
   __builtin_amdgcn_s_waitcnt(0);
@@ -166,6 +170,9 @@ __device__ __forceinline__ void wait_lora_t(const GemmArgs& a) {
   __syncthreads();
 }
 __device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coherent_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // eight consecutive floats, summed over `splits` partial planes zs apart in
@@ -342,6 +349,11 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
           const float g = (m % a.t_rows) != 0 ? a.t_scale : 0.f;
           ax[mt].u = make_uint4(pack_bf16x2(g * lo.x, g * lo.y), pack_bf16x2(g * lo.z, g * lo.w),
                                 pack_bf16x2(g * hi.x, g * hi.y), pack_bf16x2(g * hi.z, g * hi.w));
+        } else if (a.t_wait) {
+          // final T written by the same launch: device-scope loads
+          const uint32_t* tw = reinterpret_cast<const uint32_t*>(a.t + to);
+          ax[mt].u = make_uint4(ld_coherent_u32(tw), ld_coherent_u32(tw + 1),
+                                ld_coherent_u32(tw + 2), ld_coherent_u32(tw + 3));
         } else {
           ax[mt].u = ldg16(a.t + to);
         }
@@ -383,6 +395,47 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
         if (a.t_signal) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else *dst = v;
       }
+    }
+    if constexpr (!PAIR) if (a.t_signal && a.t_tile_ctr) {
+      // the last K split of this column group turns the partials into T
+      // (LoRA-A products are unpaired: their tiles share one segment)
+      __shared__ unsigned s_last;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(a.t_tile_ctr + bx, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
+      __syncthreads();
+      if (!s_last) return;
+      const size_t zstride = (size_t)a.M * ncols;
+      for (int e = threadIdx.x * 2; e < kTile; e += WV * 64 * 2) {
+        const int r = e / (NT * 16), cl = e % (NT * 16);   // two adjacent columns
+        const SegView& st = sv;
+        const int m = m0 + r, nl = sv.n0 + cl;
+        if (m >= a.M || nl >= st.n) continue;
+        // both columns' partials of every split (at most 8) in flight at once
+        const uint64_t* src =
+            reinterpret_cast<const uint64_t*>(a.part + (size_t)m * ncols + st.col_base + nl);
+        uint64_t q[8];
+#pragma unroll
+        for (int z = 0; z < 8; ++z)
+          q[z] = z < splits ? __hip_atomic_load(src + z * (zstride / 2), __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : 0ull;
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int z = 0; z < 8; ++z)
+          if (z < splits) {
+            v0 += __uint_as_float((uint32_t)q[z]);
+            v1 += __uint_as_float((uint32_t)(q[z] >> 32));
+          }
+        const float g = (m % a.rows_per_seq) != 0 ? a.scale : 0.f;
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) +
+                                                       (size_t)m * a.ldo + st.col_base + nl),
+                           pack_bf16x2(g * v0, g * v1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      signal_done(a.t_signal);
+      return;
     }
     if (a.t_signal) signal_done(a.t_signal);
     return;
@@ -767,6 +820,15 @@ hipError_t launch_gemm_lora(const GemmArgs& a, const GemmArgs& ta, float* t_part
     if (e != hipSuccess) return e;
     g.t_wait = nullptr;
     return launch_gemm(g, s, normed, roped, swiglued);
+  }
+  // one row tile of 32-column groups whose T is the projection's LoRA input:
+  // the last K split of each group writes the group's final bf16 T, so that
+  // the projection reads 2-byte T once instead of summing fp32 partials
+  if (g.t_lines_owned && tp.gy == 1 && tp.gx < kLoraSyncWords && tp.splits <= 8 &&
+      t2.out == g.t && t2.ldo == g.ldt) {
+    t2.t_tile_ctr = counter + 1;
+    g.t_part = nullptr;
+    g.t_wait_target = (unsigned)tp.gx;
   }
   *fused = true;
   if (P) {

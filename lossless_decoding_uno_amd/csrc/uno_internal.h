@@ -212,6 +212,12 @@ struct GemmArgs {
   // line of them can be cached there before the wait ends); otherwise it
   // reads them at the device coherence point
   int t_lines_owned;
+  // with t_signal and t_tile_ctr (one row tile): each column group of the
+  // LoRA-A product counts its finished K splits in t_tile_ctr[group]; the last
+  // split to arrive sums the group's partials in split order, gates, scales
+  // and rounds them into `out` (bf16 T) and only then bumps *t_signal, once
+  // per group; the projection then reads T itself (t_part null)
+  unsigned* t_tile_ctr;
   // skinny kernel: column tiles per workgroup (0: the planner's choice)
   int sk_nt;
 };
@@ -230,10 +236,14 @@ void gemm_lora_pair(const GemmArgs& a, const GemmArgs& ta, float* t_part, size_t
                     GemmArgs* a_out, GemmArgs* ta_out);
 // T partial scratch a pass of at most 64 rows carves for gemm_lora_pair
 constexpr size_t kLoraPartFloats = size_t(1) << 18;
+// counter words of one fused LoRA-A launch: the projection's wait counter and
+// one split counter per LoRA-A column group
+constexpr int kLoraSyncWords = 64;
 // A projection `a` with the LoRA-A product `ta` that feeds it.  At most 64
 // rows, when the LoRA-A product splits along K: one launch (the LoRA-A
 // workgroups first, then the projection's, which wait for them through
-// `counter`, a zeroed word of device memory used once), and *fused is set.
+// `counter`, kLoraSyncWords zeroed words of device memory used once), and
+// *fused is set.
 // Otherwise the two launches of gemm_lora_pair.  `timeout_flag` (may be
 // null) receives UNO_DEV_SYNC_TIMEOUT if a wait ran out.
 hipError_t launch_gemm_lora(const GemmArgs& a, const GemmArgs& ta, float* t_part,
