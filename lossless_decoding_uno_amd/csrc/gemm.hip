@@ -261,19 +261,30 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
   const int ks0 = n_all * zs / splits, ks1 = n_all * (zs + 1) / splits;
   constexpr bool kBlk = MT == 1;
   constexpr int kUS = kBlk ? 1 : WV;          // step distance inside a group
+  // Whole groups of UN steps, double-buffered in registers: the loads of the
+  // wave's next group are issued before the MFMAs of the current one, so two
+  // groups are in flight while the MFMAs run (with one, a wave sits idle for a
+  // whole HBM round trip per group).  The accumulation order is unchanged.
+  // Every load of a group is unconditional, so that the compiler can count
+  // exactly how many are still in flight: rows past M re-read row 0 (xrow),
+  // and their output rows are never stored.
   int s = ks0 + (kBlk ? w * UN : w);
-  for (; s + (UN - 1) * kUS < ks1; s += UN * WV) {
-    Frag bw[UN][NT];
-    Frag ax[UN][MT];
+  constexpr int kGrp = UN * WV;               // distance between a wave's groups
+  // whole groups of this wave: s + g * kGrp + (UN - 1) * kUS < ks1
+  const int span = ks1 - s - (UN - 1) * kUS;
+  const int n_grp = span > 0 ? (span + kGrp - 1) / kGrp : 0;
+  Frag bw0[UN][NT], ax0[UN][MT], bw1[UN][NT], ax1[UN][MT];
+  auto load_grp = [&](int s_, Frag (&bw)[UN][NT], Frag (&ax)[UN][MT]) {
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16_nt(wrow[t] + (size_t)(s + u * kUS) * 512);
+      for (int t = 0; t < NT; ++t) bw[u][t].u = ldg16_nt(wrow[t] + (size_t)(s_ + u * kUS) * 512);
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        ax[u][mt].u = xok[mt] ? ldg16(xrow[mt] + (s + u * kUS) * 32) : make_uint4(0, 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) ax[u][mt].u = ldg16(xrow[mt] + (s_ + u * kUS) * 32);
+  };
+  auto mma_grp = [&](const Frag (&bw)[UN][NT], const Frag (&ax)[UN][MT]) {
 #pragma unroll
     for (int u = 0; u < UN; ++u)
 #pragma unroll
@@ -281,6 +292,46 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[u][mt].v, bw[u][t].v, acc[mt][t], 0, 0, 0);
+  };
+  // Paired products only: they stream the whole K in few workgroups.  Split
+  // products run many small workgroups per CU, where the second buffer's
+  // registers cost more occupancy than it gains, and groups of more than 16
+  // fragments (the LM head's eight K steps of four tiles) already keep enough
+  // in flight.
+  constexpr bool kPipe = PAIR && UN * (NT + MT) <= 16;
+  if (!kPipe) {
+    for (int g = 0; g < n_grp; ++g, s += kGrp) {
+      load_grp(s, bw0, ax0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_grp(bw0, ax0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if (n_grp > 0) {
+    load_grp(s, bw0, ax0);
+    int g = 0;
+    // (the fences keep each group's loads ahead of the other group's MFMAs:
+    // left alone, the scheduler sinks some of them below the MFMAs)
+    for (; g + 2 < n_grp; g += 2) {             // groups g (in bw0/ax0) and g + 1
+      load_grp(s + kGrp, bw1, ax1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_grp(bw0, ax0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_grp(s + 2 * kGrp, bw0, ax0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_grp(bw1, ax1);
+      __builtin_amdgcn_sched_barrier(0);
+      s += 2 * kGrp;
+    }
+    if (g + 2 == n_grp) {                       // two left
+      load_grp(s + kGrp, bw1, ax1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_grp(bw0, ax0);
+      mma_grp(bw1, ax1);
+      s += 2 * kGrp;
+    } else {                                    // one left
+      mma_grp(bw0, ax0);
+      s += kGrp;
+    }
   }
   // the rest: the wave's partial block (blocked), or its remaining steps
   for (; s < ks1; s += kBlk ? 1 : WV) {
