@@ -149,8 +149,7 @@ __global__ void k_rope_table(const int32_t* __restrict__ kv_len, int K, int pos_
                              int32_t* __restrict__ status, unsigned* __restrict__ zero,
                              int n_zero) {
   const int r = blockIdx.x;
-  if (r == 0)
-    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0u;
+  for (int i = r * blockDim.x + threadIdx.x; i < n_zero; i += gridDim.x * blockDim.x) zero[i] = 0u;
   const int b = r / K, j = r % K;
   const double pos = (double)(kv_len[b] + pos_offset + (depth ? depth[r] : j));
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
