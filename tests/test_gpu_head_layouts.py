@@ -1,5 +1,5 @@
 """GPU parity of the draft and verify passes for head layouts the model tests
-do not use: q heads per kv head G = 1, 2, 8 and 16 with head_dim 128, G = 2
+do not use: q heads per kv head G = 1, 2, 5, 6, 8 and 16 with head_dim 128, G = 2
 and 8 with head_dim 64 (the attention kernel takes G*K query rows per kv
 head, so these change its row-group count and key split), K = 16 and 8,
 ragged contexts, shuffled pages.  Logits against the exact oracle, with the
@@ -21,8 +21,12 @@ from oracle import model as om
 pytestmark = pytest.mark.gpu
 
 
+# (12, 2, 128, 8) and (10, 2, 128, 8): model widths 1536 and 1280 at 24 rows per pass, where
+# the paired q|k|v and [gate | up] products double-buffer their load groups and a wave
+# streams three groups (1536), or two or three (1280), of its K range
 @pytest.mark.parametrize("hq,hkv,hd,K", [(2, 2, 128, 16), (4, 2, 128, 16), (8, 1, 128, 16),
-                                         (16, 1, 128, 8), (4, 2, 64, 16), (8, 1, 64, 16)])
+                                         (16, 1, 128, 8), (4, 2, 64, 16), (8, 1, 64, 16),
+                                         (12, 2, 128, 8), (10, 2, 128, 8)])
 def test_head_layout_draft_verify(hq, hkv, hd, K):
     U = gpu_or_fail()
     cfg = dict(synth.SMALL_GQA, n_q_heads=hq, n_kv_heads=hkv, head_dim=hd,
