@@ -261,13 +261,14 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const int bx, con
   const int ks0 = n_all * zs / splits, ks1 = n_all * (zs + 1) / splits;
   constexpr bool kBlk = MT == 1;
   constexpr int kUS = kBlk ? 1 : WV;          // step distance inside a group
-  // Whole groups of UN steps, double-buffered in registers: the loads of the
-  // wave's next group are issued before the MFMAs of the current one, so two
-  // groups are in flight while the MFMAs run (with one, a wave sits idle for a
-  // whole HBM round trip per group).  The accumulation order is unchanged.
-  // Every load of a group is unconditional, so that the compiler can count
-  // exactly how many are still in flight: rows past M re-read row 0 (xrow),
-  // and their output rows are never stored.
+  // Whole groups of UN steps.  Paired products double-buffer them in
+  // registers (kPipe below): the loads of the wave's next group are issued
+  // before the MFMAs of the current one, so two groups are in flight while the
+  // MFMAs run (with one, a wave sits idle for a whole HBM round trip per
+  // group).  The accumulation order is the same either way.  Every load of a
+  // group is unconditional, so that the compiler can count exactly how many
+  // are still in flight: rows past M re-read row 0 (xrow), and their output
+  // rows are never stored.
   int s = ks0 + (kBlk ? w * UN : w);
   constexpr int kGrp = UN * WV;               // distance between a wave's groups
   // whole groups of this wave: s + g * kGrp + (UN - 1) * kUS < ks1
